@@ -1,0 +1,385 @@
+/*
+ * oracle.c -- plain, slow CPU oracle for the low-bit dequantisation hot path.
+ *
+ * TEST INFRASTRUCTURE ONLY. This is the reference the HIP library is checked
+ * against. Only the test suite, the smoke check and the CPU-baseline leg of
+ * the benchmark may load it; the product path never does. It shares no code,
+ * header, table or constant generator with the HIP library: every table below
+ * is a literal written from the pages, and every helper is private to this
+ * file.
+ *
+ * Pages followed (cited by page and section; no line numbers):
+ *   [vLLM-51583]    prhub.com.cn digest of vLLM pull request 51583 (CPU MXFP4
+ *                   unpack: the zero-code special case folded into fewer
+ *                   instructions, bit-exact). Sections "功能与动机"
+ *                   (motivation), "实现拆解" (implementation breakdown) and
+ *                   "关键源码片段" (key source excerpts: vec.h and the MoE test).
+ *   [SGLang-34222]  prhub.com.cn digest of SGLang pull request 34222 (NVFP4
+ *                   token embedding, dequantised at gather time). Sections
+ *                   "实现拆解" and "关键源码片段" (modelopt_quant.py excerpt and
+ *                   the test's element-loop reference).
+ *   [FairyFuse]     blog.hotdry.top post on FairyFuse (fused ternary kernels,
+ *                   multiplication-free CPU inference). Section
+ *                   "三元 GEMV 的乘法消除原理" (ternary GEMV without multiplies).
+ *
+ * Arithmetic is fp64 throughout except the NVFP4 gather, whose page fixes
+ * fp32 (both scale factors are cast to float and multiplied in float before
+ * the final bf16 cast). Loops are scalar; OpenMP splits rows or tokens only,
+ * never a sum, so every result is independent of the thread count.
+ *
+ * Build: gcc -O2 -fopenmp -fPIC -shared -ffp-contract=off (no fast-math).
+ */
+#include <float.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#if FLT_EVAL_METHOD != 0
+#error "the NVFP4 reference needs float expressions evaluated in float"
+#endif
+
+#define OR_OK 0
+#define OR_EINVAL (-1)   /* bad shape, or an input the method leaves undefined */
+#define OR_ENOMEM (-2)
+
+/* E2M1 magnitudes, indexed by the low three bits of a 4-bit code; bit 3 is
+ * the sign. Printed as a lookup table in [SGLang-34222] "关键源码片段" (both
+ * the implementation and its test print the same eight values). */
+static const double E2M1_MAGNITUDE[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+int or_abi_version(void) { return 1; }
+
+int or_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+double or_e2m1_magnitude(int index) { return E2M1_MAGNITUDE[index & 7]; }
+
+/* ---------------------------------------------------------------- bf16 --- */
+
+/* bf16 bit pattern of a double, rounded once, to nearest with ties to even.
+ * Definition: bf16 has 7 stored fraction bits and the fp32 exponent range;
+ * below 2^-126 the spacing stays 2^-133 (subnormals). Values that round to
+ * 2^128 or beyond become infinity; NaN becomes the canonical quiet NaN. */
+uint16_t or_bf16_from_double(double v) {
+    if (isnan(v)) return 0x7FC0;
+    uint16_t sign = signbit(v) ? 0x8000 : 0x0000;
+    double a = fabs(v);
+    if (a == 0.0) return sign;
+    if (isinf(a)) return (uint16_t)(sign | 0x7F80);
+    int e2;
+    (void)frexp(a, &e2);            /* a = f * 2^e2 with f in [0.5, 1) */
+    int E = e2 - 1;                 /* a lies in [2^E, 2^(E+1)) */
+    if (E < -126) E = -126;         /* subnormal: fixed spacing */
+    int q = E - 7;                  /* spacing of representable values is 2^q */
+    double r = nearbyint(ldexp(a, -q));   /* default mode: ties to even */
+    double vr = ldexp(r, q);
+    if (vr >= ldexp(1.0, 128)) return (uint16_t)(sign | 0x7F80);
+    float f = (float)vr;            /* exact: <= 8 significant bits, in range */
+    uint32_t bits;
+    memcpy(&bits, &f, sizeof bits);
+    return (uint16_t)(sign | (uint16_t)(bits >> 16));
+}
+
+double or_double_from_bf16(uint16_t h) {
+    uint32_t bits = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+void or_bf16_from_double_array(const double* in, uint16_t* out, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) out[i] = or_bf16_from_double(in[i]);
+}
+
+/* ---------------------------------------------------------------- E4M3 --- */
+
+/* OCP FP8 E4M3 ("fn" variant): 1 sign, 4 exponent bits with bias 7, 3
+ * fraction bits, subnormals when the exponent field is 0, no infinities, and
+ * S.1111.111 is NaN. [SGLang-34222] "实现拆解" names the block scale as e4m3
+ * but prints only its cast to float; this decoding is the format's
+ * published definition. */
+double or_e4m3_to_double(uint8_t b) {
+    int s = b >> 7, e = (b >> 3) & 15, m = b & 7;
+    if (e == 15 && m == 7) return NAN;
+    double v = (e == 0) ? ldexp((double)m, -9)          /* m/8 * 2^(1-7) */
+                        : ldexp((double)(8 + m), e - 10); /* (1+m/8) * 2^(e-7) */
+    return s ? -v : v;
+}
+
+/* --------------------------------------------------------------- MXFP4 --- */
+
+/* 4-bit code of column c of a packed row: byte c/2 holds column 2j in its
+ * low nibble and column 2j+1 in its high nibble ([SGLang-34222]
+ * "关键源码片段": even channels take the low four bits). */
+static int code_at(const uint8_t* row, int64_t c) {
+    uint8_t byte = row[c / 2];
+    return (c % 2 == 0) ? (byte & 0x0F) : (byte >> 4);
+}
+
+/* bf16 pattern of the E2M1 value of a code, sign included (-0 for code 8). */
+static uint16_t e2m1_bf16(int code) {
+    double m = E2M1_MAGNITUDE[code & 7];
+    return or_bf16_from_double((code & 8) ? -m : m);
+}
+
+/* The MXFP4 -> bf16 unpack of [vLLM-51583]: look the code up in the bf16
+ * table, then apply the E8M0 block scale as an integer add of (e-127) to the
+ * bf16 exponent field, i.e. add (e-127)*2^7 to the 16-bit pattern modulo
+ * 2^16 ("功能与动机"; "关键源码片段", vec.h). The two zero codes have no
+ * exponent to shift, so a lane whose pattern is zero apart from the sign is
+ * written as +0.0 (same sections; the excerpt states both zero codes map to
+ * +0.0). For 2 <= e <= 252 the result is exactly the bf16 of
+ * (+/-)magnitude * 2^(e-127); outside that range a non-zero code's exponent
+ * field leaves 1..254 and the integer add wraps, which the page's own test
+ * avoids. */
+uint16_t or_mxfp4_decode_one(int code, int e8m0) {
+    uint16_t base = e2m1_bf16(code & 15);
+    if ((base & 0x7FFF) == 0) return 0x0000;
+    uint16_t addend = (uint16_t)((e8m0 - 127) * 128);
+    return (uint16_t)(base + addend);
+}
+
+/* Decode a packed MXFP4 matrix: packed [rows, k/2], one E8M0 byte per 32
+ * consecutive columns in scales [rows, k/32], out [rows, k] bf16 patterns. */
+int or_mxfp4_decode(const uint8_t* packed, const uint8_t* scales, uint16_t* out,
+                    int64_t rows, int64_t k) {
+    if (rows < 0 || k < 0 || k % 32 != 0) return OR_EINVAL;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        const uint8_t* prow = packed + r * (k / 2);
+        const uint8_t* srow = scales + r * (k / 32);
+        for (int64_t c = 0; c < k; ++c)
+            out[r * k + c] = or_mxfp4_decode_one(code_at(prow, c), srow[c / 32]);
+    }
+    return OR_OK;
+}
+
+/* Real value of one MXFP4 weight: (+/-)magnitude * 2^(e-127), the quantity
+ * the unpack above represents exactly for 2 <= e <= 252. */
+static double mxfp4_value(int code, int e8m0) {
+    double m = E2M1_MAGNITUDE[code & 7];
+    return ldexp((code & 8) ? -m : m, e8m0 - 127);
+}
+
+/* y[b, r] = sum_c W[r, c] * x[b, c] in fp64, for packed W [n, k] and bf16 x
+ * [batch, k]. Every product is exact in fp64; the sum runs in column order.
+ * The caller rounds y to the output type. */
+int or_mxfp4_gemv(const uint8_t* packed, const uint8_t* scales, const uint16_t* x,
+                  double* y, int64_t batch, int64_t n, int64_t k) {
+    if (batch < 0 || n < 0 || k < 0 || k % 32 != 0) return OR_EINVAL;
+    int fail = 0;
+#pragma omp parallel reduction(| : fail)
+    {
+        double* w = (double*)malloc(sizeof(double) * (size_t)(k > 0 ? k : 1));
+        if (!w) {
+            fail = 1;
+        } else {
+#pragma omp for schedule(static)
+            for (int64_t r = 0; r < n; ++r) {
+                const uint8_t* prow = packed + r * (k / 2);
+                const uint8_t* srow = scales + r * (k / 32);
+                for (int64_t c = 0; c < k; ++c) w[c] = mxfp4_value(code_at(prow, c), srow[c / 32]);
+                for (int64_t b = 0; b < batch; ++b) {
+                    double acc = 0.0;
+                    for (int64_t c = 0; c < k; ++c) acc += w[c] * or_double_from_bf16(x[b * k + c]);
+                    y[b * n + r] = acc;
+                }
+            }
+            free(w);
+        }
+    }
+    return fail ? OR_ENOMEM : OR_OK;
+}
+
+/* ------------------------------------------------------------- ternary --- */
+
+/* Ternary GEMV of [FairyFuse] "三元 GEMV 的乘法消除原理": sixteen weights per
+ * 32-bit word, weight j of word i multiplies x[16i + j]; bit 2j+1 set means
+ * +1 (add x), bit 2j set means -1 (subtract x), neither means 0. The only
+ * multiply is the per-row scale, applied once after the row sum.
+ * y64[r] = s[r] * sum (fp64); y[r] = that value rounded to fp32. A field with
+ * both bits set has no meaning on the page: it is rejected (OR_EINVAL). */
+int or_ternary_gemv(const uint32_t* packed, const float* row_scale, const float* x,
+                    float* y, double* y64, int64_t n, int64_t k) {
+    if (n < 0 || k < 0 || k % 16 != 0) return OR_EINVAL;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t r = 0; r < n; ++r) {
+        const uint32_t* row = packed + r * (k / 16);
+        double acc = 0.0;
+        for (int64_t c = 0; c < k; ++c) {
+            uint32_t word = row[c / 16];
+            int j = (int)(c % 16);
+            int plus = (int)((word >> (2 * j + 1)) & 1u);
+            int minus = (int)((word >> (2 * j)) & 1u);
+            if (plus && minus) bad = 1;
+            else if (plus) acc += (double)x[c];
+            else if (minus) acc -= (double)x[c];
+        }
+        double v = (double)row_scale[r] * acc;
+        if (y64) y64[r] = v;
+        if (y) y[r] = (float)v;
+    }
+    return bad ? OR_EINVAL : OR_OK;
+}
+
+/* --------------------------------------------------------------- NVFP4 --- */
+
+/* One NVFP4 element in the order of [SGLang-34222] "关键源码片段"
+ * (modelopt_quant.py embedding()): the E2M1 value with its sign (code 8 is
+ * -0.0), the block scale decoded from E4M3 to float, eff = float(scale *
+ * global) in fp32, value * eff in fp32, then a round-to-nearest-even cast to
+ * bf16. */
+uint16_t or_nvfp4_element(int code, uint8_t block_scale, float global_scale) {
+    float mag = (float)E2M1_MAGNITUDE[code & 7];
+    float v = (code & 8) ? -mag : mag;
+    float bs = (float)or_e4m3_to_double(block_scale);
+    float eff = bs * global_scale;
+    float p = v * eff;
+    return or_bf16_from_double((double)p);
+}
+
+/* Row gather + dequantise: table [vocab, hidden/2] packed codes, block_scale
+ * [vocab, hidden/16] E4M3 bytes (group of 16 columns), out [ntok, hidden]
+ * bf16 patterns. hidden must be a multiple of the group size (the page's
+ * create_weights guard). Ids outside [0, vocab) give a zero row and count in
+ * *bad_ids. */
+int or_nvfp4_gather(const uint8_t* table, const uint8_t* block_scale, float global_scale,
+                    const int64_t* ids, uint16_t* out, int64_t vocab, int64_t hidden,
+                    int64_t ntok, int64_t* bad_ids) {
+    if (vocab < 0 || hidden < 0 || ntok < 0 || hidden % 16 != 0) return OR_EINVAL;
+    int64_t bad = 0;
+#pragma omp parallel for schedule(static) reduction(+ : bad)
+    for (int64_t t = 0; t < ntok; ++t) {
+        int64_t id = ids[t];
+        uint16_t* orow = out + t * hidden;
+        if (id < 0 || id >= vocab) {
+            for (int64_t c = 0; c < hidden; ++c) orow[c] = 0;
+            bad += 1;
+            continue;
+        }
+        const uint8_t* prow = table + id * (hidden / 2);
+        const uint8_t* srow = block_scale + id * (hidden / 16);
+        for (int64_t c = 0; c < hidden; ++c)
+            orow[c] = or_nvfp4_element(code_at(prow, c), srow[c / 16], global_scale);
+    }
+    if (bad_ids) *bad_ids = bad;
+    return OR_OK;
+}
+
+/* ----------------------------------------------------------------- MoE --- */
+
+static double silu(double z) { return z / (1.0 + exp(-z)); }
+
+/* MXFP4 mixture-of-experts layer with routing given as input, the semantics
+ * exercised by [vLLM-51583] "关键源码片段" (the MoE test calls the fused
+ * expert op with top-k weights and ids; the first expert matrix has 2N rows
+ * and the activation is silu(gate) * up). For token t and slot j, with
+ * expert e = ids[t, j]:
+ *   h = W13[e] x_t            (2*inter outputs; rows [0, inter) are gate,
+ *                              rows [inter, 2*inter) are up)
+ *   a = silu(h[:inter]) * h[inter:]
+ *   y = W2[e] a               (hidden outputs)
+ *   out64[t] = sum_j weights[t, j] * y     (slot order)
+ * all in fp64. Weights: w13 [E, 2*inter, hidden/2] + w13s [E, 2*inter,
+ * hidden/32]; w2 [E, hidden, inter/2] + w2s [E, hidden, inter/32].
+ * Pairs are grouped by expert only so that each weight row is decoded once;
+ * every dot product still runs over its columns in order. */
+int or_mxfp4_moe(const uint16_t* x, const uint8_t* w13, const uint8_t* w13s,
+                 const uint8_t* w2, const uint8_t* w2s, const int32_t* ids,
+                 const float* weights, double* out64, int64_t tokens, int64_t hidden,
+                 int64_t inter, int64_t experts, int64_t topk) {
+    if (tokens < 0 || hidden <= 0 || inter <= 0 || experts <= 0 || topk < 0) return OR_EINVAL;
+    if (hidden % 32 != 0 || inter % 32 != 0) return OR_EINVAL;
+    int64_t npairs = tokens * topk;
+    for (int64_t p = 0; p < npairs; ++p)
+        if (ids[p] < 0 || ids[p] >= experts) return OR_EINVAL;
+
+    double* xd = (double*)malloc(sizeof(double) * (size_t)(tokens * hidden + 1));
+    double* h = (double*)malloc(sizeof(double) * (size_t)(npairs * 2 * inter + 1));
+    double* act = (double*)malloc(sizeof(double) * (size_t)(npairs * inter + 1));
+    double* y = (double*)malloc(sizeof(double) * (size_t)(npairs * hidden + 1));
+    int64_t* members = (int64_t*)malloc(sizeof(int64_t) * (size_t)(npairs + 1));
+    if (!xd || !h || !act || !y || !members) {
+        free(xd); free(h); free(act); free(y); free(members);
+        return OR_ENOMEM;
+    }
+    for (int64_t i = 0; i < tokens * hidden; ++i) xd[i] = or_double_from_bf16(x[i]);
+
+    int fail = 0;
+    for (int64_t e = 0; e < experts; ++e) {
+        int64_t m = 0;
+        for (int64_t p = 0; p < npairs; ++p)
+            if (ids[p] == e) members[m++] = p;
+        if (m == 0) continue;
+        const uint8_t* we13 = w13 + e * (2 * inter) * (hidden / 2);
+        const uint8_t* se13 = w13s + e * (2 * inter) * (hidden / 32);
+        const uint8_t* we2 = w2 + e * hidden * (inter / 2);
+        const uint8_t* se2 = w2s + e * hidden * (inter / 32);
+#pragma omp parallel reduction(| : fail)
+        {
+            int64_t len = hidden > inter ? hidden : inter;
+            double* w = (double*)malloc(sizeof(double) * (size_t)len);
+            if (!w) {
+                fail = 1;
+            } else {
+                /* h = W13[e] x_t for every pair routed to e */
+#pragma omp for schedule(static)
+                for (int64_t r = 0; r < 2 * inter; ++r) {
+                    const uint8_t* prow = we13 + r * (hidden / 2);
+                    const uint8_t* srow = se13 + r * (hidden / 32);
+                    for (int64_t c = 0; c < hidden; ++c) w[c] = mxfp4_value(code_at(prow, c), srow[c / 32]);
+                    for (int64_t i = 0; i < m; ++i) {
+                        int64_t p = members[i];
+                        const double* xt = xd + (p / topk) * hidden;
+                        double acc = 0.0;
+                        for (int64_t c = 0; c < hidden; ++c) acc += w[c] * xt[c];
+                        h[p * 2 * inter + r] = acc;
+                    }
+                }
+                /* a = silu(gate) * up */
+#pragma omp for schedule(static)
+                for (int64_t i = 0; i < m; ++i) {
+                    int64_t p = members[i];
+                    for (int64_t c = 0; c < inter; ++c)
+                        act[p * inter + c] = silu(h[p * 2 * inter + c]) * h[p * 2 * inter + inter + c];
+                }
+                /* y = W2[e] a */
+#pragma omp for schedule(static)
+                for (int64_t r = 0; r < hidden; ++r) {
+                    const uint8_t* prow = we2 + r * (inter / 2);
+                    const uint8_t* srow = se2 + r * (inter / 32);
+                    for (int64_t c = 0; c < inter; ++c) w[c] = mxfp4_value(code_at(prow, c), srow[c / 32]);
+                    for (int64_t i = 0; i < m; ++i) {
+                        int64_t p = members[i];
+                        const double* a = act + p * inter;
+                        double acc = 0.0;
+                        for (int64_t c = 0; c < inter; ++c) acc += w[c] * a[c];
+                        y[p * hidden + r] = acc;
+                    }
+                }
+                free(w);
+            }
+        }
+    }
+    /* weighted combine, slot order */
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < tokens; ++t)
+        for (int64_t c = 0; c < hidden; ++c) {
+            double acc = 0.0;
+            for (int64_t j = 0; j < topk; ++j)
+                acc += (double)weights[t * topk + j] * y[(t * topk + j) * hidden + c];
+            out64[t * hidden + c] = acc;
+        }
+    free(xd); free(h); free(act); free(y); free(members);
+    return fail ? OR_ENOMEM : OR_OK;
+}
