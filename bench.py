@@ -1,0 +1,462 @@
+#!/usr/bin/env python3
+"""Benchmark of the low-bit dequantisation hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+
+Prints ONE JSON line. The default workload is the headline: MXFP4 dequant-GEMV
+at batch 1 on the Llama-8B MLP shapes (W 14336 x 4096 and W 4096 x 14336, one
+launch each per step), bf16 output. Other workloads (for the per-kernel
+roofline tables): mlp_b4, mlp_b16, ternary, gather, moe, decode, gemv_small.
+
+Timing: inputs are resident in HBM before the timed region; W untimed warmup
+steps; then K steps bracketed by torch.cuda.synchronize() on both sides and
+timed with HIP events on the stream the kernels run on (torch's current
+stream). A second timed pass records an event pair around every launch to get
+each kernel's average duration for the roofline. Weight copies are rotated so
+that the bytes cycled per pass exceed the 256 MB Infinity Cache: every launch
+reads its weights from HBM.
+
+`cpu_baseline` is the CPU oracle (plain C, fp64, OpenMP over rows) timed on a
+bounded sample of the same workload on this host's cores -- a reported
+baseline, not a target.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+METRIC = "effective weight GB/s and % HBM peak, batch-1 low-bit dequant-GEMV"
+CSRC = os.path.join(ROOT, "gemm_e2m1_lut_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as fh:
+            h.update(name.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+# ------------------------------------------------------------- workloads ---
+
+class Workload:
+    """One step = every launch in `launches` once, on weight copy `i % copies`."""
+    name = ""
+    config: dict = {}
+    dtype = "bf16"
+    bound = "hbm"
+
+    def launches(self):  # -> list of (label, fn(copy_index))
+        raise NotImplementedError
+
+    def alg_bytes(self, label: str) -> float:  # algorithmic bytes of one launch
+        raise NotImplementedError
+
+    def alg_flops(self, label: str) -> float:
+        return 0.0
+
+    weight_bytes_per_step = 0.0
+    total_bytes_per_step = 0.0
+
+    def cpu_baseline(self, budget_s: float) -> dict | None:
+        return None
+
+
+def _gen(seed: int):
+    import torch
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    return g
+
+
+def _mxfp4_dev(g, n: int, k: int, lo: int = 120, hi: int = 134):
+    import torch
+    packed = torch.randint(0, 256, (n, k // 2), dtype=torch.uint8, device="cuda", generator=g)
+    scales = torch.randint(lo, hi + 1, (n, k // 32), dtype=torch.uint8, device="cuda", generator=g)
+    return packed, scales
+
+
+class GemvMLP(Workload):
+    SHAPES = ((14336, 4096), (4096, 14336))
+
+    def __init__(self, batch: int, rotate_bytes: float):
+        import torch
+        import gemm_e2m1_lut_amd as lib
+        self.lib = lib
+        self.batch = batch
+        self.name = f"llama8b_mlp_mxfp4_gemv_b{batch}"
+        g = _gen(4242 + batch)
+        self.w_bytes = {f"gemv_{n}x{k}": n * k // 2 + n * k // 32 for n, k in self.SHAPES}
+        per_copy = sum(self.w_bytes.values())
+        self.copies = max(2, math.ceil(rotate_bytes / per_copy))
+        self.weights = [[_mxfp4_dev(g, n, k) for n, k in self.SHAPES] for _ in range(self.copies)]
+        self.x = [torch.randn((batch, k), generator=g, device="cuda").to(torch.bfloat16)
+                  for _, k in self.SHAPES]
+        self.y = [torch.empty((batch, n), dtype=torch.bfloat16, device="cuda") for n, _ in self.SHAPES]
+        self.weight_bytes_per_step = float(per_copy)
+        self.total_bytes_per_step = float(sum(self.alg_bytes(l) for l, _ in self.launches()))
+        self.config = {"workload": self.name, "shapes_NxK": [list(s) for s in self.SHAPES],
+                       "batch": batch, "weights": "MXFP4 (E2M1 codes + E8M0 per 32)",
+                       "activations": "bf16", "out": "bf16", "accumulate": "fp32",
+                       "weight_copies_rotated": self.copies,
+                       "rotated_MB": round(self.copies * per_copy / 1e6, 1)}
+
+    def launches(self):
+        out = []
+        for j, (n, k) in enumerate(self.SHAPES):
+            def fn(i, j=j):
+                p, s = self.weights[i % self.copies][j]
+                self.lib.dequant_gemv(p, s, self.x[j], out_dtype=self.y[j].dtype, out=self.y[j])
+            out.append((f"gemv_{n}x{k}", fn))
+        return out
+
+    def alg_bytes(self, label):
+        n, k = (int(v) for v in label.split("_")[1].split("x"))
+        return n * k // 2 + n * k // 32 + self.batch * k * 2 + self.batch * n * 2
+
+    def alg_flops(self, label):
+        n, k = (int(v) for v in label.split("_")[1].split("x"))
+        return 2.0 * self.batch * n * k
+
+    def cpu_baseline(self, budget_s):
+        import oracle
+        host = [(p.cpu().numpy(), s.cpu().numpy()) for p, s in self.weights[0]]
+        xs = [x.view(__import__("torch").int16).cpu().numpy().view(np.uint16) for x in self.x]
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            for (p, s), x in zip(host, xs):
+                oracle.mxfp4_gemv_f64(p, s, x)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s or reps >= 200:
+                break
+        return {"value": round(self.weight_bytes_per_step * reps / el / 1e9, 3), "unit": "GB/s",
+                "cores": oracle.threads(), "kind": "oracle",
+                "sample": f"the full step (both MLP shapes, batch {self.batch}) repeated {reps} times, "
+                          f"{el:.1f} s, fp64 scalar C with OpenMP over rows"}
+
+
+class Ternary(Workload):
+    def __init__(self, rotate_bytes: float, n: int = 4096, k: int = 4096):
+        import torch
+        import gemm_e2m1_lut_amd as lib
+        import synth
+        self.lib, self.n, self.k = lib, n, k
+        self.name = f"ternary_gemv_{n}x{k}"
+        per_copy = n * k // 4
+        self.copies = max(2, math.ceil(rotate_bytes / per_copy))
+        r = synth.rng(synth.SEED_BASE + 1)
+        base = synth.two_bit_words(r, n, k)
+        self.host = {"packed": base, "row_scale": r.uniform(0.01, 0.1, n).astype(np.float32),
+                     "x": synth.f32_normal(r, (k,))}
+        dev0 = torch.from_numpy(base.view(np.int32)).cuda()
+        # rotated copies: the same weights rolled by whole rows (distinct addresses, same statistics)
+        self.packed = [torch.roll(dev0, shifts=7 * i, dims=0).contiguous() for i in range(self.copies)]
+        self.scale = torch.from_numpy(self.host["row_scale"]).cuda()
+        self.x = torch.from_numpy(self.host["x"]).cuda()
+        self.y = torch.empty(n, device="cuda")
+        self.weight_bytes_per_step = float(per_copy + 4 * n)
+        self.total_bytes_per_step = float(self.alg_bytes("ternary"))
+        self.dtype = "f32"
+        self.config = {"workload": self.name, "weights": "2-bit ternary, 16 per uint32",
+                       "activations": "fp32", "out": "fp32", "weight_copies_rotated": self.copies}
+
+    def launches(self):
+        def fn(i):
+            self.lib.ternary_gemv(self.packed[i % self.copies], self.scale, self.x, out=self.y)
+        return [("ternary", fn)]
+
+    def alg_bytes(self, label):
+        return self.n * self.k // 4 + 4 * self.n + 4 * self.k + 4 * self.n
+
+    def cpu_baseline(self, budget_s):
+        import oracle
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.ternary_gemv(self.host["packed"], self.host["row_scale"], self.host["x"])
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s or reps >= 2000:
+                break
+        return {"value": round(self.weight_bytes_per_step * reps / el / 1e9, 3), "unit": "GB/s",
+                "cores": oracle.threads(), "kind": "oracle",
+                "sample": f"the full 4096 x 4096 GEMV repeated {reps} times, {el:.1f} s"}
+
+
+class Gather(Workload):
+    def __init__(self, rotate_bytes: float, vocab=200000, hidden=4096, tokens=8192):
+        import torch
+        import gemm_e2m1_lut_amd as lib
+        self.lib, self.vocab, self.hidden, self.tokens = lib, vocab, hidden, tokens
+        self.name = f"nvfp4_embedding_gather_{vocab}x{hidden}_{tokens}ids"
+        g = _gen(977)
+        self.table = torch.randint(0, 256, (vocab, hidden // 2), dtype=torch.uint8, device="cuda", generator=g)
+        u = torch.rand((vocab, hidden // 16), generator=g, device="cuda") * 8 - 4
+        self.bscale = torch.exp2(u).to(torch.float8_e4m3fn).view(torch.uint8)
+        self.gscale = torch.tensor([0.01], dtype=torch.float32, device="cuda")
+        row_bytes = hidden // 2 + hidden // 16
+        self.copies = max(2, math.ceil(rotate_bytes / (tokens * row_bytes)))
+        self.ids = [torch.randint(0, vocab, (tokens,), device="cuda", generator=g) for _ in range(self.copies)]
+        self.out = torch.empty((tokens, hidden), dtype=torch.bfloat16, device="cuda")
+        self.weight_bytes_per_step = float(tokens * row_bytes)
+        self.total_bytes_per_step = float(self.alg_bytes("gather"))
+        self.config = {"workload": self.name, "table": "NVFP4 (E2M1 + E4M3 per 16 + fp32 global)",
+                       "out": "bf16", "id_sets_rotated": self.copies}
+
+    def launches(self):
+        def fn(i):
+            self.lib.nvfp4_embedding_gather(self.table, self.bscale, self.gscale, self.ids[i % self.copies],
+                                            out=self.out)
+        return [("gather", fn)]
+
+    def alg_bytes(self, label):
+        return self.tokens * (self.hidden // 2 + self.hidden // 16 + 8 + 2 * self.hidden)
+
+    def cpu_baseline(self, budget_s):
+        import oracle
+        sample = 1024
+        ids = self.ids[0][:sample].cpu().numpy()
+        # the oracle reads only the gathered rows; hand it those rows (same values, bounded memory)
+        rows = np.unique(ids)
+        remap = np.searchsorted(rows, ids)
+        rt = torch_index_rows(self.table, rows)
+        rs = torch_index_rows(self.bscale, rows)
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.nvfp4_gather(rt, rs, np.float32(0.01), remap)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s or reps >= 2000:
+                break
+        per = sample * (self.hidden // 2 + self.hidden // 16)
+        return {"value": round(per * reps / el / 1e9, 3), "unit": "GB/s", "cores": oracle.threads(),
+                "kind": "oracle",
+                "sample": f"{sample} of the {self.tokens} ids, repeated {reps} times, {el:.1f} s"}
+
+
+def torch_index_rows(t, rows: np.ndarray) -> np.ndarray:
+    import torch
+    return t[torch.from_numpy(rows).to(t.device)].cpu().numpy()
+
+
+class Decode(Workload):
+    def __init__(self, rotate_bytes: float, rows=14336, k=4096):
+        import torch
+        import gemm_e2m1_lut_amd as lib
+        self.lib, self.rows, self.k = lib, rows, k
+        self.name = f"mxfp4_decode_{rows}x{k}"
+        g = _gen(31)
+        per_copy = rows * k // 2 + rows * k // 32
+        self.copies = max(2, math.ceil(rotate_bytes / per_copy))
+        self.w = [_mxfp4_dev(g, rows, k, 0, 255) for _ in range(self.copies)]
+        self.out = torch.empty((rows, k), dtype=torch.bfloat16, device="cuda")
+        self.weight_bytes_per_step = float(per_copy)
+        self.total_bytes_per_step = float(self.alg_bytes("decode"))
+        self.dtype = "u16"
+        self.config = {"workload": self.name, "out": "bf16 bit patterns", "weight_copies_rotated": self.copies}
+
+    def launches(self):
+        def fn(i):
+            p, s = self.w[i % self.copies]
+            self.lib.dequant_decode(p, s, out=self.out)
+        return [("decode", fn)]
+
+    def alg_bytes(self, label):
+        return self.rows * self.k // 2 + self.rows * self.k // 32 + 2 * self.rows * self.k
+
+
+class GemvSmall(Workload):
+    def __init__(self, rotate_bytes: float):
+        import torch
+        import gemm_e2m1_lut_amd as lib
+        import synth
+        self.lib = lib
+        self.name = "mxfp4_gemv_256x512_b1"
+        c = synth.gemv_small()
+        self.p = torch.from_numpy(c["packed"]).cuda()
+        self.s = torch.from_numpy(c["scales"]).cuda()
+        self.x = torch.from_numpy(c["x"].view(np.int16)).view(torch.bfloat16).cuda()
+        self.y = torch.empty((1, 256), device="cuda")
+        self.copies = 1
+        self.weight_bytes_per_step = 256 * 256 + 256 * 16
+        self.total_bytes_per_step = float(self.alg_bytes("gemv_small"))
+        self.bound = "latency"
+        self.config = {"workload": self.name, "out": "fp32", "note": "fits in L2: launch-latency bound"}
+
+    def launches(self):
+        def fn(i):
+            self.lib.dequant_gemv(self.p, self.s, self.x, out=self.y)
+        return [("gemv_small", fn)]
+
+    def alg_bytes(self, label):
+        return 256 * 256 + 256 * 16 + 512 * 2 + 256 * 4
+
+
+WORKLOADS = {
+    "mlp_b1": lambda rb: GemvMLP(1, rb),
+    "mlp_b4": lambda rb: GemvMLP(4, rb),
+    "mlp_b16": lambda rb: GemvMLP(16, rb),
+    "ternary": Ternary,
+    "gather": Gather,
+    "decode": Decode,
+    "gemv_small": GemvSmall,
+}
+
+
+# ---------------------------------------------------------------- timing ---
+
+def timed_steps(launches, steps: int, offset: int) -> float:
+    """Milliseconds for `steps` full steps (events around the whole region)."""
+    import torch
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        for _, fn in launches:
+            fn(offset + i)
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end)
+
+
+def per_launch_ms(launches, steps: int, offset: int) -> dict:
+    """Average duration of each launch label, from an event pair around every launch."""
+    import torch
+    evs = {label: [] for label, _ in launches}
+    torch.cuda.synchronize()
+    for i in range(steps):
+        for label, fn in launches:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn(offset + i)
+            b.record()
+            evs[label].append((a, b))
+    torch.cuda.synchronize()
+    return {label: float(np.mean([a.elapsed_time(b) for a, b in pairs])) for label, pairs in evs.items()}
+
+
+def copy_calibration(mb: int) -> None:
+    """Plain device-to-device copies of known size, for scaling rocprof byte counters."""
+    import torch
+    n = mb * (1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+def traffic_from_profile(label: str) -> dict | None:
+    """Measured HBM bytes per launch from a committed counter summary, if the kernels
+    have not changed since it was taken."""
+    path = os.path.join(PROFILES, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    data = json.load(open(path))
+    entry = data.get(label)
+    if not entry or entry.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return entry
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="mlp_b1", choices=sorted(WORKLOADS))
+    ap.add_argument("--rotate-mb", type=float, default=600.0,
+                    help="weight bytes cycled through per pass (> 256 MB Infinity Cache)")
+    ap.add_argument("--cpu-budget-s", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mb", type=int, default=0, help="run a plain copy of this size first "
+                    "(counter calibration under rocprofv3 --pmc)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path; see DESIGN.md for how it would shard)", file=sys.stderr)
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    import gemm_e2m1_lut_amd as lib
+    lib.load_library()
+    torch.cuda.set_device(0)
+
+    if args.copy_mb:
+        copy_calibration(args.copy_mb)
+
+    wl = WORKLOADS[args.workload](args.rotate_mb * 1e6)
+    launches = wl.launches()
+    for i in range(args.warmup):
+        for _, fn in launches:
+            fn(i)
+    torch.cuda.synchronize()
+
+    total_ms = timed_steps(launches, args.steps, args.warmup)
+    ms_per_step = total_ms / args.steps
+    per_launch = per_launch_ms(launches, max(20, min(args.steps, 200)), args.warmup + args.steps)
+
+    value = wl.weight_bytes_per_step / (ms_per_step * 1e-3) / 1e9
+    pct_hbm = wl.total_bytes_per_step / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS * 100.0
+
+    kernels = []
+    for label, _ in launches:
+        ms = per_launch[label]
+        kernels.append({"label": label, "avg_us": round(ms * 1e3, 3),
+                        "alg_bytes": int(wl.alg_bytes(label)),
+                        "GBps": round(wl.alg_bytes(label) / (ms * 1e-3) / 1e9, 1)})
+    dom = max(kernels, key=lambda k: k["avg_us"])
+    achieved = dom["GBps"]
+    traffic = traffic_from_profile(dom["label"])
+    roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic["bytes_per_launch"] if traffic else None,
+                "kernel": dom["label"]}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = wl.cpu_baseline(args.cpu_budget_s)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": wl.config,
+        "pct_hbm_peak": round(pct_hbm, 2),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

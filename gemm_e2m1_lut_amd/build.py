@@ -1,0 +1,72 @@
+"""Build libe2m1lut.so in-tree with hipcc for gfx950.
+
+    python -m gemm_e2m1_lut_amd.build        # or: from gemm_e2m1_lut_amd.build import build
+
+Every .hip source under csrc/ is compiled to an object in _build/ (in
+parallel), then linked into gemm_e2m1_lut_amd/libe2m1lut.so. Each call
+recompiles everything.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD_DIR = os.path.join(ROOT, "_build")
+LIB_NAME = "libe2m1lut.so"
+LIB_PATH = os.path.join(PKG, LIB_NAME)
+
+ARCH = "gfx950"
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+# Packed fp32 VALU ops are disabled for every kernel: the compiler forms them
+# from ordinary float code, and some of their forms are not trusted here.
+HIPFLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", INCLUDE, "-I", CSRC,
+]
+
+
+def sources() -> list[str]:
+    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+
+
+def _run(cmd: list[str]) -> None:
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("command failed:\n  " + " ".join(cmd) + "\n" + res.stdout + res.stderr)
+    # hipcc's host pass warns that it does not know the packed-fp32 feature
+    noise = "is not a recognized feature for this target"
+    warnings = [ln for ln in res.stderr.splitlines() if ln.strip() and noise not in ln]
+    if warnings:
+        sys.stderr.write("\n".join(warnings) + "\n")
+
+
+def build(jobs: int | None = None) -> str:
+    """Compile every source and link the shared library; returns its path."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = sources()
+    objs = [os.path.join(BUILD_DIR, os.path.basename(s)[:-4] + ".o") for s in srcs]
+    jobs = jobs or min(len(srcs), int(os.environ.get("MAX_JOBS", "8")))
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        list(ex.map(lambda so: _run([HIPCC, *HIPFLAGS, "-c", so[0], "-o", so[1]]), zip(srcs, objs)))
+    tmp = LIB_PATH + ".tmp"
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+def clean() -> None:
+    shutil.rmtree(BUILD_DIR, ignore_errors=True)
+    if os.path.exists(LIB_PATH):
+        os.remove(LIB_PATH)
+
+
+if __name__ == "__main__":
+    print(build())

@@ -1,0 +1,150 @@
+// api.hip -- the extern "C" entry points of libe2m1lut.so (declared in
+// include/e2m1lut.h): host-side validation, then one asynchronous launch
+// sequence on the caller's stream. Nothing here allocates, copies or
+// synchronises; on a negative status nothing was launched.
+#include <limits.h>
+
+#include "e2m1lut.h"
+#include "kernels.hpp"
+
+namespace e2m1 {
+
+int device_cu_count() {
+    static int counts[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (counts[dev] == 0) {
+        int c = 0;
+        if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0)
+            c = 256;
+        counts[dev] = c;
+    }
+    return counts[dev];
+}
+
+}  // namespace e2m1
+
+namespace {
+
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// a * b without signed overflow, for non-negative operands.
+inline bool mul_ok(int64_t a, int64_t b) { return a == 0 || b <= INT64_MAX / a; }
+
+inline int launch_status(hipError_t e) { return e == hipSuccess ? E2M1_OK : E2M1_ERR_LAUNCH; }
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+hipError_t fill_zero_bytes(void* dst, int64_t bytes, hipStream_t stream) {
+    // Outputs are arrays of 2- or 4-byte elements: clear them as uint16.
+    return e2m1::launch_fill_zero_u16(reinterpret_cast<uint16_t*>(dst), bytes / 2, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int e2m1_abi_version(void) { return E2M1LUT_ABI_VERSION; }
+
+const char* e2m1_strerror(int status) {
+    switch (status) {
+        case E2M1_OK: return "ok";
+        case E2M1_ERR_NULL: return "a required pointer is NULL";
+        case E2M1_ERR_SHAPE: return "invalid extent: negative, too large, or breaking a divisibility rule";
+        case E2M1_ERR_ALIGN: return "a pointer is not aligned as the kernel's loads require";
+        case E2M1_ERR_DTYPE: return "unknown output dtype code";
+        case E2M1_ERR_WORKSPACE: return "workspace missing or smaller than mxfp4_moe_workspace_size()";
+        case E2M1_ERR_LAUNCH: return "the HIP runtime reported an error at kernel launch";
+        default: return "unknown status";
+    }
+}
+
+int dequant_decode(const uint8_t* packed, const uint8_t* scale_e8m0, uint16_t* out_bf16,
+                   int64_t rows, int64_t k, void* stream) {
+    if (rows < 0 || k < 0 || k % 32 != 0 || !mul_ok(rows, k)) return E2M1_ERR_SHAPE;
+    if (rows == 0 || k == 0) return E2M1_OK;
+    if (!packed || !scale_e8m0 || !out_bf16) return E2M1_ERR_NULL;
+    if (!aligned(packed, 16) || !aligned(out_bf16, 16)) return E2M1_ERR_ALIGN;
+    return launch_status(e2m1::launch_decode(packed, scale_e8m0, out_bf16, rows * (k / 32),
+                                             as_stream(stream)));
+}
+
+int dequant_gemv(const uint8_t* packed, const uint8_t* scale_e8m0, const uint16_t* x_bf16,
+                 void* y, int y_dtype, int64_t batch, int64_t n, int64_t k, void* stream) {
+    if (y_dtype != E2M1_DTYPE_F32 && y_dtype != E2M1_DTYPE_BF16) return E2M1_ERR_DTYPE;
+    if (batch < 1 || batch > E2M1_GEMV_MAX_BATCH || n < 0 || k < 0 || k % 32 != 0 ||
+        n > INT_MAX || k / 32 > INT_MAX / 64 || !mul_ok(n, k))
+        return E2M1_ERR_SHAPE;
+    if (n == 0) return E2M1_OK;
+    const int64_t esize = y_dtype == E2M1_DTYPE_F32 ? 4 : 2;
+    if (!y) return E2M1_ERR_NULL;
+    if (!aligned(y, (uintptr_t)esize)) return E2M1_ERR_ALIGN;
+    if (k == 0) return launch_status(fill_zero_bytes(y, batch * n * esize, as_stream(stream)));
+    if (!packed || !scale_e8m0 || !x_bf16) return E2M1_ERR_NULL;
+    if (!aligned(packed, 16) || !aligned(x_bf16, 16)) return E2M1_ERR_ALIGN;
+    return launch_status(e2m1::launch_gemv(packed, scale_e8m0, x_bf16, y, y_dtype == E2M1_DTYPE_BF16,
+                                           (int)batch, n, k, as_stream(stream)));
+}
+
+int ternary_gemv(const uint32_t* packed, const float* row_scale, const float* x, float* y,
+                 int64_t n, int64_t k, void* stream) {
+    if (n < 0 || k < 0 || k % 16 != 0 || n > INT_MAX || k / 16 > INT_MAX / 64 || !mul_ok(n, k))
+        return E2M1_ERR_SHAPE;
+    if (n == 0) return E2M1_OK;
+    if (!y) return E2M1_ERR_NULL;
+    if (!aligned(y, 4)) return E2M1_ERR_ALIGN;
+    if (k == 0) return launch_status(fill_zero_bytes(y, n * 4, as_stream(stream)));
+    if (!packed || !row_scale || !x) return E2M1_ERR_NULL;
+    if (!aligned(packed, 4) || !aligned(x, 4) || !aligned(row_scale, 4)) return E2M1_ERR_ALIGN;
+    return launch_status(e2m1::launch_ternary(packed, row_scale, x, y, n, k, as_stream(stream)));
+}
+
+int nvfp4_embedding_gather(const uint8_t* table, const uint8_t* block_scale_e4m3,
+                           const float* global_scale, const int64_t* ids, uint16_t* out_bf16,
+                           int64_t vocab, int64_t hidden, int64_t num_tokens, int32_t* err_flag,
+                           void* stream) {
+    if (vocab < 0 || hidden < 0 || num_tokens < 0 || hidden % 16 != 0 || !mul_ok(vocab, hidden) ||
+        !mul_ok(num_tokens, hidden))
+        return E2M1_ERR_SHAPE;
+    if (num_tokens == 0 || hidden == 0) return E2M1_OK;
+    if (!ids || !out_bf16 || !global_scale) return E2M1_ERR_NULL;
+    if (vocab > 0 && (!table || !block_scale_e4m3)) return E2M1_ERR_NULL;
+    if (!aligned(table, 8) || !aligned(out_bf16, 16) || !aligned(ids, 8) || !aligned(global_scale, 4) ||
+        !aligned(err_flag, 4))
+        return E2M1_ERR_ALIGN;
+    return launch_status(e2m1::launch_nvfp4_gather(table, block_scale_e4m3, global_scale, ids,
+                                                   out_bf16, vocab, hidden, num_tokens, err_flag,
+                                                   as_stream(stream)));
+}
+
+size_t mxfp4_moe_workspace_size(int64_t tokens, int64_t hidden, int64_t inter, int64_t experts,
+                                int64_t topk) {
+    if (tokens < 0 || hidden < 0 || inter < 0 || experts < 1 || topk < 1 || hidden % 32 != 0 ||
+        inter % 32 != 0 || !mul_ok(tokens, topk) || tokens * topk > INT_MAX)
+        return (size_t)-1;
+    if (tokens == 0 || hidden == 0) return 0;
+    return e2m1::moe_workspace_bytes(tokens, hidden, inter, experts, topk);
+}
+
+int mxfp4_moe_gemm(const uint16_t* x, const uint8_t* w13, const uint8_t* w13_scale,
+                   const uint8_t* w2, const uint8_t* w2_scale, const int32_t* topk_ids,
+                   const float* topk_weights, uint16_t* out, void* workspace,
+                   size_t workspace_bytes, int64_t tokens, int64_t hidden, int64_t inter,
+                   int64_t experts, int64_t topk, void* stream) {
+    const size_t need = mxfp4_moe_workspace_size(tokens, hidden, inter, experts, topk);
+    if (need == (size_t)-1 || experts > INT_MAX || hidden > INT_MAX || inter > INT_MAX)
+        return E2M1_ERR_SHAPE;
+    if (tokens == 0 || hidden == 0) return E2M1_OK;
+    if (!x || !out || !topk_ids || !topk_weights) return E2M1_ERR_NULL;
+    if (inter == 0) return launch_status(fill_zero_bytes(out, tokens * hidden * 2, as_stream(stream)));
+    if (!w13 || !w13_scale || !w2 || !w2_scale) return E2M1_ERR_NULL;
+    if (!workspace || workspace_bytes < need) return E2M1_ERR_WORKSPACE;
+    if (!aligned(x, 16) || !aligned(w13, 16) || !aligned(w2, 16) || !aligned(out, 16) ||
+        !aligned(workspace, 256) || !aligned(topk_ids, 4) || !aligned(topk_weights, 4))
+        return E2M1_ERR_ALIGN;
+    return launch_status(e2m1::launch_moe(x, w13, w13_scale, w2, w2_scale, topk_ids, topk_weights,
+                                          out, workspace, tokens, hidden, inter, experts, topk,
+                                          as_stream(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,39 @@
+// kernels.hpp -- internal launch functions of libe2m1lut.so (not part of the C ABI).
+// Arguments are validated by the C entry points in api.hip before these run.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace e2m1 {
+
+// Compute units of the current device (cached per device).
+int device_cu_count();
+
+hipError_t launch_fill_zero_u16(uint16_t* dst, int64_t count, hipStream_t stream);
+
+hipError_t launch_decode(const uint8_t* packed, const uint8_t* scales, uint16_t* out,
+                         int64_t nblocks, hipStream_t stream);
+
+hipError_t launch_gemv(const uint8_t* packed, const uint8_t* scales, const uint16_t* x, void* y,
+                       bool out_bf16, int batch, int64_t n, int64_t k, hipStream_t stream);
+
+hipError_t launch_ternary(const uint32_t* packed, const float* row_scale, const float* x, float* y,
+                          int64_t n, int64_t k, hipStream_t stream);
+
+hipError_t launch_nvfp4_gather(const uint8_t* table, const uint8_t* block_scale,
+                               const float* global_scale, const int64_t* ids, uint16_t* out,
+                               int64_t vocab, int64_t hidden, int64_t ntok, int32_t* err_flag,
+                               hipStream_t stream);
+
+size_t moe_workspace_bytes(int64_t tokens, int64_t hidden, int64_t inter, int64_t experts,
+                           int64_t topk);
+
+hipError_t launch_moe(const uint16_t* x, const uint8_t* w13, const uint8_t* w13s,
+                      const uint8_t* w2, const uint8_t* w2s, const int32_t* ids,
+                      const float* weights, uint16_t* out, void* workspace, int64_t tokens,
+                      int64_t hidden, int64_t inter, int64_t experts, int64_t topk,
+                      hipStream_t stream);
+
+}  // namespace e2m1

@@ -1,0 +1,194 @@
+/*
+ * e2m1lut.h -- C ABI of libe2m1lut.so, the MI355X (gfx950) library that
+ * decodes packed low-bit weights inside memory-bound matrix-vector and
+ * small-batch matrix products.
+ *
+ * Pages the operations follow (cited by page and section):
+ *   [vLLM-51583]   prhub.com.cn digest of vLLM pull request 51583: MXFP4 unpack
+ *                  to bf16 by table lookup plus an integer add of the E8M0
+ *                  block scale into the bf16 exponent field, both zero codes
+ *                  forced to +0.0 ("功能与动机", "实现拆解", "关键源码片段").
+ *   [SGLang-34222] prhub.com.cn digest of SGLang pull request 34222: NVFP4
+ *                  token embedding dequantised at gather time ("实现拆解",
+ *                  "关键源码片段").
+ *   [FairyFuse]    blog.hotdry.top post on FairyFuse: 2-bit ternary GEMV with
+ *                  add/sub accumulation and a per-row scale
+ *                  ("三元 GEMV 的乘法消除原理").
+ *
+ * Conventions shared by every entry point
+ *   - All array pointers are DEVICE pointers (hipMalloc'd or torch CUDA
+ *     tensors), owned by the caller, row-major and densely packed. Inputs and
+ *     outputs must not overlap.
+ *   - `stream` is a hipStream_t passed as void*; NULL means the default
+ *     stream. Every call is asynchronous on that stream: nothing allocates,
+ *     copies to or from the host, or synchronises. Device-side faults surface
+ *     at the caller's next synchronisation.
+ *   - Arguments are validated on the host before anything is launched; on a
+ *     negative status nothing was launched and no output was written.
+ *   - A call whose output is empty (a zero extent) launches nothing and
+ *     returns E2M1_OK; pointers may then be NULL.
+ *   - Formats:
+ *       E2M1 code: 4 bits, bit 3 = sign, bits 0..2 index the magnitudes
+ *         {0, 0.5, 1, 1.5, 2, 3, 4, 6}.
+ *       Packed code rows: byte j holds column 2j in its low nibble and
+ *         column 2j+1 in its high nibble.
+ *       E8M0: one uint8 per 32 consecutive columns, value 2^(e-127).
+ *       E4M3: OCP float8 e4m3fn (bias 7, no infinities, S.1111.111 = NaN).
+ *       bf16 values travel as their uint16 bit patterns.
+ */
+#ifndef E2M1LUT_H
+#define E2M1LUT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define E2M1LUT_ABI_VERSION 1
+
+/* Status codes (0 = success, negative = rejected before launch or launch error). */
+#define E2M1_OK 0
+#define E2M1_ERR_NULL (-1)      /* a required pointer is NULL */
+#define E2M1_ERR_SHAPE (-2)     /* negative extent, or a divisibility / range rule broken */
+#define E2M1_ERR_ALIGN (-3)     /* a pointer lacks the alignment the kernel loads need */
+#define E2M1_ERR_DTYPE (-4)     /* unknown output dtype code */
+#define E2M1_ERR_WORKSPACE (-5) /* workspace missing or smaller than required */
+#define E2M1_ERR_LAUNCH (-6)    /* the HIP runtime reported an error at launch (e.g. no gfx950 code for the device) */
+
+/* Output dtype codes for dequant_gemv. */
+#define E2M1_DTYPE_F32 0
+#define E2M1_DTYPE_BF16 1
+
+/* Largest batch dequant_gemv accepts. */
+#define E2M1_GEMV_MAX_BATCH 16
+
+/* ABI version of the loaded library (E2M1LUT_ABI_VERSION it was built with). */
+int e2m1_abi_version(void);
+
+/* Static, NUL-terminated description of a status code; never NULL. */
+const char* e2m1_strerror(int status);
+
+/*
+ * dequant_decode -- unpack an MXFP4 matrix to bf16 bit patterns.
+ * Operation: [vLLM-51583] "功能与动机" and "关键源码片段" (vec.h): the code's
+ * bf16 pattern from the E2M1 table, plus (e-127)*2^7 added to the 16-bit
+ * pattern modulo 2^16; a lane whose table pattern is +0 or -0 is written as
+ * +0.0 (0x0000) at every exponent. For 2 <= e <= 252 the result is exactly
+ * bf16((+/-)magnitude * 2^(e-127)); outside that range non-zero codes wrap as
+ * the integer add dictates (the method's result, not a meaningful value).
+ *   packed      uint8  [rows, k/2]   (16-byte aligned)
+ *   scale_e8m0  uint8  [rows, k/32]
+ *   out_bf16    uint16 [rows, k]     (16-byte aligned), overwritten
+ * Requires rows >= 0, k >= 0, k % 32 == 0.
+ */
+int dequant_decode(const uint8_t* packed, const uint8_t* scale_e8m0, uint16_t* out_bf16,
+                   int64_t rows, int64_t k, void* stream);
+
+/*
+ * dequant_gemv -- y = x . W^T with W decoded from MXFP4 inside the product.
+ * Operation: the decode of dequant_decode followed by a dot product per
+ * output, accumulated in fp32 (the unpack feeds the MXFP4 MoE GEMM in
+ * [vLLM-51583] "实现拆解" item 2). Defined for E8M0 values 2..252, where the
+ * decoded weights are exact; the summation order is unspecified.
+ *   packed      uint8  [n, k/2]      (16-byte aligned)
+ *   scale_e8m0  uint8  [n, k/32]
+ *   x_bf16      uint16 [batch, k]    (bf16 activations, 16-byte aligned)
+ *   y           [batch, n], fp32 (y_dtype = E2M1_DTYPE_F32) or bf16 bit
+ *               patterns rounded to nearest even (E2M1_DTYPE_BF16);
+ *               overwritten, never accumulated into. 4-byte aligned.
+ * Requires 1 <= batch <= E2M1_GEMV_MAX_BATCH, n >= 0, k >= 0, k % 32 == 0.
+ * k == 0 writes zeros.
+ */
+int dequant_gemv(const uint8_t* packed, const uint8_t* scale_e8m0, const uint16_t* x_bf16,
+                 void* y, int y_dtype, int64_t batch, int64_t n, int64_t k, void* stream);
+
+/*
+ * ternary_gemv -- y[i] = row_scale[i] * sum_k t(i,k) * x[k], t in {-1, 0, +1}.
+ * Operation: [FairyFuse] "三元 GEMV 的乘法消除原理": 16 weights per uint32,
+ * weight j of word w multiplies x[16w + j]; bit 2j+1 set = +1 (add), bit 2j
+ * set = -1 (subtract), neither = 0; the per-row scale multiplies once after
+ * the row sum. A field with both bits set is not a valid weight; the kernel
+ * reads it as 0. Accumulation is fp32.
+ *   packed     uint32 [n, k/16]  (4-byte aligned)
+ *   row_scale  fp32   [n]
+ *   x          fp32   [k]        (4-byte aligned)
+ *   y          fp32   [n], overwritten
+ * Requires n >= 0, k >= 0, k % 16 == 0. k == 0 writes zeros. The fastest
+ * kernel needs k % 64 == 0 and 16-byte aligned packed and x; other inputs
+ * take a slower kernel with the same results.
+ */
+int ternary_gemv(const uint32_t* packed, const float* row_scale, const float* x, float* y,
+                 int64_t n, int64_t k, void* stream);
+
+/*
+ * nvfp4_embedding_gather -- gather token rows of an NVFP4 table and
+ * dequantise them to bf16.
+ * Operation: [SGLang-34222] "实现拆解" item 2 and "关键源码片段"
+ * (embedding()): for output row i and column c with r = ids[i]: the code is
+ * the low nibble of table[r, c/2] for even c and the high nibble for odd c;
+ * v = (+/-)magnitude in fp32 (code 8 is -0.0, sign kept); eff =
+ * fp32(e4m3(block_scale[r, c/16]) * global_scale); out = bf16_rne(fp32(v *
+ * eff)). NaN results are written as 0x7FC0.
+ *   table             uint8  [vocab, hidden/2]   (8-byte aligned; 16-byte
+ *                     alignment and hidden % 32 == 0 select the widest loads)
+ *   block_scale_e4m3  uint8  [vocab, hidden/16]
+ *   global_scale      fp32   [1] on the device (read by the kernel, so the
+ *                     call needs no host synchronisation)
+ *   ids               int64  [num_tokens]
+ *   out_bf16          uint16 [num_tokens, hidden], overwritten (16-byte aligned)
+ *   err_flag          int32  [1] on the device, or NULL. An id outside
+ *                     [0, vocab) gives an all-zero output row and, when
+ *                     err_flag is given, stores 1 there (never cleared by
+ *                     the library).
+ * Requires vocab >= 0, hidden >= 0, hidden % 16 == 0 (the page's
+ * create_weights divisibility guard), num_tokens >= 0.
+ */
+int nvfp4_embedding_gather(const uint8_t* table, const uint8_t* block_scale_e4m3,
+                           const float* global_scale, const int64_t* ids, uint16_t* out_bf16,
+                           int64_t vocab, int64_t hidden, int64_t num_tokens, int32_t* err_flag,
+                           void* stream);
+
+/*
+ * mxfp4_moe_workspace_size -- bytes of device workspace mxfp4_moe_gemm needs
+ * for these extents (0 for an empty problem; (size_t)-1 for invalid extents).
+ */
+size_t mxfp4_moe_workspace_size(int64_t tokens, int64_t hidden, int64_t inter, int64_t experts,
+                                int64_t topk);
+
+/*
+ * mxfp4_moe_gemm -- MXFP4 mixture-of-experts layer with routing as input.
+ * Operation: the fused expert op exercised by [vLLM-51583] "关键源码片段"
+ * (the MoE test): per token t and slot j, e = topk_ids[t, j]:
+ *   h = W13[e] . x_t (2*inter outputs; rows [0, inter) gate, [inter, 2*inter) up),
+ *   a = silu(gate) * up, y = W2[e] . a,
+ *   out[t] = bf16_rne(sum_j topk_weights[t, j] * y).
+ * Products run on bf16 MFMA with fp32 accumulation; `a` is rounded to bf16
+ * before the second product. The combine over slots runs in slot order
+ * (deterministic).
+ *   x              uint16 [tokens, hidden]  bf16
+ *   w13            uint8  [experts, 2*inter, hidden/2]   (16-byte aligned)
+ *   w13_scale      uint8  [experts, 2*inter, hidden/32]
+ *   w2             uint8  [experts, hidden, inter/2]     (16-byte aligned)
+ *   w2_scale       uint8  [experts, hidden, inter/32]
+ *   topk_ids       int32  [tokens, topk], each in [0, experts)
+ *   topk_weights   fp32   [tokens, topk]
+ *   out            uint16 [tokens, hidden]  bf16, overwritten
+ *   workspace      device buffer of at least mxfp4_moe_workspace_size()
+ *                  bytes, 256-byte aligned; contents need no initialisation
+ * Requires hidden % 32 == 0, inter % 32 == 0, experts >= 1, topk >= 1,
+ * tokens >= 0. Ids outside [0, experts) are not checked on the host (they
+ * live on the device); the kernels skip such slots.
+ */
+int mxfp4_moe_gemm(const uint16_t* x, const uint8_t* w13, const uint8_t* w13_scale,
+                   const uint8_t* w2, const uint8_t* w2_scale, const int32_t* topk_ids,
+                   const float* topk_weights, uint16_t* out, void* workspace,
+                   size_t workspace_bytes, int64_t tokens, int64_t hidden, int64_t inter,
+                   int64_t experts, int64_t topk, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* E2M1LUT_H */

@@ -1,0 +1,146 @@
+"""CPU checks of the C ABI: the library loads, exports every function include/*.h
+declares, and rejects bad arguments on the host before anything is launched.
+
+No call here reaches a kernel launch: every argument set is rejected by
+validation (or is an empty problem), so these run without a GPU.
+"""
+from __future__ import annotations
+
+import ctypes
+import glob
+import os
+import re
+import subprocess
+
+import pytest
+
+from conftest import ROOT
+
+E2M1_OK, E_NULL, E_SHAPE, E_ALIGN, E_DTYPE, E_WS = 0, -1, -2, -3, -4, -5
+
+
+def declared_functions() -> set[str]:
+    names = set()
+    for path in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(path, encoding="utf-8").read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?(?:int|size_t|char|void)\s*\*?\s*(\w+)\s*\(", text, re.M):
+            names.add(m.group(1))
+    return names
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import gemm_e2m1_lut_amd as g
+    return g.load_library()
+
+
+def test_header_declares_the_five_operations():
+    names = declared_functions()
+    for op in ("dequant_decode", "dequant_gemv", "ternary_gemv", "nvfp4_embedding_gather",
+               "mxfp4_moe_gemm", "mxfp4_moe_workspace_size", "e2m1_abi_version", "e2m1_strerror"):
+        assert op in names
+
+
+def test_library_exports_every_declared_function(lib):
+    import gemm_e2m1_lut_amd as g
+    out = subprocess.run(["nm", "-D", "--defined-only", g.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
+    missing = declared_functions() - exported
+    assert not missing, missing
+    for name in declared_functions():
+        assert hasattr(lib, name)
+
+
+def test_version_and_messages(lib):
+    assert lib.e2m1_abi_version() == 1
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        assert lib.e2m1_strerror(code)
+    assert lib.e2m1_strerror(12345) == b"unknown status"
+
+
+def P(addr: int) -> ctypes.c_void_p:
+    """A fake device address: only ever seen by host-side validation here."""
+    return ctypes.c_void_p(addr)
+
+
+NULL = ctypes.c_void_p(0)
+A, B, C, D = P(0x10000), P(0x20000), P(0x30000), P(0x40000)   # 16-byte aligned
+
+
+def test_decode_validation(lib):
+    f = lib.dequant_decode
+    assert f(A, B, C, 4, 48, NULL) == E_SHAPE          # k % 32
+    assert f(A, B, C, -1, 64, NULL) == E_SHAPE
+    assert f(NULL, NULL, NULL, 0, 64, NULL) == E2M1_OK  # empty: nothing launched
+    assert f(NULL, NULL, NULL, 5, 0, NULL) == E2M1_OK
+    assert f(NULL, B, C, 4, 64, NULL) == E_NULL
+    assert f(P(0x10008), B, C, 4, 64, NULL) == E_ALIGN
+    assert f(A, B, P(0x30004), 4, 64, NULL) == E_ALIGN
+    assert f(A, B, C, 2**62, 64, NULL) == E_SHAPE      # rows * k overflows
+
+
+def test_gemv_validation(lib):
+    f = lib.dequant_gemv
+    assert f(A, B, C, D, 7, 1, 8, 64, NULL) == E_DTYPE
+    assert f(A, B, C, D, 0, 0, 8, 64, NULL) == E_SHAPE   # batch 0
+    assert f(A, B, C, D, 0, 17, 8, 64, NULL) == E_SHAPE  # batch above 16
+    assert f(A, B, C, D, 0, 1, 8, 40, NULL) == E_SHAPE   # k % 32
+    assert f(A, B, C, D, 0, 1, 2**31, 64, NULL) == E_SHAPE
+    assert f(NULL, NULL, NULL, NULL, 0, 1, 0, 64, NULL) == E2M1_OK
+    assert f(A, B, C, NULL, 0, 1, 8, 64, NULL) == E_NULL
+    assert f(NULL, B, C, D, 1, 1, 8, 64, NULL) == E_NULL
+    assert f(A, B, C, P(0x40002), 0, 1, 8, 64, NULL) == E_ALIGN   # fp32 y needs 4 bytes
+    assert f(A, B, P(0x30008), D, 1, 1, 8, 64, NULL) == E_ALIGN   # x needs 16 bytes
+    assert f(P(0x10001), B, C, D, 1, 1, 8, 64, NULL) == E_ALIGN
+
+
+def test_ternary_validation(lib):
+    f = lib.ternary_gemv
+    assert f(A, B, C, D, 4, 24, NULL) == E_SHAPE   # k % 16
+    assert f(A, B, C, D, -3, 16, NULL) == E_SHAPE
+    assert f(NULL, NULL, NULL, NULL, 0, 16, NULL) == E2M1_OK
+    assert f(A, B, C, NULL, 4, 16, NULL) == E_NULL
+    assert f(NULL, B, C, D, 4, 16, NULL) == E_NULL
+    assert f(P(0x10002), B, C, D, 4, 16, NULL) == E_ALIGN
+
+
+def test_gather_validation(lib):
+    f = lib.nvfp4_embedding_gather
+    assert f(A, B, C, D, P(0x50000), 10, 24, 3, NULL, NULL) == E_SHAPE   # hidden % 16 (page guard)
+    assert f(A, B, C, D, P(0x50000), -1, 32, 3, NULL, NULL) == E_SHAPE
+    assert f(NULL, NULL, NULL, NULL, NULL, 10, 32, 0, NULL, NULL) == E2M1_OK
+    assert f(A, B, NULL, D, P(0x50000), 10, 32, 3, NULL, NULL) == E_NULL
+    assert f(NULL, B, C, D, P(0x50000), 10, 32, 3, NULL, NULL) == E_NULL
+    assert f(A, B, C, D, P(0x50008), 10, 32, 3, NULL, NULL) == E_ALIGN   # out needs 16 bytes
+    assert f(P(0x10004), B, C, D, P(0x50000), 10, 32, 3, NULL, NULL) == E_ALIGN
+
+
+def test_moe_validation(lib):
+    ws = lib.mxfp4_moe_workspace_size
+    bad = ctypes.c_size_t(-1).value
+    assert ws(4, 48, 64, 2, 1) == bad         # hidden % 32
+    assert ws(4, 64, 40, 2, 1) == bad         # inter % 32
+    assert ws(4, 64, 64, 0, 1) == bad         # no experts
+    assert ws(4, 64, 64, 2, 0) == bad         # topk 0
+    assert ws(0, 64, 64, 2, 1) == 0
+    need = ws(256, 2880, 2880, 32, 4)
+    assert 0 < need < 2**40
+    f = lib.mxfp4_moe_gemm
+    args = [A, B, C, D, P(0x50000), P(0x60000), P(0x70000), P(0x80000)]
+    assert f(*args, P(0x90000), 0, 4, 64, 64, 2, 1, NULL) == E_WS
+    small = ws(4, 64, 64, 2, 1)
+    assert f(*args, P(0x90000), small - 1 if small else 0, 4, 64, 64, 2, 1, NULL) == E_WS
+    assert f(*args, P(0x90010), small, 4, 64, 64, 2, 1, NULL) == E_ALIGN   # workspace 256-byte aligned
+    assert f(*args, P(0x90000), small, 4, 48, 64, 2, 1, NULL) == E_SHAPE
+    assert f(NULL, *args[1:], P(0x90000), small, 4, 64, 64, 2, 1, NULL) == E_NULL
+    assert f(NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 0, 0, 64, 64, 2, 1, NULL) == E2M1_OK
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
+    import gemm_e2m1_lut_amd._binding as b
+    monkeypatch.setattr(b, "_lib", None)
+    monkeypatch.setattr(b, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        b.load_library()

@@ -1,0 +1,84 @@
+"""GPU parity of nvfp4_embedding_gather: bit-exact against the oracle.
+
+Covers the 200000 x 4096 table with 8192 ids (every gathered element), every
+E4M3 scale byte against every code, the 16-channel path (hidden % 32 != 0),
+ids outside the vocabulary (zero rows + flag), ids of any shape, and the
+empty call. Outputs are poisoned before each launch.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_util import bits, f32, i64, say, u8
+
+pytestmark = pytest.mark.gpu
+
+
+def run_gather(g, table, bscale, gscale, ids, flag=None):
+    hidden = 2 * table.shape[1]
+    out = torch.full((*np.shape(ids), hidden), -1, dtype=torch.int16, device="cuda:0")
+    g.nvfp4_embedding_gather(u8(table), u8(bscale), f32(np.array([gscale], np.float32)),
+                             i64(np.asarray(ids)), out=out, err_flag=flag)
+    return bits(out)
+
+
+@pytest.mark.slow
+def test_workload_200k_vocab(gpu, orc):
+    say("gather: 200000 x 4096 table, 8192 ids")
+    c = synth.nvfp4_case()
+    got = run_gather(gpu, c["table"], c["block_scale"], c["global_scale"], c["ids"])
+    want, bad = orc.nvfp4_gather(c["table"], c["block_scale"], c["global_scale"], c["ids"])
+    assert bad == 0
+    assert np.array_equal(got, want)
+
+
+def test_every_scale_byte_and_code(gpu, orc):
+    say("gather: all 256 scale bytes x 16 codes")
+    # row b: scale byte b in every group; the row holds all 256 byte values = all code pairs
+    table = np.tile(np.arange(256, dtype=np.uint8), (256, 1))        # hidden 512
+    bscale = np.repeat(np.arange(256, dtype=np.uint8)[:, None], 32, axis=1)
+    ids = np.arange(256, dtype=np.int64)
+    for gs in (0.01, 1.0, 0.37):
+        got = run_gather(gpu, table, bscale, gs, ids)
+        want, _ = orc.nvfp4_gather(table, bscale, gs, ids)
+        assert np.array_equal(got, want), gs
+
+
+@pytest.mark.parametrize("vocab,hidden,ntok", [(50, 16, 7), (300, 48, 33), (1000, 2048 + 32, 129),
+                                               (64, 4096, 1), (10, 272, 64)])
+def test_shapes(gpu, orc, vocab, hidden, ntok):
+    say(f"gather: vocab={vocab} hidden={hidden} ntok={ntok}")
+    r = np.random.default_rng(vocab + hidden + ntok)
+    table = synth.uniform_bytes(r, (vocab, hidden // 2))
+    bscale = synth.e4m3_log2_uniform(r, (vocab, hidden // 16))
+    ids = synth.token_ids(r, ntok, vocab)
+    got = run_gather(gpu, table, bscale, 0.01, ids)
+    want, _ = orc.nvfp4_gather(table, bscale, 0.01, ids)
+    assert np.array_equal(got, want)
+
+
+def test_out_of_range_ids(gpu, orc):
+    say("gather: out-of-range ids")
+    r = np.random.default_rng(5)
+    table = synth.uniform_bytes(r, (20, 64))
+    bscale = synth.e4m3_log2_uniform(r, (20, 8))
+    ids = np.array([[3, -1], [20, 19], [0, 2**40]], dtype=np.int64)
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    got = run_gather(gpu, table, bscale, 0.01, ids, flag)
+    want, bad = orc.nvfp4_gather(table, bscale, 0.01, ids.reshape(-1))
+    assert bad == 3 and int(flag.item()) == 1
+    assert np.array_equal(got.reshape(-1, 128), want)
+    ok = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    run_gather(gpu, table, bscale, 0.01, np.array([0, 19]), ok)
+    assert int(ok.item()) == 0
+
+
+def test_empty(gpu):
+    say("gather: empty")
+    out = gpu.nvfp4_embedding_gather(u8(np.zeros((4, 8), np.uint8)), u8(np.zeros((4, 1), np.uint8)),
+                                     f32(np.array([1.0], np.float32)),
+                                     torch.zeros((0,), dtype=torch.int64, device="cuda:0"))
+    assert out.shape == (0, 16)
