@@ -5,16 +5,17 @@
 // E8M0 block scale is applied as an integer add of (e-127)*2^7 to the 16-bit
 // pattern, and lanes holding one of the two zero codes are written as +0.0.
 //
-// gfx950 design. One thread owns one 32-column scale block: a 16-byte load of
-// codes, one scale byte, 64 bytes of bf16 out. Because every code of the block
-// shares one addend, the thread adds it to the eight magnitude patterns once
-// (packed 16-bit adds) instead of once per lane -- the same integer sum -- and
-// keeps the zero magnitude at +0 (the zero forcing). The scaled table is then
+// gfx950 design. One thread owns one packed word (8 codes of one 32-column
+// scale block): a 4-byte load, the block's scale byte, 16 bytes of bf16 out,
+// so each wave stores one contiguous kilobyte per instruction. Because the
+// codes of a block share one addend, the thread adds it to the eight magnitude
+// patterns once (packed 16-bit adds) instead of once per lane -- the same
+// integer sum -- and keeps the zero magnitude at +0 (the zero forcing). The scaled table is then
 // split into a low-byte plane and a high-byte plane of 8 bytes each, so one
 // v_perm_b32 looks up four codes in one plane. The sign (bit 3 of the code) is
 // XORed into the high byte for non-zero magnitudes: adding 0x8000 modulo 2^16
 // is the same as flipping bit 15, so signed and unsigned codes share a table.
-// Memory-bound: 16.5 bytes in, 64 bytes out per 32 codes.
+// Memory-bound: 16.5 bytes in, 64 bytes out per 32 codes (write-dominated).
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -90,24 +91,21 @@ __device__ __forceinline__ void decode_word(uint32_t p, const BytePlanes& t, uin
 
 constexpr int kThreads = 256;
 
-__global__ __launch_bounds__(kThreads) void decode_kernel(const uint4* __restrict__ packed,
+// One thread per packed word (8 codes): a 4-byte load, the word's scale byte
+// (shared by the 4 words of a 32-column block), one 16-byte store. Consecutive
+// lanes read consecutive words and write consecutive 16-byte pieces, so every
+// wave-wide store instruction writes one contiguous kilobyte.
+__global__ __launch_bounds__(kThreads) void decode_kernel(const uint32_t* __restrict__ packed,
                                                           const uint8_t* __restrict__ scales,
                                                           uint4* __restrict__ out,
-                                                          int64_t nblocks) {
+                                                          int64_t nwords) {
     const int64_t stride = (int64_t)gridDim.x * kThreads;
-    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nblocks; i += stride) {
-        const uint4 p = load_nt16(packed + i);
-        const BytePlanes t = scaled_planes(scales[i]);
-        uint32_t w[16];
-        decode_word(p.x, t, w + 0);
-        decode_word(p.y, t, w + 4);
-        decode_word(p.z, t, w + 8);
-        decode_word(p.w, t, w + 12);
-        uint4* o = out + 4 * i;
-        store_nt16(o + 0, w[0], w[1], w[2], w[3]);
-        store_nt16(o + 1, w[4], w[5], w[6], w[7]);
-        store_nt16(o + 2, w[8], w[9], w[10], w[11]);
-        store_nt16(o + 3, w[12], w[13], w[14], w[15]);
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nwords; i += stride) {
+        const uint32_t p = __builtin_nontemporal_load(packed + i);
+        const BytePlanes t = scaled_planes(scales[i >> 2]);
+        uint32_t w[4];
+        decode_word(p, t, w);
+        store_nt16(out + i, w[0], w[1], w[2], w[3]);
     }
 }
 
@@ -122,11 +120,12 @@ __global__ __launch_bounds__(kThreads) void fill_zero_kernel(uint16_t* __restric
 
 hipError_t launch_decode(const uint8_t* packed, const uint8_t* scales, uint16_t* out,
                          int64_t nblocks, hipStream_t stream) {
-    const int64_t want = (nblocks + kThreads - 1) / kThreads;
+    const int64_t nwords = nblocks * 4;
+    const int64_t want = (nwords + kThreads - 1) / kThreads;
     const int64_t cap = (int64_t)device_cu_count() * 32;
     const int grid = (int)(want < cap ? want : cap);
-    decode_kernel<<<grid, kThreads, 0, stream>>>(reinterpret_cast<const uint4*>(packed), scales,
-                                                 reinterpret_cast<uint4*>(out), nblocks);
+    decode_kernel<<<grid, kThreads, 0, stream>>>(reinterpret_cast<const uint32_t*>(packed), scales,
+                                                 reinterpret_cast<uint4*>(out), nwords);
     return hipGetLastError();
 }
 

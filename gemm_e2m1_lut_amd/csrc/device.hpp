@@ -44,9 +44,15 @@ __device__ __forceinline__ void store_nt16(void* p, uint32_t a, uint32_t b, uint
 
 // ---------------------------------------------------------------- E8M0 ----
 
-// fp32 whose exponent field is the E8M0 byte: exactly 2^(e-127) for
-// 1 <= e <= 254. This is the scale operand of the hardware FP4 conversions.
-__device__ __forceinline__ float e8m0_as_f32(uint32_t e) { return __uint_as_float(e << 23); }
+// Scale operand of the hardware FP4 conversions for an E8M0 byte. The
+// conversions use only the exponent field of this fp32, with the E8M0 meaning
+// (0 -> 2^-127, 255 -> NaN). The method keeps both zero codes at +0.0 for
+// every exponent, 255 included (vLLM pull request 51583 digest, "实现拆解"
+// item 4 and its zero-code test), so 255 is read as 254: zero codes then
+// convert to zero, and non-zero codes are defined only for 2 <= e <= 252.
+__device__ __forceinline__ float e8m0_scale(uint32_t e) {
+    return __uint_as_float((e < 254u ? e : 254u) << 23);
+}
 
 // ------------------------------------------------- hardware FP4 -> bf16/f32 --
 // v_cvt_scalef32_pk_{bf16,f32}_fp4 decode the two E2M1 codes of one byte of

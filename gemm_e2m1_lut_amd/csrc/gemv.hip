@@ -13,12 +13,14 @@
 //     multiplies the pair by the matching pair of x and accumulates in fp32:
 //     per byte of weights one conversion and one dot2.
 //   * Batch 1 (the bandwidth-bound case): each lane owns fixed 32-column
-//     chunks of K, so its slice of x sits in registers for the whole kernel
-//     (staged once per workgroup through LDS). A group of G lanes covers one
-//     row (G = 64 for K >= 2048, smaller for short rows so a wave works on
-//     several rows at once); every weight byte is read once with a 16-byte
-//     load, the next row is prefetched while the current one is reduced, and
-//     the row total comes from a DPP / cross-row shuffle reduction.
+//     chunks of K, so its slice of x sits in registers for the whole kernel.
+//     A group of G lanes covers one row (G = 64 for K >= 2048, smaller for
+//     short rows so a wave works on several rows at once) and takes R
+//     consecutive rows per pass, R sized so one resident generation of waves
+//     covers the matrix. Every weight byte is read once with a 16-byte load,
+//     all of a pass's loads are in flight before the first row is computed,
+//     and the row total comes from a DPP-only reduction (row_bcast for the
+//     cross-row steps), so the decode and dot products hide under the loads.
 //   * Other batches: one wave per row, lanes across K, x read through the
 //     cache hierarchy per chunk.
 #include "device.hpp"
@@ -64,72 +66,80 @@ __device__ __forceinline__ void store_out(void* y, int64_t idx, float v) {
 
 // ------------------------------------------------------------- batch 1 ----
 
-template <int G, int CPL>
-__device__ __forceinline__ void load_row(const uint8_t* __restrict__ packed,
-                                         const uint8_t* __restrict__ scales, int row, int n,
-                                         int kc, int gl, uint4 (&w)[CPL], uint32_t (&e)[CPL]) {
-#pragma unroll
-    for (int ci = 0; ci < CPL; ++ci) {
-        const int c = gl + G * ci;
-        if (row < n && c < kc) {
-            const int64_t blk = (int64_t)row * kc + c;
-            w[ci] = load_nt16(reinterpret_cast<const uint4*>(packed) + blk);
-            e[ci] = scales[blk];
-        } else {
-            w[ci] = make_uint4(0u, 0u, 0u, 0u);
-            e[ci] = 0u;
-        }
-    }
+// Row total of groups of G lanes (G in {8, 16, 32, 64}) with DPP only: the
+// total ends up in the last lane of each group (lane G-1 mod G).
+template <int G>
+__device__ __forceinline__ float group_total(float v) {
+    v += dpp_f32<0xB1>(v);    // quad_perm [1,0,3,2]
+    v += dpp_f32<0x4E>(v);    // quad_perm [2,3,0,1]
+    v += dpp_f32<0x141>(v);   // row_half_mirror: every lane holds its 8-lane sum
+    if constexpr (G >= 16) v += dpp_f32<0x140>(v);   // row_mirror: 16-lane sum
+    if constexpr (G >= 32)   // row_bcast:15 into rows 1 and 3
+        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));
+    if constexpr (G >= 64)   // row_bcast:31 into rows 2 and 3
+        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xC, 0xF, false));
+    return v;
 }
 
-template <int G, int CPL, bool kBf16Out>
+// Batch 1. A group of G lanes covers one row; lane gl owns the 32-column chunks
+// gl, gl + G, ... (CPL of them) for every row it visits, so its slice of x is
+// loaded once into registers. A group takes R consecutive rows per pass. All
+// loads are unconditional (indices clamped into range, out-of-range lanes and
+// rows masked at use): guarded loads with a zero in the other branch would
+// make each load wait for the previous one. x is requested first, then every
+// weight chunk and scale of the pass, so computing row 0 waits only for x and
+// row 0 while the later rows are still in flight.
+template <int G, int CPL, int R, bool kBf16Out>
 __global__ __launch_bounds__(kThreads) void gemv_b1_kernel(const uint8_t* __restrict__ packed,
                                                            const uint8_t* __restrict__ scales,
                                                            const uint16_t* __restrict__ x,
                                                            void* __restrict__ y, int n, int kc) {
-    extern __shared__ uint4 xs[];   // kc * 4 uint4 = all of x
-    constexpr int kRowsPerWave = kWave / G;
+    constexpr int kGroupsPerWave = kWave / G;
     const int lane = threadIdx.x & (kWave - 1);
     const int gl = lane & (G - 1);
     const int grp = lane / G;
-    const int wave = blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
-    const int row_stride = gridDim.x * kWavesPerBlock * kRowsPerWave;
-    int base = wave * kRowsPerWave;   // wave-uniform first row of this wave
+    const int wave = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+    const int units = gridDim.x * kWavesPerBlock * kGroupsPerWave;   // row groups in the grid
+    const int unit = wave * kGroupsPerWave + grp;
+    const uint4* xv = reinterpret_cast<const uint4*>(x);
+    const uint4* pv = reinterpret_cast<const uint4*>(packed);
 
-    uint4 wcur[CPL];
-    uint32_t ecur[CPL];
-    load_row<G, CPL>(packed, scales, base + grp, n, kc, gl, wcur, ecur);
-
-    for (int i = threadIdx.x; i < kc * 4; i += kThreads) xs[i] = reinterpret_cast<const uint4*>(x)[i];
-    __syncthreads();
     uint32_t xr[CPL][16];
 #pragma unroll
     for (int ci = 0; ci < CPL; ++ci) {
-        const int c = gl + G * ci;
+        const int c = min(gl + G * ci, kc - 1);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const uint4 v = (c < kc) ? xs[c * 4 + q] : make_uint4(0u, 0u, 0u, 0u);
+            const uint4 v = xv[c * 4 + q];
             xr[ci][4 * q + 0] = v.x;
             xr[ci][4 * q + 1] = v.y;
             xr[ci][4 * q + 2] = v.z;
             xr[ci][4 * q + 3] = v.w;
         }
     }
-
-    for (; base < n; base += row_stride) {
-        uint4 wnxt[CPL];
-        uint32_t enxt[CPL];
-        load_row<G, CPL>(packed, scales, base + row_stride + grp, n, kc, gl, wnxt, enxt);
-        float acc = 0.f;
+    // wave-uniform pass count: passes while the wave's first group has rows
+    for (int pass = 0; (pass * units + wave * kGroupsPerWave) * R < n; ++pass) {
+        const int row0 = (pass * units + unit) * R;
+        uint4 w[R][CPL];
+        uint32_t e[R][CPL];
 #pragma unroll
-        for (int ci = 0; ci < CPL; ++ci) acc = block_dot(wcur[ci], e8m0_as_f32(ecur[ci]), xr[ci], acc);
-        acc = group_sum<G>(acc);
-        const int row = base + grp;
-        if (gl == 0 && row < n) store_out<kBf16Out>(y, row, acc);
+        for (int r = 0; r < R; ++r)
 #pragma unroll
-        for (int ci = 0; ci < CPL; ++ci) {
-            wcur[ci] = wnxt[ci];
-            ecur[ci] = enxt[ci];
+            for (int ci = 0; ci < CPL; ++ci) {
+                const int64_t blk = (int64_t)min(row0 + r, n - 1) * kc + min(gl + G * ci, kc - 1);
+                w[r][ci] = load_nt16(pv + blk);
+                e[r][ci] = scales[blk];
+            }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            float acc = 0.f;
+#pragma unroll
+            for (int ci = 0; ci < CPL; ++ci) {
+                const uint4 wv = (gl + G * ci < kc) ? w[r][ci] : make_uint4(0u, 0u, 0u, 0u);
+                acc = block_dot(wv, e8m0_scale(e[r][ci]), xr[ci], acc);
+            }
+            acc = group_total<G>(acc);
+            if (gl == G - 1 && row0 + r < n) store_out<kBf16Out>(y, row0 + r, acc);
         }
     }
 }
@@ -150,7 +160,7 @@ __global__ __launch_bounds__(kThreads) void gemv_generic_kernel(
         for (int c = lane; c < kc; c += kWave) {
             const int64_t blk = (int64_t)row * kc + c;
             const uint4 w = load_nt16(reinterpret_cast<const uint4*>(packed) + blk);
-            const float s = e8m0_as_f32(scales[blk]);
+            const float s = e8m0_scale(scales[blk]);
             uint32_t wd[16];
             const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
@@ -195,20 +205,33 @@ int resident_blocks(Kernel kernel, size_t lds_bytes) {
     return per_cu * device_cu_count();
 }
 
-template <int G, int CPL, bool kBf16Out>
-hipError_t run_b1(const uint8_t* packed, const uint8_t* scales, const uint16_t* x, void* y,
-                  int n, int kc, hipStream_t stream) {
-    auto kernel = gemv_b1_kernel<G, CPL, kBf16Out>;
-    const size_t lds = (size_t)kc * 64;
-    const int rows_per_block = kWavesPerBlock * (kWave / G);
+template <int G, int CPL, int R, bool kBf16Out>
+hipError_t run_b1_r(const uint8_t* packed, const uint8_t* scales, const uint16_t* x, void* y, int n,
+                    int kc, int cap, hipStream_t stream) {
+    const int rows_per_block = kWavesPerBlock * (kWave / G) * R;
     const int want = (n + rows_per_block - 1) / rows_per_block;
-    // Residency with the most LDS this instantiation can ask for (kc <= G*CPL);
-    // cached per instantiation, the same on every gfx950 device.
-    static int cap = 0;
-    if (cap == 0) cap = resident_blocks(kernel, (size_t)64 * G * CPL);
     const int grid = want < cap ? want : cap;
-    kernel<<<grid, kThreads, lds, stream>>>(packed, scales, x, y, n, kc);
+    gemv_b1_kernel<G, CPL, R, kBf16Out><<<grid, kThreads, 0, stream>>>(packed, scales, x, y, n, kc);
     return hipGetLastError();
+}
+
+// Rows per group and pass: the fewest (1, 2 or 4) that let every row group of
+// one resident wave generation finish the matrix in a single pass.
+template <int G, int CPL, bool kBf16Out>
+hipError_t run_b1(const uint8_t* packed, const uint8_t* scales, const uint16_t* x, void* y, int n,
+                  int kc, hipStream_t stream) {
+    static int cap1 = 0, cap2 = 0, cap4 = 0;   // resident blocks per R, same on every gfx950
+    if (cap1 == 0) {
+        cap1 = resident_blocks(gemv_b1_kernel<G, CPL, 1, kBf16Out>, 0);
+        cap2 = resident_blocks(gemv_b1_kernel<G, CPL, 2, kBf16Out>, 0);
+        cap4 = resident_blocks(gemv_b1_kernel<G, CPL, 4, kBf16Out>, 0);
+    }
+    const int groups_per_block = kWavesPerBlock * (kWave / G);
+    if ((int64_t)cap1 * groups_per_block >= n)
+        return run_b1_r<G, CPL, 1, kBf16Out>(packed, scales, x, y, n, kc, cap1, stream);
+    if ((int64_t)cap2 * groups_per_block * 2 >= n || CPL > 4)
+        return run_b1_r<G, CPL, 2, kBf16Out>(packed, scales, x, y, n, kc, cap2, stream);
+    return run_b1_r<G, CPL, 4, kBf16Out>(packed, scales, x, y, n, kc, cap4, stream);
 }
 
 template <bool kBf16Out>

@@ -6,13 +6,19 @@
 // scale is the only multiply and is applied once, after the row sum.
 //
 // gfx950 design. The page's CPU kernel extracts +1/-1 lane masks with BMI2
-// pext so that AVX-512 masked adds can use them; a GPU has no pext, but it
-// does not need one: each lane owns fixed 64-column chunks of K (one 16-byte
-// load = four words), keeps those 64 activations in registers for the whole
-// kernel (staged once per workgroup through LDS), and tests the two bits of
-// each field directly to add, subtract or skip. Lanes cover a row in groups
-// (64 lanes for K >= 4096, fewer for short rows); the row total comes from a
-// DPP / shuffle reduction and is multiplied by the row scale once.
+// pext so that AVX-512 masked adds can use them. A GPU has no pext and a
+// per-field compare-and-select costs about six VALU operations per weight, so
+// the fast kernel decodes two fields at a time instead: a rotate and a mask
+// turn them into a v_perm_b32 selector that looks up bf16 +0.5 / -0.5 / 0,
+// and v_dot2_f32_bf16 accumulates the pair against x held as bf16 hi + lo
+// parts (x = hi + lo to a relative 2^-18), about 2.5 operations per weight;
+// the exact factor 2 goes into the row scale. Each lane owns one 64-column
+// chunk of K (one 16-byte load of four words) with its x pairs in registers;
+// lanes cover a row in groups (64 lanes for K = 4096, fewer for short rows),
+// the row total comes from a DPP-only reduction and is multiplied by the row
+// scale once. Inputs the fast kernel cannot take (K % 64 != 0, K > 4096,
+// unaligned pointers) use a one-wave-per-row kernel that adds, subtracts or
+// skips each x directly.
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -22,7 +28,23 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWavesPerBlock = kThreads / kWave;
 
-// Add / subtract / skip for the 16 fields of one word against 16 activations.
+// Row total of groups of G lanes (G in {8, 16, 32, 64}) with DPP only: the
+// total ends up in the last lane of each group.
+template <int G>
+__device__ __forceinline__ float group_total(float v) {
+    v += dpp_f32<0xB1>(v);
+    v += dpp_f32<0x4E>(v);
+    v += dpp_f32<0x141>(v);
+    if constexpr (G >= 16) v += dpp_f32<0x140>(v);
+    if constexpr (G >= 32)
+        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));
+    if constexpr (G >= 64)
+        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xC, 0xF, false));
+    return v;
+}
+
+// Add / subtract / skip for the 16 fields of one word against 16 activations
+// (the slower kernel for unaligned or ragged inputs).
 __device__ __forceinline__ float ternary_word(uint32_t w, const float* xv, float acc) {
     float a0 = 0.f, a1 = 0.f;
 #pragma unroll
@@ -35,53 +57,104 @@ __device__ __forceinline__ float ternary_word(uint32_t w, const float* xv, float
     return acc + (a0 + a1);
 }
 
-// Fast path: K % 64 == 0, rows 16-byte aligned, K <= 64 * G * CPL.
-template <int G, int CPL>
+// Weight pairs for v_dot2_f32_bf16. Fields p and p + 8 of a word (bits 2p,
+// 2p+1 and 2p+16, 2p+17) are rotated to bits 8-9 and 24-25 and masked; the
+// result is a v_perm_b32 selector that picks, from a 4-byte pool, the high
+// byte of bf16 -0.5 (field 01), +0.5 (field 10) or 0 (fields 00 and 11), and
+// 0x00 for the low bytes (selector byte 0 -> pool byte 0 = 0x00). One rotate,
+// one mask and one perm give two weights as a bf16 pair of +/-0.5 or 0; the
+// factor 2 is applied exactly with the row scale.
+constexpr uint32_t kHalfPool = 0x003FBF00u;   // pool bytes: 00, BF (-0.5), 3F (+0.5), 00
+
+template <int P>
+__device__ __forceinline__ uint32_t ternary_pair(uint32_t w) {
+    constexpr int kRotl = 8 - 2 * P;                     // bring bits 2P.. to bit 8
+    const uint32_t r = kRotl == 0 ? w : __builtin_amdgcn_alignbit(w, w, (32 - kRotl) & 31);
+    return __builtin_amdgcn_perm(0u, kHalfPool, r & 0x03000300u);
+}
+
+// x prepared for the pairs of one word: for pair P, the low half is x[P] and
+// the high half x[P + 8], each as bf16 hi + bf16 lo (x = hi + lo to 2^-18).
+struct XPairs {
+    uint32_t hi[8], lo[8];
+};
+
+__device__ __forceinline__ uint32_t bf16_bits_rne(float f) { return f32_to_bf16_rne(f); }
+
+__device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi, uint32_t& lo) {
+    const uint32_t ah = bf16_bits_rne(a), bh = bf16_bits_rne(b);
+    const float ar = a - __uint_as_float(ah << 16), br = b - __uint_as_float(bh << 16);
+    hi = ah | (bh << 16);
+    lo = bf16_bits_rne(ar) | (bf16_bits_rne(br) << 16);
+}
+
+__device__ __forceinline__ float ternary_word_dot(uint32_t w, const XPairs& xp, float acc) {
+    float a0 = acc, a1 = 0.f;
+#define E2M1_TPAIR(P)                                         \
+    {                                                         \
+        const uint32_t wp = ternary_pair<P>(w);               \
+        a0 = dot2_bf16(wp, xp.hi[P], a0);                     \
+        a1 = dot2_bf16(wp, xp.lo[P], a1);                     \
+    }
+    E2M1_TPAIR(0) E2M1_TPAIR(1) E2M1_TPAIR(2) E2M1_TPAIR(3)
+    E2M1_TPAIR(4) E2M1_TPAIR(5) E2M1_TPAIR(6) E2M1_TPAIR(7)
+#undef E2M1_TPAIR
+    return a0 + a1;
+}
+
+// Fast path: K % 64 == 0, packed and x 16-byte aligned, K <= 64 * G. A group
+// of G lanes covers one row; lane gl owns the 64-column chunk gl (one 16-byte
+// load of 4 words) for every row, with its x pairs in registers. R rows per
+// group and pass; all loads unconditional (clamped, masked at use).
+template <int G, int R>
 __global__ __launch_bounds__(kThreads) void ternary_kernel(const uint32_t* __restrict__ packed,
                                                            const float* __restrict__ row_scale,
                                                            const float* __restrict__ x,
                                                            float* __restrict__ y, int n, int kq) {
-    extern __shared__ float4 xs4[];   // kq * 16 float4 = all of x
-    constexpr int kRowsPerWave = kWave / G;
+    constexpr int kGroupsPerWave = kWave / G;
     const int lane = threadIdx.x & (kWave - 1);
     const int gl = lane & (G - 1);
     const int grp = lane / G;
     const int wave = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
-    const int row_stride = gridDim.x * kWavesPerBlock * kRowsPerWave;
-    const uint4* pk = reinterpret_cast<const uint4*>(packed);
+    const int units = gridDim.x * kWavesPerBlock * kGroupsPerWave;
+    const int unit = wave * kGroupsPerWave + grp;
+    const int c = min(gl, kq - 1);
+    const bool cvalid = gl < kq;
 
-    for (int i = threadIdx.x; i < kq * 16; i += kThreads) xs4[i] = reinterpret_cast<const float4*>(x)[i];
-    __syncthreads();
-    float xr[CPL][64];
-#pragma unroll
-    for (int ci = 0; ci < CPL; ++ci) {
-        const int c = gl + G * ci;
+    XPairs xp[4];
+    {
+        const float4* xv = reinterpret_cast<const float4*>(x) + c * 16;
+        float xs[64];
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
-            const float4 v = (c < kq) ? xs4[c * 16 + q] : make_float4(0.f, 0.f, 0.f, 0.f);
-            xr[ci][4 * q + 0] = v.x;
-            xr[ci][4 * q + 1] = v.y;
-            xr[ci][4 * q + 2] = v.z;
-            xr[ci][4 * q + 3] = v.w;
+            const float4 v = xv[q];
+            xs[4 * q + 0] = v.x;
+            xs[4 * q + 1] = v.y;
+            xs[4 * q + 2] = v.z;
+            xs[4 * q + 3] = v.w;
         }
-    }
-
-    for (int base = wave * kRowsPerWave; base < n; base += row_stride) {
-        const int row = base + grp;
-        float acc = 0.f;
 #pragma unroll
-        for (int ci = 0; ci < CPL; ++ci) {
-            const int c = gl + G * ci;
-            if (row < n && c < kq) {
-                const uint4 w = load_nt16(pk + (int64_t)row * kq + c);
-                acc = ternary_word(w.x, xr[ci] + 0, acc);
-                acc = ternary_word(w.y, xr[ci] + 16, acc);
-                acc = ternary_word(w.z, xr[ci] + 32, acc);
-                acc = ternary_word(w.w, xr[ci] + 48, acc);
-            }
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int p = 0; p < 8; ++p) split_pair(xs[16 * q + p], xs[16 * q + p + 8], xp[q].hi[p], xp[q].lo[p]);
+    }
+    const uint4* pk = reinterpret_cast<const uint4*>(packed);
+    for (int pass = 0; (pass * units + wave * kGroupsPerWave) * R < n; ++pass) {
+        const int row0 = (pass * units + unit) * R;
+        uint4 w[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) w[r] = load_nt16(pk + (int64_t)min(row0 + r, n - 1) * kq + c);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const uint4 wv = cvalid ? w[r] : make_uint4(0u, 0u, 0u, 0u);
+            float acc = ternary_word_dot(wv.x, xp[0], 0.f);
+            acc = ternary_word_dot(wv.y, xp[1], acc);
+            acc = ternary_word_dot(wv.z, xp[2], acc);
+            acc = ternary_word_dot(wv.w, xp[3], acc);
+            acc = group_total<G>(acc);
+            const int row = row0 + r;
+            if (gl == G - 1 && row < n) y[row] = row_scale[row] * (2.0f * acc);
         }
-        acc = group_sum<G>(acc);
-        if (gl == 0 && row < n) y[row] = row_scale[row] * acc;
     }
 }
 
@@ -109,18 +182,27 @@ int resident_blocks(Kernel kernel, size_t lds_bytes) {
     return per_cu * device_cu_count();
 }
 
-template <int G, int CPL>
-hipError_t run_fast(const uint32_t* packed, const float* s, const float* x, float* y, int n,
-                    int kq, hipStream_t stream) {
-    auto kernel = ternary_kernel<G, CPL>;
-    const size_t lds = (size_t)kq * 256;
-    const int rows_per_block = kWavesPerBlock * (kWave / G);
+template <int G, int R>
+hipError_t run_fast_r(const uint32_t* packed, const float* s, const float* x, float* y, int n,
+                      int kq, int cap, hipStream_t stream) {
+    const int rows_per_block = kWavesPerBlock * (kWave / G) * R;
     const int want = (n + rows_per_block - 1) / rows_per_block;
-    static int cap = 0;
-    if (cap == 0) cap = resident_blocks(kernel, (size_t)256 * G * CPL);
     const int grid = want < cap ? want : cap;
-    kernel<<<grid, kThreads, lds, stream>>>(packed, s, x, y, n, kq);
+    ternary_kernel<G, R><<<grid, kThreads, 0, stream>>>(packed, s, x, y, n, kq);
     return hipGetLastError();
+}
+
+template <int G>
+hipError_t run_fast(const uint32_t* packed, const float* s, const float* x, float* y, int n, int kq,
+                    hipStream_t stream) {
+    static int cap1 = 0, cap2 = 0;
+    if (cap1 == 0) {
+        cap1 = resident_blocks(ternary_kernel<G, 1>, 0);
+        cap2 = resident_blocks(ternary_kernel<G, 2>, 0);
+    }
+    if ((int64_t)cap1 * kWavesPerBlock * (kWave / G) >= n)
+        return run_fast_r<G, 1>(packed, s, x, y, n, kq, cap1, stream);
+    return run_fast_r<G, 2>(packed, s, x, y, n, kq, cap2, stream);
 }
 
 }  // namespace
@@ -130,13 +212,12 @@ hipError_t launch_ternary(const uint32_t* packed, const float* row_scale, const 
     const int nn = (int)n;
     const bool aligned = (reinterpret_cast<uintptr_t>(packed) & 15u) == 0 &&
                          (reinterpret_cast<uintptr_t>(x) & 15u) == 0 && k % 64 == 0;
-    if (aligned && k <= 64 * 64 * 2) {
+    if (aligned && k <= 64 * 64) {
         const int kq = (int)(k / 64);
-        if (kq <= 8) return run_fast<8, 1>(packed, row_scale, x, y, nn, kq, stream);
-        if (kq <= 16) return run_fast<16, 1>(packed, row_scale, x, y, nn, kq, stream);
-        if (kq <= 32) return run_fast<32, 1>(packed, row_scale, x, y, nn, kq, stream);
-        if (kq <= 64) return run_fast<64, 1>(packed, row_scale, x, y, nn, kq, stream);
-        return run_fast<64, 2>(packed, row_scale, x, y, nn, kq, stream);
+        if (kq <= 8) return run_fast<8>(packed, row_scale, x, y, nn, kq, stream);
+        if (kq <= 16) return run_fast<16>(packed, row_scale, x, y, nn, kq, stream);
+        if (kq <= 32) return run_fast<32>(packed, row_scale, x, y, nn, kq, stream);
+        return run_fast<64>(packed, row_scale, x, y, nn, kq, stream);
     }
     const int want = (nn + kWavesPerBlock - 1) / kWavesPerBlock;
     static int cap = 0;

@@ -64,6 +64,9 @@ extern "C" {
 /* Largest batch dequant_gemv accepts. */
 #define E2M1_GEMV_MAX_BATCH 16
 
+/* Most experts mxfp4_moe_gemm accepts. */
+#define E2M1_MOE_MAX_EXPERTS 512
+
 /* ABI version of the loaded library (E2M1LUT_ABI_VERSION it was built with). */
 int e2m1_abi_version(void);
 
@@ -177,9 +180,10 @@ size_t mxfp4_moe_workspace_size(int64_t tokens, int64_t hidden, int64_t inter, i
  *   out            uint16 [tokens, hidden]  bf16, overwritten
  *   workspace      device buffer of at least mxfp4_moe_workspace_size()
  *                  bytes, 256-byte aligned; contents need no initialisation
- * Requires hidden % 32 == 0, inter % 32 == 0, experts >= 1, topk >= 1,
- * tokens >= 0. Ids outside [0, experts) are not checked on the host (they
- * live on the device); the kernels skip such slots.
+ * Requires hidden % 32 == 0, inter % 32 == 0, 1 <= experts <=
+ * E2M1_MOE_MAX_EXPERTS, topk >= 1, tokens >= 0, tokens * topk <= INT_MAX.
+ * Ids outside [0, experts) are not checked on the host (they live on the
+ * device); the kernels skip such slots (they contribute nothing).
  */
 int mxfp4_moe_gemm(const uint16_t* x, const uint8_t* w13, const uint8_t* w13_scale,
                    const uint8_t* w2, const uint8_t* w2_scale, const int32_t* topk_ids,

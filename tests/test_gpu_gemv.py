@@ -72,8 +72,9 @@ def test_zero_codes_give_exact_zero(gpu):
     r = np.random.default_rng(3)
     zb = np.array(golden_ints("mxfp4_zero_codes.txt", "zero_bytes"), dtype=np.uint8)
     packed = r.choice(zb, size=(128, 2048))
-    scales = r.integers(2, 253, size=(128, 128), dtype=np.uint8)
-    for batch in (1, 4):
+    scales = r.integers(0, 256, size=(128, 128), dtype=np.uint8)   # every exponent, 255 included
+    scales[:, :2] = [0, 255]
+    for batch in (1, 4, 16):
         y = gpu.dequant_gemv(u8(packed), u8(scales), bf16(synth.bf16_normal(r, (batch, 4096))))
         assert (host_f32(y) == 0).all()
 
