@@ -35,12 +35,18 @@ __device__ __forceinline__ void dequant_word(uint32_t w, float eff, uint32_t* ou
     out[3] = pack_bf16x2(v3.x * eff, v3.y * eff);
 }
 
-// One thread per packed word (8 channels, half of a 16-channel scale group):
-// a 4-byte load, the group's E4M3 byte, one 16-byte store. A block covers
+// One thread per packed word (8 channels, half of a 16-channel scale group)
+// and token row, kRows rows per thread: a 4-byte load, the group's E4M3 byte
+// and one 16-byte store per row. A block covers kRows groups of
 // `rows_per_block` token rows with `tpr` threads each (tpr a power of two) or,
-// for long rows, one row in `blocks_per_row` consecutive blocks; consecutive
-// lanes read consecutive words of a row and write one contiguous kilobyte per
-// wave-wide store.
+// for long rows, a row segment of `tpr` words in each of `blocks_per_row`
+// consecutive blocks. Consecutive lanes read consecutive words of a row and
+// write one contiguous kilobyte per wave-wide store. Every id, code word and
+// scale of a thread's rows is requested (indices clamped into range) before
+// any of them is used, so the dependent id -> row loads of different rows
+// overlap.
+constexpr int kRows = 4;
+
 __global__ __launch_bounds__(kThreads) void gather_kernel(
     const uint32_t* __restrict__ table, const uint8_t* __restrict__ block_scale,
     const float* __restrict__ global_scale, const int64_t* __restrict__ ids,
@@ -50,25 +56,40 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(
     const int tpr = 1 << tpr_log2;
     const int rows_per_block = kThreads >> tpr_log2;
     const int sub = threadIdx.x & (tpr - 1);
-    const int64_t groups = (ntok + rows_per_block - 1) / rows_per_block;
+    const int64_t rows_per_iter = (int64_t)rows_per_block * kRows;
+    const int64_t groups = (ntok + rows_per_iter - 1) / rows_per_iter;
     for (int64_t b = blockIdx.x; b < groups * blocks_per_row; b += gridDim.x) {
         const int64_t rg = b / blocks_per_row;
         const int64_t part = b - rg * blocks_per_row;
-        const int64_t t = rg * rows_per_block + (threadIdx.x >> tpr_log2);
         const int64_t c = part * tpr + sub;
-        if (t >= ntok || c >= wpr) continue;
-        const int64_t id = ids[t];
-        uint4* o = out + t * wpr + c;
-        if (id < 0 || id >= vocab) {
-            *o = make_uint4(0u, 0u, 0u, 0u);
-            if (err_flag != nullptr) *err_flag = 1;
-            continue;
+        const int64_t cc = c < wpr ? c : wpr - 1;
+        int64_t t[kRows], id[kRows];
+#pragma unroll
+        for (int i = 0; i < kRows; ++i) {
+            t[i] = rg * rows_per_iter + (int64_t)i * rows_per_block + (threadIdx.x >> tpr_log2);
+            id[i] = ids[t[i] < ntok ? t[i] : ntok - 1];
         }
-        const uint32_t p = __builtin_nontemporal_load(table + id * wpr + c);
-        const float eff = e4m3_to_f32(block_scale[id * (wpr / 2) + (c >> 1)]) * g;
-        uint32_t w[4];
-        dequant_word(p, eff, w);
-        store_nt16(o, w[0], w[1], w[2], w[3]);
+        uint32_t p[kRows];
+        uint32_t sb[kRows];
+#pragma unroll
+        for (int i = 0; i < kRows; ++i) {
+            const int64_t r = (id[i] >= 0 && id[i] < vocab) ? id[i] : 0;
+            p[i] = __builtin_nontemporal_load(table + r * wpr + cc);
+            sb[i] = block_scale[r * (wpr / 2) + (cc >> 1)];
+        }
+#pragma unroll
+        for (int i = 0; i < kRows; ++i) {
+            if (t[i] >= ntok || c >= wpr) continue;
+            uint4* o = out + t[i] * wpr + c;
+            if (id[i] < 0 || id[i] >= vocab) {
+                *o = make_uint4(0u, 0u, 0u, 0u);
+                if (err_flag != nullptr) *err_flag = 1;
+                continue;
+            }
+            uint32_t w[4];
+            dequant_word(p[i], e4m3_to_f32(sb[i]) * g, w);
+            store_nt16(o, w[0], w[1], w[2], w[3]);
+        }
     }
 }
 
@@ -84,7 +105,8 @@ hipError_t launch_nvfp4_gather(const uint8_t* table, const uint8_t* block_scale,
     const int tpr = 1 << tpr_log2;
     const int64_t blocks_per_row = (wpr + tpr - 1) / tpr;
     const int rows_per_block = kThreads / tpr;
-    const int64_t blocks = (ntok + rows_per_block - 1) / rows_per_block * blocks_per_row;
+    const int64_t blocks = (ntok + (int64_t)rows_per_block * kRows - 1) / ((int64_t)rows_per_block * kRows) *
+                           blocks_per_row;
     const int64_t cap = (int64_t)device_cu_count() * 64;
     const int grid = (int)(blocks < cap ? blocks : cap);
     gather_kernel<<<grid, kThreads, 0, stream>>>(reinterpret_cast<const uint32_t*>(table), block_scale,

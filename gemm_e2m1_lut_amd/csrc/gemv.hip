@@ -144,6 +144,63 @@ __global__ __launch_bounds__(kThreads) void gemv_b1_kernel(const uint8_t* __rest
     }
 }
 
+// Batch 1, long rows (K > 8192). Holding all of a row's x slice per wave
+// would make every wave pull the whole of x through its compute unit, more
+// bytes than the weights it streams. Here the WR waves of a workgroup split
+// K: lane l of wave w owns the single chunk 64 w + l (16 x registers), the
+// workgroup takes RB consecutive rows per pass, every wave reduces its part
+// of each row with DPP, and the WR partial sums meet in LDS.
+template <int WR, int RB, bool kBf16Out>
+__global__ __launch_bounds__(kWave * WR) void gemv_b1_slab_kernel(const uint8_t* __restrict__ packed,
+                                                                  const uint8_t* __restrict__ scales,
+                                                                  const uint16_t* __restrict__ x,
+                                                                  void* __restrict__ y, int n, int kc) {
+    __shared__ float part[RB][WR];
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wig = tid / kWave;
+    const int c_raw = wig * kWave + lane;
+    const bool cvalid = c_raw < kc;
+    const int c = min(c_raw, kc - 1);
+    const uint4* pv = reinterpret_cast<const uint4*>(packed);
+    uint32_t xr[16];
+    {
+        const uint4* xv = reinterpret_cast<const uint4*>(x) + c * 4;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint4 v = xv[q];
+            xr[4 * q + 0] = v.x;
+            xr[4 * q + 1] = v.y;
+            xr[4 * q + 2] = v.z;
+            xr[4 * q + 3] = v.w;
+        }
+    }
+    for (int rb = blockIdx.x * RB; rb < n; rb += gridDim.x * RB) {   // workgroup-uniform
+        uint4 w[RB];
+        uint32_t e[RB];
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+            const int64_t blk = (int64_t)min(rb + i, n - 1) * kc + c;
+            w[i] = load_nt16(pv + blk);
+            e[i] = scales[blk];
+        }
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+            const uint4 wv = cvalid ? w[i] : make_uint4(0u, 0u, 0u, 0u);
+            const float acc = group_total<kWave>(block_dot(wv, e8m0_scale(e[i]), xr, 0.f));
+            if (lane == kWave - 1) part[i][wig] = acc;
+        }
+        __syncthreads();
+        if (tid < RB && rb + tid < n) {
+            float s = 0.f;
+#pragma unroll
+            for (int w2 = 0; w2 < WR; ++w2) s += part[tid][w2];
+            store_out<kBf16Out>(y, rb + tid, s);
+        }
+        __syncthreads();
+    }
+}
+
 // --------------------------------------------------------- any batch ----
 
 template <int B, bool kBf16Out>
@@ -197,9 +254,9 @@ __global__ __launch_bounds__(kThreads) void gemv_generic_kernel(
 // ------------------------------------------------------------- launch ----
 
 template <typename Kernel>
-int resident_blocks(Kernel kernel, size_t lds_bytes) {
+int resident_blocks(Kernel kernel, size_t lds_bytes, int threads = kThreads) {
     int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, lds_bytes) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, lds_bytes) != hipSuccess ||
         per_cu < 1)
         per_cu = 1;
     return per_cu * device_cu_count();
@@ -234,9 +291,50 @@ hipError_t run_b1(const uint8_t* packed, const uint8_t* scales, const uint16_t* 
     return run_b1_r<G, CPL, 4, kBf16Out>(packed, scales, x, y, n, kc, cap4, stream);
 }
 
+template <int WR, int RB, bool kBf16Out>
+hipError_t run_slab_r(const uint8_t* packed, const uint8_t* scales, const uint16_t* x, void* y, int n,
+                      int kc, int cap, hipStream_t stream) {
+    const int want = (n + RB - 1) / RB;
+    const int grid = want < cap ? want : cap;
+    gemv_b1_slab_kernel<WR, RB, kBf16Out><<<grid, kWave * WR, 0, stream>>>(packed, scales, x, y, n, kc);
+    return hipGetLastError();
+}
+
+// Rows per workgroup pass: the fewest (2, 4 or 8) that cover the matrix with
+// one resident generation of workgroups.
+template <int WR, bool kBf16Out>
+hipError_t run_slab(const uint8_t* packed, const uint8_t* scales, const uint16_t* x, void* y, int n,
+                    int kc, hipStream_t stream) {
+    static int cap2 = 0, cap4 = 0, cap8 = 0;
+    if (cap2 == 0) {
+        cap2 = resident_blocks(gemv_b1_slab_kernel<WR, 2, kBf16Out>, 0, kWave * WR);
+        cap4 = resident_blocks(gemv_b1_slab_kernel<WR, 4, kBf16Out>, 0, kWave * WR);
+        cap8 = resident_blocks(gemv_b1_slab_kernel<WR, 8, kBf16Out>, 0, kWave * WR);
+    }
+    if ((int64_t)cap2 * 2 >= n) return run_slab_r<WR, 2, kBf16Out>(packed, scales, x, y, n, kc, cap2, stream);
+    if ((int64_t)cap4 * 4 >= n) return run_slab_r<WR, 4, kBf16Out>(packed, scales, x, y, n, kc, cap4, stream);
+    return run_slab_r<WR, 8, kBf16Out>(packed, scales, x, y, n, kc, cap8, stream);
+}
+
 template <bool kBf16Out>
 hipError_t dispatch_b1(const uint8_t* packed, const uint8_t* scales, const uint16_t* x, void* y,
                        int n, int kc, hipStream_t stream) {
+    if (kc > 4 * kWave) {
+        switch ((kc + kWave - 1) / kWave) {
+            case 5: return run_slab<5, kBf16Out>(packed, scales, x, y, n, kc, stream);
+            case 6: return run_slab<6, kBf16Out>(packed, scales, x, y, n, kc, stream);
+            case 7: return run_slab<7, kBf16Out>(packed, scales, x, y, n, kc, stream);
+            case 8: return run_slab<8, kBf16Out>(packed, scales, x, y, n, kc, stream);
+            case 9: return run_slab<9, kBf16Out>(packed, scales, x, y, n, kc, stream);
+            case 10: return run_slab<10, kBf16Out>(packed, scales, x, y, n, kc, stream);
+            case 11: return run_slab<11, kBf16Out>(packed, scales, x, y, n, kc, stream);
+            case 12: return run_slab<12, kBf16Out>(packed, scales, x, y, n, kc, stream);
+            case 13: return run_slab<13, kBf16Out>(packed, scales, x, y, n, kc, stream);
+            case 14: return run_slab<14, kBf16Out>(packed, scales, x, y, n, kc, stream);
+            case 15: return run_slab<15, kBf16Out>(packed, scales, x, y, n, kc, stream);
+            default: return run_slab<16, kBf16Out>(packed, scales, x, y, n, kc, stream);
+        }
+    }
     if (kc <= 8) return run_b1<8, 1, kBf16Out>(packed, scales, x, y, n, kc, stream);
     if (kc <= 16) return run_b1<16, 1, kBf16Out>(packed, scales, x, y, n, kc, stream);
     if (kc <= 32) return run_b1<32, 1, kBf16Out>(packed, scales, x, y, n, kc, stream);
@@ -244,11 +342,7 @@ hipError_t dispatch_b1(const uint8_t* packed, const uint8_t* scales, const uint1
         case 1: return run_b1<64, 1, kBf16Out>(packed, scales, x, y, n, kc, stream);
         case 2: return run_b1<64, 2, kBf16Out>(packed, scales, x, y, n, kc, stream);
         case 3: return run_b1<64, 3, kBf16Out>(packed, scales, x, y, n, kc, stream);
-        case 4: return run_b1<64, 4, kBf16Out>(packed, scales, x, y, n, kc, stream);
-        case 5: return run_b1<64, 5, kBf16Out>(packed, scales, x, y, n, kc, stream);
-        case 6: return run_b1<64, 6, kBf16Out>(packed, scales, x, y, n, kc, stream);
-        case 7: return run_b1<64, 7, kBf16Out>(packed, scales, x, y, n, kc, stream);
-        default: return run_b1<64, 8, kBf16Out>(packed, scales, x, y, n, kc, stream);
+        default: return run_b1<64, 4, kBf16Out>(packed, scales, x, y, n, kc, stream);
     }
 }
 
@@ -281,8 +375,9 @@ hipError_t dispatch_generic(int batch, const uint8_t* packed, const uint8_t* sca
 
 }  // namespace
 
-// Largest K the batch-1 kernel keeps in registers (8 chunks of 32 per lane).
-constexpr int64_t kB1MaxK = 64 * 8 * 32;
+// Largest K of the batch-1 kernels: 16 waves of 64 lanes, one 32-column chunk
+// per lane (the register-resident kernel stops at 4 chunks per lane, K = 8192).
+constexpr int64_t kB1MaxK = 16 * 64 * 32;
 
 hipError_t launch_gemv(const uint8_t* packed, const uint8_t* scales, const uint16_t* x, void* y,
                        bool out_bf16, int batch, int64_t n, int64_t k, hipStream_t stream) {

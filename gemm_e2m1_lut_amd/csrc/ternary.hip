@@ -11,7 +11,7 @@
 // the fast kernel decodes two fields at a time instead: a rotate and a mask
 // turn them into a v_perm_b32 selector that looks up bf16 +0.5 / -0.5 / 0,
 // and v_dot2_f32_bf16 accumulates the pair against x held as bf16 hi + lo
-// parts (x = hi + lo to a relative 2^-18), about 2.5 operations per weight;
+// parts (x = hi + lo to a relative 2^-16), about 2.5 operations per weight;
 // the exact factor 2 goes into the row scale. Each lane owns one 64-column
 // chunk of K (one 16-byte load of four words) with its x pairs in registers;
 // lanes cover a row in groups (64 lanes for K = 4096, fewer for short rows),
@@ -74,18 +74,20 @@ __device__ __forceinline__ uint32_t ternary_pair(uint32_t w) {
 }
 
 // x prepared for the pairs of one word: for pair P, the low half is x[P] and
-// the high half x[P + 8], each as bf16 hi + bf16 lo (x = hi + lo to 2^-18).
+// the high half x[P + 8], each as bf16 hi + bf16 lo (x = hi + lo to 2^-16).
 struct XPairs {
     uint32_t hi[8], lo[8];
 };
 
-__device__ __forceinline__ uint32_t bf16_bits_rne(float f) { return f32_to_bf16_rne(f); }
-
+// x = hi + lo exactly with hi = x truncated to bf16 (the top 16 bits); lo is
+// then rounded to bf16 (round to nearest even), so hi + bf16(lo) matches x to
+// a relative 2^-16. One perm packs the two hi halves of a pair.
 __device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi, uint32_t& lo) {
-    const uint32_t ah = bf16_bits_rne(a), bh = bf16_bits_rne(b);
-    const float ar = a - __uint_as_float(ah << 16), br = b - __uint_as_float(bh << 16);
-    hi = ah | (bh << 16);
-    lo = bf16_bits_rne(ar) | (bf16_bits_rne(br) << 16);
+    const uint32_t ab = __float_as_uint(a), bb = __float_as_uint(b);
+    hi = __builtin_amdgcn_perm(bb, ab, 0x07060302u);   // {a.hi16, b.hi16}
+    const float ar = a - __uint_as_float(ab & 0xFFFF0000u);
+    const float br = b - __uint_as_float(bb & 0xFFFF0000u);
+    lo = f32_to_bf16_rne(ar) | (f32_to_bf16_rne(br) << 16);
 }
 
 __device__ __forceinline__ float ternary_word_dot(uint32_t w, const XPairs& xp, float acc) {
@@ -192,17 +194,25 @@ hipError_t run_fast_r(const uint32_t* packed, const float* s, const float* x, fl
     return hipGetLastError();
 }
 
+// Rows per group and pass: each group splits its x slice once (about as many
+// VALU operations as two rows of weights), so a group takes 4 rows while that
+// still leaves at least one wave per SIMD on every compute unit, else fewer.
 template <int G>
 hipError_t run_fast(const uint32_t* packed, const float* s, const float* x, float* y, int n, int kq,
                     hipStream_t stream) {
-    static int cap1 = 0, cap2 = 0;
+    static int cap1 = 0, cap2 = 0, cap4 = 0;
     if (cap1 == 0) {
         cap1 = resident_blocks(ternary_kernel<G, 1>, 0);
         cap2 = resident_blocks(ternary_kernel<G, 2>, 0);
+        cap4 = resident_blocks(ternary_kernel<G, 4>, 0);
     }
-    if ((int64_t)cap1 * kWavesPerBlock * (kWave / G) >= n)
-        return run_fast_r<G, 1>(packed, s, x, y, n, kq, cap1, stream);
-    return run_fast_r<G, 2>(packed, s, x, y, n, kq, cap2, stream);
+    const int64_t groups_per_block = kWavesPerBlock * (kWave / G);
+    const int64_t min_blocks = device_cu_count();   // one block (4 waves) per compute unit
+    if ((n + 4 * groups_per_block - 1) / (4 * groups_per_block) >= min_blocks)
+        return run_fast_r<G, 4>(packed, s, x, y, n, kq, cap4, stream);
+    if ((n + 2 * groups_per_block - 1) / (2 * groups_per_block) >= min_blocks || cap1 * groups_per_block < n)
+        return run_fast_r<G, 2>(packed, s, x, y, n, kq, cap2, stream);
+    return run_fast_r<G, 1>(packed, s, x, y, n, kq, cap1, stream);
 }
 
 }  // namespace
