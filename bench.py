@@ -43,11 +43,27 @@ CSRC = os.path.join(ROOT, "gemm_e2m1_lut_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
-def kernel_source_hash() -> str:
+# Source files each launch label is built from (plus the shared headers and the
+# C-ABI dispatch in api.hip): a counter summary stays valid only while these are
+# unchanged.
+KERNEL_SOURCES = {
+    "gemv": ["gemv.hip", "mfma_stream.hpp"],
+    "moe": ["moe.hip", "mfma_stream.hpp"],
+    "ternary": ["ternary.hip"],
+    "gather": ["gather.hip"],
+    "decode": ["decode.hip"],
+}
+COMMON_SOURCES = ["device.hpp", "kernels.hpp", "api.hip"]
+
+
+def kernel_source_hash(label: str) -> str:
+    family = label.split("_")[0]
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        with open(os.path.join(CSRC, name), "rb") as fh:
-            h.update(name.encode() + fh.read())
+    for name in sorted(KERNEL_SOURCES.get(family, []) + COMMON_SOURCES):
+        path = os.path.join(CSRC, name)
+        if os.path.exists(path):
+            with open(path, "rb") as fh:
+                h.update(name.encode() + fh.read())
     return h.hexdigest()[:16]
 
 
@@ -100,8 +116,7 @@ class GemvMLP(Workload):
         self.batch = batch
         self.name = f"llama8b_mlp_mxfp4_gemv_b{batch}"
         g = _gen(4242 + batch)
-        self.w_bytes = {f"gemv_{n}x{k}": n * k // 2 + n * k // 32 for n, k in self.SHAPES}
-        per_copy = sum(self.w_bytes.values())
+        per_copy = sum(n * k // 2 + n * k // 32 for n, k in self.SHAPES)
         self.copies = max(2, math.ceil(rotate_bytes / per_copy))
         self.weights = [[_mxfp4_dev(g, n, k) for n, k in self.SHAPES] for _ in range(self.copies)]
         self.x = [torch.randn((batch, k), generator=g, device="cuda").to(torch.bfloat16)
@@ -121,15 +136,15 @@ class GemvMLP(Workload):
             def fn(i, j=j):
                 p, s = self.weights[i % self.copies][j]
                 self.lib.dequant_gemv(p, s, self.x[j], out_dtype=self.y[j].dtype, out=self.y[j])
-            out.append((f"gemv_{n}x{k}", fn))
+            out.append((f"gemv_b{self.batch}_{n}x{k}", fn))
         return out
 
     def alg_bytes(self, label):
-        n, k = (int(v) for v in label.split("_")[1].split("x"))
+        n, k = (int(v) for v in label.split("_")[2].split("x"))
         return n * k // 2 + n * k // 32 + self.batch * k * 2 + self.batch * n * 2
 
     def alg_flops(self, label):
-        n, k = (int(v) for v in label.split("_")[1].split("x"))
+        n, k = (int(v) for v in label.split("_")[2].split("x"))
         return 2.0 * self.batch * n * k
 
     def cpu_baseline(self, budget_s):
@@ -444,14 +459,14 @@ def per_launch_ms(launches, copies: int, steps: int) -> dict:
 
 
 def copy_calibration(mb: int) -> None:
-    """Plain device-to-device copies of known size, for scaling rocprof byte counters."""
+    """A plain elementwise copy (read mb MiB, write mb MiB), run three times, for
+    scaling the rocprof FETCH_SIZE / WRITE_SIZE counters to bytes."""
     import torch
-    n = mb * (1 << 20)
-    src = torch.empty(n, dtype=torch.uint8, device="cuda")
-    src.fill_(1)
+    n = mb * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
     for _ in range(3):
-        dst.copy_(src)
+        torch.mul(src, 1.0, out=dst)
     torch.cuda.synchronize()
 
 
@@ -463,7 +478,7 @@ def traffic_from_profile(label: str) -> dict | None:
         return None
     data = json.load(open(path))
     entry = data.get(label)
-    if not entry or entry.get("kernel_source_hash") != kernel_source_hash():
+    if not entry or entry.get("kernel_source_hash") != kernel_source_hash(label):
         return None
     return entry
 
