@@ -31,6 +31,7 @@
 //   and the token rows are read from LDS with the same k order.
 #include "device.hpp"
 #include "kernels.hpp"
+#include "mfma_panel.hpp"
 
 namespace e2m1 {
 namespace {
@@ -39,13 +40,14 @@ constexpr int kMaxExperts = 512;
 constexpr int kRouteThreads = 1024;
 constexpr int kRouteWaves = kRouteThreads / kWave;
 
-constexpr int kThreads = 256;               // 4 waves
-constexpr int kTilesPerWave = 2;            // 16-row tiles per wave (per matrix half in gemm1)
-constexpr int kRowsPerBlock = 4 * kTilesPerWave * 16;   // 128 output rows (gemm1: 128 j) per block
-constexpr int kMTiles = 4;                  // token tiles of 16 per pass
-constexpr int kTokensPerPass = kMTiles * 16;            // 64
-constexpr int kKStep = 128;                 // columns per LDS stage
-constexpr int kLdsStride = kKStep * 2 + 16; // bytes per staged row (padding spreads banks)
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * kWave;
+constexpr int kMTiles = 4;                            // token tiles of 16 per pass
+constexpr int kTokensPerPass = kMTiles * 16;          // 64
+constexpr int kGemm1Tiles = 4;                        // per wave: 2 gate + 2 up tiles of 16 rows
+constexpr int kGemm1Cols = kWaves * (kGemm1Tiles / 2) * 16;   // 128 intermediate columns per block
+constexpr int kGemm2Tiles = 2;                        // per wave: 2 tiles of 16 W2 rows
+constexpr int kGemm2Rows = kWaves * kGemm2Tiles * 16; // 128 hidden rows per block
 
 struct MoeLayout {
     size_t cnt, off, pair_row, row_pair, act, y, total;
@@ -141,135 +143,69 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(const int32_t*
     }
 }
 
-// ----------------------------------------------------------- GEMM engine --
-
-// One lane's 16-byte weight chunk (32 codes of one scale block) -> the A
-// operands of four MFMAs (8 consecutive codes each), scaled by 2^(e-127).
-__device__ __forceinline__ void decode_frags(const uint4 w, float s, bf16x8 (&a)[4]) {
-    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const u32x4 v = {fp4x2_to_bf16x2<0>(ws[i], s), fp4x2_to_bf16x2<1>(ws[i], s),
-                         fp4x2_to_bf16x2<2>(ws[i], s), fp4x2_to_bf16x2<3>(ws[i], s)};
-        a[i] = __builtin_bit_cast(bf16x8, v);
-    }
-}
-
-// Stage 64 operand rows x kKStep columns (bf16) into LDS. Thread t copies the
-// 32 columns [kk + 32 (t % 4), +32) of row t / 4 from `src` (nullptr = zeros).
-__device__ __forceinline__ void stage_rows(uint8_t* lds, const uint16_t* src, int kk, int K) {
-    const int row = threadIdx.x >> 2, seg = threadIdx.x & 3;
-    const int col = kk + 32 * seg;
-    uint4 v[4];
-    if (src != nullptr && col < K) {
-        const uint4* p = reinterpret_cast<const uint4*>(src + col);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) v[q] = p[q];
-    } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) v[q] = make_uint4(0u, 0u, 0u, 0u);
-    }
-    uint4* d = reinterpret_cast<uint4*>(lds + row * kLdsStride + 64 * seg);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) d[q] = v[q];
-}
-
-// acc[t][m] += W tile t (rows wrow[t], this k step) x operand tile m, for the
-// `mt` token tiles in LDS. NT weight tiles; invalid tiles carry zero codes.
-template <int NT>
-__device__ __forceinline__ void mfma_step(const uint8_t* __restrict__ w, const uint8_t* __restrict__ ws,
-                                          const int (&wrow)[NT], const bool (&tvalid)[NT], int K,
-                                          int kk, const uint8_t* lds, int mt, f32x4 (&acc)[NT][kMTiles]) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int g = lane >> 4, r16 = lane & 15;
-    const int kb = kk / 32 + g;
-    const bool kvalid = kb < K / 32;
-    bf16x8 a[NT][4];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-        uint4 wv = make_uint4(0u, 0u, 0u, 0u);
-        float s = 1.0f;
-        if (tvalid[t] && kvalid) {
-            wv = load_nt16(w + (size_t)wrow[t] * (K / 2) + (size_t)kb * 16);
-            s = e8m0_scale(ws[(size_t)wrow[t] * (K / 32) + kb]);
-        }
-        decode_frags(wv, s, a[t]);
-    }
-#pragma unroll
-    for (int m = 0; m < kMTiles; ++m) {
-        if (m < mt) {
-            bf16x8 b[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                b[i] = *reinterpret_cast<const bf16x8*>(lds + (16 * m + r16) * kLdsStride + 64 * g + 16 * i);
-#pragma unroll
-            for (int t = 0; t < NT; ++t)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    acc[t][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[t][i], b[i], acc[t][m], 0, 0, 0);
-        }
-    }
-}
-
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
 
 // ----------------------------------------------------------------- gemm1 --
 
+using Gemm1 = PanelGemm<kGemm1Tiles, kMTiles, kWaves>;
+using Gemm2 = PanelGemm<kGemm2Tiles, kMTiles, kWaves>;
+
+// Workgroup (j block, expert): wave w streams gate rows j and up rows inter + j
+// for the 16 kGemm1Tiles / 2 consecutive j of its slice, against all of the
+// expert's tokens (kTokensPerPass per pass), then act = silu(gate) * up.
 __global__ __launch_bounds__(kThreads) void moe_gemm1_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ w13, const uint8_t* __restrict__ w13s,
     const int* __restrict__ cnt, const int* __restrict__ off, const int* __restrict__ row_pair,
     uint16_t* __restrict__ act, int H, int I, int topk) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[kTokensPerPass * kLdsStride];
+    __shared__ __attribute__((aligned(16))) uint16_t lds[Gemm1::kLdsElems];
+    __shared__ int rowidx[kTokensPerPass];
     const int e = blockIdx.y;
     const int n_e = cnt[e];
     if (n_e == 0) return;
     const int base = off[e];
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wave-uniform
     const int g = lane >> 4, r16 = lane & 15;
-    const int j0 = blockIdx.x * kRowsPerBlock + wave * (kTilesPerWave * 16);
-    constexpr int NT = 2 * kTilesPerWave;   // gate tiles then up tiles
-    int wrow[NT];
-    bool tvalid[NT];
+    constexpr int NH = kGemm1Tiles / 2;      // gate tiles (then as many up tiles)
+    const int j0 = blockIdx.x * kGemm1Cols + wave * (NH * 16);
+    int wrow[kGemm1Tiles];
+    bool tvalid[kGemm1Tiles];
 #pragma unroll
-    for (int t = 0; t < kTilesPerWave; ++t) {
+    for (int t = 0; t < NH; ++t) {
         const int jt = j0 + 16 * t;
-        tvalid[t] = tvalid[kTilesPerWave + t] = jt < I;
-        wrow[t] = jt + r16;
-        wrow[kTilesPerWave + t] = I + jt + r16;
+        tvalid[t] = tvalid[NH + t] = jt < I;
+        const int j = min(jt + r16, I - 1);
+        wrow[t] = j;
+        wrow[NH + t] = I + j;
     }
     const uint8_t* we = w13 + (size_t)e * 2 * I * (H / 2);
     const uint8_t* se = w13s + (size_t)e * 2 * I * (H / 32);
 
     for (int m0 = 0; m0 < n_e; m0 += kTokensPerPass) {
-        const int mt = min(kMTiles, (n_e - m0 + 15) / 16);
-        const int srow = threadIdx.x >> 2;
-        const uint16_t* src = nullptr;
-        if (m0 + srow < n_e) src = x + (size_t)(row_pair[base + m0 + srow] / topk) * H;
-        f32x4 acc[NT][kMTiles];
+        const int nv = min(kTokensPerPass, n_e - m0);
+        const int mt = (nv + 15) / 16;
+        __syncthreads();   // the previous pass is done with rowidx and the panels
+        if (threadIdx.x < nv) rowidx[threadIdx.x] = row_pair[base + m0 + threadIdx.x] / topk;
+        __syncthreads();
+        f32x4 acc[kGemm1Tiles][kMTiles];
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
+        for (int t = 0; t < kGemm1Tiles; ++t)
 #pragma unroll
             for (int m = 0; m < kMTiles; ++m) acc[t][m] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int kk = 0; kk < H; kk += kKStep) {
-            __syncthreads();
-            stage_rows(lds, src, kk, H);
-            __syncthreads();
-            mfma_step<NT>(we, se, wrow, tvalid, H, kk, lds, mt, acc);
-        }
+        Gemm1::run_mt(mt, we, se, H, wrow, tvalid, x, (size_t)H, rowidx, nv, lds, acc);
         // epilogue: act = silu(gate) * up -> bf16, 4 consecutive j per lane
 #pragma unroll
-        for (int t = 0; t < kTilesPerWave; ++t) {
+        for (int t = 0; t < NH; ++t) {
             if (!tvalid[t]) continue;
 #pragma unroll
             for (int m = 0; m < kMTiles; ++m) {
-                const int r = m0 + 16 * m + r16;
-                if (m < mt && r < n_e) {
-                    const f32x4 gt = acc[t][m], up = acc[kTilesPerWave + t][m];
+                const int r = 16 * m + r16;
+                if (m < mt && r < nv) {
+                    const f32x4 gt = acc[t][m], up = acc[NH + t][m];
                     const uint32_t lo = pack_bf16x2(silu_f32(gt[0]) * up[0], silu_f32(gt[1]) * up[1]);
                     const uint32_t hi = pack_bf16x2(silu_f32(gt[2]) * up[2], silu_f32(gt[3]) * up[3]);
                     const int j = j0 + 16 * t + 4 * g;
-                    *reinterpret_cast<uint2*>(act + (size_t)(base + r) * I + j) = make_uint2(lo, hi);
+                    *reinterpret_cast<uint2*>(act + (size_t)(base + m0 + r) * I + j) = make_uint2(lo, hi);
                 }
             }
         }
@@ -278,53 +214,53 @@ __global__ __launch_bounds__(kThreads) void moe_gemm1_kernel(
 
 // ----------------------------------------------------------------- gemm2 --
 
+// Workgroup (hidden block, expert): wave w streams kGemm2Tiles row tiles of W2
+// against the expert's activation rows; fp32 results per (expert row, hidden).
 __global__ __launch_bounds__(kThreads) void moe_gemm2_kernel(
     const uint16_t* __restrict__ act, const uint8_t* __restrict__ w2, const uint8_t* __restrict__ w2s,
     const int* __restrict__ cnt, const int* __restrict__ off, float* __restrict__ y, int H, int I) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[kTokensPerPass * kLdsStride];
+    __shared__ __attribute__((aligned(16))) uint16_t lds[Gemm2::kLdsElems];
+    __shared__ int rowidx[kTokensPerPass];
     const int e = blockIdx.y;
     const int n_e = cnt[e];
     if (n_e == 0) return;
     const int base = off[e];
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wave-uniform
     const int g = lane >> 4, r16 = lane & 15;
-    constexpr int NT = kTilesPerWave;
-    const int h0 = blockIdx.x * kRowsPerBlock + wave * (kTilesPerWave * 16);
+    constexpr int NT = kGemm2Tiles;
+    const int h0 = blockIdx.x * kGemm2Rows + wave * (NT * 16);
     int wrow[NT];
     bool tvalid[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
         tvalid[t] = h0 + 16 * t < H;
-        wrow[t] = h0 + 16 * t + r16;
+        wrow[t] = min(h0 + 16 * t + r16, H - 1);
     }
     const uint8_t* we = w2 + (size_t)e * H * (I / 2);
     const uint8_t* se = w2s + (size_t)e * H * (I / 32);
 
     for (int m0 = 0; m0 < n_e; m0 += kTokensPerPass) {
-        const int mt = min(kMTiles, (n_e - m0 + 15) / 16);
-        const int srow = threadIdx.x >> 2;
-        const uint16_t* src = (m0 + srow < n_e) ? act + (size_t)(base + m0 + srow) * I : nullptr;
+        const int nv = min(kTokensPerPass, n_e - m0);
+        const int mt = (nv + 15) / 16;
+        __syncthreads();
+        if (threadIdx.x < nv) rowidx[threadIdx.x] = base + m0 + threadIdx.x;
+        __syncthreads();
         f32x4 acc[NT][kMTiles];
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int m = 0; m < kMTiles; ++m) acc[t][m] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int kk = 0; kk < I; kk += kKStep) {
-            __syncthreads();
-            stage_rows(lds, src, kk, I);
-            __syncthreads();
-            mfma_step<NT>(we, se, wrow, tvalid, I, kk, lds, mt, acc);
-        }
+        Gemm2::run_mt(mt, we, se, I, wrow, tvalid, act, (size_t)I, rowidx, nv, lds, acc);
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             if (!tvalid[t]) continue;
 #pragma unroll
             for (int m = 0; m < kMTiles; ++m) {
-                const int r = m0 + 16 * m + r16;
-                if (m < mt && r < n_e) {
+                const int r = 16 * m + r16;
+                if (m < mt && r < nv) {
                     const int h = h0 + 16 * t + 4 * g;
-                    *reinterpret_cast<f32x4*>(y + (size_t)(base + r) * H + h) = acc[t][m];
+                    *reinterpret_cast<f32x4*>(y + (size_t)(base + m0 + r) * H + h) = acc[t][m];
                 }
             }
         }
@@ -392,10 +328,10 @@ hipError_t launch_moe(const uint16_t* x, const uint8_t* w13, const uint8_t* w13s
     moe_route_kernel<<<1, kRouteThreads, 0, stream>>>(ids, P, E, cnt, off, pair_row, row_pair);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    const dim3 g1((I + kRowsPerBlock - 1) / kRowsPerBlock, E);
+    const dim3 g1((I + kGemm1Cols - 1) / kGemm1Cols, E);
     moe_gemm1_kernel<<<g1, kThreads, 0, stream>>>(x, w13, w13s, cnt, off, row_pair, act, H, I, (int)topk);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    const dim3 g2((H + kRowsPerBlock - 1) / kRowsPerBlock, E);
+    const dim3 g2((H + kGemm2Rows - 1) / kGemm2Rows, E);
     moe_gemm2_kernel<<<g2, kThreads, 0, stream>>>(act, w2, w2s, cnt, off, y, H, I);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     const int64_t chunks = tokens * (hidden / 8);
