@@ -13,14 +13,18 @@
 //     multiplies the pair by the matching pair of x and accumulates in fp32:
 //     per byte of weights one conversion and one dot2.
 //   * Batch 1 (the bandwidth-bound case): each lane owns fixed 32-column
-//     chunks of K, so its slice of x sits in registers for the whole kernel.
-//     A group of G lanes covers one row (G = 64 for K >= 2048, smaller for
-//     short rows so a wave works on several rows at once) and takes R
-//     consecutive rows per pass, R sized so one resident generation of waves
-//     covers the matrix. Every weight byte is read once with a 16-byte load,
-//     all of a pass's loads are in flight before the first row is computed,
-//     and the row total comes from a DPP-only reduction (row_bcast for the
-//     cross-row steps), so the decode and dot products hide under the loads.
+//     chunks of K, so its slice of x sits in registers for the whole kernel,
+//     and every weight byte is read once with a 16-byte load. Rows are dealt
+//     to waves grid-stride (row = wave + i * waves) and streamed through a
+//     three-buffer register pipeline: the loads of row i + 2 are issued before
+//     row i is decoded, so two rows per wave are always in flight and the
+//     decode never delays the next request. About 4 MB in flight over the
+//     chip measured best for these sizes: one workgroup of four waves per
+//     compute unit. Rows up to 8192 columns belong to one wave (row totals by
+//     DPP); longer rows are split over the waves of a workgroup, one
+//     64-chunk slice each, whose partial sums meet in LDS. A lane keeps the
+//     total of its i-th row in register lane i and stores 64 rows at a time.
+//     Short rows (K < 2048) use groups of 8 to 32 lanes per row instead.
 //   * Other batches: one wave per row, lanes across K, x read through the
 //     cache hierarchy per chunk.
 #include "device.hpp"
@@ -144,60 +148,170 @@ __global__ __launch_bounds__(kThreads) void gemv_b1_kernel(const uint8_t* __rest
     }
 }
 
-// Batch 1, long rows (K > 8192). Holding all of a row's x slice per wave
-// would make every wave pull the whole of x through its compute unit, more
-// bytes than the weights it streams. Here the WR waves of a workgroup split
-// K: lane l of wave w owns the single chunk 64 w + l (16 x registers), the
-// workgroup takes RB consecutive rows per pass, every wave reduces its part
-// of each row with DPP, and the WR partial sums meet in LDS.
-template <int WR, int RB, bool kBf16Out>
-__global__ __launch_bounds__(kWave * WR) void gemv_b1_slab_kernel(const uint8_t* __restrict__ packed,
-                                                                  const uint8_t* __restrict__ scales,
-                                                                  const uint16_t* __restrict__ x,
-                                                                  void* __restrict__ y, int n, int kc) {
-    __shared__ float part[RB][WR];
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int wig = tid / kWave;
-    const int c_raw = wig * kWave + lane;
-    const bool cvalid = c_raw < kc;
-    const int c = min(c_raw, kc - 1);
-    const uint4* pv = reinterpret_cast<const uint4*>(packed);
-    uint32_t xr[16];
-    {
-        const uint4* xv = reinterpret_cast<const uint4*>(x) + c * 4;
+// Keeps loads where they are written (issued early) instead of letting the
+// compiler sink them next to their uses; emits no instruction. The weight
+// pointers of the kernels that rely on it are not __restrict__: loads through
+// a restrict pointer to read-only memory may be moved across the fence.
+__device__ __forceinline__ void issue_here() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// Stores the row totals a wave keeps in register lanes: lane l holds the total
+// of its row number base + l (rows wave + (base + l) * stride).
+template <bool kBf16Out>
+__device__ __forceinline__ void store_row_totals(void* y, float res, int lane, int base, int count,
+                                                 int wave, int stride) {
+    if (lane < count) store_out<kBf16Out>(y, (int64_t)wave + (int64_t)(base + lane) * stride, res);
+}
+
+constexpr int kRowsInFlight = 2;   // per wave, while one more row is decoded
+
+template <int CPL>
+struct RowBuf {
+    uint4 w[CPL];
+    uint8_t e[CPL];   // kept as bytes: widened at use, so no instruction touches a pending load
+};
+
+template <int CPL>
+__device__ __forceinline__ void issue_row(RowBuf<CPL>& b, const uint4* pv, const uint8_t* scales, int row, int kc,
+                                          int lane) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const uint4 v = xv[q];
-            xr[4 * q + 0] = v.x;
-            xr[4 * q + 1] = v.y;
-            xr[4 * q + 2] = v.z;
-            xr[4 * q + 3] = v.w;
+    for (int ci = 0; ci < CPL; ++ci) {
+        const int64_t blk = (int64_t)row * kc + min(lane + kWave * ci, kc - 1);
+        b.w[ci] = load_nt16(pv + blk);
+        b.e[ci] = scales[blk];
+    }
+}
+
+// x words of 32-column chunk min(c, kc - 1) (16 bf16 pairs). Lanes whose
+// chunk lies past the row end drop their partial sums at use instead (a
+// select here would make the first weight loads wait for x).
+__device__ __forceinline__ void load_x_chunk(uint32_t (&xr)[16], const uint16_t* __restrict__ x, int c, int kc) {
+    const uint4* xv = reinterpret_cast<const uint4*>(x) + 4 * min(c, kc - 1);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint4 v = xv[q];
+        xr[4 * q + 0] = v.x;
+        xr[4 * q + 1] = v.y;
+        xr[4 * q + 2] = v.z;
+        xr[4 * q + 3] = v.w;
+    }
+}
+
+// Batch 1, 64 < K/32 <= 64 CPL: whole rows per wave. Lane l owns chunks
+// l + 64 ci; chunks past the row end are loaded clamped and their partial
+// sums dropped (E2M1 codes times a clamped E8M0 scale are always finite).
+// Row r of the wave lives in buffer r % 3; the loop starts two rows early so
+// that the first two sub-iterations only issue loads (there is no separate
+// prologue, and every pass through the loop issues its loads in the same
+// order, so each wait counts exactly the loads issued after the one it
+// needs). Loads past a wave's last row re-read that row.
+template <int CPL, bool kBf16Out>
+__global__ __launch_bounds__(kThreads) void gemv_b1_rows_kernel(const uint8_t* packed,
+                                                                const uint8_t* scales,
+                                                                const uint16_t* __restrict__ x,
+                                                                void* __restrict__ y, int n, int kc) {
+    constexpr int kBufs = kRowsInFlight + 1;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerBlock + threadIdx.x / kWave);
+    if (wave >= n) return;
+    const int nw = gridDim.x * kWavesPerBlock;
+    const uint4* pv = reinterpret_cast<const uint4*>(packed);
+
+    uint32_t xr[CPL][16];
+#pragma unroll
+    for (int ci = 0; ci < CPL; ++ci) load_x_chunk(xr[ci], x, lane + kWave * ci, kc);
+    issue_here();
+    const int iters = (n - 1 - wave) / nw + 1;
+    const int last = wave + (iters - 1) * nw;
+    RowBuf<CPL> buf[kBufs];
+    float res = 0.f;
+    for (int it = -kRowsInFlight; it < iters; it += kBufs) {
+#pragma unroll
+        for (int b = 0; b < kBufs; ++b) {
+            const int i = it + b;   // row being decoded; row i + 2 is issued
+            issue_row(buf[b], pv, scales, min(wave + (i + kRowsInFlight) * nw, last), kc, lane);
+            issue_here();
+            if (i >= 0 && i < iters) {
+                const RowBuf<CPL>& cur = buf[(b + 1) % kBufs];
+                float acc = 0.f;
+#pragma unroll
+                for (int ci = 0; ci < CPL; ++ci) {
+                    const float p = block_dot(cur.w[ci], e8m0_scale(cur.e[ci]), xr[ci], 0.f);
+                    acc += (lane + kWave * ci < kc) ? p : 0.f;
+                }
+                acc = group_total<kWave>(acc);
+                const float t = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc), kWave - 1));
+                const int slot = i & (kWave - 1);
+                if (lane == slot) res = t;
+                if (slot == kWave - 1 || i == iters - 1)
+                    store_row_totals<kBf16Out>(y, res, lane, i - slot, slot + 1, wave, nw);
+            }
+            issue_here();
         }
     }
-    for (int rb = blockIdx.x * RB; rb < n; rb += gridDim.x * RB) {   // workgroup-uniform
-        uint4 w[RB];
-        uint32_t e[RB];
+}
+
+// Batch 1, K/32 > 256: rows split over the S waves of a workgroup, lane l of
+// wave w owning chunk 64 w + l. Rows blockIdx.x + i * gridDim.x, three in
+// flight per wave (buffer r % 4 for row r, loop started three rows early as
+// above); the S partial totals of each row meet in LDS, 64 rows at a time,
+// and are summed in a fixed order.
+template <int S, bool kBf16Out>
+__global__ __launch_bounds__(kWave * S) void gemv_b1_split_kernel(const uint8_t* packed,
+                                                                  const uint8_t* scales,
+                                                                  const uint16_t* __restrict__ x,
+                                                                  void* __restrict__ y, int n, int kc) {
+    constexpr int kDepth = 3;
+    constexpr int kBufs = kDepth + 1;
+    __shared__ float part[S][kWave];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int c_raw = wv * kWave + lane;
+    const int c = min(c_raw, kc - 1);
+    const int nb = gridDim.x;
+    const int row0 = blockIdx.x;
+    const uint4* pv = reinterpret_cast<const uint4*>(packed);
+
+    uint32_t xr[16];
+    load_x_chunk(xr, x, c_raw, kc);
+    issue_here();
+    const int iters = (n - 1 - row0) / nb + 1;   // grid <= n: at least one row
+    const int last = row0 + (iters - 1) * nb;
+    RowBuf<1> buf[kBufs];
+    float res = 0.f;
+    for (int it = -kDepth; it < iters; it += kBufs) {
 #pragma unroll
-        for (int i = 0; i < RB; ++i) {
-            const int64_t blk = (int64_t)min(rb + i, n - 1) * kc + c;
-            w[i] = load_nt16(pv + blk);
-            e[i] = scales[blk];
-        }
+        for (int b = 0; b < kBufs; ++b) {
+            const int i = it + b;   // row being summed; row i + 3 is issued into buffer b
+            {
+                const int64_t blk = (int64_t)min(row0 + (i + kDepth) * nb, last) * kc + c;
+                buf[b].w[0] = load_nt16(pv + blk);
+                buf[b].e[0] = scales[blk];
+            }
+            issue_here();
+            if (i >= 0 && i < iters) {   // workgroup-uniform
+                const RowBuf<1>& cur = buf[(b + 1) % kBufs];
+                const float p = block_dot(cur.w[0], e8m0_scale(cur.e[0]), xr, 0.f);
+                const float acc = group_total<kWave>(c_raw < kc ? p : 0.f);
+                const float t = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc), kWave - 1));
+                const int slot = i & (kWave - 1);
+                if (lane == slot) res = t;
+                if (slot == kWave - 1 || i == iters - 1) {
+                    part[wv][lane] = res;
+                    __syncthreads();
+                    if ((int)threadIdx.x <= slot) {
+                        float s = 0.f;
 #pragma unroll
-        for (int i = 0; i < RB; ++i) {
-            const uint4 wv = cvalid ? w[i] : make_uint4(0u, 0u, 0u, 0u);
-            const float acc = group_total<kWave>(block_dot(wv, e8m0_scale(e[i]), xr, 0.f));
-            if (lane == kWave - 1) part[i][wig] = acc;
+                        for (int j = 0; j < S; ++j) s += part[j][threadIdx.x];
+                        store_out<kBf16Out>(y, (int64_t)row0 + (int64_t)(i - slot + threadIdx.x) * nb, s);
+                    }
+                    __syncthreads();
+                }
+            }
+            issue_here();
         }
-        __syncthreads();
-        if (tid < RB && rb + tid < n) {
-            float s = 0.f;
-#pragma unroll
-            for (int w2 = 0; w2 < WR; ++w2) s += part[tid][w2];
-            store_out<kBf16Out>(y, rb + tid, s);
-        }
-        __syncthreads();
     }
 }
 
@@ -291,58 +405,47 @@ hipError_t run_b1(const uint8_t* packed, const uint8_t* scales, const uint16_t* 
     return run_b1_r<G, CPL, 4, kBf16Out>(packed, scales, x, y, n, kc, cap4, stream);
 }
 
-template <int WR, int RB, bool kBf16Out>
-hipError_t run_slab_r(const uint8_t* packed, const uint8_t* scales, const uint16_t* x, void* y, int n,
-                      int kc, int cap, hipStream_t stream) {
-    const int want = (n + RB - 1) / RB;
-    const int grid = want < cap ? want : cap;
-    gemv_b1_slab_kernel<WR, RB, kBf16Out><<<grid, kWave * WR, 0, stream>>>(packed, scales, x, y, n, kc);
+template <int CPL, bool kBf16Out>
+hipError_t run_b1_rows(const uint8_t* packed, const uint8_t* scales, const uint16_t* x, void* y, int n, int kc,
+                       hipStream_t stream) {
+    // one workgroup of four waves per compute unit (fewer if there are fewer rows)
+    const int waves = min(n, kWavesPerBlock * device_cu_count());
+    const int grid = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
+    gemv_b1_rows_kernel<CPL, kBf16Out><<<grid, kThreads, 0, stream>>>(packed, scales, x, y, n, kc);
     return hipGetLastError();
 }
 
-// Rows per workgroup pass: the fewest (2, 4 or 8) that cover the matrix with
-// one resident generation of workgroups.
-template <int WR, bool kBf16Out>
-hipError_t run_slab(const uint8_t* packed, const uint8_t* scales, const uint16_t* x, void* y, int n,
-                    int kc, hipStream_t stream) {
-    static int cap2 = 0, cap4 = 0, cap8 = 0;
-    if (cap2 == 0) {
-        cap2 = resident_blocks(gemv_b1_slab_kernel<WR, 2, kBf16Out>, 0, kWave * WR);
-        cap4 = resident_blocks(gemv_b1_slab_kernel<WR, 4, kBf16Out>, 0, kWave * WR);
-        cap8 = resident_blocks(gemv_b1_slab_kernel<WR, 8, kBf16Out>, 0, kWave * WR);
-    }
-    if ((int64_t)cap2 * 2 >= n) return run_slab_r<WR, 2, kBf16Out>(packed, scales, x, y, n, kc, cap2, stream);
-    if ((int64_t)cap4 * 4 >= n) return run_slab_r<WR, 4, kBf16Out>(packed, scales, x, y, n, kc, cap4, stream);
-    return run_slab_r<WR, 8, kBf16Out>(packed, scales, x, y, n, kc, cap8, stream);
+template <int S, bool kBf16Out>
+hipError_t run_b1_split(const uint8_t* packed, const uint8_t* scales, const uint16_t* x, void* y, int n, int kc,
+                        hipStream_t stream) {
+    const int grid = min(n, device_cu_count());   // one workgroup of S waves per compute unit
+    gemv_b1_split_kernel<S, kBf16Out><<<grid, kWave * S, 0, stream>>>(packed, scales, x, y, n, kc);
+    return hipGetLastError();
 }
 
 template <bool kBf16Out>
 hipError_t dispatch_b1(const uint8_t* packed, const uint8_t* scales, const uint16_t* x, void* y,
                        int n, int kc, hipStream_t stream) {
-    if (kc > 4 * kWave) {
-        switch ((kc + kWave - 1) / kWave) {
-            case 5: return run_slab<5, kBf16Out>(packed, scales, x, y, n, kc, stream);
-            case 6: return run_slab<6, kBf16Out>(packed, scales, x, y, n, kc, stream);
-            case 7: return run_slab<7, kBf16Out>(packed, scales, x, y, n, kc, stream);
-            case 8: return run_slab<8, kBf16Out>(packed, scales, x, y, n, kc, stream);
-            case 9: return run_slab<9, kBf16Out>(packed, scales, x, y, n, kc, stream);
-            case 10: return run_slab<10, kBf16Out>(packed, scales, x, y, n, kc, stream);
-            case 11: return run_slab<11, kBf16Out>(packed, scales, x, y, n, kc, stream);
-            case 12: return run_slab<12, kBf16Out>(packed, scales, x, y, n, kc, stream);
-            case 13: return run_slab<13, kBf16Out>(packed, scales, x, y, n, kc, stream);
-            case 14: return run_slab<14, kBf16Out>(packed, scales, x, y, n, kc, stream);
-            case 15: return run_slab<15, kBf16Out>(packed, scales, x, y, n, kc, stream);
-            default: return run_slab<16, kBf16Out>(packed, scales, x, y, n, kc, stream);
-        }
-    }
     if (kc <= 8) return run_b1<8, 1, kBf16Out>(packed, scales, x, y, n, kc, stream);
     if (kc <= 16) return run_b1<16, 1, kBf16Out>(packed, scales, x, y, n, kc, stream);
     if (kc <= 32) return run_b1<32, 1, kBf16Out>(packed, scales, x, y, n, kc, stream);
     switch ((kc + kWave - 1) / kWave) {
-        case 1: return run_b1<64, 1, kBf16Out>(packed, scales, x, y, n, kc, stream);
-        case 2: return run_b1<64, 2, kBf16Out>(packed, scales, x, y, n, kc, stream);
-        case 3: return run_b1<64, 3, kBf16Out>(packed, scales, x, y, n, kc, stream);
-        default: return run_b1<64, 4, kBf16Out>(packed, scales, x, y, n, kc, stream);
+        case 1: return run_b1_rows<1, kBf16Out>(packed, scales, x, y, n, kc, stream);
+        case 2: return run_b1_rows<2, kBf16Out>(packed, scales, x, y, n, kc, stream);
+        case 3: return run_b1_rows<3, kBf16Out>(packed, scales, x, y, n, kc, stream);
+        case 4: return run_b1_rows<4, kBf16Out>(packed, scales, x, y, n, kc, stream);
+        case 5: return run_b1_split<5, kBf16Out>(packed, scales, x, y, n, kc, stream);
+        case 6: return run_b1_split<6, kBf16Out>(packed, scales, x, y, n, kc, stream);
+        case 7: return run_b1_split<7, kBf16Out>(packed, scales, x, y, n, kc, stream);
+        case 8: return run_b1_split<8, kBf16Out>(packed, scales, x, y, n, kc, stream);
+        case 9: return run_b1_split<9, kBf16Out>(packed, scales, x, y, n, kc, stream);
+        case 10: return run_b1_split<10, kBf16Out>(packed, scales, x, y, n, kc, stream);
+        case 11: return run_b1_split<11, kBf16Out>(packed, scales, x, y, n, kc, stream);
+        case 12: return run_b1_split<12, kBf16Out>(packed, scales, x, y, n, kc, stream);
+        case 13: return run_b1_split<13, kBf16Out>(packed, scales, x, y, n, kc, stream);
+        case 14: return run_b1_split<14, kBf16Out>(packed, scales, x, y, n, kc, stream);
+        case 15: return run_b1_split<15, kBf16Out>(packed, scales, x, y, n, kc, stream);
+        default: return run_b1_split<16, kBf16Out>(packed, scales, x, y, n, kc, stream);
     }
 }
 
@@ -376,7 +479,7 @@ hipError_t dispatch_generic(int batch, const uint8_t* packed, const uint8_t* sca
 }  // namespace
 
 // Largest K of the batch-1 kernels: 16 waves of 64 lanes, one 32-column chunk
-// per lane (the register-resident kernel stops at 4 chunks per lane, K = 8192).
+// per lane (whole rows per wave stop at 4 chunks per lane, K = 8192).
 constexpr int64_t kB1MaxK = 16 * 64 * 32;
 
 hipError_t launch_gemv(const uint8_t* packed, const uint8_t* scales, const uint16_t* x, void* y,

@@ -52,6 +52,8 @@ SHAPES = [
     (64, 8192 + 32, 1),               # first size of the K-split kernel (5 waves, ragged)
     (1001, 14336, 1), (40, 16384 + 32 * 3, 1), (50, 32768, 1),   # K-split kernel, 7 to 16 waves
     (20, 32768 + 32, 1),              # beyond the batch-1 kernels -> generic kernel
+    (70001, 2048, 1),                 # > 64 rows per wave: row totals stored 64 at a time
+    (20000, 8192 + 32, 1),            # > 64 rows per workgroup in the K-split kernel
     (31, 512, 2), (17, 4096 + 32, 3), (9, 1024, 4), (65, 2048, 8), (12, 768, 16),
 ]
 
