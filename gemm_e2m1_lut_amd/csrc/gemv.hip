@@ -25,8 +25,16 @@
 //     64-chunk slice each, whose partial sums meet in LDS. A lane keeps the
 //     total of its i-th row in register lane i and stores 64 rows at a time.
 //     Short rows (K < 2048) use groups of 8 to 32 lanes per row instead.
-//   * Other batches: one wave per row, lanes across K, x read through the
-//     cache hierarchy per chunk.
+//   * Batch 2..16: the same weight bytes feed bf16 MFMA
+//     (v_mfma_f32_16x16x32_bf16) with the batch as the N dimension: a
+//     workgroup takes a tile of 16 rows, its S waves split K into slices of
+//     1024 columns, each lane decodes its 16-byte chunks straight into A
+//     operands and reads the matching x words from the cache hierarchy as B
+//     operands (columns past the batch or the row end read as zero). Every
+//     weight byte is still read once; the S partial 16 x 16 tiles meet in LDS
+//     and are summed in a fixed order.
+//   * K beyond the tiled kernels (K > 16384 at batch 2..16, K > 32768 at
+//     batch 1): one wave per row, lanes across K, x read per chunk.
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -315,6 +323,100 @@ __global__ __launch_bounds__(kWave * S) void gemv_b1_split_kernel(const uint8_t*
     }
 }
 
+// ------------------------------------------------------- batch 2..16 ----
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+constexpr int kTileSteps = 4;                        // 256-column steps per wave slice
+constexpr int kSliceBlocks = 8 * kTileSteps;         // 32 scale blocks = 1024 columns per wave
+constexpr int kMaxSliceWaves = 16;
+
+// Workgroup = S waves on one tile of 16 rows (tiles blockIdx.x, + gridDim.x,
+// ...); wave w owns scale blocks [32 w, 32 w + 32). Lane l = 16 g + r: row r
+// of the tile for the A operand and batch column r for the B operand; in step
+// s it loads blocks b = 32 w + 8 s + g + 4 h (h = 0, 1: both halves of a
+// 128-byte line of the row). MFMA (s, h, i) takes codes [8 i, 8 i + 8) of
+// block b as A k-slots 8 g .. 8 g + 7 and the same columns of x as B k-slots,
+// so both operands share one column -> k-slot map and the sum over k is
+// complete. D element (row 4 g + j, batch r) is component j of acc in lane l.
+// All of a slice's weight loads are issued first, the x operands of step
+// s + 1 before the MFMAs of step s.
+template <bool kBf16Out>
+__global__ __launch_bounds__(kWave * kMaxSliceWaves) void gemv_mfma_kernel(
+    const uint8_t* packed, const uint8_t* scales, const uint16_t* __restrict__ x, void* __restrict__ y,
+    int batch, int n, int kc) {
+    __shared__ f32x4 part[kMaxSliceWaves][kWave];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int nwaves = blockDim.x / kWave;
+    const int r = lane & 15, g = lane >> 4;
+    const int K = kc * 32;
+    const int ntiles = (n + 15) / 16;
+    const int xrow = min(r, batch - 1);
+    const bool bvalid = r < batch;
+    const uint16_t* xr = x + (size_t)xrow * K;
+
+    for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {   // workgroup-uniform
+        const int row = min(tile * 16 + r, n - 1);
+        const uint8_t* wrow = packed + (size_t)row * (K / 2);
+        const uint8_t* srow = scales + (size_t)row * kc;
+        uint4 w[kTileSteps][2];
+        uint32_t e[kTileSteps][2];
+#pragma unroll
+        for (int st = 0; st < kTileSteps; ++st)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int b = min(wv * kSliceBlocks + 8 * st + g + 4 * h, kc - 1);
+                w[st][h] = load_nt16(wrow + (size_t)b * 16);
+                e[st][h] = srow[b];
+            }
+        issue_here();
+        // x operands of one half step (block b of step st, h), one half step ahead
+        constexpr int kXAhead = 1;
+        bf16x8_t xb[kXAhead + 1][4];
+        auto load_x = [&](bf16x8_t (&dst)[4], int hs) {
+            const int b = min(wv * kSliceBlocks + 8 * (hs >> 1) + g + 4 * (hs & 1), kc - 1);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dst[i] = *reinterpret_cast<const bf16x8_t*>(xr + 32 * b + 8 * i);
+        };
+#pragma unroll
+        for (int hs = 0; hs < kXAhead; ++hs) {
+            load_x(xb[hs], hs);
+            issue_here();
+        }
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int hs = 0; hs < 2 * kTileSteps; ++hs) {
+            const int st = hs >> 1, h = hs & 1;
+            if (hs + kXAhead < 2 * kTileSteps) load_x(xb[(hs + kXAhead) % (kXAhead + 1)], hs + kXAhead);
+            issue_here();
+            const bool valid = bvalid && (wv * kSliceBlocks + 8 * st + g + 4 * h < kc);
+            const float sc = e8m0_scale(e[st][h]);
+            const uint32_t ws[4] = {w[st][h].x, w[st][h].y, w[st][h].z, w[st][h].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const u32x4 a = {fp4x2_to_bf16x2<0>(ws[i], sc), fp4x2_to_bf16x2<1>(ws[i], sc),
+                                 fp4x2_to_bf16x2<2>(ws[i], sc), fp4x2_to_bf16x2<3>(ws[i], sc)};
+                const u32x4 xv = __builtin_bit_cast(u32x4, xb[hs % (kXAhead + 1)][i]);
+                const u32x4 bz = {valid ? xv.x : 0u, valid ? xv.y : 0u, valid ? xv.z : 0u, valid ? xv.w : 0u};
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                               __builtin_bit_cast(bf16x8, bz), acc, 0, 0, 0);
+            }
+        }
+        part[wv][lane] = acc;
+        __syncthreads();
+        // thread t sums element (row 4 g + j, batch c) over the slices: t = 64 j + 16 g + c
+        for (int t = threadIdx.x; t < 4 * kWave; t += blockDim.x) {
+            const int j = t / kWave, l = t & (kWave - 1);
+            const int c = l & 15, orow = tile * 16 + 4 * (l >> 4) + j;
+            float sum = 0.f;
+            for (int q = 0; q < nwaves; ++q) sum += part[q][l][j];
+            if (c < batch && orow < n) store_out<kBf16Out>(y, (int64_t)c * n + orow, sum);
+        }
+        __syncthreads();
+    }
+}
+
 // --------------------------------------------------------- any batch ----
 
 template <int B, bool kBf16Out>
@@ -476,6 +578,18 @@ hipError_t dispatch_generic(int batch, const uint8_t* packed, const uint8_t* sca
 #undef E2M1_GEMV_CASE
 }
 
+template <bool kBf16Out>
+hipError_t run_mfma(int batch, const uint8_t* packed, const uint8_t* scales, const uint16_t* x, void* y, int n,
+                    int kc, hipStream_t stream) {
+    const int waves = (kc + kSliceBlocks - 1) / kSliceBlocks;
+    const int ntiles = (n + 15) / 16;
+    // workgroups resident at once: 16 waves per compute unit
+    const int per_cu = max(1, kMaxSliceWaves / waves);
+    const int grid = min(ntiles, per_cu * device_cu_count());
+    gemv_mfma_kernel<kBf16Out><<<grid, kWave * waves, 0, stream>>>(packed, scales, x, y, batch, n, kc);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 // Largest K of the batch-1 kernels: 16 waves of 64 lanes, one 32-column chunk
@@ -489,6 +603,9 @@ hipError_t launch_gemv(const uint8_t* packed, const uint8_t* scales, const uint1
     if (batch == 1 && k <= kB1MaxK)
         return out_bf16 ? dispatch_b1<true>(packed, scales, x, y, nn, kc, stream)
                         : dispatch_b1<false>(packed, scales, x, y, nn, kc, stream);
+    if (batch > 1 && kc <= kMaxSliceWaves * kSliceBlocks)
+        return out_bf16 ? run_mfma<true>(batch, packed, scales, x, y, nn, kc, stream)
+                        : run_mfma<false>(batch, packed, scales, x, y, nn, kc, stream);
     return out_bf16 ? dispatch_generic<true>(batch, packed, scales, x, y, nn, kc, stream)
                     : dispatch_generic<false>(batch, packed, scales, x, y, nn, kc, stream);
 }
