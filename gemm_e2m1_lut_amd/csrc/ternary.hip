@@ -13,12 +13,14 @@
 // and v_dot2_f32_bf16 accumulates the pair against x held as bf16 hi + lo
 // parts (x = hi + lo to a relative 2^-16), about 2.5 operations per weight;
 // the exact factor 2 goes into the row scale. Each lane owns one 64-column
-// chunk of K (one 16-byte load of four words) with its x pairs in registers;
-// lanes cover a row in groups (64 lanes for K = 4096, fewer for short rows),
-// the row total comes from a DPP-only reduction and is multiplied by the row
-// scale once. Inputs the fast kernel cannot take (K % 64 != 0, K > 4096,
-// unaligned pointers) use a one-wave-per-row kernel that adds, subtracts or
-// skips each x directly.
+// chunk of K (one 16-byte load of four words); lanes cover a row in groups
+// (64 lanes for K = 4096, fewer for short rows) and the row total comes from
+// a DPP-only reduction, multiplied by the row scale once. The hi/lo split of
+// x is done once per workgroup of 16 waves into LDS (a few operations per
+// thread) rather than once per wave, and every weight load is issued before
+// the split so that its latency is hidden behind it. Inputs the fast kernel
+// cannot take (K % 64 != 0, K > 4096, unaligned pointers) use a
+// one-wave-per-row kernel that adds, subtracts or skips each x directly.
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -104,59 +106,76 @@ __device__ __forceinline__ float ternary_word_dot(uint32_t w, const XPairs& xp, 
     return a0 + a1;
 }
 
-// Fast path: K % 64 == 0, packed and x 16-byte aligned, K <= 64 * G. A group
-// of G lanes covers one row; lane gl owns the 64-column chunk gl (one 16-byte
-// load of 4 words) for every row, with its x pairs in registers. R rows per
-// group and pass; all loads unconditional (clamped, masked at use).
-template <int G, int R>
-__global__ __launch_bounds__(kThreads) void ternary_kernel(const uint32_t* __restrict__ packed,
-                                                           const float* __restrict__ row_scale,
-                                                           const float* __restrict__ x,
-                                                           float* __restrict__ y, int n, int kq) {
-    constexpr int kGroupsPerWave = kWave / G;
+// Fast path: K % 64 == 0, packed and x 16-byte aligned, K <= 4096. A group of
+// G lanes covers one row (64 / G rows per wave, 16 waves per workgroup); lane
+// gl owns the 64-column chunk gl. Per workgroup and pass: every thread first
+// requests its x values for the split and its 16-byte weight chunk, then
+// splits its share of x into bf16 hi/lo pairs in LDS; after one barrier each
+// lane reads the pairs of its chunk and sums its row.
+constexpr int kTernaryWaves = 16;
+constexpr int kPairPitch = 68;   // dwords per chunk in LDS: 64 pair words + 4 (spreads the banks)
+
+template <int G>
+__global__ __launch_bounds__(kWave * kTernaryWaves) void ternary_kernel(const uint32_t* __restrict__ packed,
+                                                                        const float* __restrict__ row_scale,
+                                                                        const float* __restrict__ x,
+                                                                        float* __restrict__ y, int n, int kq) {
+    constexpr int kRowsPerWave = kWave / G;
+    constexpr int kRowsPerBlock = kTernaryWaves * kRowsPerWave;
+    __shared__ __attribute__((aligned(16))) uint32_t pairs[64 * kPairPitch];
     const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
     const int gl = lane & (G - 1);
-    const int grp = lane / G;
-    const int wave = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
-    const int units = gridDim.x * kWavesPerBlock * kGroupsPerWave;
-    const int unit = wave * kGroupsPerWave + grp;
     const int c = min(gl, kq - 1);
     const bool cvalid = gl < kq;
-
-    XPairs xp[4];
-    {
-        const float4* xv = reinterpret_cast<const float4*>(x) + c * 16;
-        float xs[64];
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            const float4 v = xv[q];
-            xs[4 * q + 0] = v.x;
-            xs[4 * q + 1] = v.y;
-            xs[4 * q + 2] = v.z;
-            xs[4 * q + 3] = v.w;
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int p = 0; p < 8; ++p) split_pair(xs[16 * q + p], xs[16 * q + p + 8], xp[q].hi[p], xp[q].lo[p]);
-    }
+    const int npairs = kq * 32;   // (x[16 w + p], x[16 w + p + 8]) for p < 8, four words per chunk
     const uint4* pk = reinterpret_cast<const uint4*>(packed);
-    for (int pass = 0; (pass * units + wave * kGroupsPerWave) * R < n; ++pass) {
-        const int row0 = (pass * units + unit) * R;
-        uint4 w[R];
+
+    for (int row0 = blockIdx.x * kRowsPerBlock; row0 < n; row0 += gridDim.x * kRowsPerBlock) {
+        // x values of this thread's pairs, then its weight chunk (vector loads complete in order)
+        float xa[2], xb[2];
 #pragma unroll
-        for (int r = 0; r < R; ++r) w[r] = load_nt16(pk + (int64_t)min(row0 + r, n - 1) * kq + c);
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const uint4 wv = cvalid ? w[r] : make_uint4(0u, 0u, 0u, 0u);
-            float acc = ternary_word_dot(wv.x, xp[0], 0.f);
-            acc = ternary_word_dot(wv.y, xp[1], acc);
-            acc = ternary_word_dot(wv.z, xp[2], acc);
-            acc = ternary_word_dot(wv.w, xp[3], acc);
-            acc = group_total<G>(acc);
-            const int row = row0 + r;
-            if (gl == G - 1 && row < n) y[row] = row_scale[row] * (2.0f * acc);
+        for (int j = 0; j < 2; ++j) {
+            const int t = min((int)threadIdx.x + j * kWave * kTernaryWaves, npairs - 1);
+            const int base = 64 * (t >> 5) + 16 * ((t >> 3) & 3) + (t & 7);
+            xa[j] = x[base];
+            xb[j] = x[base + 8];
         }
+        const int row = row0 + wave * kRowsPerWave + lane / G;
+        const uint4 w = load_nt16(pk + (int64_t)min(row, n - 1) * kq + c);
+        const float s = row_scale[min(row, n - 1)];
+        __syncthreads();   // the previous pass is done reading the pairs
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int t = (int)threadIdx.x + j * kWave * kTernaryWaves;
+            if (t < npairs) {
+                uint32_t hi, lo;
+                split_pair(xa[j], xb[j], hi, lo);
+                const int at = (t >> 5) * kPairPitch + 16 * ((t >> 3) & 3) + (t & 7);
+                pairs[at] = hi;
+                pairs[at + 8] = lo;
+            }
+        }
+        __syncthreads();
+        XPairs xp[4];
+        {
+            const uint4* pp = reinterpret_cast<const uint4*>(pairs + c * kPairPitch);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint4 h0 = pp[4 * q + 0], h1 = pp[4 * q + 1], l0 = pp[4 * q + 2], l1 = pp[4 * q + 3];
+                xp[q].hi[0] = h0.x; xp[q].hi[1] = h0.y; xp[q].hi[2] = h0.z; xp[q].hi[3] = h0.w;
+                xp[q].hi[4] = h1.x; xp[q].hi[5] = h1.y; xp[q].hi[6] = h1.z; xp[q].hi[7] = h1.w;
+                xp[q].lo[0] = l0.x; xp[q].lo[1] = l0.y; xp[q].lo[2] = l0.z; xp[q].lo[3] = l0.w;
+                xp[q].lo[4] = l1.x; xp[q].lo[5] = l1.y; xp[q].lo[6] = l1.z; xp[q].lo[7] = l1.w;
+            }
+        }
+        const uint4 wv = cvalid ? w : make_uint4(0u, 0u, 0u, 0u);
+        float acc = ternary_word_dot(wv.x, xp[0], 0.f);
+        acc = ternary_word_dot(wv.y, xp[1], acc);
+        acc = ternary_word_dot(wv.z, xp[2], acc);
+        acc = ternary_word_dot(wv.w, xp[3], acc);
+        acc = group_total<G>(acc);
+        if (gl == G - 1 && row < n) y[row] = s * (2.0f * acc);
     }
 }
 
@@ -184,35 +203,15 @@ int resident_blocks(Kernel kernel, size_t lds_bytes) {
     return per_cu * device_cu_count();
 }
 
-template <int G, int R>
-hipError_t run_fast_r(const uint32_t* packed, const float* s, const float* x, float* y, int n,
-                      int kq, int cap, hipStream_t stream) {
-    const int rows_per_block = kWavesPerBlock * (kWave / G) * R;
-    const int want = (n + rows_per_block - 1) / rows_per_block;
-    const int grid = want < cap ? want : cap;
-    ternary_kernel<G, R><<<grid, kThreads, 0, stream>>>(packed, s, x, y, n, kq);
-    return hipGetLastError();
-}
-
-// Rows per group and pass: each group splits its x slice once (about as many
-// VALU operations as two rows of weights), so a group takes 4 rows while that
-// still leaves at least one wave per SIMD on every compute unit, else fewer.
 template <int G>
 hipError_t run_fast(const uint32_t* packed, const float* s, const float* x, float* y, int n, int kq,
                     hipStream_t stream) {
-    static int cap1 = 0, cap2 = 0, cap4 = 0;
-    if (cap1 == 0) {
-        cap1 = resident_blocks(ternary_kernel<G, 1>, 0);
-        cap2 = resident_blocks(ternary_kernel<G, 2>, 0);
-        cap4 = resident_blocks(ternary_kernel<G, 4>, 0);
-    }
-    const int64_t groups_per_block = kWavesPerBlock * (kWave / G);
-    const int64_t min_blocks = device_cu_count();   // one block (4 waves) per compute unit
-    if ((n + 4 * groups_per_block - 1) / (4 * groups_per_block) >= min_blocks)
-        return run_fast_r<G, 4>(packed, s, x, y, n, kq, cap4, stream);
-    if ((n + 2 * groups_per_block - 1) / (2 * groups_per_block) >= min_blocks || cap1 * groups_per_block < n)
-        return run_fast_r<G, 2>(packed, s, x, y, n, kq, cap2, stream);
-    return run_fast_r<G, 1>(packed, s, x, y, n, kq, cap1, stream);
+    constexpr int kRowsPerBlock = kTernaryWaves * (kWave / G);
+    // every row group its own workgroup up to four per compute unit, then passes
+    const int want = (n + kRowsPerBlock - 1) / kRowsPerBlock;
+    const int grid = min(want, 4 * device_cu_count());
+    ternary_kernel<G><<<grid, kWave * kTernaryWaves, 0, stream>>>(packed, s, x, y, n, kq);
+    return hipGetLastError();
 }
 
 }  // namespace
