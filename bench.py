@@ -47,8 +47,8 @@ PROFILES = os.path.join(ROOT, "profiles")
 # C-ABI dispatch in api.hip): a counter summary stays valid only while these are
 # unchanged.
 KERNEL_SOURCES = {
-    "gemv": ["gemv.hip", "mfma_stream.hpp"],
-    "moe": ["moe.hip", "mfma_stream.hpp"],
+    "gemv": ["gemv.hip"],
+    "moe": ["moe.hip", "moe_engine.hpp"],
     "ternary": ["ternary.hip"],
     "gather": ["gather.hip"],
     "decode": ["decode.hip"],

@@ -12,17 +12,16 @@
 //   1. route: one workgroup turns topk_ids into per-expert counts, offsets
 //      and a stable (token, slot)-ordered list of rows per expert, using
 //      wave ballots for the ranks (no atomics, so the layout is deterministic).
-//   2. gemm1: a workgroup owns one expert and 128 intermediate columns j: its
-//      four waves each stream 2 gate and 2 up row tiles (16 rows each) of W13
-//      with 16-byte loads, decode them in registers with
-//      v_cvt_scalef32_pk_bf16_fp4 (block scale applied by the conversion)
-//      directly into the A operand of v_mfma_f32_16x16x32_bf16, and multiply
-//      them with the expert's token rows staged 128 columns at a time in LDS.
-//      Every weight byte is read once for all tokens of its expert (up to 64
-//      tokens per pass). The epilogue applies silu(gate) * up in fp32 and
-//      stores the activation as bf16 (the MFMA operand type of gemm2).
-//   3. gemm2: the same engine over W2 rows with the activations as operand,
-//      fp32 results per (expert row, hidden).
+//   2. gemm1: a workgroup of eight waves owns one expert and 128 intermediate
+//      columns j: wave w streams the gate rows j0 + 16 w .. + 15 and the
+//      matching up rows of W13 through the engine of moe_engine.hpp against
+//      the expert's token rows (up to 64 per pass), so every weight byte is
+//      read once for all tokens of its expert; the epilogue applies
+//      silu(gate) * up in fp32 and stores the activation as bf16 (the MFMA
+//      operand type of gemm2).
+//   3. gemm2: the same engine over W2, one 16-row tile per wave, 128 hidden
+//      rows per workgroup, with the activations as operand; fp32 results per
+//      (expert row, hidden).
 //   4. combine: out[t] = bf16(sum over slots, in slot order, of weight * y).
 //   Lane layout of the MFMA (checked on the device): lane l holds row l % 16
 //   of A and column l % 16 of B, k = 8 * (l / 16) + 0..7; D row 4 * (l / 16) +
@@ -31,7 +30,7 @@
 //   and the token rows are read from LDS with the same k order.
 #include "device.hpp"
 #include "kernels.hpp"
-#include "mfma_panel.hpp"
+#include "moe_engine.hpp"
 
 namespace e2m1 {
 namespace {
@@ -40,14 +39,9 @@ constexpr int kMaxExperts = 512;
 constexpr int kRouteThreads = 1024;
 constexpr int kRouteWaves = kRouteThreads / kWave;
 
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * kWave;
-constexpr int kMTiles = 4;                            // token tiles of 16 per pass
-constexpr int kTokensPerPass = kMTiles * 16;          // 64
-constexpr int kGemm1Tiles = 4;                        // per wave: 2 gate + 2 up tiles of 16 rows
-constexpr int kGemm1Cols = kWaves * (kGemm1Tiles / 2) * 16;   // 128 intermediate columns per block
-constexpr int kGemm2Tiles = 2;                        // per wave: 2 tiles of 16 W2 rows
-constexpr int kGemm2Rows = kWaves * kGemm2Tiles * 16; // 128 hidden rows per block
+constexpr int kThreads = kEngineThreads;             // 8 waves
+constexpr int kGemm1Cols = kEngineWaves * 16;         // 128 intermediate columns per block (gate + up tiles)
+constexpr int kGemm2Rows = kEngineWaves * 16;         // 128 hidden rows per block
 
 struct MoeLayout {
     size_t cnt, off, pair_row, row_pair, act, y, total;
@@ -147,18 +141,17 @@ __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-
 
 // ----------------------------------------------------------------- gemm1 --
 
-using Gemm1 = PanelGemm<kGemm1Tiles, kMTiles, kWaves>;
-using Gemm2 = PanelGemm<kGemm2Tiles, kMTiles, kWaves>;
+using Gemm1 = MoeEngine<2>;
+using Gemm2 = MoeEngine<1>;
 
-// Workgroup (j block, expert): wave w streams gate rows j and up rows inter + j
-// for the 16 kGemm1Tiles / 2 consecutive j of its slice, against all of the
-// expert's tokens (kTokensPerPass per pass), then act = silu(gate) * up.
+// Workgroup (j block, expert): wave w streams gate rows j0 + 16 w .. + 15 and
+// up rows inter + the same j against all of the expert's tokens (64 per pass),
+// then act = silu(gate) * up.
 __global__ __launch_bounds__(kThreads) void moe_gemm1_kernel(
-    const uint16_t* __restrict__ x, const uint8_t* __restrict__ w13, const uint8_t* __restrict__ w13s,
+    const uint16_t* x, const uint8_t* w13, const uint8_t* w13s,
     const int* __restrict__ cnt, const int* __restrict__ off, const int* __restrict__ row_pair,
     uint16_t* __restrict__ act, int H, int I, int topk) {
-    __shared__ __attribute__((aligned(16))) uint16_t lds[Gemm1::kLdsElems];
-    __shared__ int rowidx[kTokensPerPass];
+    __shared__ Gemm1::Shared sh;
     const int e = blockIdx.y;
     const int n_e = cnt[e];
     if (n_e == 0) return;
@@ -166,45 +159,34 @@ __global__ __launch_bounds__(kThreads) void moe_gemm1_kernel(
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wave-uniform
     const int g = lane >> 4, r16 = lane & 15;
-    constexpr int NH = kGemm1Tiles / 2;      // gate tiles (then as many up tiles)
-    const int j0 = blockIdx.x * kGemm1Cols + wave * (NH * 16);
-    int wrow[kGemm1Tiles];
-    bool tvalid[kGemm1Tiles];
-#pragma unroll
-    for (int t = 0; t < NH; ++t) {
-        const int jt = j0 + 16 * t;
-        tvalid[t] = tvalid[NH + t] = jt < I;
-        const int j = min(jt + r16, I - 1);
-        wrow[t] = j;
-        wrow[NH + t] = I + j;
-    }
+    const int jt = blockIdx.x * kGemm1Cols + wave * 16;   // this wave's 16 columns j
+    const bool tvalid = jt < I;
+    const int tile_row[2] = {jt, I + jt};
     const uint8_t* we = w13 + (size_t)e * 2 * I * (H / 2);
     const uint8_t* se = w13s + (size_t)e * 2 * I * (H / 32);
 
-    for (int m0 = 0; m0 < n_e; m0 += kTokensPerPass) {
-        const int nv = min(kTokensPerPass, n_e - m0);
+    for (int m0 = 0; m0 < n_e; m0 += kEngineMaxTokens) {
+        const int nv = min(kEngineMaxTokens, n_e - m0);
         const int mt = (nv + 15) / 16;
         __syncthreads();   // the previous pass is done with rowidx and the panels
-        if (threadIdx.x < nv) rowidx[threadIdx.x] = row_pair[base + m0 + threadIdx.x] / topk;
+        if ((int)threadIdx.x < nv) sh.rowidx[threadIdx.x] = row_pair[base + m0 + threadIdx.x] / topk;
         __syncthreads();
-        f32x4 acc[kGemm1Tiles][kMTiles];
+        f32x4 acc[2][4];
 #pragma unroll
-        for (int t = 0; t < kGemm1Tiles; ++t)
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int m = 0; m < kMTiles; ++m) acc[t][m] = f32x4{0.f, 0.f, 0.f, 0.f};
-        Gemm1::run_mt(mt, we, se, H, wrow, tvalid, x, (size_t)H, rowidx, nv, lds, acc);
+            for (int m = 0; m < 4; ++m) acc[t][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+        Gemm1::run_mt(mt, sh, we, se, H, tile_row, 2 * I, x, (size_t)H, nv, acc);
         // epilogue: act = silu(gate) * up -> bf16, 4 consecutive j per lane
+        if (tvalid) {
 #pragma unroll
-        for (int t = 0; t < NH; ++t) {
-            if (!tvalid[t]) continue;
-#pragma unroll
-            for (int m = 0; m < kMTiles; ++m) {
+            for (int m = 0; m < 4; ++m) {
                 const int r = 16 * m + r16;
                 if (m < mt && r < nv) {
-                    const f32x4 gt = acc[t][m], up = acc[NH + t][m];
+                    const f32x4 gt = acc[0][m], up = acc[1][m];
                     const uint32_t lo = pack_bf16x2(silu_f32(gt[0]) * up[0], silu_f32(gt[1]) * up[1]);
                     const uint32_t hi = pack_bf16x2(silu_f32(gt[2]) * up[2], silu_f32(gt[3]) * up[3]);
-                    const int j = j0 + 16 * t + 4 * g;
+                    const int j = jt + 4 * g;
                     *reinterpret_cast<uint2*>(act + (size_t)(base + m0 + r) * I + j) = make_uint2(lo, hi);
                 }
             }
@@ -214,13 +196,12 @@ __global__ __launch_bounds__(kThreads) void moe_gemm1_kernel(
 
 // ----------------------------------------------------------------- gemm2 --
 
-// Workgroup (hidden block, expert): wave w streams kGemm2Tiles row tiles of W2
+// Workgroup (hidden block, expert): wave w streams W2 rows h0 + 16 w .. + 15
 // against the expert's activation rows; fp32 results per (expert row, hidden).
 __global__ __launch_bounds__(kThreads) void moe_gemm2_kernel(
-    const uint16_t* __restrict__ act, const uint8_t* __restrict__ w2, const uint8_t* __restrict__ w2s,
+    const uint16_t* act, const uint8_t* w2, const uint8_t* w2s,
     const int* __restrict__ cnt, const int* __restrict__ off, float* __restrict__ y, int H, int I) {
-    __shared__ __attribute__((aligned(16))) uint16_t lds[Gemm2::kLdsElems];
-    __shared__ int rowidx[kTokensPerPass];
+    __shared__ Gemm2::Shared sh;
     const int e = blockIdx.y;
     const int n_e = cnt[e];
     if (n_e == 0) return;
@@ -228,39 +209,29 @@ __global__ __launch_bounds__(kThreads) void moe_gemm2_kernel(
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wave-uniform
     const int g = lane >> 4, r16 = lane & 15;
-    constexpr int NT = kGemm2Tiles;
-    const int h0 = blockIdx.x * kGemm2Rows + wave * (NT * 16);
-    int wrow[NT];
-    bool tvalid[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-        tvalid[t] = h0 + 16 * t < H;
-        wrow[t] = min(h0 + 16 * t + r16, H - 1);
-    }
+    const int ht = blockIdx.x * kGemm2Rows + wave * 16;
+    const bool tvalid = ht < H;
+    const int tile_row[1] = {ht};
     const uint8_t* we = w2 + (size_t)e * H * (I / 2);
     const uint8_t* se = w2s + (size_t)e * H * (I / 32);
 
-    for (int m0 = 0; m0 < n_e; m0 += kTokensPerPass) {
-        const int nv = min(kTokensPerPass, n_e - m0);
+    for (int m0 = 0; m0 < n_e; m0 += kEngineMaxTokens) {
+        const int nv = min(kEngineMaxTokens, n_e - m0);
         const int mt = (nv + 15) / 16;
         __syncthreads();
-        if (threadIdx.x < nv) rowidx[threadIdx.x] = base + m0 + threadIdx.x;
+        if ((int)threadIdx.x < nv) sh.rowidx[threadIdx.x] = base + m0 + threadIdx.x;
         __syncthreads();
-        f32x4 acc[NT][kMTiles];
+        f32x4 acc[1][4];
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
+        for (int m = 0; m < 4; ++m) acc[0][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+        Gemm2::run_mt(mt, sh, we, se, I, tile_row, H, act, (size_t)I, nv, acc);
+        if (tvalid) {
 #pragma unroll
-            for (int m = 0; m < kMTiles; ++m) acc[t][m] = f32x4{0.f, 0.f, 0.f, 0.f};
-        Gemm2::run_mt(mt, we, se, I, wrow, tvalid, act, (size_t)I, rowidx, nv, lds, acc);
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            if (!tvalid[t]) continue;
-#pragma unroll
-            for (int m = 0; m < kMTiles; ++m) {
+            for (int m = 0; m < 4; ++m) {
                 const int r = 16 * m + r16;
                 if (m < mt && r < nv) {
-                    const int h = h0 + 16 * t + 4 * g;
-                    *reinterpret_cast<f32x4*>(y + (size_t)(base + m0 + r) * H + h) = acc[t][m];
+                    const int h = ht + 4 * g;
+                    *reinterpret_cast<f32x4*>(y + (size_t)(base + m0 + r) * H + h) = acc[0][m];
                 }
             }
         }

@@ -1,0 +1,226 @@
+// moe_engine.hpp -- weight-streaming bf16 MFMA engine of the MoE expert GEMMs:
+// an MXFP4 weight matrix read once from HBM against up to 64 bf16 token rows.
+//
+// Computes acc[t][m] += sum_k W[row of tile t, k] * X[token 16 m + column, k]
+// with v_mfma_f32_16x16x32_bf16 (fp32 accumulation) for NT weight tiles of 16
+// rows per wave and up to four token tiles of 16 rows per pass.
+//
+// MFMA lane layout: lane l = 16 g + r holds row r of the A operand (weights)
+// and column r of the B operand (tokens), k slots 8 g .. 8 g + 7; D element
+// (row 4 g + j, column r) is component j of the accumulator in lane l.
+//
+// A step is 256 columns, eight E8M0 blocks, one 128-byte line per weight row.
+//   * Weights: each wave loads its tiles' lines with coalesced 16-byte loads
+//     (one instruction = 8 rows x 128 bytes), two steps ahead of use, and
+//     passes them through a private LDS buffer to reach the MFMA layout: lane
+//     (r, g) then holds blocks g and g + 4 of row r. Block b = g + 4 h feeds
+//     four MFMAs, MFMA i taking codes [8 i, 8 i + 8) of the block as k slots
+//     8 g .. 8 g + 7; v_cvt_scalef32_pk_bf16_fp4 decodes two codes and applies
+//     the block scale in one instruction. The E8M0 byte of each chunk is
+//     loaded by the lane that loads the chunk and takes the same LDS route.
+//   * Tokens: the workgroup stages the step's 256 columns of the pass's token
+//     rows in a triple-buffered LDS panel, requested two steps ahead and
+//     written one step ahead (an L2 round trip per step would otherwise sit
+//     in front of every barrier), and every wave reads
+//     its B operands from it at the same columns as the A operands, so the
+//     column -> k-slot map is the same for both and the sum over k is
+//     complete. Columns past K are staged as zeros, so weight blocks past the
+//     row end (loaded clamped, finite) add nothing.
+//
+// Every load is issued on every path (indices clamped), the token loads of a
+// step before its weight loads, so each wait the compiler places counts
+// exactly the loads issued after the one it needs: the weights of step s are
+// waited for only when step s is computed, two steps after their request.
+#pragma once
+
+#include "device.hpp"
+
+namespace e2m1 {
+
+constexpr int kEngineWaves = 8;
+constexpr int kEngineThreads = kEngineWaves * kWave;
+constexpr int kEngineStepCols = 256;
+constexpr int kEngineMaxTokens = 64;                 // token rows per pass (four MFMA tiles)
+constexpr int kPanelPitch = kEngineStepCols + 8;     // bf16 per staged token row (16-byte pad spreads banks)
+constexpr int kPanelElems = kEngineMaxTokens * kPanelPitch;
+constexpr int kWBufPitch = 9;                        // uint4 per transposed weight row (8 blocks + pad)
+
+// Compiler-only fence: keeps loads where they are written (issued early).
+// Emits no instruction. The weight and token pointers reaching it are not
+// __restrict__: loads through a restrict pointer to read-only memory may be
+// moved across.
+__device__ __forceinline__ void engine_fence() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int NT>
+struct EngineStep {
+    uint4 w[NT][2];       // coalesced: rows 8 q + lane / 8 of each tile, block lane % 8
+    uint8_t e[NT][2];     // E8M0 bytes of the same chunks (bytes: widened at use)
+};
+
+template <int NT>
+struct MoeEngine {
+    static constexpr int kWBufElems = NT * 16 * kWBufPitch;   // uint4 per wave
+
+    // Shared state of one pass (in LDS, owned by the caller's kernel).
+    struct Shared {
+        uint16_t panel[3][kPanelElems];
+        uint4 wbuf[kEngineWaves][kWBufElems];
+        uint8_t sbuf[kEngineWaves][NT * 16 * 8];   // E8M0 bytes, [tile][row][block]
+        int rowidx[kEngineMaxTokens];
+    };
+
+    // Weight lines and scales of step `step` for this wave's tiles. tile_row[t]:
+    // first row of tile t; rows are clamped to nrows - 1, blocks to kb - 1.
+    static __device__ __forceinline__ void issue_weights(EngineStep<NT>& b, const uint8_t* w, const uint8_t* ws,
+                                                         int K, const int (&tile_row)[NT], int nrows, int step) {
+        const int lane = threadIdx.x & (kWave - 1);
+        const int kb = K / 32;
+        const int cb = min(8 * step + (lane & 7), kb - 1);
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int row = min(tile_row[t] + 8 * q + (lane >> 3), nrows - 1);
+                b.w[t][q] = load_nt16(w + (size_t)row * (K / 2) + (size_t)cb * 16);
+                b.e[t][q] = ws[(size_t)row * kb + cb];
+            }
+    }
+
+    // Token columns [256 step, +256) of the pass's first 16 MTA rows: thread t
+    // takes 16-byte chunks t + 512 j of the panel (row = chunk / 32), whose
+    // source rows src[j] are fixed for the pass.
+    template <int MTA>
+    static __device__ __forceinline__ void issue_tokens(uint4 (&tr)[MTA], const uint16_t* const (&src)[MTA], int K,
+                                                        int step) {
+#pragma unroll
+        for (int j = 0; j < MTA; ++j) {
+            const int ch = ((int)threadIdx.x + kEngineThreads * j) & 31;
+            const int col = min(step * kEngineStepCols + 8 * ch, K - 8);
+            tr[j] = *reinterpret_cast<const uint4*>(src[j] + col);
+        }
+    }
+
+    template <int MTA>
+    static __device__ __forceinline__ void store_tokens(const uint4 (&tr)[MTA], uint16_t* panel, int K, int step) {
+#pragma unroll
+        for (int j = 0; j < MTA; ++j) {
+            const int id = (int)threadIdx.x + kEngineThreads * j;
+            const int row = id >> 5, ch = id & 31;
+            // columns past K stage as zeros (a mask, not a select: a select lets the
+            // compiler turn the load into a conditional one placed after the weights)
+            const uint32_t keep = step * kEngineStepCols + 8 * ch < K ? ~0u : 0u;
+            *reinterpret_cast<uint4*>(panel + row * kPanelPitch + 8 * ch) =
+                make_uint4(tr[j].x & keep, tr[j].y & keep, tr[j].z & keep, tr[j].w & keep);
+        }
+    }
+
+    // acc += step held in b (weights) x token panel.
+    template <int MTA>
+    static __device__ __forceinline__ void compute(const EngineStep<NT>& b, uint4* wbuf, uint8_t* sbuf,
+                                                   const uint16_t* panel, f32x4 (&acc)[NT][4]) {
+        const int lane = threadIdx.x & (kWave - 1);
+        const int r = lane & 15, g = lane >> 4;
+        // coalesced lines (and their scale bytes) -> MFMA layout through the wave's LDS buffers
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int row = t * 16 + 8 * q + (lane >> 3);
+                wbuf[row * kWBufPitch + (lane & 7)] = b.w[t][q];
+                sbuf[row * 8 + (lane & 7)] = b.e[t][q];
+            }
+        uint4 a4[NT][2];
+        uint32_t e4[NT][2];
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                a4[t][h] = wbuf[(t * 16 + r) * kWBufPitch + g + 4 * h];
+                e4[t][h] = sbuf[(t * 16 + r) * 8 + g + 4 * h];
+            }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            float sc[NT];
+#pragma unroll
+            for (int t = 0; t < NT; ++t) sc[t] = e8m0_scale(e4[t][h]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                bf16x8 a[NT];
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    const uint32_t wd = i == 0 ? a4[t][h].x : i == 1 ? a4[t][h].y : i == 2 ? a4[t][h].z : a4[t][h].w;
+                    const u32x4 u = {fp4x2_to_bf16x2<0>(wd, sc[t]), fp4x2_to_bf16x2<1>(wd, sc[t]),
+                                     fp4x2_to_bf16x2<2>(wd, sc[t]), fp4x2_to_bf16x2<3>(wd, sc[t])};
+                    a[t] = __builtin_bit_cast(bf16x8, u);
+                }
+                const int col = 32 * (g + 4 * h) + 8 * i;
+#pragma unroll
+                for (int m = 0; m < MTA; ++m) {
+                    const bf16x8 bx = *reinterpret_cast<const bf16x8*>(panel + (16 * m + r) * kPanelPitch + col);
+#pragma unroll
+                    for (int t = 0; t < NT; ++t)
+                        acc[t][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[t], bx, acc[t][m], 0, 0, 0);
+                }
+            }
+        }
+    }
+
+    // The whole product over K for one pass of MTA token tiles. sh.rowidx
+    // holds the pass's source rows (written and synchronised by the caller).
+    template <int MTA>
+    static __device__ __forceinline__ void run(Shared& sh, const uint8_t* w, const uint8_t* ws, int K,
+                                               const int (&tile_row)[NT], int nrows, const uint16_t* xb,
+                                               size_t xpitch, int nvalid, f32x4 (&acc)[NT][4]) {
+        const int nsteps = (K + kEngineStepCols - 1) / kEngineStepCols;
+        const int wave = threadIdx.x / kWave;
+        uint4* wbuf = sh.wbuf[wave];
+        uint8_t* sbuf = sh.sbuf[wave];
+        const uint16_t* src[MTA];
+#pragma unroll
+        for (int j = 0; j < MTA; ++j) {
+            const int row = ((int)threadIdx.x + kEngineThreads * j) >> 5;
+            src[j] = xb + (size_t)sh.rowidx[min(row, nvalid - 1)] * xpitch;
+        }
+        EngineStep<NT> buf[3];
+        uint4 tr[2][MTA];
+        // step s: weights requested at s - 2 into buffer s % 3, tokens requested
+        // at s - 2 into registers s % 2, written to panel s % 3 at the end of
+        // sub-iteration s - 1. The loop starts two steps early so that the first
+        // sub-iterations only issue loads (and write panel 0). Sub-iterations
+        // are unrolled by six so that every buffer index is static.
+        for (int it = -2; it < nsteps; it += 6) {
+#pragma unroll
+            for (int bsub = 0; bsub < 6; ++bsub) {
+                const int s = it + bsub;   // s + 2 == it + 2 + bsub, it + 2 is a multiple of 6
+                if (s >= nsteps) break;    // workgroup-uniform
+                const int next = min(s + 2, nsteps - 1);
+                issue_tokens<MTA>(tr[bsub & 1], src, K, next);
+                engine_fence();
+                issue_weights(buf[bsub % 3], w, ws, K, tile_row, nrows, next);
+                engine_fence();
+                if (s >= 0) compute<MTA>(buf[(bsub + 1) % 3], wbuf, sbuf, sh.panel[(bsub + 1) % 3], acc);
+                engine_fence();
+                // tokens of step s + 1 (requested one sub-iteration ago) -> panel (s + 1) % 3
+                store_tokens<MTA>(tr[(bsub + 1) & 1], sh.panel[(bsub + 2) % 3], K, min(max(s + 1, 0), nsteps - 1));
+                __syncthreads();
+            }
+        }
+    }
+
+    // run<MTA> for MTA = mt (1 <= mt <= 4), chosen once per pass.
+    static __device__ __forceinline__ void run_mt(int mt, Shared& sh, const uint8_t* w, const uint8_t* ws, int K,
+                                                  const int (&tile_row)[NT], int nrows, const uint16_t* xb,
+                                                  size_t xpitch, int nvalid, f32x4 (&acc)[NT][4]) {
+        switch (mt) {
+            case 1: run<1>(sh, w, ws, K, tile_row, nrows, xb, xpitch, nvalid, acc); break;
+            case 2: run<2>(sh, w, ws, K, tile_row, nrows, xb, xpitch, nvalid, acc); break;
+            case 3: run<3>(sh, w, ws, K, tile_row, nrows, xb, xpitch, nvalid, acc); break;
+            default: run<4>(sh, w, ws, K, tile_row, nrows, xb, xpitch, nvalid, acc); break;
+        }
+    }
+};
+
+}  // namespace e2m1
