@@ -12,19 +12,18 @@
 //     (zero codes give +/-0, which add nothing to a sum). v_dot2_f32_bf16
 //     multiplies the pair by the matching pair of x and accumulates in fp32:
 //     per byte of weights one conversion and one dot2.
-//   * Batch 1 (the bandwidth-bound case): each lane owns fixed 32-column
-//     chunks of K, so its slice of x sits in registers for the whole kernel,
-//     and every weight byte is read once with a 16-byte load. Rows are dealt
-//     to waves grid-stride (row = wave + i * waves) and streamed through a
-//     three-buffer register pipeline: the loads of row i + 2 are issued before
-//     row i is decoded, so two rows per wave are always in flight and the
-//     decode never delays the next request. About 4 MB in flight over the
-//     chip measured best for these sizes: one workgroup of four waves per
-//     compute unit. Rows up to 8192 columns belong to one wave (row totals by
-//     DPP); longer rows are split over the waves of a workgroup, one
-//     64-chunk slice each, whose partial sums meet in LDS. A lane keeps the
-//     total of its i-th row in register lane i and stores 64 rows at a time.
-//     Short rows (K < 2048) use groups of 8 to 32 lanes per row instead.
+//   * Batch 1 (the bandwidth-bound case): a wave owns a tile of 16 rows x
+//     1024 columns (32 chunks of one scale block each): eight coalesced
+//     16-byte loads, each covering two rows x 512 bytes, issued at once, with
+//     the 32 lanes of a half-wave on one row and each lane's slice of x in
+//     registers. A workgroup holds the S = K / 1024 waves of one row tile,
+//     whose partial row sums meet in LDS; the hardware streams through the
+//     tiles (one workgroup each), which measured faster on these sizes than
+//     keeping rows in flight from a resident grid. Every weight byte is read
+//     once and the row totals come from DPP reductions over 32 lanes.
+//     Longer rows (K > 16384) are split over the waves of a workgroup, one
+//     chunk per lane, with three rows in flight; short rows (K <= 1024) use
+//     groups of 8 to 32 lanes per row.
 //   * Batch 2..16: the same weight bytes feed bf16 MFMA
 //     (v_mfma_f32_16x16x32_bf16) with the batch as the N dimension: a
 //     workgroup takes a tile of 16 rows, its S waves split K into slices of
@@ -165,32 +164,11 @@ __device__ __forceinline__ void issue_here() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// Stores the row totals a wave keeps in register lanes: lane l holds the total
-// of its row number base + l (rows wave + (base + l) * stride).
-template <bool kBf16Out>
-__device__ __forceinline__ void store_row_totals(void* y, float res, int lane, int base, int count,
-                                                 int wave, int stride) {
-    if (lane < count) store_out<kBf16Out>(y, (int64_t)wave + (int64_t)(base + lane) * stride, res);
-}
-
-constexpr int kRowsInFlight = 2;   // per wave, while one more row is decoded
-
 template <int CPL>
 struct RowBuf {
     uint4 w[CPL];
     uint8_t e[CPL];   // kept as bytes: widened at use, so no instruction touches a pending load
 };
-
-template <int CPL>
-__device__ __forceinline__ void issue_row(RowBuf<CPL>& b, const uint4* pv, const uint8_t* scales, int row, int kc,
-                                          int lane) {
-#pragma unroll
-    for (int ci = 0; ci < CPL; ++ci) {
-        const int64_t blk = (int64_t)row * kc + min(lane + kWave * ci, kc - 1);
-        b.w[ci] = load_nt16(pv + blk);
-        b.e[ci] = scales[blk];
-    }
-}
 
 // x words of 32-column chunk min(c, kc - 1) (16 bf16 pairs). Lanes whose
 // chunk lies past the row end drop their partial sums at use instead (a
@@ -207,61 +185,60 @@ __device__ __forceinline__ void load_x_chunk(uint32_t (&xr)[16], const uint16_t*
     }
 }
 
-// Batch 1, 64 < K/32 <= 64 CPL: whole rows per wave. Lane l owns chunks
-// l + 64 ci; chunks past the row end are loaded clamped and their partial
-// sums dropped (E2M1 codes times a clamped E8M0 scale are always finite).
-// Row r of the wave lives in buffer r % 3; the loop starts two rows early so
-// that the first two sub-iterations only issue loads (there is no separate
-// prologue, and every pass through the loop issues its loads in the same
-// order, so each wait counts exactly the loads issued after the one it
-// needs). Loads past a wave's last row re-read that row.
-template <int CPL, bool kBf16Out>
-__global__ __launch_bounds__(kThreads) void gemv_b1_rows_kernel(const uint8_t* packed,
-                                                                const uint8_t* scales,
-                                                                const uint16_t* __restrict__ x,
-                                                                void* __restrict__ y, int n, int kc) {
-    constexpr int kBufs = kRowsInFlight + 1;
+// Batch 1, 32 < K/32 <= 32 S: one workgroup of S waves per tile of 16 rows.
+// Wave w owns chunks 32 w .. 32 w + 31; lane l takes chunk 32 w + (l % 32)
+// of rows 2 q + l / 32 (q = 0..7), so each load instruction reads two rows
+// x 512 contiguous bytes. Chunks past the row end are loaded clamped and
+// their partial sums dropped (E2M1 codes times a clamped E8M0 scale are
+// always finite). The 32-lane row sums of the S waves meet in LDS and are
+// summed in a fixed order.
+template <int S, bool kBf16Out>
+__global__ __launch_bounds__(kWave * S) void gemv_b1_tile_kernel(const uint8_t* packed, const uint8_t* scales,
+                                                                 const uint16_t* __restrict__ x,
+                                                                 void* __restrict__ y, int n, int kc) {
+    __shared__ float part[S][16];
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerBlock + threadIdx.x / kWave);
-    if (wave >= n) return;
-    const int nw = gridDim.x * kWavesPerBlock;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int half = lane >> 5, cl = lane & 31;
+    const int c_raw = wv * 32 + cl;
+    const bool cvalid = c_raw < kc;
+    const int c = min(c_raw, kc - 1);
     const uint4* pv = reinterpret_cast<const uint4*>(packed);
-
-    uint32_t xr[CPL][16];
-#pragma unroll
-    for (int ci = 0; ci < CPL; ++ci) load_x_chunk(xr[ci], x, lane + kWave * ci, kc);
+    uint32_t xr[16];
+    load_x_chunk(xr, x, c, kc);
     issue_here();
-    const int iters = (n - 1 - wave) / nw + 1;
-    const int last = wave + (iters - 1) * nw;
-    RowBuf<CPL> buf[kBufs];
-    float res = 0.f;
-    for (int it = -kRowsInFlight; it < iters; it += kBufs) {
+    const int tile = blockIdx.x;
+    uint4 w[8];
+    uint8_t e[8];   // kept as bytes: widened at use
 #pragma unroll
-        for (int b = 0; b < kBufs; ++b) {
-            const int i = it + b;   // row being decoded; row i + 2 is issued
-            issue_row(buf[b], pv, scales, min(wave + (i + kRowsInFlight) * nw, last), kc, lane);
-            issue_here();
-            if (i >= 0 && i < iters) {
-                const RowBuf<CPL>& cur = buf[(b + 1) % kBufs];
-                float acc = 0.f;
+    for (int q = 0; q < 8; ++q) {
+        const int row = min(tile * 16 + 2 * q + half, n - 1);
+        const int64_t blk = (int64_t)row * kc + c;
+        w[q] = load_nt16(pv + blk);
+        e[q] = scales[blk];
+    }
+    issue_here();
+    float tot[8];
 #pragma unroll
-                for (int ci = 0; ci < CPL; ++ci) {
-                    const float p = block_dot(cur.w[ci], e8m0_scale(cur.e[ci]), xr[ci], 0.f);
-                    acc += (lane + kWave * ci < kc) ? p : 0.f;
-                }
-                acc = group_total<kWave>(acc);
-                const float t = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc), kWave - 1));
-                const int slot = i & (kWave - 1);
-                if (lane == slot) res = t;
-                if (slot == kWave - 1 || i == iters - 1)
-                    store_row_totals<kBf16Out>(y, res, lane, i - slot, slot + 1, wave, nw);
-            }
-            issue_here();
-        }
+    for (int q = 0; q < 8; ++q) {
+        const float p = block_dot(w[q], e8m0_scale(e[q]), xr, 0.f);
+        tot[q] = group_total<32>(cvalid ? p : 0.f);   // lanes 31 and 63 hold the half-wave sums
+    }
+    if (cl == 31) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) part[wv][2 * q + half] = tot[q];
+    }
+    __syncthreads();
+    if (threadIdx.x < 16) {
+        float sum = 0.f;
+#pragma unroll
+        for (int j = 0; j < S; ++j) sum += part[j][threadIdx.x];
+        const int row = tile * 16 + threadIdx.x;
+        if (row < n) store_out<kBf16Out>(y, row, sum);
     }
 }
 
-// Batch 1, K/32 > 256: rows split over the S waves of a workgroup, lane l of
+// Batch 1, K/32 > 512: rows split over the S waves of a workgroup, lane l of
 // wave w owning chunk 64 w + l. Rows blockIdx.x + i * gridDim.x, three in
 // flight per wave (buffer r % 4 for row r, loop started three rows early as
 // above); the S partial totals of each row meet in LDS, 64 rows at a time,
@@ -507,13 +484,11 @@ hipError_t run_b1(const uint8_t* packed, const uint8_t* scales, const uint16_t* 
     return run_b1_r<G, CPL, 4, kBf16Out>(packed, scales, x, y, n, kc, cap4, stream);
 }
 
-template <int CPL, bool kBf16Out>
-hipError_t run_b1_rows(const uint8_t* packed, const uint8_t* scales, const uint16_t* x, void* y, int n, int kc,
+template <int S, bool kBf16Out>
+hipError_t run_b1_tile(const uint8_t* packed, const uint8_t* scales, const uint16_t* x, void* y, int n, int kc,
                        hipStream_t stream) {
-    // one workgroup of four waves per compute unit (fewer if there are fewer rows)
-    const int waves = min(n, kWavesPerBlock * device_cu_count());
-    const int grid = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
-    gemv_b1_rows_kernel<CPL, kBf16Out><<<grid, kThreads, 0, stream>>>(packed, scales, x, y, n, kc);
+    const int tiles = (n + 15) / 16;   // one workgroup per tile of 16 rows
+    gemv_b1_tile_kernel<S, kBf16Out><<<tiles, kWave * S, 0, stream>>>(packed, scales, x, y, n, kc);
     return hipGetLastError();
 }
 
@@ -531,15 +506,18 @@ hipError_t dispatch_b1(const uint8_t* packed, const uint8_t* scales, const uint1
     if (kc <= 8) return run_b1<8, 1, kBf16Out>(packed, scales, x, y, n, kc, stream);
     if (kc <= 16) return run_b1<16, 1, kBf16Out>(packed, scales, x, y, n, kc, stream);
     if (kc <= 32) return run_b1<32, 1, kBf16Out>(packed, scales, x, y, n, kc, stream);
+    if (kc <= 16 * 32) {
+        switch ((kc + 31) / 32) {
+#define E2M1_TILE_CASE(S) \
+    case S: return run_b1_tile<S, kBf16Out>(packed, scales, x, y, n, kc, stream);
+            E2M1_TILE_CASE(2) E2M1_TILE_CASE(3) E2M1_TILE_CASE(4) E2M1_TILE_CASE(5) E2M1_TILE_CASE(6)
+            E2M1_TILE_CASE(7) E2M1_TILE_CASE(8) E2M1_TILE_CASE(9) E2M1_TILE_CASE(10) E2M1_TILE_CASE(11)
+            E2M1_TILE_CASE(12) E2M1_TILE_CASE(13) E2M1_TILE_CASE(14) E2M1_TILE_CASE(15)
+            default: return run_b1_tile<16, kBf16Out>(packed, scales, x, y, n, kc, stream);
+#undef E2M1_TILE_CASE
+        }
+    }
     switch ((kc + kWave - 1) / kWave) {
-        case 1: return run_b1_rows<1, kBf16Out>(packed, scales, x, y, n, kc, stream);
-        case 2: return run_b1_rows<2, kBf16Out>(packed, scales, x, y, n, kc, stream);
-        case 3: return run_b1_rows<3, kBf16Out>(packed, scales, x, y, n, kc, stream);
-        case 4: return run_b1_rows<4, kBf16Out>(packed, scales, x, y, n, kc, stream);
-        case 5: return run_b1_split<5, kBf16Out>(packed, scales, x, y, n, kc, stream);
-        case 6: return run_b1_split<6, kBf16Out>(packed, scales, x, y, n, kc, stream);
-        case 7: return run_b1_split<7, kBf16Out>(packed, scales, x, y, n, kc, stream);
-        case 8: return run_b1_split<8, kBf16Out>(packed, scales, x, y, n, kc, stream);
         case 9: return run_b1_split<9, kBf16Out>(packed, scales, x, y, n, kc, stream);
         case 10: return run_b1_split<10, kBf16Out>(packed, scales, x, y, n, kc, stream);
         case 11: return run_b1_split<11, kBf16Out>(packed, scales, x, y, n, kc, stream);

@@ -46,14 +46,15 @@ def test_small_workload_fp32(gpu, orc):
 
 
 SHAPES = [
-    (8, 32, 1), (5, 96, 1), (33, 256, 1), (70, 512, 1), (129, 1024, 1),
-    (300, 32 * (64 * 2 + 5), 1),      # three chunks per lane, the last one ragged
-    (257, 4096, 1), (77, 8192, 1),    # register-resident x, up to four chunks per lane
-    (64, 8192 + 32, 1),               # first size of the K-split kernel (5 waves, ragged)
-    (1001, 14336, 1), (40, 16384 + 32 * 3, 1), (50, 32768, 1),   # K-split kernel, 7 to 16 waves
+    (8, 32, 1), (5, 96, 1), (33, 256, 1), (70, 512, 1), (129, 1024, 1),   # 8 to 32 lanes per row
+    (300, 32 * (64 * 2 + 5), 1),      # row tiles of 16, five waves, the last one ragged
+    (257, 4096, 1), (77, 8192, 1),    # row tiles: four and eight waves, ragged last tile
+    (64, 8192 + 32, 1),               # nine waves, one chunk in the last
+    (1001, 14336, 1),                 # fourteen waves (the down projection's K)
+    (40, 16384 + 32 * 3, 1), (50, 32768, 1),   # K-split kernel, 9 and 16 waves
     (20, 32768 + 32, 1),              # beyond the batch-1 kernels -> generic kernel
-    (70001, 2048, 1),                 # > 64 rows per wave: row totals stored 64 at a time
-    (20000, 8192 + 32, 1),            # > 64 rows per workgroup in the K-split kernel
+    (70001, 2048, 1),                 # many row tiles, ragged last one
+    (17000, 16384 + 32, 1),           # > 64 rows per workgroup in the K-split kernel
     (31, 512, 2), (17, 4096 + 32, 3), (9, 1024, 4), (65, 2048, 8), (12, 768, 16),
 ]
 
