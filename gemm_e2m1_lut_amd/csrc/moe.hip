@@ -139,6 +139,34 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(const int32_t*
 
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
 
+// Workgroups go to the eight XCDs round-robin by launch index, and each XCD
+// has its own L2. The launch index is remapped so that XCD x gets the
+// contiguous range [x * per, (x + 1) * per) of (expert, block) work items in
+// expert-major order: the token or activation rows of an expert are then read
+// into one L2 only (the activations of all experts are larger than one L2).
+constexpr int kXcds = 8;
+
+struct MoeWork {
+    int e, blk;
+    bool valid;
+};
+
+__device__ __forceinline__ MoeWork moe_work(int blocks_per_expert, int experts) {
+    const int total = blocks_per_expert * experts;
+    const int per = (total + kXcds - 1) / kXcds;
+    const int w = (int)(blockIdx.x % kXcds) * per + (int)(blockIdx.x / kXcds);
+    MoeWork m;
+    m.valid = w < total;
+    m.e = m.valid ? w / blocks_per_expert : 0;
+    m.blk = m.valid ? w % blocks_per_expert : 0;
+    return m;
+}
+
+inline int moe_grid(int blocks_per_expert, int experts) {
+    const int total = blocks_per_expert * experts;
+    return kXcds * ((total + kXcds - 1) / kXcds);
+}
+
 // ----------------------------------------------------------------- gemm1 --
 
 using Gemm1 = MoeEngine<2>;
@@ -150,16 +178,18 @@ using Gemm2 = MoeEngine<1>;
 __global__ __launch_bounds__(kThreads) void moe_gemm1_kernel(
     const uint16_t* x, const uint8_t* w13, const uint8_t* w13s,
     const int* __restrict__ cnt, const int* __restrict__ off, const int* __restrict__ row_pair,
-    uint16_t* __restrict__ act, int H, int I, int topk) {
+    uint16_t* __restrict__ act, int H, int I, int E, int topk) {
     __shared__ Gemm1::Shared sh;
-    const int e = blockIdx.y;
+    const MoeWork work = moe_work((I + kGemm1Cols - 1) / kGemm1Cols, E);
+    if (!work.valid) return;
+    const int e = work.e;
     const int n_e = cnt[e];
     if (n_e == 0) return;
     const int base = off[e];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wave-uniform
     const int g = lane >> 4, r16 = lane & 15;
-    const int jt = blockIdx.x * kGemm1Cols + wave * 16;   // this wave's 16 columns j
+    const int jt = work.blk * kGemm1Cols + wave * 16;   // this wave's 16 columns j
     const bool tvalid = jt < I;
     const int tile_row[2] = {jt, I + jt};
     const uint8_t* we = w13 + (size_t)e * 2 * I * (H / 2);
@@ -200,16 +230,18 @@ __global__ __launch_bounds__(kThreads) void moe_gemm1_kernel(
 // against the expert's activation rows; fp32 results per (expert row, hidden).
 __global__ __launch_bounds__(kThreads) void moe_gemm2_kernel(
     const uint16_t* act, const uint8_t* w2, const uint8_t* w2s,
-    const int* __restrict__ cnt, const int* __restrict__ off, float* __restrict__ y, int H, int I) {
+    const int* __restrict__ cnt, const int* __restrict__ off, float* __restrict__ y, int H, int I, int E) {
     __shared__ Gemm2::Shared sh;
-    const int e = blockIdx.y;
+    const MoeWork work = moe_work((H + kGemm2Rows - 1) / kGemm2Rows, E);
+    if (!work.valid) return;
+    const int e = work.e;
     const int n_e = cnt[e];
     if (n_e == 0) return;
     const int base = off[e];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wave-uniform
     const int g = lane >> 4, r16 = lane & 15;
-    const int ht = blockIdx.x * kGemm2Rows + wave * 16;
+    const int ht = work.blk * kGemm2Rows + wave * 16;
     const bool tvalid = ht < H;
     const int tile_row[1] = {ht};
     const uint8_t* we = w2 + (size_t)e * H * (I / 2);
@@ -299,11 +331,11 @@ hipError_t launch_moe(const uint16_t* x, const uint8_t* w13, const uint8_t* w13s
     moe_route_kernel<<<1, kRouteThreads, 0, stream>>>(ids, P, E, cnt, off, pair_row, row_pair);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    const dim3 g1((I + kGemm1Cols - 1) / kGemm1Cols, E);
-    moe_gemm1_kernel<<<g1, kThreads, 0, stream>>>(x, w13, w13s, cnt, off, row_pair, act, H, I, (int)topk);
+    const int g1 = moe_grid((I + kGemm1Cols - 1) / kGemm1Cols, E);
+    moe_gemm1_kernel<<<g1, kThreads, 0, stream>>>(x, w13, w13s, cnt, off, row_pair, act, H, I, E, (int)topk);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    const dim3 g2((H + kGemm2Rows - 1) / kGemm2Rows, E);
-    moe_gemm2_kernel<<<g2, kThreads, 0, stream>>>(act, w2, w2s, cnt, off, y, H, I);
+    const int g2 = moe_grid((H + kGemm2Rows - 1) / kGemm2Rows, E);
+    moe_gemm2_kernel<<<g2, kThreads, 0, stream>>>(act, w2, w2s, cnt, off, y, H, I, E);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     const int64_t chunks = tokens * (hidden / 8);
     const int64_t want = (chunks + kThreads - 1) / kThreads;
