@@ -17,7 +17,8 @@ function):
   * SGLang pull request 34222 digest (prhub.com.cn): NVFP4 embedding,
     dequantised at gather time.
   * FairyFuse blog post (blog.hotdry.top): 2-bit ternary GEMV with a per-row
-    scale.
+    scale, and the widely-linear complex layer y = U x + W conj(x) over four
+    such matrices.
 
 Every function here is pinned by ``tests/test_oracle_*.py`` against values
 the pages print, closed forms, library routines (torch casts, numpy matmul)
@@ -57,11 +58,11 @@ def _p(t):
 
 
 def load():
-    """Load liboracle.so, building it first if it is not there."""
+    """Load liboracle.so, building it first if it is missing or older than oracle.c."""
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_PATH):
+    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
         build()
     lib = ctypes.CDLL(_LIB_PATH)
     i64, u8, u16, u32, f32, f64 = (ctypes.c_int64, ctypes.c_uint8, ctypes.c_uint16,
@@ -78,6 +79,8 @@ def load():
         "or_mxfp4_decode": (ctypes.c_int, [_p(u8), _p(u8), _p(u16), i64, i64]),
         "or_mxfp4_gemv": (ctypes.c_int, [_p(u8), _p(u8), _p(u16), _p(f64), i64, i64, i64]),
         "or_ternary_gemv": (ctypes.c_int, [_p(u32), _p(f32), _p(f32), _p(f32), _p(f64), i64, i64]),
+        "or_ternary_wl_gemv": (ctypes.c_int, [_p(_p(u32)), _p(f32), _p(f32), _p(f32), _p(f32), _p(f32),
+                                              _p(f64), _p(f64), i64, i64]),
         "or_nvfp4_element": (u16, [ctypes.c_int, u8, f32]),
         "or_nvfp4_gather": (ctypes.c_int, [_p(u8), _p(u8), f32, _p(i64), _p(u16), i64, i64, i64,
                                            _p(i64)]),
@@ -204,6 +207,32 @@ def ternary_gemv(packed, row_scale, x, want_f64: bool = False):
                                   _ptr(xv, ctypes.c_float), _ptr(y, ctypes.c_float),
                                   _ptr(y64, ctypes.c_double), n, k), "ternary_gemv")
     return (y, y64) if want_f64 else y
+
+
+def ternary_wl_gemv(packed, scale, x_re, x_im, want_f64: bool = False):
+    """Widely-linear complex ternary layer y = U x + W conj(x).
+
+    packed: four uint32 [n, k/16] matrices (U_re, U_im, W_re, W_im), as a
+    sequence or a [4, n, k/16] array; scale: f32 [4, n] in the same order;
+    x_re, x_im: f32 [k]. Returns (y_re, y_im) as f32 [n], plus their fp64
+    values when want_f64."""
+    mats = [_arr(m, np.uint32) for m in packed]
+    assert len(mats) == 4
+    n, words = mats[0].shape
+    k = 16 * words
+    assert all(m.shape == (n, words) for m in mats)
+    s = _arr(scale, np.float32)
+    xr = _arr(x_re, np.float32)
+    xi = _arr(x_im, np.float32)
+    assert s.shape == (4, n) and xr.shape == (k,) and xi.shape == (k,)
+    ptrs = (ctypes.POINTER(ctypes.c_uint32) * 4)(*[_ptr(m, ctypes.c_uint32) for m in mats])
+    y = np.empty((2, n), dtype=np.float32)
+    y64 = np.empty((2, n), dtype=np.float64)
+    _check(load().or_ternary_wl_gemv(ptrs, _ptr(s, ctypes.c_float), _ptr(xr, ctypes.c_float),
+                                     _ptr(xi, ctypes.c_float), _ptr(y[0], ctypes.c_float),
+                                     _ptr(y[1], ctypes.c_float), _ptr(y64[0], ctypes.c_double),
+                                     _ptr(y64[1], ctypes.c_double), n, k), "ternary_wl_gemv")
+    return ((y[0], y[1]), (y64[0], y64[1])) if want_f64 else (y[0], y[1])
 
 
 def nvfp4_gather(table, block_scale, global_scale, ids):

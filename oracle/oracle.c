@@ -232,6 +232,65 @@ int or_ternary_gemv(const uint32_t* packed, const float* row_scale, const float*
     return bad ? OR_EINVAL : OR_OK;
 }
 
+/* The ternary weight in field j of a packed word (the encoding above): +1, -1
+ * or 0; a field with both bits set sets *bad and reads as 0. */
+static int ternary_field(uint32_t word, int j, int* bad) {
+    int plus = (int)((word >> (2 * j + 1)) & 1u);
+    int minus = (int)((word >> (2 * j)) & 1u);
+    if (plus && minus) {
+        *bad = 1;
+        return 0;
+    }
+    return plus - minus;
+}
+
+/* Widely-linear complex layer of [FairyFuse] "复杂值广泛线性层的融合核调度":
+ * y = U x + W conj(x), with x complex [k] and U, W complex [n, k]. Reading of
+ * the page: each of the four real parts U_re, U_im, W_re, W_im is a ternary
+ * matrix in the packing of the ternary GEMV above and carries its own per-row
+ * scale, as every ternary GEMV on the page does, so that
+ *   U[r][c] = s_Ure[r] t_Ure[r][c] + i s_Uim[r] t_Uim[r][c]   (W likewise).
+ * This is that definition written out: the complex entries of U and W are
+ * formed, multiplied with x and with its conjugate, and summed, in fp64 complex
+ * arithmetic (real and imaginary parts kept as two doubles). The page's eight
+ * real sub-GEMVs are not used here; the tests check the decomposition against
+ * this definition.
+ *   packed: four pointers, U_re, U_im, W_re, W_im, each uint32 [n, k/16]
+ *   scale:  fp32 [4, n] in the same order
+ *   y_re/y_im: fp32 [n] (the fp64 values rounded once); y64_re/y64_im: fp64
+ *   (either pair may be NULL). */
+int or_ternary_wl_gemv(const uint32_t* const packed[4], const float* scale, const float* x_re,
+                       const float* x_im, float* y_re, float* y_im, double* y64_re,
+                       double* y64_im, int64_t n, int64_t k) {
+    if (n < 0 || k < 0 || k % 16 != 0) return OR_EINVAL;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t r = 0; r < n; ++r) {
+        const uint32_t* row[4];
+        for (int m = 0; m < 4; ++m) row[m] = packed[m] + r * (k / 16);
+        double acc_re = 0.0, acc_im = 0.0;
+        for (int64_t c = 0; c < k; ++c) {
+            int j = (int)(c % 16);
+            double t[4];
+            for (int m = 0; m < 4; ++m) t[m] = (double)ternary_field(row[m][c / 16], j, &bad);
+            /* complex entries U[r][c] = a + ib and W[r][c] = p + iq */
+            double a = (double)scale[0 * n + r] * t[0], b = (double)scale[1 * n + r] * t[1];
+            double p = (double)scale[2 * n + r] * t[2], q = (double)scale[3 * n + r] * t[3];
+            /* x = u + iv and its conjugate u - iv */
+            double u = (double)x_re[c], v = (double)x_im[c];
+            double cu = u, cv = -v;
+            /* (a + ib)(u + iv) + (p + iq)(cu + i cv) */
+            acc_re += (a * u - b * v) + (p * cu - q * cv);
+            acc_im += (a * v + b * u) + (p * cv + q * cu);
+        }
+        if (y64_re) y64_re[r] = acc_re;
+        if (y64_im) y64_im[r] = acc_im;
+        if (y_re) y_re[r] = (float)acc_re;
+        if (y_im) y_im[r] = (float)acc_im;
+    }
+    return bad ? OR_EINVAL : OR_OK;
+}
+
 /* --------------------------------------------------------------- NVFP4 --- */
 
 /* One NVFP4 element in the order of [SGLang-34222] "关键源码片段"

@@ -13,6 +13,9 @@ Workload shapes (value distributions as stated for each):
     bytes over all 256 exponents.
   * Ternary GEMV, W 4096 x 4096, each 2-bit pattern 00/01/10 with probability
     1/3; per-row fp32 scale U[0.01, 0.1]; x fp32 N(0,1).
+  * Widely-linear complex ternary layer, four such 4096 x 4096 matrices
+    (U_re, U_im, W_re, W_im), four per-row scales U[0.01, 0.1], x_re and x_im
+    fp32 N(0,1).
   * NVFP4 gather, table 200000 x 4096 (uniform bytes), E4M3 block scale per 16
     columns = 2^u with u ~ U[-4, 4] cast to float8_e4m3fn, global scale
     fp32(0.01), 8192 token ids uniform over the vocabulary.
@@ -128,6 +131,18 @@ def ternary_case(seed: int = SEED_BASE + 1, n: int = 4096, k: int = 4096):
     scale = r.uniform(0.01, 0.1, size=n).astype(np.float32)
     x = f32_normal(r, (k,))
     return {"packed": packed, "row_scale": scale, "x": x}
+
+
+def ternary_wl_case(seed: int = SEED_BASE + 5, n: int = 4096, k: int = 4096):
+    """Widely-linear complex ternary layer: four ternary matrices U_re, U_im,
+    W_re, W_im [n, k] (weights -1/0/+1 at 1/3 each, packed 16 per word), four
+    per-row scales uniform [0.01, 0.1], x_re and x_im ~N(0, 1)."""
+    r = rng(seed)
+    packed = np.stack([two_bit_words(r, n, k) for _ in range(4)])
+    scale = r.uniform(0.01, 0.1, size=(4, n)).astype(np.float32)
+    x_re = f32_normal(r, (k,))
+    x_im = f32_normal(r, (k,))
+    return {"packed": packed, "scale": scale, "x_re": x_re, "x_im": x_im}
 
 
 def nvfp4_case(seed: int = SEED_BASE + 2, vocab: int = 200000, hidden: int = 4096,
