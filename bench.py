@@ -6,7 +6,8 @@
 Prints ONE JSON line. The default workload is the headline: MXFP4 dequant-GEMV
 at batch 1 on the Llama-8B MLP shapes (W 14336 x 4096 and W 4096 x 14336, one
 launch each per step), bf16 output. Other workloads (for the per-kernel
-roofline tables): mlp_b4, mlp_b16, ternary, gather, moe, decode, gemv_small.
+roofline tables): mlp_b4, mlp_b16, ternary, ternary_wl, gather, moe, decode,
+gemv_small.
 
 Timing: inputs are resident in HBM before the timed region. The launches of
 one step per weight copy are captured into a HIP graph; W warmup steps are
@@ -50,6 +51,7 @@ KERNEL_SOURCES = {
     "gemv": ["gemv.hip"],
     "moe": ["moe.hip", "moe_engine.hpp"],
     "ternary": ["ternary.hip"],
+    "ternarywl": ["ternary_wl.hip"],
     "gather": ["gather.hip"],
     "decode": ["decode.hip"],
 }
@@ -210,6 +212,58 @@ class Ternary(Workload):
         return {"value": round(self.weight_bytes_per_step * reps / el / 1e9, 3), "unit": "GB/s",
                 "cores": oracle.threads(), "kind": "oracle",
                 "sample": f"the full 4096 x 4096 GEMV repeated {reps} times, {el:.1f} s"}
+
+
+class TernaryWL(Workload):
+    """Widely-linear complex ternary layer y = U x + W conj(x): four ternary
+    matrices (U_re, U_im, W_re, W_im) of n x k, four per-row scales."""
+
+    def __init__(self, rotate_bytes: float, n: int = 4096, k: int = 4096):
+        import torch
+        import gemm_e2m1_lut_amd as lib
+        import synth
+        self.lib, self.n, self.k = lib, n, k
+        self.name = f"ternary_wl_{n}x{k}"
+        per_copy = 4 * (n * k // 4)
+        self.copies = max(2, math.ceil(rotate_bytes / per_copy))
+        self.host = synth.ternary_wl_case(n=n, k=k)
+        dev0 = torch.from_numpy(self.host["packed"].view(np.int32)).cuda()
+        # rotated copies: the same weights rolled by whole rows (distinct addresses, same statistics)
+        self.packed = [torch.roll(dev0, shifts=7 * i, dims=1).contiguous() for i in range(self.copies)]
+        self.scale = torch.from_numpy(self.host["scale"]).cuda()
+        self.x_re = torch.from_numpy(self.host["x_re"]).cuda()
+        self.x_im = torch.from_numpy(self.host["x_im"]).cuda()
+        self.y = (torch.empty(n, device="cuda"), torch.empty(n, device="cuda"))
+        self.weight_bytes_per_step = float(per_copy + 16 * n)
+        self.total_bytes_per_step = float(self.alg_bytes("ternarywl"))
+        self.dtype = "f32"
+        self.config = {"workload": self.name, "weights": "four 2-bit ternary matrices, 16 per uint32",
+                       "activations": "complex fp32 (planar)", "out": "complex fp32 (planar)",
+                       "weight_copies_rotated": self.copies}
+
+    def launches(self):
+        def fn(i):
+            self.lib.ternary_wl_gemv(self.packed[i % self.copies], self.scale, self.x_re, self.x_im,
+                                     out=self.y)
+        return [("ternarywl", fn)]
+
+    def alg_bytes(self, label):
+        # four weight matrices and scale vectors, x_re and x_im, y_re and y_im
+        return 4 * (self.n * self.k // 4) + 16 * self.n + 8 * self.k + 8 * self.n
+
+    def cpu_baseline(self, budget_s):
+        import oracle
+        h = self.host
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.ternary_wl_gemv(h["packed"], h["scale"], h["x_re"], h["x_im"])
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s or reps >= 2000:
+                break
+        return {"value": round(self.weight_bytes_per_step * reps / el / 1e9, 3), "unit": "GB/s",
+                "cores": oracle.threads(), "kind": "oracle",
+                "sample": f"the full {self.n} x {self.k} complex layer repeated {reps} times, {el:.1f} s"}
 
 
 class Gather(Workload):
@@ -394,6 +448,7 @@ WORKLOADS = {
     "mlp_b4": lambda rb: GemvMLP(4, rb),
     "mlp_b16": lambda rb: GemvMLP(16, rb),
     "ternary": Ternary,
+    "ternary_wl": TernaryWL,
     "gather": Gather,
     "decode": Decode,
     "gemv_small": GemvSmall,

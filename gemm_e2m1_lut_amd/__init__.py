@@ -6,8 +6,8 @@ the HIP sources in csrc/ by build.py. This package is its thin Python binding:
 torch supplies device memory and streams; every step of every operation runs
 in the library's kernels.
 
-Operations: dequant_decode, dequant_gemv, ternary_gemv, nvfp4_embedding_gather,
-mxfp4_moe_gemm (+ mxfp4_moe_workspace_size).
+Operations: dequant_decode, dequant_gemv, ternary_gemv, ternary_wl_gemv,
+nvfp4_embedding_gather, mxfp4_moe_gemm (+ mxfp4_moe_workspace_size).
 """
 from ._binding import (  # noqa: F401
     ABI_VERSION,
@@ -26,4 +26,5 @@ from ._binding import (  # noqa: F401
     nvfp4_embedding_gather,
     strerror,
     ternary_gemv,
+    ternary_wl_gemv,
 )

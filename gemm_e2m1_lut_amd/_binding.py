@@ -53,6 +53,7 @@ def load_library() -> ctypes.CDLL:
         "dequant_decode": (ctypes.c_int, [vp, vp, vp, i64, i64, vp]),
         "dequant_gemv": (ctypes.c_int, [vp, vp, vp, vp, i32, i64, i64, i64, vp]),
         "ternary_gemv": (ctypes.c_int, [vp, vp, vp, vp, i64, i64, vp]),
+        "ternary_wl_gemv": (ctypes.c_int, [ctypes.POINTER(vp), vp, vp, vp, vp, vp, i64, i64, vp]),
         "nvfp4_embedding_gather": (ctypes.c_int, [vp, vp, vp, vp, vp, i64, i64, i64, vp, vp]),
         "mxfp4_moe_workspace_size": (sz, [i64, i64, i64, i64, i64]),
         "mxfp4_moe_gemm": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i64, i64,
@@ -169,6 +170,40 @@ def ternary_gemv(packed: torch.Tensor, row_scale: torch.Tensor, x: torch.Tensor,
     _need(out, "out", (torch.float32,), (n,))
     _check("ternary_gemv", load_library().ternary_gemv(_ptr(packed), _ptr(row_scale), _ptr(x), _ptr(out),
                                                         n, k, _stream(stream)))
+    return out
+
+
+def ternary_wl_gemv(packed, scale: torch.Tensor, x_re: torch.Tensor, x_im: torch.Tensor,
+                    out: tuple[torch.Tensor, torch.Tensor] | None = None,
+                    stream=None) -> tuple[torch.Tensor, torch.Tensor]:
+    """Widely-linear complex ternary layer y = U x + W conj(x).
+
+    packed: the four ternary matrices U_re, U_im, W_re, W_im, each int32/uint32
+    [n, k/16] (a sequence of four tensors, or one [4, n, k/16] tensor);
+    scale: fp32 [4, n] in the same order; x_re, x_im: fp32 [k].
+    Returns (y_re, y_im), fp32 [n] each."""
+    mats = list(packed.unbind(0)) if isinstance(packed, torch.Tensor) else list(packed)
+    if len(mats) != 4:
+        raise ValueError("packed must hold four matrices (U_re, U_im, W_re, W_im)")
+    for i, m in enumerate(mats):
+        _need(m, f"packed[{i}]", (torch.int32, torch.uint32))
+    n, words = mats[0].shape
+    for i, m in enumerate(mats):
+        if tuple(m.shape) != (n, words):
+            raise ValueError(f"packed[{i}] has shape {tuple(m.shape)}, expected {(n, words)}")
+    k = 16 * words
+    _need(scale, "scale", (torch.float32,), (4, n))
+    _need(x_re, "x_re", (torch.float32,), (k,))
+    _need(x_im, "x_im", (torch.float32,), (k,))
+    if out is None:
+        out = (torch.empty((n,), dtype=torch.float32, device=x_re.device),
+               torch.empty((n,), dtype=torch.float32, device=x_re.device))
+    _need(out[0], "out[0]", (torch.float32,), (n,))
+    _need(out[1], "out[1]", (torch.float32,), (n,))
+    ptrs = (ctypes.c_void_p * 4)(*[m.data_ptr() for m in mats])
+    _check("ternary_wl_gemv", load_library().ternary_wl_gemv(ptrs, _ptr(scale), _ptr(x_re), _ptr(x_im),
+                                                              _ptr(out[0]), _ptr(out[1]), n, k,
+                                                              _stream(stream)))
     return out
 
 

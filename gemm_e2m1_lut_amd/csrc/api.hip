@@ -99,6 +99,29 @@ int ternary_gemv(const uint32_t* packed, const float* row_scale, const float* x,
     return launch_status(e2m1::launch_ternary(packed, row_scale, x, y, n, k, as_stream(stream)));
 }
 
+int ternary_wl_gemv(const uint32_t* const packed[4], const float* scale, const float* x_re,
+                    const float* x_im, float* y_re, float* y_im, int64_t n, int64_t k, void* stream) {
+    if (n < 0 || k < 0 || k % 16 != 0 || n > INT_MAX || k / 16 > INT_MAX / 64 || !mul_ok(n, k) ||
+        !mul_ok(n, 4))
+        return E2M1_ERR_SHAPE;
+    if (n == 0) return E2M1_OK;
+    if (!y_re || !y_im) return E2M1_ERR_NULL;
+    if (!aligned(y_re, 4) || !aligned(y_im, 4)) return E2M1_ERR_ALIGN;
+    if (k == 0) {
+        hipError_t e = fill_zero_bytes(y_re, n * 4, as_stream(stream));
+        if (e == hipSuccess) e = fill_zero_bytes(y_im, n * 4, as_stream(stream));
+        return launch_status(e);
+    }
+    if (!packed || !scale || !x_re || !x_im) return E2M1_ERR_NULL;
+    for (int m = 0; m < 4; ++m) {
+        if (!packed[m]) return E2M1_ERR_NULL;
+        if (!aligned(packed[m], 4)) return E2M1_ERR_ALIGN;
+    }
+    if (!aligned(scale, 4) || !aligned(x_re, 4) || !aligned(x_im, 4)) return E2M1_ERR_ALIGN;
+    return launch_status(e2m1::launch_ternary_wl(packed, scale, x_re, x_im, y_re, y_im, n, k,
+                                                 as_stream(stream)));
+}
+
 int nvfp4_embedding_gather(const uint8_t* table, const uint8_t* block_scale_e4m3,
                            const float* global_scale, const int64_t* ids, uint16_t* out_bf16,
                            int64_t vocab, int64_t hidden, int64_t num_tokens, int32_t* err_flag,

@@ -22,6 +22,10 @@ hipError_t launch_gemv(const uint8_t* packed, const uint8_t* scales, const uint1
 hipError_t launch_ternary(const uint32_t* packed, const float* row_scale, const float* x, float* y,
                           int64_t n, int64_t k, hipStream_t stream);
 
+hipError_t launch_ternary_wl(const uint32_t* const mats[4], const float* scale, const float* x_re,
+                             const float* x_im, float* y_re, float* y_im, int64_t n, int64_t k,
+                             hipStream_t stream);
+
 hipError_t launch_nvfp4_gather(const uint8_t* table, const uint8_t* block_scale,
                                const float* global_scale, const int64_t* ids, uint16_t* out,
                                int64_t vocab, int64_t hidden, int64_t ntok, int32_t* err_flag,

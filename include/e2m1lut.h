@@ -13,7 +13,9 @@
  *                  "关键源码片段").
  *   [FairyFuse]    blog.hotdry.top post on FairyFuse: 2-bit ternary GEMV with
  *                  add/sub accumulation and a per-row scale
- *                  ("三元 GEMV 的乘法消除原理").
+ *                  ("三元 GEMV 的乘法消除原理"), and the widely-linear complex
+ *                  layer fused over four ternary matrices
+ *                  ("复杂值广泛线性层的融合核调度").
  *
  * Conventions shared by every entry point
  *   - All array pointers are DEVICE pointers (hipMalloc'd or torch CUDA
@@ -124,6 +126,30 @@ int dequant_gemv(const uint8_t* packed, const uint8_t* scale_e8m0, const uint16_
  */
 int ternary_gemv(const uint32_t* packed, const float* row_scale, const float* x, float* y,
                  int64_t n, int64_t k, void* stream);
+
+/*
+ * ternary_wl_gemv -- widely-linear complex ternary layer y = U x + W conj(x).
+ * Operation: [FairyFuse] "复杂值广泛线性层的融合核调度": x is complex [k], U
+ * and W complex [n, k]; the layer splits into eight real ternary GEMVs, all
+ * evaluated in one pass. Each real part is a ternary matrix packed as for
+ * ternary_gemv, with its own per-row scale (applied once after the row sum):
+ *   U = diag(s_Ure) T_Ure + i diag(s_Uim) T_Uim,  W likewise, so
+ *   y_re = s_Ure (T_Ure x_re) - s_Uim (T_Uim x_im) + s_Wre (T_Wre x_re) + s_Wim (T_Wim x_im)
+ *   y_im = s_Ure (T_Ure x_im) + s_Uim (T_Uim x_re) - s_Wre (T_Wre x_im) + s_Wim (T_Wim x_re)
+ *   packed     HOST array of four DEVICE pointers, in the order U_re, U_im,
+ *              W_re, W_im; each uint32 [n, k/16], 4-byte aligned
+ *   scale      fp32 [4, n]: the per-row scales, same order
+ *   x_re, x_im fp32 [k]
+ *   y_re, y_im fp32 [n], overwritten
+ * Requires n >= 0, k >= 0, k % 16 == 0. k == 0 writes zeros. A field with
+ * both bits set reads as 0. x must be finite: the fast kernel multiplies
+ * zero weights by x, so an Inf or NaN in x can turn outputs NaN where the
+ * method would skip it. Accumulation is fp32 with x at full fp32 precision.
+ * The fast kernel needs k % 64 == 0 and 16-byte aligned matrices; other
+ * inputs take a slower kernel with the same results up to rounding.
+ */
+int ternary_wl_gemv(const uint32_t* const packed[4], const float* scale, const float* x_re,
+                    const float* x_im, float* y_re, float* y_im, int64_t n, int64_t k, void* stream);
 
 /*
  * nvfp4_embedding_gather -- gather token rows of an NVFP4 table and

@@ -37,7 +37,7 @@ def lib():
 
 def test_header_declares_the_five_operations():
     names = declared_functions()
-    for op in ("dequant_decode", "dequant_gemv", "ternary_gemv", "nvfp4_embedding_gather",
+    for op in ("dequant_decode", "dequant_gemv", "ternary_gemv", "ternary_wl_gemv", "nvfp4_embedding_gather",
                "mxfp4_moe_gemm", "mxfp4_moe_workspace_size", "e2m1_abi_version", "e2m1_strerror"):
         assert op in names
 
@@ -104,6 +104,26 @@ def test_ternary_validation(lib):
     assert f(A, B, C, NULL, 4, 16, NULL) == E_NULL
     assert f(NULL, B, C, D, 4, 16, NULL) == E_NULL
     assert f(P(0x10002), B, C, D, 4, 16, NULL) == E_ALIGN
+
+
+def test_ternary_wl_validation(lib):
+    f = lib.ternary_wl_gemv
+    mats = (ctypes.c_void_p * 4)(0x10000, 0x20000, 0x30000, 0x40000)
+    E = P(0x50000)
+    assert f(mats, A, B, C, D, E, 4, 24, NULL) == E_SHAPE    # k % 16
+    assert f(mats, A, B, C, D, E, -1, 16, NULL) == E_SHAPE
+    assert f(mats, A, B, C, D, E, 2**31, 16, NULL) == E_SHAPE
+    assert f(None, NULL, NULL, NULL, NULL, NULL, 0, 16, NULL) == E2M1_OK   # empty
+    assert f(mats, A, B, C, NULL, E, 4, 16, NULL) == E_NULL   # y_re
+    assert f(mats, A, B, C, D, NULL, 4, 16, NULL) == E_NULL   # y_im
+    assert f(None, A, B, C, D, E, 4, 16, NULL) == E_NULL      # no pointer array
+    assert f(mats, NULL, B, C, D, E, 4, 16, NULL) == E_NULL   # scale
+    gap = (ctypes.c_void_p * 4)(0x10000, 0x20000, 0, 0x40000)
+    assert f(gap, A, B, C, D, E, 4, 16, NULL) == E_NULL
+    odd = (ctypes.c_void_p * 4)(0x10000, 0x20002, 0x30000, 0x40000)
+    assert f(odd, A, B, C, D, E, 4, 16, NULL) == E_ALIGN
+    assert f(mats, A, B, P(0x30002), D, E, 4, 16, NULL) == E_ALIGN
+    assert f(mats, A, B, C, D, P(0x50001), 4, 16, NULL) == E_ALIGN
 
 
 def test_gather_validation(lib):
