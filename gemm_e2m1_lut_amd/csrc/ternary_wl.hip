@@ -4,7 +4,7 @@
 // complex layer y = U x + W conj(x) whose matrices have ternary real and
 // imaginary parts, evaluated as eight coupled real ternary GEMVs in one pass
 // over the weights: each decoded weight serves both the real and the
-// imaginary part of x (mask reuse), x is staged once for all eight (input
+// imaginary part of x (mask reuse), x is prepared once for all eight (input
 // reuse), the conjugate enters as a sign and never as a second copy of x, and
 // the eight partial sums stay in registers until the final reduction. Each of
 // U_re, U_im, W_re, W_im is packed like the real ternary GEMV (section
@@ -12,42 +12,54 @@
 // with its own per-row scale, applied once after the row sum.
 //
 // gfx950 design. The eight sub-GEMVs are a contraction of four ternary
-// matrices against the same few columns of x, so the fast kernel runs them on
-// the matrix cores: weights decode two at a time to bf16 +/-0.5 or 0 (a
-// rotate, a mask and a v_perm_b32; the factor 2 goes into the scale) as the A
-// operand of v_mfma_f32_16x16x32_bf16, and the B operand holds x_re and x_im,
-// each split exactly into three bf16 pieces (hi = x truncated to bf16, mid =
-// the remainder truncated, lo = what is left, at most 8 significant bits), in
-// six of its sixteen columns. Products are exact and accumulate in fp32, so x
-// is used at full fp32 precision. A dot2-based decode would need 32 dot
-// products per 16-weight word against x_re and x_im (hi + lo each); here the
-// matrix cores take that work and the vector ALU only decodes.
+// matrices against a few columns derived from x, so the fast kernel runs them
+// on the matrix cores with exact integer arithmetic:
+//   * A operand: ternary weights as int8 -1 / 0 / +1. One mask of a shifted
+//     word gives the fields j, j + 4, j + 8, j + 12 as v_perm_b32 selectors
+//     into a 4-byte pool, so one perm decodes four weights (11 VALU
+//     operations per 16-weight word).
+//   * B operand: x_re and x_im in fixed point, X = rint(x 2^S) with
+//     |X| <= 2^30 and one exponent S per part and 256-column slice (from the
+//     slice's largest |x|), written as four signed base-256 digits (one add
+//     and one xor of 0x00808080 turn X into its digit bytes). The eight digit
+//     columns of x_re and x_im fill half of the sixteen B columns.
+//   * v_mfma_i32_16x16x64_i8 sums ternary times digit exactly in int32; per
+//     slice the four digit columns are scaled by 2^(8 i - S) into fp32.
+// So every row sum is exact for x on its slice's grid of 2^-S: x is used to
+// within 2^-31 of the slice's largest |x| (more than fp32's own precision
+// for the elements near that maximum), and the only other roundings are a
+// few fp32 additions per row.
 //
-// Work split: a workgroup owns a tile of 16 rows; its waves split K into
-// slices of 256 columns (lane l = 16 g + r loads the 16-byte chunk 4 s + g of
-// row r of each matrix: four words, 64 columns). The matrix-core k-slots of a
-// lane group are the columns of its chunk, in the order in which the pairs
-// decode (fields p and p + 8 of word q), and the B operand of the same lanes
-// lists x in that order, so the sum over k is complete whatever the order.
-// D element (row 4 g + j, column c) sits in component j of lane 16 g + c. The
-// three pieces of x_re (columns 0..2) and of x_im (3..5) are added by DPP
-// within each 16-lane row, the slices through LDS, and one thread per row
-// and component applies the four scales and the signs of the complex product.
-// x is split into LDS once per workgroup when K fits one staged block (4096
-// columns), else once per block and tile. Inputs the fast kernel cannot take
+// Work split: a workgroup owns a tile of 16 rows; its waves take 256-column
+// slices (slice s of wave w = w, w + waves, ...). Lane l = 16 g + r loads the
+// 16-byte chunk 4 s + g of row r of each matrix (four words, 64 columns) and
+// decodes word q as the A operand of one MFMA; in that operand byte b of
+// dword j is the weight of column 16 q + j + 4 b of the chunk, and the B
+// operand of lane 16 g + c holds digit column c for the same columns in the
+// same order, so the sum over k is complete. Each wave prepares the digits of
+// its own slice (lane l: columns 16 q + j + 4 b of chunk l >> 4, word
+// l >> 2 & 3, dword j = l & 3, b = 0..3, for both parts) in its own LDS area
+// and reads them back as B operands, with no workgroup barrier. D element
+// (row 4 g + j, column c) sits in component j of lane 16 g + c: the digit
+// columns of each part are added by DPP within each 16-lane row, the waves
+// through LDS, and one thread per row and component applies the four scales
+// and the signs of the complex product. Inputs the fast kernel cannot take
 // (K % 64 != 0, unaligned matrices) use a one-wave-per-row kernel that adds,
-// subtracts or skips each x directly.
+// subtracts or skips each x directly in fp32.
 #include "device.hpp"
 #include "kernels.hpp"
 
 namespace e2m1 {
 namespace {
 
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int kMaxWaves = 16;
 constexpr int kSliceChunks = 4;                          // 64-column chunks per wave slice
-constexpr int kVariants = 6;                             // x_re hi/mid/lo, x_im hi/mid/lo
-constexpr int kRowDwords = 32;                           // bf16 pairs of one (chunk, variant)
-constexpr int kRowPitch = 36;                            // dwords per row in LDS (spreads the banks)
+constexpr int kVariants = 8;                             // digits 0..3 of x_re, then of x_im
+constexpr int kRowDwords = 16;                           // B operand dwords of one (chunk, variant)
+constexpr int kRowPitch = 20;                            // dwords per row in LDS (spreads the banks)
+constexpr int kWaveDwords = kSliceChunks * kVariants * kRowPitch;
 constexpr int kPartFloats = 4 * 2 * 16;                  // (matrix, part, row) partial sums
 
 struct WlMats {
@@ -59,222 +71,202 @@ __device__ __forceinline__ void issue_fence() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// x = hi + mid + lo exactly: hi and mid are truncations to bf16, the rest
-// has at most 8 significant bits and so is a bf16 value as well.
-__device__ __forceinline__ void split3(float v, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
-    const uint32_t h = __float_as_uint(v) & 0xFFFF0000u;
-    const float r1 = v - __uint_as_float(h);
-    const uint32_t m = __float_as_uint(r1) & 0xFFFF0000u;
-    const float r2 = r1 - __uint_as_float(m);
-    hi = h;
-    mid = m;
-    lo = __float_as_uint(r2);
+// Largest value over the wave (DPP only), returned uniform.
+__device__ __forceinline__ float wave_max(float v) {
+    v = fmaxf(v, dpp_f32<0xB1>(v));
+    v = fmaxf(v, dpp_f32<0x4E>(v));
+    v = fmaxf(v, dpp_f32<0x141>(v));
+    v = fmaxf(v, dpp_f32<0x140>(v));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xC, 0xF, false)));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
-// {a.high16, b.high16}: two bf16 pieces as one pair (a in the low half).
-__device__ __forceinline__ uint32_t pair_hi16(uint32_t a, uint32_t b) {
-    return __builtin_amdgcn_perm(b, a, 0x07060302u);
+// Exponent S with |x 2^S| <= 2^30 for every |x| <= m (m = 0 gives 30).
+__device__ __forceinline__ int slice_exponent(float m) {
+    return 30 - __builtin_amdgcn_frexp_expf(m);
 }
 
-// Layout of the dynamic LDS of one workgroup with `bc` chunks per block.
-struct WlLds {
-    uint32_t* table;   // [bc][kVariants][kRowPitch]
-    uint32_t* zero;    // kRowDwords zeros (B columns 6..15)
-    float* part;       // [waves][kPartFloats]
-    float* tot;        // [kPartFloats]
-};
-
-__device__ __forceinline__ WlLds wl_lds(uint32_t* base, int bc, int waves) {
-    WlLds l;
-    l.table = base;
-    l.zero = base + bc * kVariants * kRowPitch;
-    l.part = reinterpret_cast<float*>(l.zero + kRowDwords);
-    l.tot = l.part + waves * kPartFloats;
-    return l;
+// The four signed base-256 digits of X = rint(x 2^S), |X| <= 2^30, as the
+// bytes of one word: X + 0x808080 has unsigned low bytes u_i with
+// X = sum (u_i - 128) 256^i + u_3 256^3, and xor 0x80 turns u_i into the
+// int8 pattern of u_i - 128.
+__device__ __forceinline__ uint32_t digits(float x, int S) {
+    const int X = (int)rintf(ldexpf(x, S));
+    return ((uint32_t)X + 0x00808080u) ^ 0x00808080u;
 }
 
-size_t wl_lds_bytes(int bc, int waves) {
-    return 4u * ((size_t)bc * kVariants * kRowPitch + kRowDwords + (size_t)waves * kPartFloats + kPartFloats);
+// 4 x 4 byte transpose: byte b of out[i] = byte i of in[b].
+__device__ __forceinline__ void transpose4(const uint32_t (&in)[4], uint32_t (&out)[4]) {
+    const uint32_t lo01 = __builtin_amdgcn_perm(in[1], in[0], 0x05010400u);
+    const uint32_t hi01 = __builtin_amdgcn_perm(in[1], in[0], 0x07030602u);
+    const uint32_t lo23 = __builtin_amdgcn_perm(in[3], in[2], 0x05010400u);
+    const uint32_t hi23 = __builtin_amdgcn_perm(in[3], in[2], 0x07030602u);
+    out[0] = __builtin_amdgcn_perm(lo23, lo01, 0x05040100u);
+    out[1] = __builtin_amdgcn_perm(lo23, lo01, 0x07060302u);
+    out[2] = __builtin_amdgcn_perm(hi23, hi01, 0x05040100u);
+    out[3] = __builtin_amdgcn_perm(hi23, hi01, 0x07060302u);
 }
 
-// Pair slot s of block chunk `cl`: columns k0 = 64 c + 16 q + 4 h + d and
-// k0 + 8 with (q, h, d) = (s >> 3 & 3, s >> 2 & 1, s & 3): the two fields that
-// one perm decodes (p = 4 h + d and p + 8 of word q).
-__device__ __forceinline__ int slot_column(int chunk, int s) {
-    return 64 * chunk + 16 * ((s >> 3) & 3) + 4 * ((s >> 2) & 1) + (s & 3);
+// Ternary fields j, j + 4, j + 8, j + 12 of a word as int8 bytes 0..3: the
+// masked field is a v_perm_b32 selector into the pool 00 (0), FF (-1 for
+// field 01), 01 (+1 for field 10), 00 (field 11, not a valid weight: 0).
+constexpr uint32_t kI8Pool = 0x0001FF00u;
+
+template <int J>
+__device__ __forceinline__ uint32_t ternary_quad(uint32_t w) {
+    const uint32_t sel = (J == 0 ? w : (w >> (2 * J))) & 0x03030303u;
+    return __builtin_amdgcn_perm(0u, kI8Pool, sel);
 }
 
-struct XSlot {
-    float r0, r1, i0, i1;
-};
-
-__device__ __forceinline__ XSlot load_slot(const float* x_re, const float* x_im, int chunk, int s, int K) {
-    const int k0 = min(slot_column(chunk, s), K - 1);
-    const int k1 = min(k0 + 8, K - 1);
-    return XSlot{x_re[k0], x_re[k1], x_im[k0], x_im[k1]};
-}
-
-__device__ __forceinline__ void store_slot(uint32_t* table, int cl, int s, const XSlot& v) {
-    uint32_t h0, m0, l0, h1, m1, l1;
-    uint32_t* row = table + cl * kVariants * kRowPitch + (s & 31);
-    split3(v.r0, h0, m0, l0);
-    split3(v.r1, h1, m1, l1);
-    row[0 * kRowPitch] = pair_hi16(h0, h1);
-    row[1 * kRowPitch] = pair_hi16(m0, m1);
-    row[2 * kRowPitch] = pair_hi16(l0, l1);
-    split3(v.i0, h0, m0, l0);
-    split3(v.i1, h1, m1, l1);
-    row[3 * kRowPitch] = pair_hi16(h0, h1);
-    row[4 * kRowPitch] = pair_hi16(m0, m1);
-    row[5 * kRowPitch] = pair_hi16(l0, l1);
-}
-
-// A operand for MFMA (q, h): fields 4 h .. 4 h + 3 of word q and the fields 8 above them.
-template <int H>
-__device__ __forceinline__ u32x4 decode_half(uint32_t w) {
-    u32x4 a;
-    a.x = ternary_pair<4 * H + 0>(w);
-    a.y = ternary_pair<4 * H + 1>(w);
-    a.z = ternary_pair<4 * H + 2>(w);
-    a.w = ternary_pair<4 * H + 3>(w);
+__device__ __forceinline__ i32x4 decode_word(uint32_t w) {
+    i32x4 a;
+    a.x = (int)ternary_quad<0>(w);
+    a.y = (int)ternary_quad<1>(w);
+    a.z = (int)ternary_quad<2>(w);
+    a.w = (int)ternary_quad<3>(w);
     return a;
 }
 
-__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
-                                                   c, 0, 0, 0);
+size_t wl_lds_bytes(int waves) {
+    return 4u * ((size_t)waves * kWaveDwords + kRowDwords + (size_t)waves * kPartFloats + kPartFloats);
 }
 
-// One wave slice: four weight chunks (one per matrix) against the B operands of the chunk.
-__device__ __forceinline__ void slice_mfma(const uint4 (&w)[4], uint32_t mask, const u32x4 (&b)[8], f32x4 (&acc)[4]) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const uint32_t ws[4] = {w[m].x, w[m].y, w[m].z, w[m].w};
-            const uint32_t word = ws[q] & mask;
-            acc[m] = mfma_bf16(decode_half<0>(word), b[2 * q + 0], acc[m]);
-            acc[m] = mfma_bf16(decode_half<1>(word), b[2 * q + 1], acc[m]);
-        }
-    }
-}
-
-__device__ __forceinline__ void load_b(const uint32_t* src, u32x4 (&b)[8]) {
-    const u32x4* p = reinterpret_cast<const u32x4*>(src);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) b[i] = p[i];
-}
-
-// Row totals of one tile: DPP sums of the x pieces, LDS sums over the waves,
-// then scales and the signs of the complex product; writes y_re, y_im.
-__device__ __forceinline__ void tile_epilogue(const f32x4 (&acc)[4], const WlLds& l, int wave, int nwaves,
-                                              int lane, const float (&sc)[4], float* y_re, float* y_im,
-                                              int tile, int n) {
-    const int g = lane >> 4, c = lane & 15;
-    float s[4][4];   // lane c: D(c) + D(c - 1) + D(c - 2) within its 16-lane row
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float v = acc[m][j];
-            s[m][j] = v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xF, 0xF, true)) +
-                      __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xF, 0xF, true));
-        }
-    }
-    if (c == 2 || c == 5) {   // x_re pieces (columns 0..2), x_im pieces (3..5)
-        float* dst = l.part + wave * kPartFloats + (c == 5 ? 16 : 0) + 4 * g;
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) dst[32 * m + j] = s[m][j];
-    }
-    __syncthreads();
-    const int t = threadIdx.x;
-    for (int i = t; i < kPartFloats; i += blockDim.x) {   // one-wave workgroups take two rounds
-        float sum = 0.f;
-        for (int w = 0; w < nwaves; ++w) sum += l.part[w * kPartFloats + i];
-        l.tot[i] = sum;
-    }
-    __syncthreads();
-    if (t < 32) {
-        const int r = t & 15, row = tile * 16 + r;
-        // P(m, part) = half the ternary row sum of matrix m against x_part
-        const float* P = l.tot;
-        const float ur_re = P[0 * 16 + r], ur_im = P[1 * 16 + r], ui_re = P[2 * 16 + r], ui_im = P[3 * 16 + r];
-        const float wr_re = P[4 * 16 + r], wr_im = P[5 * 16 + r], wi_re = P[6 * 16 + r], wi_im = P[7 * 16 + r];
-        float y;
-        if (t < 16)   // Re: U_re x_re - U_im x_im + W_re x_re + W_im x_im
-            y = (sc[0] * (2.f * ur_re) - sc[1] * (2.f * ui_im)) + (sc[2] * (2.f * wr_re) + sc[3] * (2.f * wi_im));
-        else          // Im: U_re x_im + U_im x_re - W_re x_im + W_im x_re
-            y = (sc[0] * (2.f * ur_im) + sc[1] * (2.f * ui_re)) + (sc[3] * (2.f * wi_re) - sc[2] * (2.f * wr_im));
-        if (row < n) (t < 16 ? y_re : y_im)[row] = y;
-    }
-}
-
-// Fast kernel: K % 64 == 0, matrices 16-byte aligned. kOneBlock: all of K
-// fits one staged block of 4 * waves chunks, so x is split once per
-// workgroup and each wave keeps its B operands in registers across tiles.
-template <bool kOneBlock>
+// Fast kernel: K % 64 == 0, matrices 16-byte aligned.
 __global__ __launch_bounds__(kWave * kMaxWaves) void ternary_wl_kernel(WlMats mats, const float* scale,
                                                                        const float* x_re, const float* x_im,
                                                                        float* y_re, float* y_im, int n, int kq) {
     extern __shared__ __attribute__((aligned(16))) uint32_t wl_smem[];
     const int nwaves = blockDim.x / kWave;
-    const int bc = kSliceChunks * nwaves;
-    const WlLds l = wl_lds(wl_smem, bc, nwaves);
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    uint32_t* tab = wl_smem + wave * kWaveDwords;
+    uint32_t* zero = wl_smem + nwaves * kWaveDwords;
+    float* part = reinterpret_cast<float*>(zero + kRowDwords);
+    float* tot = part + nwaves * kPartFloats;
     const int g = lane >> 4, r = lane & 15, c = lane & 15;
     const int K = 64 * kq;
+    const int nslices = (kq + kSliceChunks - 1) / kSliceChunks;
     const int ntiles = (n + 15) / 16;
-    const int nblocks = (kq + bc - 1) / bc;
+    // digit preparation: lane -> chunk pg, word pq, dword pj; columns 64 pg + 16 pq + pj + 4 b
+    const int pg = lane >> 4, pq = (lane >> 2) & 3, pj = lane & 3;
+    uint32_t* prep_row = tab + pg * kVariants * kRowPitch + 4 * pq + pj;
+    const i32x4* b_row = reinterpret_cast<const i32x4*>(c < kVariants ? tab + (g * kVariants + c) * kRowPitch : zero);
 
-    if (threadIdx.x < kRowDwords) l.zero[threadIdx.x] = 0u;
+    if (threadIdx.x < kRowDwords) zero[threadIdx.x] = 0u;
+    __syncthreads();
 
-    for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {   // workgroup-uniform
         const int row = min(tile * 16 + r, n - 1);
         float sc[4] = {0.f, 0.f, 0.f, 0.f};
         if (wave == 0) {
 #pragma unroll
             for (int m = 0; m < 4; ++m) sc[m] = scale[(int64_t)m * n + row];
         }
-        f32x4 acc[4];
+        float f[4][4];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int blk = 0; blk < nblocks; ++blk) {
-            const int chunk = blk * bc + wave * kSliceChunks + g;
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) f[m][j] = 0.f;
+
+        for (int sl = wave; sl < nslices; sl += nwaves) {   // wave-uniform
+            float xr[4], xi[4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const int col = min(256 * sl + 64 * pg + 16 * pq + pj + 4 * b, K - 1);
+                xr[b] = x_re[col];
+                xi[b] = x_im[col];
+            }
+            issue_fence();
+            const int chunk = sl * kSliceChunks + g;
             const int cc = min(chunk, kq - 1);
             const uint32_t mask = chunk < kq ? 0xFFFFFFFFu : 0u;
-            const bool split = !kOneBlock || tile == (int)blockIdx.x;
-            XSlot xs[2];
-            if (split) {
-#pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    const int s = threadIdx.x + i * blockDim.x;
-                    xs[i] = load_slot(x_re, x_im, blk * bc + (s >> 5), s, K);
-                }
-            }
-            issue_fence();
             uint4 w[4];
 #pragma unroll
-            for (int m = 0; m < 4; ++m)
-                w[m] = load_nt16(mats.m[m] + ((int64_t)row * kq + cc) * 4);
+            for (int m = 0; m < 4; ++m) w[m] = load_nt16(mats.m[m] + ((int64_t)row * kq + cc) * 4);
             issue_fence();
-            if (split) {
-                if (!kOneBlock) __syncthreads();   // the previous block's B reads are done
+            // digits of this slice's x into the wave's LDS area
+            const int Sr = slice_exponent(wave_max(fmaxf(fmaxf(fabsf(xr[0]), fabsf(xr[1])),
+                                                         fmaxf(fabsf(xr[2]), fabsf(xr[3])))));
+            const int Si = slice_exponent(wave_max(fmaxf(fmaxf(fabsf(xi[0]), fabsf(xi[1])),
+                                                         fmaxf(fabsf(xi[2]), fabsf(xi[3])))));
+            uint32_t dr[4], di[4], tr[4], ti[4];
 #pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    const int s = threadIdx.x + i * blockDim.x;
-                    store_slot(l.table, s >> 5, s, xs[i]);
-                }
-                __syncthreads();
+            for (int b = 0; b < 4; ++b) {
+                dr[b] = digits(xr[b], Sr);
+                di[b] = digits(xi[b], Si);
             }
-            u32x4 b[8];
-            const int cl = cc - blk * bc;
-            load_b(c < kVariants ? l.table + (cl * kVariants + c) * kRowPitch : l.zero, b);
-            slice_mfma(w, mask, b, acc);
+            transpose4(dr, tr);
+            transpose4(di, ti);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                prep_row[i * kRowPitch] = tr[i];
+                prep_row[(4 + i) * kRowPitch] = ti[i];
+            }
+            __builtin_amdgcn_wave_barrier();   // LDS accesses of one wave complete in order
+            i32x4 bq[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) bq[q] = b_row[q];
+            i32x4 acc[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) acc[m] = i32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const uint32_t ws[4] = {w[m].x, w[m].y, w[m].z, w[m].w};
+                    acc[m] = __builtin_amdgcn_mfma_i32_16x16x64_i8(decode_word(ws[q] & mask), bq[q], acc[m], 0, 0, 0);
+                }
+            }
+            // digit column c is worth 2^(8 (c & 3) - S) of its part; |acc| <= 2^15, exact in fp32
+            const int e = 8 * (c & 3) - ((c & 4) ? Si : Sr);
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) f[m][j] += ldexpf((float)acc[m][j], e);
+            __builtin_amdgcn_wave_barrier();   // the B reads are done before the next slice's digits
         }
-        tile_epilogue(acc, l, wave, nwaves, lane, sc, y_re, y_im, tile, n);
+
+        // digits of x_re (columns 0..3) and of x_im (4..7): the sums land in lanes c = 3 and c = 7
+        float s[4][4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float v = f[m][j];
+                v += dpp_f32<0x111>(v);   // row_shr:1
+                v += dpp_f32<0x112>(v);   // row_shr:2
+                s[m][j] = v;
+            }
+        if (c == 3 || c == 7) {
+            float* dst = part + wave * kPartFloats + (c == 7 ? 16 : 0) + 4 * g;
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) dst[32 * m + j] = s[m][j];
+        }
+        __syncthreads();
+        for (int i = threadIdx.x; i < kPartFloats; i += blockDim.x) {   // one-wave workgroups take two rounds
+            float sum = 0.f;
+            for (int wv = 0; wv < nwaves; ++wv) sum += part[wv * kPartFloats + i];
+            tot[i] = sum;
+        }
+        __syncthreads();
+        const int t = threadIdx.x;
+        if (t < 32) {
+            const int rr = t & 15, orow = tile * 16 + rr;
+            // tot[(2 m + p) 16 + row]: ternary row sum of matrix m against x_re (p = 0) or x_im (p = 1)
+            const float ur_re = tot[0 * 16 + rr], ur_im = tot[1 * 16 + rr];
+            const float ui_re = tot[2 * 16 + rr], ui_im = tot[3 * 16 + rr];
+            const float wr_re = tot[4 * 16 + rr], wr_im = tot[5 * 16 + rr];
+            const float wi_re = tot[6 * 16 + rr], wi_im = tot[7 * 16 + rr];
+            float y;
+            if (t < 16)   // Re: U_re x_re - U_im x_im + W_re x_re + W_im x_im
+                y = (sc[0] * ur_re - sc[1] * ui_im) + (sc[2] * wr_re + sc[3] * wi_im);
+            else          // Im: U_re x_im + U_im x_re - W_re x_im + W_im x_re
+                y = (sc[0] * ur_im + sc[1] * ui_re) + (sc[3] * wi_re - sc[2] * wr_im);
+            if (orow < n) (t < 16 ? y_re : y_im)[orow] = y;
+        }
     }
 }
 
@@ -322,17 +314,9 @@ __global__ __launch_bounds__(256) void ternary_wl_generic_kernel(WlMats mats, co
     }
 }
 
-struct WlConfig {
-    int waves;
-    size_t lds;
-    int resident;   // workgroups per compute unit
-};
-
-template <bool kOneBlock>
 int wl_resident(int waves, size_t lds) {
     int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, ternary_wl_kernel<kOneBlock>, kWave * waves, lds) !=
-            hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, ternary_wl_kernel, kWave * waves, lds) != hipSuccess ||
         per_cu < 1)
         per_cu = 1;
     return per_cu;
@@ -350,19 +334,12 @@ hipError_t launch_ternary_wl(const uint32_t* const mats[4], const float* scale, 
     if (aligned) {
         const int kq = (int)(k / 64);
         const int waves = min(kMaxWaves, (kq + kSliceChunks - 1) / kSliceChunks);
-        const int bc = kSliceChunks * waves;
-        const bool one = kq <= bc;
-        const size_t lds = wl_lds_bytes(bc, waves);
-        // resident workgroups per compute unit, per (wave count, variant)
-        static int cache[2][kMaxWaves + 1] = {};
-        int& per_cu = cache[one][waves];
-        if (per_cu == 0) per_cu = one ? wl_resident<true>(waves, lds) : wl_resident<false>(waves, lds);
+        const size_t lds = wl_lds_bytes(waves);
+        static int cache[kMaxWaves + 1] = {};   // resident workgroups per compute unit, per wave count
+        if (cache[waves] == 0) cache[waves] = wl_resident(waves, lds);
         const int ntiles = (nn + 15) / 16;
-        const int grid = min(ntiles, per_cu * device_cu_count());
-        if (one)
-            ternary_wl_kernel<true><<<grid, kWave * waves, lds, stream>>>(wm, scale, x_re, x_im, y_re, y_im, nn, kq);
-        else
-            ternary_wl_kernel<false><<<grid, kWave * waves, lds, stream>>>(wm, scale, x_re, x_im, y_re, y_im, nn, kq);
+        const int grid = min(ntiles, cache[waves] * device_cu_count());
+        ternary_wl_kernel<<<grid, kWave * waves, lds, stream>>>(wm, scale, x_re, x_im, y_re, y_im, nn, kq);
         return hipGetLastError();
     }
     const int want = (nn + 3) / 4;
