@@ -79,6 +79,7 @@ def load():
         "or_mxfp4_decode": (ctypes.c_int, [_p(u8), _p(u8), _p(u16), i64, i64]),
         "or_mxfp4_gemv": (ctypes.c_int, [_p(u8), _p(u8), _p(u16), _p(f64), i64, i64, i64]),
         "or_ternary_gemv": (ctypes.c_int, [_p(u32), _p(f32), _p(f32), _p(f32), _p(f64), i64, i64]),
+        "or_ternary_gemm": (ctypes.c_int, [_p(u32), _p(f32), _p(f32), _p(f32), _p(f64), i64, i64, i64]),
         "or_ternary_wl_gemv": (ctypes.c_int, [_p(_p(u32)), _p(f32), _p(f32), _p(f32), _p(f32), _p(f32),
                                               _p(f64), _p(f64), i64, i64]),
         "or_nvfp4_element": (u16, [ctypes.c_int, u8, f32]),
@@ -206,6 +207,23 @@ def ternary_gemv(packed, row_scale, x, want_f64: bool = False):
     _check(load().or_ternary_gemv(_ptr(p, ctypes.c_uint32), _ptr(s, ctypes.c_float),
                                   _ptr(xv, ctypes.c_float), _ptr(y, ctypes.c_float),
                                   _ptr(y64, ctypes.c_double), n, k), "ternary_gemv")
+    return (y, y64) if want_f64 else y
+
+
+def ternary_gemm(packed, row_scale, x, want_f64: bool = False):
+    """packed uint32 [n, k/16], row_scale f32 [n], x f32 [batch, k] -> y f32 [batch, n]."""
+    p = _arr(packed, np.uint32)
+    s = _arr(row_scale, np.float32)
+    xv = _arr(x, np.float32)
+    n, words = p.shape
+    k = 16 * words
+    batch = xv.shape[0]
+    assert s.shape == (n,) and xv.shape == (batch, k)
+    y = np.empty((batch, n), dtype=np.float32)
+    y64 = np.empty((batch, n), dtype=np.float64)
+    _check(load().or_ternary_gemm(_ptr(p, ctypes.c_uint32), _ptr(s, ctypes.c_float),
+                                  _ptr(xv, ctypes.c_float), _ptr(y, ctypes.c_float),
+                                  _ptr(y64, ctypes.c_double), batch, n, k), "ternary_gemm")
     return (y, y64) if want_f64 else y
 
 

@@ -19,8 +19,11 @@
  *                   "实现拆解" and "关键源码片段" (modelopt_quant.py excerpt and
  *                   the test's element-loop reference).
  *   [FairyFuse]     blog.hotdry.top post on FairyFuse (fused ternary kernels,
- *                   multiplication-free CPU inference). Section
- *                   "三元 GEMV 的乘法消除原理" (ternary GEMV without multiplies).
+ *                   multiplication-free CPU inference). Sections
+ *                   "三元 GEMV 的乘法消除原理" (ternary GEMV without multiplies),
+ *                   "复杂值广泛线性层的融合核调度" (the widely-linear complex
+ *                   layer) and "总结与启示" (batched GEMM for speculative
+ *                   decoding as the next step).
  *
  * Arithmetic is fp64 throughout except the NVFP4 gather, whose page fixes
  * fp32 (both scale factors are cast to float and multiplied in float before
@@ -228,6 +231,23 @@ int or_ternary_gemv(const uint32_t* packed, const float* row_scale, const float*
         double v = (double)row_scale[r] * acc;
         if (y64) y64[r] = v;
         if (y) y[r] = (float)v;
+    }
+    return bad ? OR_EINVAL : OR_OK;
+}
+
+/* Small-batch ternary GEMM: the ternary GEMV above applied to each of
+ * `batch` rows of x ([FairyFuse] "总结与启示" names batched GEMM fusion for
+ * speculative decoding as the next step; the computation is the same row
+ * sum per activation row): y[b][r] = s[r] * sum_c t(r, c) x[b][c], fp64 sum,
+ * rounded to fp32 once. x is [batch, k], y is [batch, n]. */
+int or_ternary_gemm(const uint32_t* packed, const float* row_scale, const float* x, float* y,
+                    double* y64, int64_t batch, int64_t n, int64_t k) {
+    if (batch < 0 || n < 0 || k < 0 || k % 16 != 0) return OR_EINVAL;
+    int bad = 0;
+    for (int64_t b = 0; b < batch; ++b) {
+        int st = or_ternary_gemv(packed, row_scale, x + b * k, y ? y + b * n : NULL,
+                                 y64 ? y64 + b * n : NULL, n, k);
+        if (st != OR_OK) bad = 1;
     }
     return bad ? OR_EINVAL : OR_OK;
 }

@@ -13,6 +13,8 @@ Workload shapes (value distributions as stated for each):
     bytes over all 256 exponents.
   * Ternary GEMV, W 4096 x 4096, each 2-bit pattern 00/01/10 with probability
     1/3; per-row fp32 scale U[0.01, 0.1]; x fp32 N(0,1).
+  * Small-batch ternary GEMM: the ternary GEMV matrix with x fp32
+    [batch, k] ~N(0,1), batch 1..16 (4 and 8 measured).
   * Widely-linear complex ternary layer, four such 4096 x 4096 matrices
     (U_re, U_im, W_re, W_im), four per-row scales U[0.01, 0.1], x_re and x_im
     fp32 N(0,1).
@@ -130,6 +132,16 @@ def ternary_case(seed: int = SEED_BASE + 1, n: int = 4096, k: int = 4096):
     packed = two_bit_words(r, n, k)
     scale = r.uniform(0.01, 0.1, size=n).astype(np.float32)
     x = f32_normal(r, (k,))
+    return {"packed": packed, "row_scale": scale, "x": x}
+
+
+def ternary_batch_case(seed: int = SEED_BASE + 6, batch: int = 4, n: int = 4096, k: int = 4096):
+    """Ternary GEMM for a few activation rows (speculative decoding): the
+    ternary GEMV matrix and scales, x fp32 [batch, k] ~N(0, 1)."""
+    r = rng(seed)
+    packed = two_bit_words(r, n, k)
+    scale = r.uniform(0.01, 0.1, size=n).astype(np.float32)
+    x = f32_normal(r, (batch, k))
     return {"packed": packed, "row_scale": scale, "x": x}
 
 

@@ -288,3 +288,32 @@ def test_moe_rejects_bad_expert_ids(orc):
     with pytest.raises(ValueError):
         orc.mxfp4_moe(x, w13[None], w13s[None], w2[None], w2s[None],
                       np.array([[1]], dtype=np.int32), np.ones((1, 1), np.float32))
+
+
+# ------------------------------------------------------- small-batch ternary --
+
+@pytest.mark.parametrize("batch,n,k", [(1, 9, 64), (3, 17, 256), (16, 40, 512)])
+def test_ternary_gemm_matches_dense_product(orc, batch, n, k):
+    """Each output row is the scaled ternary product of its activation row: a
+    dense fp64 matmul of the decode (from the page's packing rule, applied in
+    the encode direction here) against all rows at once."""
+    r = np.random.default_rng(batch * 100 + n)
+    t = r.integers(-1, 2, size=(n, k))
+    s = r.uniform(0.01, 0.1, n).astype(np.float32)
+    x = r.standard_normal((batch, k)).astype(np.float32)
+    y, y64 = orc.ternary_gemm(pack_ternary(t), s, x, want_f64=True)
+    want = (x.astype(np.float64) @ t.T.astype(np.float64)) * s.astype(np.float64)[None, :]
+    bound = 1e-13 * (np.abs(x).astype(np.float64) @ np.abs(t).T) * s[None, :]
+    assert (np.abs(y64 - want) <= bound).all()
+    assert np.array_equal(y, y64.astype(np.float32))
+
+
+def test_ternary_gemm_rows_are_independent(orc):
+    """Permuting the activation rows permutes the output rows, and a zero row gives zeros."""
+    case = synth.ternary_batch_case(5, 6, 64, 1024)
+    perm = np.array([3, 0, 5, 1, 4, 2])
+    x = case["x"].copy()
+    x[4] = 0
+    y = orc.ternary_gemm(case["packed"], case["row_scale"], x)
+    yp = orc.ternary_gemm(case["packed"], case["row_scale"], x[perm])
+    assert np.array_equal(yp, y[perm]) and (y[4] == 0).all()
