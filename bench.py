@@ -6,8 +6,8 @@
 Prints ONE JSON line. The default workload is the headline: MXFP4 dequant-GEMV
 at batch 1 on the Llama-8B MLP shapes (W 14336 x 4096 and W 4096 x 14336, one
 launch each per step), bf16 output. Other workloads (for the per-kernel
-roofline tables): mlp_b4, mlp_b16, ternary, ternary_wl, gather, moe, decode,
-gemv_small.
+roofline tables): mlp_b4, mlp_b16, ternary, ternary_b1 .. ternary_b16
+(small-batch ternary GEMM), ternary_wl, gather, moe, decode, gemv_small.
 
 Timing: inputs are resident in HBM before the timed region. The launches of
 one step per weight copy are captured into a HIP graph; W warmup steps are
@@ -50,8 +50,9 @@ PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
     "gemv": ["gemv.hip"],
     "moe": ["moe.hip", "moe_engine.hpp"],
-    "ternary": ["ternary.hip"],
-    "ternarywl": ["ternary_wl.hip"],
+    "ternary": ["ternary.hip", "ternary_batch.hip", "ternary_int8.hpp"],
+    "ternarywl": ["ternary_wl.hip", "ternary_int8.hpp"],
+    "ternarygemm": ["ternary_batch.hip", "ternary_int8.hpp"],
     "gather": ["gather.hip"],
     "decode": ["decode.hip"],
 }
@@ -212,6 +213,55 @@ class Ternary(Workload):
         return {"value": round(self.weight_bytes_per_step * reps / el / 1e9, 3), "unit": "GB/s",
                 "cores": oracle.threads(), "kind": "oracle",
                 "sample": f"the full 4096 x 4096 GEMV repeated {reps} times, {el:.1f} s"}
+
+
+class TernaryBatch(Workload):
+    """Small-batch ternary GEMM: the 4096 x 4096 ternary matrix against
+    `batch` activation rows (speculative decoding)."""
+
+    def __init__(self, batch: int, rotate_bytes: float, n: int = 4096, k: int = 4096):
+        import torch
+        import gemm_e2m1_lut_amd as lib
+        import synth
+        self.lib, self.batch, self.n, self.k = lib, batch, n, k
+        self.name = f"ternary_gemm_b{batch}_{n}x{k}"
+        per_copy = n * k // 4
+        self.copies = max(2, math.ceil(rotate_bytes / per_copy))
+        self.host = synth.ternary_batch_case(batch=batch, n=n, k=k)
+        dev0 = torch.from_numpy(self.host["packed"].view(np.int32)).cuda()
+        # rotated copies: the same weights rolled by whole rows (distinct addresses, same statistics)
+        self.packed = [torch.roll(dev0, shifts=7 * i, dims=0).contiguous() for i in range(self.copies)]
+        self.scale = torch.from_numpy(self.host["row_scale"]).cuda()
+        self.x = torch.from_numpy(self.host["x"]).cuda()
+        self.y = torch.empty(batch, n, device="cuda")
+        self.weight_bytes_per_step = float(per_copy + 4 * n)
+        self.total_bytes_per_step = float(self.alg_bytes("ternarygemm"))
+        self.dtype = "f32"
+        self.config = {"workload": self.name, "weights": "2-bit ternary, 16 per uint32", "batch": batch,
+                       "activations": "fp32", "out": "fp32", "weight_copies_rotated": self.copies}
+
+    def launches(self):
+        def fn(i):
+            self.lib.ternary_gemm(self.packed[i % self.copies], self.scale, self.x, out=self.y)
+        return [("ternarygemm", fn)]
+
+    def alg_bytes(self, label):
+        return self.n * self.k // 4 + 4 * self.n + 4 * self.batch * (self.k + self.n)
+
+    def cpu_baseline(self, budget_s):
+        import oracle
+        h = self.host
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.ternary_gemm(h["packed"], h["row_scale"], h["x"])
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s or reps >= 2000:
+                break
+        return {"value": round(self.weight_bytes_per_step * reps / el / 1e9, 3), "unit": "GB/s",
+                "cores": oracle.threads(), "kind": "oracle",
+                "sample": f"the full {self.n} x {self.k} GEMM at batch {self.batch} repeated {reps} times, "
+                          f"{el:.1f} s"}
 
 
 class TernaryWL(Workload):
@@ -449,6 +499,11 @@ WORKLOADS = {
     "mlp_b16": lambda rb: GemvMLP(16, rb),
     "ternary": Ternary,
     "ternary_wl": TernaryWL,
+    "ternary_b1": lambda rb: TernaryBatch(1, rb),
+    "ternary_b2": lambda rb: TernaryBatch(2, rb),
+    "ternary_b4": lambda rb: TernaryBatch(4, rb),
+    "ternary_b8": lambda rb: TernaryBatch(8, rb),
+    "ternary_b16": lambda rb: TernaryBatch(16, rb),
     "gather": Gather,
     "decode": Decode,
     "gemv_small": GemvSmall,

@@ -6,14 +6,16 @@ the HIP sources in csrc/ by build.py. This package is its thin Python binding:
 torch supplies device memory and streams; every step of every operation runs
 in the library's kernels.
 
-Operations: dequant_decode, dequant_gemv, ternary_gemv, ternary_wl_gemv,
-nvfp4_embedding_gather, mxfp4_moe_gemm (+ mxfp4_moe_workspace_size).
+Operations: dequant_decode, dequant_gemv, ternary_gemv, ternary_gemm,
+ternary_wl_gemv, nvfp4_embedding_gather, mxfp4_moe_gemm (+
+mxfp4_moe_workspace_size).
 """
 from ._binding import (  # noqa: F401
     ABI_VERSION,
     DTYPE_BF16,
     DTYPE_F32,
     GEMV_MAX_BATCH,
+    TERNARY_MAX_BATCH,
     LIB_PATH,
     E2M1Error,
     abi_version,
@@ -25,6 +27,7 @@ from ._binding import (  # noqa: F401
     mxfp4_moe_workspace_size,
     nvfp4_embedding_gather,
     strerror,
+    ternary_gemm,
     ternary_gemv,
     ternary_wl_gemv,
 )

@@ -21,6 +21,7 @@ ABI_VERSION = 1
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
 GEMV_MAX_BATCH = 16
+TERNARY_MAX_BATCH = 16
 
 _lib = None
 
@@ -53,6 +54,7 @@ def load_library() -> ctypes.CDLL:
         "dequant_decode": (ctypes.c_int, [vp, vp, vp, i64, i64, vp]),
         "dequant_gemv": (ctypes.c_int, [vp, vp, vp, vp, i32, i64, i64, i64, vp]),
         "ternary_gemv": (ctypes.c_int, [vp, vp, vp, vp, i64, i64, vp]),
+        "ternary_gemm": (ctypes.c_int, [vp, vp, vp, vp, i64, i64, i64, vp]),
         "ternary_wl_gemv": (ctypes.c_int, [ctypes.POINTER(vp), vp, vp, vp, vp, vp, i64, i64, vp]),
         "nvfp4_embedding_gather": (ctypes.c_int, [vp, vp, vp, vp, vp, i64, i64, i64, vp, vp]),
         "mxfp4_moe_workspace_size": (sz, [i64, i64, i64, i64, i64]),
@@ -170,6 +172,25 @@ def ternary_gemv(packed: torch.Tensor, row_scale: torch.Tensor, x: torch.Tensor,
     _need(out, "out", (torch.float32,), (n,))
     _check("ternary_gemv", load_library().ternary_gemv(_ptr(packed), _ptr(row_scale), _ptr(x), _ptr(out),
                                                         n, k, _stream(stream)))
+    return out
+
+
+def ternary_gemm(packed: torch.Tensor, row_scale: torch.Tensor, x: torch.Tensor,
+                 out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Ternary W packed int32/uint32 [n, k/16], fp32 scale [n], fp32 x [batch, k] -> y [batch, n]."""
+    _need(packed, "packed", (torch.int32, torch.uint32))
+    n, words = packed.shape
+    k = 16 * words
+    _need(row_scale, "row_scale", (torch.float32,), (n,))
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise ValueError("x must be a [batch, k] tensor")
+    batch = x.shape[0]
+    _need(x, "x", (torch.float32,), (batch, k))
+    if out is None:
+        out = torch.empty((batch, n), dtype=torch.float32, device=packed.device)
+    _need(out, "out", (torch.float32,), (batch, n))
+    _check("ternary_gemm", load_library().ternary_gemm(_ptr(packed), _ptr(row_scale), _ptr(x), _ptr(out),
+                                                        batch, n, k, _stream(stream)))
     return out
 
 

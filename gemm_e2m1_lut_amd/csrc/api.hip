@@ -99,6 +99,20 @@ int ternary_gemv(const uint32_t* packed, const float* row_scale, const float* x,
     return launch_status(e2m1::launch_ternary(packed, row_scale, x, y, n, k, as_stream(stream)));
 }
 
+int ternary_gemm(const uint32_t* packed, const float* row_scale, const float* x, float* y,
+                 int64_t batch, int64_t n, int64_t k, void* stream) {
+    if (batch < 1 || batch > E2M1_TERNARY_MAX_BATCH || n < 0 || k < 0 || k % 16 != 0 || n > INT_MAX ||
+        k / 16 > INT_MAX / 64 || !mul_ok(n, k) || !mul_ok(batch * 4, k) || !mul_ok(batch * 4, n))
+        return E2M1_ERR_SHAPE;
+    if (n == 0) return E2M1_OK;
+    if (!y) return E2M1_ERR_NULL;
+    if (!aligned(y, 4)) return E2M1_ERR_ALIGN;
+    if (k == 0) return launch_status(fill_zero_bytes(y, batch * n * 4, as_stream(stream)));
+    if (!packed || !row_scale || !x) return E2M1_ERR_NULL;
+    if (!aligned(packed, 4) || !aligned(x, 4) || !aligned(row_scale, 4)) return E2M1_ERR_ALIGN;
+    return launch_status(e2m1::launch_ternary_gemm(packed, row_scale, x, y, batch, n, k, as_stream(stream)));
+}
+
 int ternary_wl_gemv(const uint32_t* const packed[4], const float* scale, const float* x_re,
                     const float* x_im, float* y_re, float* y_im, int64_t n, int64_t k, void* stream) {
     if (n < 0 || k < 0 || k % 16 != 0 || n > INT_MAX || k / 16 > INT_MAX / 64 || !mul_ok(n, k) ||

@@ -120,24 +120,4 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
     return __uint_as_float(s | ((e + 120u) << 23) | (m << 20));
 }
 
-// ------------------------------------------------------------- ternary ----
-
-// Ternary weight pairs (FairyFuse blog post, section "三元 GEMV 的乘法消除原理":
-// bit 2j+1 of a word = +1, bit 2j = -1, neither = 0), as bf16 pairs for
-// v_dot2_f32_bf16 or a bf16 MFMA operand. Fields p and p + 8 of a word (bits 2p,
-// 2p+1 and 2p+16, 2p+17) are rotated to bits 8-9 and 24-25 and masked; the
-// result is a v_perm_b32 selector that picks, from a 4-byte pool, the high
-// byte of bf16 -0.5 (field 01), +0.5 (field 10) or 0 (fields 00 and 11), and
-// 0x00 for the low bytes (selector byte 0 -> pool byte 0 = 0x00). One rotate,
-// one mask and one perm give two weights as a bf16 pair of +/-0.5 or 0; the
-// factor 2 is applied exactly with the row scale.
-constexpr uint32_t kHalfPool = 0x003FBF00u;   // pool bytes: 00, BF (-0.5), 3F (+0.5), 00
-
-template <int P>
-__device__ __forceinline__ uint32_t ternary_pair(uint32_t w) {
-    constexpr int kRotl = 8 - 2 * P;                     // bring bits 2P.. to bit 8
-    const uint32_t r = kRotl == 0 ? w : __builtin_amdgcn_alignbit(w, w, (32 - kRotl) & 31);
-    return __builtin_amdgcn_perm(0u, kHalfPool, r & 0x03000300u);
-}
-
 }  // namespace e2m1

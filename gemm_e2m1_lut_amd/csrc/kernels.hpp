@@ -22,6 +22,9 @@ hipError_t launch_gemv(const uint8_t* packed, const uint8_t* scales, const uint1
 hipError_t launch_ternary(const uint32_t* packed, const float* row_scale, const float* x, float* y,
                           int64_t n, int64_t k, hipStream_t stream);
 
+hipError_t launch_ternary_gemm(const uint32_t* packed, const float* row_scale, const float* x, float* y,
+                               int64_t batch, int64_t n, int64_t k, hipStream_t stream);
+
 hipError_t launch_ternary_wl(const uint32_t* const mats[4], const float* scale, const float* x_re,
                              const float* x_im, float* y_re, float* y_im, int64_t n, int64_t k,
                              hipStream_t stream);

@@ -1,0 +1,102 @@
+// ternary_int8.hpp -- ternary weights and fp32 activations on the int8 matrix
+// cores (v_mfma_i32_16x16x64_i8), shared by the widely-linear layer and the
+// small-batch ternary GEMM.
+//
+// Ternary packing: FairyFuse blog post, section "三元 GEMV 的乘法消除原理"
+// (16 weights per word, bit 2j+1 = +1, bit 2j = -1, neither = 0).
+//
+// Weights: one mask of a shifted word gives the fields j, j + 4, j + 8,
+// j + 12 as v_perm_b32 selectors into a 4-byte pool, so one perm decodes four
+// weights to int8 (11 VALU operations per 16-weight word). In the resulting
+// A operand of word q, byte b of dword j is the weight of column
+// 16 q + j + 4 b.
+//
+// Activations: X = rint(x 2^S) with |X| <= 2^30, one exponent S per group of
+// values sharing a scale (from their largest |x|), written as four signed
+// base-256 digits. Digit columns of the B operand list, for the same columns
+// and in the same order as the A operand, digit i of X; the int32 products
+// are exact and digit column i is worth 2^(8 i - S).
+#pragma once
+
+#include "device.hpp"
+
+namespace e2m1 {
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void issue_fence() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// Largest value over the wave (DPP only), returned uniform.
+__device__ __forceinline__ float wave_max(float v) {
+    v = fmaxf(v, dpp_f32<0xB1>(v));
+    v = fmaxf(v, dpp_f32<0x4E>(v));
+    v = fmaxf(v, dpp_f32<0x141>(v));
+    v = fmaxf(v, dpp_f32<0x140>(v));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xC, 0xF, false)));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// Exponent S with |x 2^S| <= 2^30 for every |x| <= m (m = 0 gives 30).
+__device__ __forceinline__ int slice_exponent(float m) {
+    return 30 - __builtin_amdgcn_frexp_expf(m);
+}
+
+// The four signed base-256 digits of X = rint(x 2^S), |X| <= 2^30, as the
+// bytes of one word: X + 0x808080 has unsigned low bytes u_i with
+// X = sum (u_i - 128) 256^i + u_3 256^3, and xor 0x80 turns u_i into the
+// int8 pattern of u_i - 128.
+__device__ __forceinline__ uint32_t digits(float x, int S) {
+    const int X = (int)rintf(ldexpf(x, S));
+    return ((uint32_t)X + 0x00808080u) ^ 0x00808080u;
+}
+
+// 4 x 4 byte transpose: byte b of out[i] = byte i of in[b].
+__device__ __forceinline__ void transpose4(const uint32_t (&in)[4], uint32_t (&out)[4]) {
+    const uint32_t lo01 = __builtin_amdgcn_perm(in[1], in[0], 0x05010400u);
+    const uint32_t hi01 = __builtin_amdgcn_perm(in[1], in[0], 0x07030602u);
+    const uint32_t lo23 = __builtin_amdgcn_perm(in[3], in[2], 0x05010400u);
+    const uint32_t hi23 = __builtin_amdgcn_perm(in[3], in[2], 0x07030602u);
+    out[0] = __builtin_amdgcn_perm(lo23, lo01, 0x05040100u);
+    out[1] = __builtin_amdgcn_perm(lo23, lo01, 0x07060302u);
+    out[2] = __builtin_amdgcn_perm(hi23, hi01, 0x05040100u);
+    out[3] = __builtin_amdgcn_perm(hi23, hi01, 0x07060302u);
+}
+
+// Ternary fields j, j + 4, j + 8, j + 12 of a word as int8 bytes 0..3: the
+// masked field is a v_perm_b32 selector into the pool 00 (0), FF (-1 for
+// field 01), 01 (+1 for field 10), 00 (field 11, not a valid weight: 0).
+constexpr uint32_t kI8Pool = 0x0001FF00u;
+
+template <int J>
+__device__ __forceinline__ uint32_t ternary_quad(uint32_t w) {
+    const uint32_t sel = (J == 0 ? w : (w >> (2 * J))) & 0x03030303u;
+    return __builtin_amdgcn_perm(0u, kI8Pool, sel);
+}
+
+__device__ __forceinline__ i32x4 decode_word(uint32_t w) {
+    i32x4 a;
+    a.x = (int)ternary_quad<0>(w);
+    a.y = (int)ternary_quad<1>(w);
+    a.z = (int)ternary_quad<2>(w);
+    a.w = (int)ternary_quad<3>(w);
+    return a;
+}
+
+// Largest value over each 16-lane row (DPP only), in every lane of the row.
+__device__ __forceinline__ float row16_max(float v) {
+    v = fmaxf(v, dpp_f32<0xB1>(v));
+    v = fmaxf(v, dpp_f32<0x4E>(v));
+    v = fmaxf(v, dpp_f32<0x141>(v));
+    v = fmaxf(v, dpp_f32<0x140>(v));
+    return v;
+}
+
+__device__ __forceinline__ i32x4 mfma_i8(i32x4 a, i32x4 b, i32x4 c) {
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+}  // namespace e2m1

@@ -13,9 +13,10 @@
  *                  "关键源码片段").
  *   [FairyFuse]    blog.hotdry.top post on FairyFuse: 2-bit ternary GEMV with
  *                  add/sub accumulation and a per-row scale
- *                  ("三元 GEMV 的乘法消除原理"), and the widely-linear complex
+ *                  ("三元 GEMV 的乘法消除原理"), the widely-linear complex
  *                  layer fused over four ternary matrices
- *                  ("复杂值广泛线性层的融合核调度").
+ *                  ("复杂值广泛线性层的融合核调度") and batched ternary GEMM
+ *                  for speculative decoding ("总结与启示").
  *
  * Conventions shared by every entry point
  *   - All array pointers are DEVICE pointers (hipMalloc'd or torch CUDA
@@ -115,17 +116,39 @@ int dequant_gemv(const uint8_t* packed, const uint8_t* scale_e8m0, const uint16_
  * weight j of word w multiplies x[16w + j]; bit 2j+1 set = +1 (add), bit 2j
  * set = -1 (subtract), neither = 0; the per-row scale multiplies once after
  * the row sum. A field with both bits set is not a valid weight; the kernel
- * reads it as 0. Accumulation is fp32.
+ * reads it as 0.
  *   packed     uint32 [n, k/16]  (4-byte aligned)
  *   row_scale  fp32   [n]
  *   x          fp32   [k]        (4-byte aligned)
  *   y          fp32   [n], overwritten
- * Requires n >= 0, k >= 0, k % 16 == 0. k == 0 writes zeros. The fastest
- * kernel needs k % 64 == 0 and 16-byte aligned packed and x; other inputs
- * take a slower kernel with the same results.
+ * Requires n >= 0, k >= 0, k % 16 == 0. k == 0 writes zeros. x must be
+ * finite. With k % 64 == 0 and 16-byte aligned packed this is ternary_gemm at
+ * batch 1 (exact sums over a fixed-point rendering of x, then a few fp32
+ * roundings); other inputs take a slower kernel that adds in fp32.
  */
 int ternary_gemv(const uint32_t* packed, const float* row_scale, const float* x, float* y,
                  int64_t n, int64_t k, void* stream);
+
+/*
+ * ternary_gemm -- small-batch ternary GEMM: y[b][i] = row_scale[i] * sum_k t(i,k) * x[b][k].
+ * Operation: [FairyFuse] "三元 GEMV 的乘法消除原理" applied to `batch`
+ * activation rows at once, the batched fusion for speculative decoding that
+ * "总结与启示" names as the next step; packing and scale as for ternary_gemv.
+ *   packed     uint32 [n, k/16]  (4-byte aligned)
+ *   row_scale  fp32   [n]
+ *   x          fp32   [batch, k] (4-byte aligned)
+ *   y          fp32   [batch, n], overwritten
+ * Requires 1 <= batch <= E2M1_TERNARY_MAX_BATCH, n >= 0, k >= 0,
+ * k % 16 == 0. k == 0 writes zeros. A field with both bits set reads as 0;
+ * x must be finite. The fast kernel (k % 64 == 0, 16-byte aligned packed)
+ * sums ternary times a fixed-point rendering of x exactly (each element to
+ * within 2^-31 of the largest |x| of its row and 256-column slice) and rounds
+ * in fp32 only a few times per output; other inputs run ternary_gemv once
+ * per row of x.
+ */
+#define E2M1_TERNARY_MAX_BATCH 16
+int ternary_gemm(const uint32_t* packed, const float* row_scale, const float* x, float* y,
+                 int64_t batch, int64_t n, int64_t k, void* stream);
 
 /*
  * ternary_wl_gemv -- widely-linear complex ternary layer y = U x + W conj(x).

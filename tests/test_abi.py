@@ -37,7 +37,7 @@ def lib():
 
 def test_header_declares_the_five_operations():
     names = declared_functions()
-    for op in ("dequant_decode", "dequant_gemv", "ternary_gemv", "ternary_wl_gemv", "nvfp4_embedding_gather",
+    for op in ("dequant_decode", "dequant_gemv", "ternary_gemv", "ternary_gemm", "ternary_wl_gemv", "nvfp4_embedding_gather",
                "mxfp4_moe_gemm", "mxfp4_moe_workspace_size", "e2m1_abi_version", "e2m1_strerror"):
         assert op in names
 
@@ -104,6 +104,19 @@ def test_ternary_validation(lib):
     assert f(A, B, C, NULL, 4, 16, NULL) == E_NULL
     assert f(NULL, B, C, D, 4, 16, NULL) == E_NULL
     assert f(P(0x10002), B, C, D, 4, 16, NULL) == E_ALIGN
+
+
+def test_ternary_gemm_validation(lib):
+    f = lib.ternary_gemm
+    assert f(A, B, C, D, 0, 4, 16, NULL) == E_SHAPE    # batch 0
+    assert f(A, B, C, D, 17, 4, 16, NULL) == E_SHAPE   # batch above 16
+    assert f(A, B, C, D, 2, 4, 24, NULL) == E_SHAPE    # k % 16
+    assert f(A, B, C, D, 2, -1, 16, NULL) == E_SHAPE
+    assert f(NULL, NULL, NULL, NULL, 3, 0, 16, NULL) == E2M1_OK
+    assert f(A, B, C, NULL, 2, 4, 16, NULL) == E_NULL
+    assert f(A, NULL, C, D, 2, 4, 16, NULL) == E_NULL
+    assert f(A, B, P(0x30002), D, 2, 4, 16, NULL) == E_ALIGN
+    assert f(P(0x10001), B, C, D, 2, 4, 16, NULL) == E_ALIGN
 
 
 def test_ternary_wl_validation(lib):
