@@ -308,77 +308,103 @@ constexpr int kTileSteps = 4;                        // 256-column steps per wav
 constexpr int kSliceBlocks = 8 * kTileSteps;         // 32 scale blocks = 1024 columns per wave
 constexpr int kMaxSliceWaves = 16;
 
+constexpr int kXPitch = 128 + 8;                     // bf16 per staged x row (16-byte pad spreads the banks)
+constexpr int kBufferWord3 = 0x00020000;             // buffer descriptor word 3 for raw 32-bit access (gfx9 family)
+
 // Workgroup = S waves on one tile of 16 rows (tiles blockIdx.x, + gridDim.x,
 // ...); wave w owns scale blocks [32 w, 32 w + 32). Lane l = 16 g + r: row r
-// of the tile for the A operand and batch column r for the B operand; in step
-// s it loads blocks b = 32 w + 8 s + g + 4 h (h = 0, 1: both halves of a
-// 128-byte line of the row). MFMA (s, h, i) takes codes [8 i, 8 i + 8) of
-// block b as A k-slots 8 g .. 8 g + 7 and the same columns of x as B k-slots,
-// so both operands share one column -> k-slot map and the sum over k is
-// complete. D element (row 4 g + j, batch r) is component j of acc in lane l.
-// All of a slice's weight loads are issued first, the x operands of step
-// s + 1 before the MFMAs of step s.
-template <bool kBf16Out>
+// of the tile for the A operand and batch column r for the B operand; in half
+// step hs = 2 s + h it loads block b = 32 w + 8 s + g + 4 h (the two halves of
+// a 128-byte line of the row are half steps h = 0, 1). MFMA (hs, i) takes
+// codes [8 i, 8 i + 8) of block b as A k-slots 8 g .. 8 g + 7 and the same
+// columns of x as B k-slots, so both operands share one column -> k-slot map
+// and the sum over k is complete. D element (row 4 g + j, batch r) is
+// component j of acc in lane l.
+// x reaches the B operands through the wave's own LDS area: the half step's
+// 128 columns of all batch rows are loaded with coalesced 16-byte loads (16
+// lanes per 256-byte row, NJ = ceil(batch / 4) loads per lane), written to
+// LDS and read back per MFMA; loading them per lane straight from memory
+// would make each B operand a separate 16-byte request into a different row
+// of x. The x loads of half step 0 go out first, then every weight load of the
+// slice, then the x loads of half step hs + 1 right after half step hs is
+// staged; one wave writes and reads its own area, and LDS accesses of a wave
+// complete in order, so no barrier is needed.
+template <bool kBf16Out, int NJ>
 __global__ __launch_bounds__(kWave * kMaxSliceWaves) void gemv_mfma_kernel(
-    const uint8_t* packed, const uint8_t* scales, const uint16_t* __restrict__ x, void* __restrict__ y,
+    const uint8_t* packed, const uint8_t* scales, const uint16_t* x, void* __restrict__ y,
     int batch, int n, int kc) {
     __shared__ f32x4 part[kMaxSliceWaves][kWave];
+    extern __shared__ __attribute__((aligned(16))) uint16_t gemv_xs[];
+    constexpr int kXRows = 4 * NJ;
+    constexpr int kHalfSteps = 2 * kTileSteps;
     const int lane = threadIdx.x & (kWave - 1);
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int nwaves = blockDim.x / kWave;
     const int r = lane & 15, g = lane >> 4;
     const int K = kc * 32;
     const int ntiles = (n + 15) / 16;
-    const int xrow = min(r, batch - 1);
     const bool bvalid = r < batch;
-    const uint16_t* xr = x + (size_t)xrow * K;
+    uint16_t* xs = gemv_xs + wv * kXRows * kXPitch;
+    // staging: chunk j of a lane is row 4 j + (lane >> 4), columns 8 (lane & 15) .. + 7 of the half step
+    uint16_t* xdst = xs + (lane >> 4) * kXPitch + 8 * (lane & 15);
+    const uint16_t* xread = xs + min(r, batch - 1) * kXPitch + 32 * g;
+    // x through a buffer resource of exactly batch * K elements: the hardware
+    // range check returns zeros for the rows past the batch and the columns past
+    // the last row (columns past K on earlier rows read the next row, in blocks
+    // whose B operand is masked). One 32-bit lane offset serves every load;
+    // per-load address pairs would be hoisted out of the tile loop and pinned.
+    const __amdgpu_buffer_rsrc_t xres =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x), 0, batch * K * 2, kBufferWord3);
+    const int xlane = 2 * ((lane >> 4) * K + 8 * (lane & 15));
+    auto load_x = [&](uint4 (&xg)[NJ], int hs) {
+        const int col = wv * kSliceBlocks * 32 + hs * 128;
+        int xl = xlane;
+        asm volatile("" : "+v"(xl));   // offsets are formed here, not kept for every half step
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(xres, xl + 2 * (4 * j * K + col), 0, 0);
+            xg[j] = make_uint4(v.x, v.y, v.z, v.w);
+        }
+    };
 
     for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {   // workgroup-uniform
         const int row = min(tile * 16 + r, n - 1);
         const uint8_t* wrow = packed + (size_t)row * (K / 2);
         const uint8_t* srow = scales + (size_t)row * kc;
-        uint4 w[kTileSteps][2];
-        uint32_t e[kTileSteps][2];
-#pragma unroll
-        for (int st = 0; st < kTileSteps; ++st)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int b = min(wv * kSliceBlocks + 8 * st + g + 4 * h, kc - 1);
-                w[st][h] = load_nt16(wrow + (size_t)b * 16);
-                e[st][h] = srow[b];
-            }
+        uint4 xg[NJ];
+        load_x(xg, 0);
         issue_here();
-        // x operands of one half step (block b of step st, h), one half step ahead
-        constexpr int kXAhead = 1;
-        bf16x8_t xb[kXAhead + 1][4];
-        auto load_x = [&](bf16x8_t (&dst)[4], int hs) {
+        uint4 w[kHalfSteps];
+        uint32_t e[kHalfSteps];
+#pragma unroll
+        for (int hs = 0; hs < kHalfSteps; ++hs) {
             const int b = min(wv * kSliceBlocks + 8 * (hs >> 1) + g + 4 * (hs & 1), kc - 1);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) dst[i] = *reinterpret_cast<const bf16x8_t*>(xr + 32 * b + 8 * i);
-        };
-#pragma unroll
-        for (int hs = 0; hs < kXAhead; ++hs) {
-            load_x(xb[hs], hs);
-            issue_here();
+            w[hs] = load_nt16(wrow + (size_t)b * 16);
+            e[hs] = srow[b];
         }
+        issue_here();
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int hs = 0; hs < 2 * kTileSteps; ++hs) {
-            const int st = hs >> 1, h = hs & 1;
-            if (hs + kXAhead < 2 * kTileSteps) load_x(xb[(hs + kXAhead) % (kXAhead + 1)], hs + kXAhead);
+        for (int hs = 0; hs < kHalfSteps; ++hs) {
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) *reinterpret_cast<uint4*>(xdst + 4 * j * kXPitch) = xg[j];
+            issue_here();   // the registers are free before the next half step's loads reuse them
+            if (hs + 1 < kHalfSteps) load_x(xg, hs + 1);
             issue_here();
-            const bool valid = bvalid && (wv * kSliceBlocks + 8 * st + g + 4 * h < kc);
-            const float sc = e8m0_scale(e[st][h]);
-            const uint32_t ws[4] = {w[st][h].x, w[st][h].y, w[st][h].z, w[st][h].w};
+            __builtin_amdgcn_wave_barrier();
+            const bool valid = bvalid && (wv * kSliceBlocks + 8 * (hs >> 1) + g + 4 * (hs & 1) < kc);
+            const float sc = e8m0_scale(e[hs]);
+            const uint32_t ws[4] = {w[hs].x, w[hs].y, w[hs].z, w[hs].w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const u32x4 a = {fp4x2_to_bf16x2<0>(ws[i], sc), fp4x2_to_bf16x2<1>(ws[i], sc),
                                  fp4x2_to_bf16x2<2>(ws[i], sc), fp4x2_to_bf16x2<3>(ws[i], sc)};
-                const u32x4 xv = __builtin_bit_cast(u32x4, xb[hs % (kXAhead + 1)][i]);
+                const u32x4 xv = *reinterpret_cast<const u32x4*>(xread + 8 * i);
                 const u32x4 bz = {valid ? xv.x : 0u, valid ? xv.y : 0u, valid ? xv.z : 0u, valid ? xv.w : 0u};
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                                __builtin_bit_cast(bf16x8, bz), acc, 0, 0, 0);
             }
+            __builtin_amdgcn_wave_barrier();   // this half step's reads come before the next one's writes
         }
         part[wv][lane] = acc;
         __syncthreads();
@@ -556,16 +582,36 @@ hipError_t dispatch_generic(int batch, const uint8_t* packed, const uint8_t* sca
 #undef E2M1_GEMV_CASE
 }
 
+template <bool kBf16Out, int NJ>
+hipError_t run_mfma_nj(int batch, const uint8_t* packed, const uint8_t* scales, const uint16_t* x, void* y,
+                       int n, int kc, hipStream_t stream) {
+    const int waves = (kc + kSliceBlocks - 1) / kSliceBlocks;
+    const int ntiles = (n + 15) / 16;
+    const size_t lds = (size_t)waves * 4 * NJ * kXPitch * sizeof(uint16_t);
+    static int cache[kMaxSliceWaves + 1] = {};   // resident workgroups per compute unit, per wave count
+    int& per_cu = cache[waves];
+    if (per_cu == 0) {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(gemv_mfma_kernel<kBf16Out, NJ>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gemv_mfma_kernel<kBf16Out, NJ>, kWave * waves,
+                                                         lds) != hipSuccess ||
+            per_cu < 1)
+            per_cu = 1;
+    }
+    const int grid = min(ntiles, per_cu * device_cu_count());
+    gemv_mfma_kernel<kBf16Out, NJ><<<grid, kWave * waves, lds, stream>>>(packed, scales, x, y, batch, n, kc);
+    return hipGetLastError();
+}
+
 template <bool kBf16Out>
 hipError_t run_mfma(int batch, const uint8_t* packed, const uint8_t* scales, const uint16_t* x, void* y, int n,
                     int kc, hipStream_t stream) {
-    const int waves = (kc + kSliceBlocks - 1) / kSliceBlocks;
-    const int ntiles = (n + 15) / 16;
-    // workgroups resident at once: 16 waves per compute unit
-    const int per_cu = max(1, kMaxSliceWaves / waves);
-    const int grid = min(ntiles, per_cu * device_cu_count());
-    gemv_mfma_kernel<kBf16Out><<<grid, kWave * waves, 0, stream>>>(packed, scales, x, y, batch, n, kc);
-    return hipGetLastError();
+    switch ((batch + 3) / 4) {   // x loads per lane and half step: four batch rows per 64-lane load
+        case 1: return run_mfma_nj<kBf16Out, 1>(batch, packed, scales, x, y, n, kc, stream);
+        case 2: return run_mfma_nj<kBf16Out, 2>(batch, packed, scales, x, y, n, kc, stream);
+        case 3: return run_mfma_nj<kBf16Out, 3>(batch, packed, scales, x, y, n, kc, stream);
+        default: return run_mfma_nj<kBf16Out, 4>(batch, packed, scales, x, y, n, kc, stream);
+    }
 }
 
 }  // namespace
