@@ -309,6 +309,7 @@ constexpr int kSliceBlocks = 8 * kTileSteps;         // 32 scale blocks = 1024 c
 constexpr int kMaxSliceWaves = 16;
 
 constexpr int kXPitch = 128 + 8;                     // bf16 per staged x row (16-byte pad spreads the banks)
+constexpr int kWPitch = 9;                           // uint4 per transposed code row (8 blocks + pad)
 constexpr int kBufferWord3 = 0x00020000;             // buffer descriptor word 3 for raw 32-bit access (gfx9 family)
 
 // Workgroup = S waves on one tile of 16 rows (tiles blockIdx.x, + gridDim.x,
@@ -344,7 +345,8 @@ __global__ __launch_bounds__(kWave * kMaxSliceWaves) void gemv_mfma_kernel(
     const int K = kc * 32;
     const int ntiles = (n + 15) / 16;
     const bool bvalid = r < batch;
-    uint16_t* xs = gemv_xs + wv * kXRows * kXPitch;
+    uint16_t* xs = gemv_xs + wv * (kXRows * kXPitch + 8 * kWPitch * 16);
+    uint4* wbuf = reinterpret_cast<uint4*>(xs + kXRows * kXPitch);   // 16 rows x kWPitch uint4
     // staging: chunk j of a lane is row 4 j + (lane >> 4), columns 8 (lane & 15) .. + 7 of the half step
     uint16_t* xdst = xs + (lane >> 4) * kXPitch + 8 * (lane & 15);
     const uint16_t* xread = xs + min(r, batch - 1) * kXPitch + 32 * g;
@@ -369,32 +371,49 @@ __global__ __launch_bounds__(kWave * kMaxSliceWaves) void gemv_mfma_kernel(
 
     for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {   // workgroup-uniform
         const int row = min(tile * 16 + r, n - 1);
-        const uint8_t* wrow = packed + (size_t)row * (K / 2);
         const uint8_t* srow = scales + (size_t)row * kc;
         uint4 xg[NJ];
         load_x(xg, 0);
         issue_here();
-        uint4 w[kHalfSteps];
+        // code lines: load (st, q) of lane l is row 8 q + l / 8 of the tile, block 8 st + l % 8
+        // (eight rows x 128 contiguous bytes per instruction); scale bytes straight in MFMA layout
+        uint4 wl[kTileSteps][2];
         uint32_t e[kHalfSteps];
+        const uint8_t* lrow[2];
 #pragma unroll
-        for (int hs = 0; hs < kHalfSteps; ++hs) {
-            const int b = min(wv * kSliceBlocks + 8 * (hs >> 1) + g + 4 * (hs & 1), kc - 1);
-            w[hs] = load_nt16(wrow + (size_t)b * 16);
-            e[hs] = srow[b];
+        for (int q = 0; q < 2; ++q) lrow[q] = packed + (size_t)min(tile * 16 + 8 * q + (lane >> 3), n - 1) * (K / 2);
+#pragma unroll
+        for (int st = 0; st < kTileSteps; ++st) {
+            const int b = min(wv * kSliceBlocks + 8 * st + (lane & 7), kc - 1);
+#pragma unroll
+            for (int q = 0; q < 2; ++q) wl[st][q] = load_nt16(lrow[q] + (size_t)b * 16);
         }
+#pragma unroll
+        for (int hs = 0; hs < kHalfSteps; ++hs)
+            e[hs] = srow[min(wv * kSliceBlocks + 8 * (hs >> 1) + g + 4 * (hs & 1), kc - 1)];
         issue_here();
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        uint4 wm[2];   // this step's blocks g and g + 4 of row r (MFMA layout)
 #pragma unroll
         for (int hs = 0; hs < kHalfSteps; ++hs) {
+            if ((hs & 1) == 0) {   // a new step: its code lines through the wave's LDS transpose
+#pragma unroll
+                for (int q = 0; q < 2; ++q) wbuf[(8 * q + (lane >> 3)) * kWPitch + (lane & 7)] = wl[hs >> 1][q];
+            }
 #pragma unroll
             for (int j = 0; j < NJ; ++j) *reinterpret_cast<uint4*>(xdst + 4 * j * kXPitch) = xg[j];
             issue_here();   // the registers are free before the next half step's loads reuse them
             if (hs + 1 < kHalfSteps) load_x(xg, hs + 1);
             issue_here();
             __builtin_amdgcn_wave_barrier();
+            if ((hs & 1) == 0) {
+                wm[0] = wbuf[r * kWPitch + g];
+                wm[1] = wbuf[r * kWPitch + g + 4];
+            }
             const bool valid = bvalid && (wv * kSliceBlocks + 8 * (hs >> 1) + g + 4 * (hs & 1) < kc);
             const float sc = e8m0_scale(e[hs]);
-            const uint32_t ws[4] = {w[hs].x, w[hs].y, w[hs].z, w[hs].w};
+            const uint4 wh = wm[hs & 1];
+            const uint32_t ws[4] = {wh.x, wh.y, wh.z, wh.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const u32x4 a = {fp4x2_to_bf16x2<0>(ws[i], sc), fp4x2_to_bf16x2<1>(ws[i], sc),
@@ -404,7 +423,7 @@ __global__ __launch_bounds__(kWave * kMaxSliceWaves) void gemv_mfma_kernel(
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                                __builtin_bit_cast(bf16x8, bz), acc, 0, 0, 0);
             }
-            __builtin_amdgcn_wave_barrier();   // this half step's reads come before the next one's writes
+            __builtin_amdgcn_wave_barrier();   // this half step's reads come before the next writes
         }
         part[wv][lane] = acc;
         __syncthreads();
@@ -587,7 +606,7 @@ hipError_t run_mfma_nj(int batch, const uint8_t* packed, const uint8_t* scales, 
                        int n, int kc, hipStream_t stream) {
     const int waves = (kc + kSliceBlocks - 1) / kSliceBlocks;
     const int ntiles = (n + 15) / 16;
-    const size_t lds = (size_t)waves * 4 * NJ * kXPitch * sizeof(uint16_t);
+    const size_t lds = (size_t)waves * (4 * NJ * kXPitch * sizeof(uint16_t) + 16 * kWPitch * sizeof(uint4));
     static int cache[kMaxSliceWaves + 1] = {};   // resident workgroups per compute unit, per wave count
     int& per_cu = cache[waves];
     if (per_cu == 0) {
