@@ -235,7 +235,8 @@ class TernaryBatch(Workload):
         self.x = torch.from_numpy(self.host["x"]).cuda()
         self.y = torch.empty(batch, n, device="cuda")
         self.weight_bytes_per_step = float(per_copy + 4 * n)
-        self.total_bytes_per_step = float(self.alg_bytes("ternarygemm"))
+        self.label = f"ternarygemm_b{batch}"
+        self.total_bytes_per_step = float(self.alg_bytes(self.label))
         self.dtype = "f32"
         self.config = {"workload": self.name, "weights": "2-bit ternary, 16 per uint32", "batch": batch,
                        "activations": "fp32", "out": "fp32", "weight_copies_rotated": self.copies}
@@ -243,7 +244,7 @@ class TernaryBatch(Workload):
     def launches(self):
         def fn(i):
             self.lib.ternary_gemm(self.packed[i % self.copies], self.scale, self.x, out=self.y)
-        return [("ternarygemm", fn)]
+        return [(self.label, fn)]
 
     def alg_bytes(self, label):
         return self.n * self.k // 4 + 4 * self.n + 4 * self.batch * (self.k + self.n)
@@ -410,7 +411,9 @@ class GemvSmall(Workload):
         self.s = torch.from_numpy(c["scales"]).cuda()
         self.x = torch.from_numpy(c["x"].view(np.int16)).view(torch.bfloat16).cuda()
         self.y = torch.empty((1, 256), device="cuda")
-        self.copies = 1
+        # the same buffers, 256 launches per graph: a graph of one launch would time the
+        # host's graph launch rather than the kernel
+        self.copies = 256
         self.weight_bytes_per_step = 256 * 256 + 256 * 16
         self.total_bytes_per_step = float(self.alg_bytes("gemv_small"))
         self.bound = "latency"
