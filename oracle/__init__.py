@@ -85,6 +85,10 @@ def load():
         "or_nvfp4_element": (u16, [ctypes.c_int, u8, f32]),
         "or_nvfp4_gather": (ctypes.c_int, [_p(u8), _p(u8), f32, _p(i64), _p(u16), i64, i64, i64,
                                            _p(i64)]),
+        "or_e2m1_encode": (u8, [f64]),
+        "or_e4m3_encode": (u8, [f64]),
+        "or_mxfp4_quantize": (ctypes.c_int, [_p(u16), _p(u8), _p(u8), i64, i64]),
+        "or_nvfp4_quantize": (ctypes.c_int, [_p(u16), f32, _p(u8), _p(u8), i64, i64]),
         "or_mxfp4_moe": (ctypes.c_int, [_p(u16), _p(u8), _p(u8), _p(u8), _p(u8), _p(ctypes.c_int32),
                                         _p(f32), _p(f64), i64, i64, i64, i64, i64]),
     }
@@ -251,6 +255,37 @@ def ternary_wl_gemv(packed, scale, x_re, x_im, want_f64: bool = False):
                                      _ptr(y[1], ctypes.c_float), _ptr(y64[0], ctypes.c_double),
                                      _ptr(y64[1], ctypes.c_double), n, k), "ternary_wl_gemv")
     return ((y[0], y[1]), (y64[0], y64[1])) if want_f64 else (y[0], y[1])
+
+
+def e2m1_encode(v: float) -> int:
+    return int(load().or_e2m1_encode(float(v)))
+
+
+def e4m3_encode(t: float) -> int:
+    return int(load().or_e4m3_encode(float(t)))
+
+
+def mxfp4_quantize(x_bf16_bits):
+    """bf16 bit patterns [rows, k] -> (codes uint8 [rows, k/2], E8M0 uint8 [rows, k/32])."""
+    xv = _arr(x_bf16_bits, np.uint16)
+    rows, k = xv.shape
+    packed = np.empty((rows, k // 2), dtype=np.uint8)
+    scales = np.empty((rows, k // 32), dtype=np.uint8)
+    _check(load().or_mxfp4_quantize(_ptr(xv, ctypes.c_uint16), _ptr(packed, ctypes.c_uint8),
+                                    _ptr(scales, ctypes.c_uint8), rows, k), "mxfp4_quantize")
+    return packed, scales
+
+
+def nvfp4_quantize(x_bf16_bits, global_scale: float):
+    """bf16 bit patterns [rows, k], fp32 global scale -> (codes [rows, k/2], E4M3 bytes [rows, k/16])."""
+    xv = _arr(x_bf16_bits, np.uint16)
+    rows, k = xv.shape
+    packed = np.empty((rows, k // 2), dtype=np.uint8)
+    bs = np.empty((rows, k // 16), dtype=np.uint8)
+    _check(load().or_nvfp4_quantize(_ptr(xv, ctypes.c_uint16), ctypes.c_float(float(np.float32(global_scale))),
+                                    _ptr(packed, ctypes.c_uint8), _ptr(bs, ctypes.c_uint8), rows, k),
+           "nvfp4_quantize")
+    return packed, bs
 
 
 def nvfp4_gather(table, block_scale, global_scale, ids):

@@ -355,6 +355,133 @@ int or_nvfp4_gather(const uint8_t* table, const uint8_t* block_scale, float glob
     return OR_OK;
 }
 
+/* ----------------------------------------------------------- quantizers --- */
+
+/* The pages use quantized weights but print no encoder: the MoE test of
+ * [vLLM-51583] ("关键源码片段") calls an MXFP4 quantizer on bf16 weights and
+ * shows only its outputs (codes [.., K/2], E8M0 scales [.., K/32]); the NVFP4
+ * page ([SGLang-34222]) shows only the dequantisation. Reading taken (the
+ * OCP microscaling rule for MXFP4, and the same element rounding for NVFP4):
+ * an element is the E2M1 value nearest to its scaled input, ties to the code
+ * whose last bit is 0, magnitudes above 6 saturate to 6, and the sign bit is
+ * the input's (so a small negative input gives code 8). */
+static int e2m1_encode(double v) {
+    int sign = signbit(v) ? 8 : 0;
+    double a = fabs(v);
+    if (a >= 6.0) return sign | 7;
+    int best = 0;
+    double bd = a;
+    for (int i = 1; i < 8; ++i) {
+        double d = fabs(a - E2M1_MAGNITUDE[i]);
+        if (d < bd || (d == bd && (i % 2) == 0)) {
+            best = i;
+            bd = d;
+        }
+    }
+    return sign | best;
+}
+
+/* OCP E4M3 (e4m3fn) byte nearest to a non-negative value, ties to an even
+ * mantissa, saturating at 448 (the format has no infinity; S.1111.111 is NaN). */
+static uint8_t e4m3_encode(double t) {
+    if (t >= 448.0) return 0x7E;
+    uint8_t best = 0;
+    double bd = t;
+    for (int b = 1; b <= 0x7E; ++b) {
+        double d = fabs(t - or_e4m3_to_double((uint8_t)b));
+        if (d < bd || (d == bd && (b % 2) == 0)) {
+            best = (uint8_t)b;
+            bd = d;
+        }
+    }
+    return best;
+}
+
+uint8_t or_e2m1_encode(double v) { return (uint8_t)e2m1_encode(v); }
+uint8_t or_e4m3_encode(double t) { return e4m3_encode(t); }
+
+/* MXFP4 quantizer for bf16 rows x [rows, k]: per 32 consecutive columns the
+ * E8M0 exponent is floor(log2(amax)) - 2 (so that amax / 2^e lies in [4, 8),
+ * the top binade of E2M1), biased by 127 and clamped to 0..254; an all-zero
+ * block gets 0. Each element is then encoded from x / 2^(e - 127) (exact).
+ * Codes pack as the decoder reads them (low nibble = even column). A
+ * non-finite input is rejected (OR_EINVAL). */
+int or_mxfp4_quantize(const uint16_t* x, uint8_t* packed, uint8_t* scales, int64_t rows, int64_t k) {
+    if (rows < 0 || k < 0 || k % 32 != 0) return OR_EINVAL;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t b = 0; b < k / 32; ++b) {
+            const uint16_t* xb = x + r * k + 32 * b;
+            double amax = 0.0;
+            for (int i = 0; i < 32; ++i) {
+                double v = or_double_from_bf16(xb[i]);
+                if (!isfinite(v)) bad = 1;
+                else if (fabs(v) > amax) amax = fabs(v);
+            }
+            int e = 0;
+            if (amax > 0.0) {
+                int ex;
+                (void)frexp(amax, &ex);         /* amax in [2^(ex-1), 2^ex) */
+                e = (ex - 1) - 2 + 127;
+                if (e < 0) e = 0;
+                if (e > 254) e = 254;
+            }
+            scales[r * (k / 32) + b] = (uint8_t)e;
+            for (int i = 0; i < 32; i += 2) {
+                int lo = e2m1_encode(ldexp(or_double_from_bf16(xb[i]), 127 - e));
+                int hi = e2m1_encode(ldexp(or_double_from_bf16(xb[i + 1]), 127 - e));
+                packed[r * (k / 2) + 16 * b + i / 2] = (uint8_t)(lo | (hi << 4));
+            }
+        }
+    }
+    return bad ? OR_EINVAL : OR_OK;
+}
+
+/* NVFP4 quantizer for bf16 rows x [rows, k] with a given fp32 global scale g
+ * (the per-tensor factor of [SGLang-34222]): per 16 consecutive columns the
+ * block scale is the E4M3 value nearest to fl32(amax / fl32(6 g)), so that the
+ * block's largest element maps to about 6; the element decoded scale is
+ * eff = fl32(e4m3(bs) * g) in the order the dequantisation of that page uses,
+ * and each element is encoded from fl32(x / eff) (eff = 0 gives signed zero
+ * codes). Every fp32 step is an IEEE fp32 operation, so that a GPU taking the
+ * same steps takes the same decisions. Rejects non-finite inputs and g <= 0. */
+int or_nvfp4_quantize(const uint16_t* x, float g, uint8_t* packed, uint8_t* block_scale, int64_t rows,
+                      int64_t k) {
+    if (rows < 0 || k < 0 || k % 16 != 0 || !(g > 0.0f) || !isfinite(g)) return OR_EINVAL;
+    const float d = 6.0f * g;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t b = 0; b < k / 16; ++b) {
+            const uint16_t* xb = x + r * k + 16 * b;
+            float amax = 0.0f;
+            for (int i = 0; i < 16; ++i) {
+                float v = (float)or_double_from_bf16(xb[i]);
+                if (!isfinite(v)) bad = 1;
+                else if (fabsf(v) > amax) amax = fabsf(v);
+            }
+            float t = amax / d;
+            uint8_t bs = e4m3_encode((double)t);
+            block_scale[r * (k / 16) + b] = bs;
+            float eff = (float)or_e4m3_to_double(bs) * g;
+            for (int i = 0; i < 16; i += 2) {
+                int c[2];
+                for (int h = 0; h < 2; ++h) {
+                    float v = (float)or_double_from_bf16(xb[i + h]);
+                    if (eff == 0.0f) c[h] = signbit(v) ? 8 : 0;
+                    else {
+                        float q = v / eff;
+                        c[h] = e2m1_encode((double)q);
+                    }
+                }
+                packed[r * (k / 2) + 8 * b + i / 2] = (uint8_t)(c[0] | (c[1] << 4));
+            }
+        }
+    }
+    return bad ? OR_EINVAL : OR_OK;
+}
+
 /* ----------------------------------------------------------------- MoE --- */
 
 static double silu(double z) { return z / (1.0 + exp(-z)); }
