@@ -7,7 +7,8 @@ Prints ONE JSON line. The default workload is the headline: MXFP4 dequant-GEMV
 at batch 1 on the Llama-8B MLP shapes (W 14336 x 4096 and W 4096 x 14336, one
 launch each per step), bf16 output. Other workloads (for the per-kernel
 roofline tables): mlp_b4, mlp_b16, ternary, ternary_b1 .. ternary_b16
-(small-batch ternary GEMM), ternary_wl, gather, moe, decode, gemv_small.
+(small-batch ternary GEMM), ternary_wl, gather, moe, decode, quantize,
+gemv_small.
 
 Timing: inputs are resident in HBM before the timed region. The launches of
 one step per weight copy are captured into a HIP graph; W warmup steps are
@@ -55,6 +56,8 @@ KERNEL_SOURCES = {
     "ternarygemm": ["ternary_batch.hip", "ternary_int8.hpp"],
     "gather": ["gather.hip"],
     "decode": ["decode.hip"],
+    "mxquant": ["quantize.hip"],
+    "nvquant": ["quantize.hip"],
 }
 COMMON_SOURCES = ["device.hpp", "kernels.hpp", "api.hip"]
 
@@ -399,6 +402,60 @@ class Decode(Workload):
         return self.rows * self.k // 2 + self.rows * self.k // 32 + 2 * self.rows * self.k
 
 
+class Quantize(Workload):
+    """MXFP4 and NVFP4 quantizers on a bf16 matrix of the Llama-8B MLP shape
+    14336 x 4096 (weights N(0, 0.02)): one launch of each per step."""
+
+    def __init__(self, rotate_bytes: float, n: int = 14336, k: int = 4096):
+        import torch
+        import gemm_e2m1_lut_amd as lib
+        self.lib, self.n, self.k = lib, n, k
+        self.name = f"quantize_mxfp4_nvfp4_{n}x{k}"
+        per_copy = 2 * n * k
+        self.copies = max(2, math.ceil(rotate_bytes / per_copy))
+        g = _gen(6161)
+        self.x = [(torch.randn(n, k, generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+                  for _ in range(self.copies)]
+        self.gs = torch.tensor([0.02 * 4 / (6 * 448)], dtype=torch.float32, device="cuda")
+        self.mx = (torch.empty(n, k // 2, dtype=torch.uint8, device="cuda"),
+                   torch.empty(n, k // 32, dtype=torch.uint8, device="cuda"))
+        self.nv = (torch.empty(n, k // 2, dtype=torch.uint8, device="cuda"),
+                   torch.empty(n, k // 16, dtype=torch.uint8, device="cuda"))
+        self.weight_bytes_per_step = float(2 * per_copy)   # bf16 read by each quantizer
+        self.total_bytes_per_step = float(self.alg_bytes("mxquant") + self.alg_bytes("nvquant"))
+        self.config = {"workload": self.name, "in": "bf16", "out": "MXFP4 (E8M0 per 32) and NVFP4 (E4M3 per 16)",
+                       "weight_copies_rotated": self.copies}
+
+    def launches(self):
+        def mx(i):
+            self.lib.mxfp4_quantize(self.x[i % self.copies], out=self.mx)
+
+        def nv(i):
+            self.lib.nvfp4_quantize(self.x[i % self.copies], self.gs, out=self.nv)
+        return [("mxquant", mx), ("nvquant", nv)]
+
+    def alg_bytes(self, label):
+        nk = self.n * self.k
+        return 2 * nk + nk // 2 + (nk // 32 if label == "mxquant" else nk // 16)
+
+    def cpu_baseline(self, budget_s):
+        import oracle
+        import synth
+        rows = 1024
+        x = oracle.bf16_from_f64(synth.rng(6161).standard_normal((rows, self.k)) * 0.02)
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.mxfp4_quantize(x)
+            oracle.nvfp4_quantize(x, 0.02 * 4 / (6 * 448))
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s or reps >= 2000:
+                break
+        return {"value": round(2 * 2 * rows * self.k * reps / el / 1e9, 3), "unit": "GB/s",
+                "cores": oracle.threads(), "kind": "oracle",
+                "sample": f"both quantizers on {rows} of the {self.n} rows, repeated {reps} times, {el:.1f} s"}
+
+
 class GemvSmall(Workload):
     def __init__(self, rotate_bytes: float):
         import torch
@@ -509,6 +566,7 @@ WORKLOADS = {
     "ternary_b16": lambda rb: TernaryBatch(16, rb),
     "gather": Gather,
     "decode": Decode,
+    "quantize": Quantize,
     "gemv_small": GemvSmall,
 }
 

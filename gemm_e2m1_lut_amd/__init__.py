@@ -8,7 +8,7 @@ in the library's kernels.
 
 Operations: dequant_decode, dequant_gemv, ternary_gemv, ternary_gemm,
 ternary_wl_gemv, nvfp4_embedding_gather, mxfp4_moe_gemm (+
-mxfp4_moe_workspace_size).
+mxfp4_moe_workspace_size), and the encoders mxfp4_quantize, nvfp4_quantize.
 """
 from ._binding import (  # noqa: F401
     ABI_VERSION,
@@ -25,7 +25,9 @@ from ._binding import (  # noqa: F401
     load_library,
     mxfp4_moe_gemm,
     mxfp4_moe_workspace_size,
+    mxfp4_quantize,
     nvfp4_embedding_gather,
+    nvfp4_quantize,
     strerror,
     ternary_gemm,
     ternary_gemv,

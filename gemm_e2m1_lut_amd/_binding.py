@@ -53,6 +53,8 @@ def load_library() -> ctypes.CDLL:
         "e2m1_strerror": (ctypes.c_char_p, [ctypes.c_int]),
         "dequant_decode": (ctypes.c_int, [vp, vp, vp, i64, i64, vp]),
         "dequant_gemv": (ctypes.c_int, [vp, vp, vp, vp, i32, i64, i64, i64, vp]),
+        "mxfp4_quantize": (ctypes.c_int, [vp, vp, vp, i64, i64, vp]),
+        "nvfp4_quantize": (ctypes.c_int, [vp, vp, vp, vp, i64, i64, vp]),
         "ternary_gemv": (ctypes.c_int, [vp, vp, vp, vp, i64, i64, vp]),
         "ternary_gemm": (ctypes.c_int, [vp, vp, vp, vp, i64, i64, i64, vp]),
         "ternary_wl_gemv": (ctypes.c_int, [ctypes.POINTER(vp), vp, vp, vp, vp, vp, i64, i64, vp]),
@@ -155,6 +157,47 @@ def dequant_gemv(packed: torch.Tensor, scales: torch.Tensor, x: torch.Tensor,
     _check("dequant_gemv", load_library().dequant_gemv(_ptr(packed), _ptr(scales), _ptr(xb), _ptr(out),
                                                         code, batch, n, k, _stream(stream)))
     return out[0] if squeeze else out
+
+
+# -------------------------------------------------------------- quantize --
+
+def _bf16_rows(x: torch.Tensor, name: str):
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise ValueError(f"{name} must be a [rows, k] tensor")
+    _need(x, name, (torch.bfloat16, torch.int16, torch.uint16))
+    return x.shape
+
+
+def mxfp4_quantize(x: torch.Tensor, out: tuple[torch.Tensor, torch.Tensor] | None = None,
+                   stream=None) -> tuple[torch.Tensor, torch.Tensor]:
+    """bf16 [rows, k] -> (codes uint8 [rows, k/2], E8M0 uint8 [rows, k/32])."""
+    rows, k = _bf16_rows(x, "x")
+    if out is None:
+        out = (torch.empty((rows, k // 2), dtype=torch.uint8, device=x.device),
+               torch.empty((rows, k // 32), dtype=torch.uint8, device=x.device))
+    _need(out[0], "out[0]", _U8, (rows, k // 2))
+    _need(out[1], "out[1]", _U8, (rows, k // 32))
+    _check("mxfp4_quantize", load_library().mxfp4_quantize(_ptr(x), _ptr(out[0]), _ptr(out[1]), rows, k,
+                                                            _stream(stream)))
+    return out
+
+
+def nvfp4_quantize(x: torch.Tensor, global_scale: torch.Tensor,
+                   out: tuple[torch.Tensor, torch.Tensor] | None = None,
+                   stream=None) -> tuple[torch.Tensor, torch.Tensor]:
+    """bf16 [rows, k], fp32 global scale [1] -> (codes uint8 [rows, k/2], E4M3 bytes uint8 [rows, k/16])."""
+    rows, k = _bf16_rows(x, "x")
+    _need(global_scale, "global_scale", (torch.float32,))
+    if global_scale.numel() != 1:
+        raise ValueError("global_scale must hold one value")
+    if out is None:
+        out = (torch.empty((rows, k // 2), dtype=torch.uint8, device=x.device),
+               torch.empty((rows, k // 16), dtype=torch.uint8, device=x.device))
+    _need(out[0], "out[0]", _U8, (rows, k // 2))
+    _need(out[1], "out[1]", _SCALE8, (rows, k // 16))
+    _check("nvfp4_quantize", load_library().nvfp4_quantize(_ptr(x), _ptr(global_scale), _ptr(out[0]),
+                                                            _ptr(out[1]), rows, k, _stream(stream)))
+    return out
 
 
 # ---------------------------------------------------------------- ternary --

@@ -86,6 +86,26 @@ int dequant_gemv(const uint8_t* packed, const uint8_t* scale_e8m0, const uint16_
                                            (int)batch, n, k, as_stream(stream)));
 }
 
+int mxfp4_quantize(const uint16_t* x_bf16, uint8_t* packed, uint8_t* scale_e8m0, int64_t rows,
+                   int64_t k, void* stream) {
+    if (rows < 0 || k < 0 || k % 32 != 0 || !mul_ok(rows, k)) return E2M1_ERR_SHAPE;
+    if (rows == 0 || k == 0) return E2M1_OK;
+    if (!x_bf16 || !packed || !scale_e8m0) return E2M1_ERR_NULL;
+    if (!aligned(x_bf16, 16) || !aligned(packed, 8)) return E2M1_ERR_ALIGN;
+    return launch_status(e2m1::launch_mxfp4_quantize(x_bf16, packed, scale_e8m0, rows * (k / 32),
+                                                     as_stream(stream)));
+}
+
+int nvfp4_quantize(const uint16_t* x_bf16, const float* global_scale, uint8_t* packed,
+                   uint8_t* block_scale_e4m3, int64_t rows, int64_t k, void* stream) {
+    if (rows < 0 || k < 0 || k % 16 != 0 || !mul_ok(rows, k)) return E2M1_ERR_SHAPE;
+    if (rows == 0 || k == 0) return E2M1_OK;
+    if (!x_bf16 || !global_scale || !packed || !block_scale_e4m3) return E2M1_ERR_NULL;
+    if (!aligned(x_bf16, 16) || !aligned(packed, 8) || !aligned(global_scale, 4)) return E2M1_ERR_ALIGN;
+    return launch_status(e2m1::launch_nvfp4_quantize(x_bf16, global_scale, packed, block_scale_e4m3,
+                                                     rows * (k / 16), as_stream(stream)));
+}
+
 int ternary_gemv(const uint32_t* packed, const float* row_scale, const float* x, float* y,
                  int64_t n, int64_t k, void* stream) {
     if (n < 0 || k < 0 || k % 16 != 0 || n > INT_MAX || k / 16 > INT_MAX / 64 || !mul_ok(n, k))

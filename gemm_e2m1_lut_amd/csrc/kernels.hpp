@@ -16,6 +16,12 @@ hipError_t launch_fill_zero_u16(uint16_t* dst, int64_t count, hipStream_t stream
 hipError_t launch_decode(const uint8_t* packed, const uint8_t* scales, uint16_t* out,
                          int64_t nblocks, hipStream_t stream);
 
+hipError_t launch_mxfp4_quantize(const uint16_t* x, uint8_t* packed, uint8_t* scales, int64_t nblocks,
+                                 hipStream_t stream);
+
+hipError_t launch_nvfp4_quantize(const uint16_t* x, const float* global_scale, uint8_t* packed,
+                                 uint8_t* block_scale, int64_t nblocks, hipStream_t stream);
+
 hipError_t launch_gemv(const uint8_t* packed, const uint8_t* scales, const uint16_t* x, void* y,
                        bool out_bf16, int batch, int64_t n, int64_t k, hipStream_t stream);
 

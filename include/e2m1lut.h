@@ -111,6 +111,44 @@ int dequant_gemv(const uint8_t* packed, const uint8_t* scale_e8m0, const uint16_
                  void* y, int y_dtype, int64_t batch, int64_t n, int64_t k, void* stream);
 
 /*
+ * mxfp4_quantize -- bf16 rows to MXFP4 codes and E8M0 block scales (the
+ * encode side of dequant_decode / dequant_gemv / mxfp4_moe_gemm).
+ * Operation: the quantizer the MoE test of [vLLM-51583] "关键源码片段" applies
+ * to bf16 weights; the page prints no rounding rule. Rule taken: per 32
+ * consecutive columns e = clamp(floor(log2(amax)) - 2 + 127, 0, 254) (0 for an
+ * all-zero block); each element becomes the E2M1 code of the value nearest to
+ * x / 2^(e-127), ties to the code whose last bit is 0, magnitudes above 6
+ * saturating to 6, sign bit from x (so a small negative x gives code 8).
+ * Decoding the result returns each element within half an E2M1 step (or 6
+ * units, for the elements above 6 units).
+ *   x_bf16      uint16 [rows, k]   bf16 patterns (16-byte aligned)
+ *   packed      uint8  [rows, k/2] byte j = column 2j (low nibble), 2j+1 (high) (8-byte aligned)
+ *   scale_e8m0  uint8  [rows, k/32]
+ * Requires rows >= 0, k >= 0, k % 32 == 0; x must be finite.
+ */
+int mxfp4_quantize(const uint16_t* x_bf16, uint8_t* packed, uint8_t* scale_e8m0, int64_t rows,
+                   int64_t k, void* stream);
+
+/*
+ * nvfp4_quantize -- bf16 rows to NVFP4 codes and E4M3 block scales for a given
+ * fp32 global scale (the encode side of nvfp4_embedding_gather).
+ * Operation: [SGLang-34222] "关键源码片段" dequantises value = E2M1 code *
+ * fl32(e4m3(block scale) * global); the page prints no encoder. Rule taken:
+ * per 16 consecutive columns the block scale byte is the E4M3 value nearest
+ * to fl32(amax / fl32(6 * global)), ties to an even mantissa, saturating at
+ * 448; eff = fl32(e4m3(bs) * global); each element is the E2M1 code nearest
+ * to fl32(x / eff) with the rounding of mxfp4_quantize (eff == 0 gives
+ * signed zero codes). Every fp32 step is an IEEE fp32 operation.
+ *   x_bf16            uint16 [rows, k]    bf16 patterns (16-byte aligned)
+ *   global_scale      fp32   [1] on the device, > 0
+ *   packed            uint8  [rows, k/2]  as for mxfp4_quantize (8-byte aligned)
+ *   block_scale_e4m3  uint8  [rows, k/16]
+ * Requires rows >= 0, k >= 0, k % 16 == 0; x must be finite.
+ */
+int nvfp4_quantize(const uint16_t* x_bf16, const float* global_scale, uint8_t* packed,
+                   uint8_t* block_scale_e4m3, int64_t rows, int64_t k, void* stream);
+
+/*
  * ternary_gemv -- y[i] = row_scale[i] * sum_k t(i,k) * x[k], t in {-1, 0, +1}.
  * Operation: [FairyFuse] "三元 GEMV 的乘法消除原理": 16 weights per uint32,
  * weight j of word w multiplies x[16w + j]; bit 2j+1 set = +1 (add), bit 2j

@@ -37,7 +37,7 @@ def lib():
 
 def test_header_declares_the_five_operations():
     names = declared_functions()
-    for op in ("dequant_decode", "dequant_gemv", "ternary_gemv", "ternary_gemm", "ternary_wl_gemv", "nvfp4_embedding_gather",
+    for op in ("dequant_decode", "dequant_gemv", "ternary_gemv", "ternary_gemm", "ternary_wl_gemv", "mxfp4_quantize", "nvfp4_quantize", "nvfp4_embedding_gather",
                "mxfp4_moe_gemm", "mxfp4_moe_workspace_size", "e2m1_abi_version", "e2m1_strerror"):
         assert op in names
 
@@ -104,6 +104,22 @@ def test_ternary_validation(lib):
     assert f(A, B, C, NULL, 4, 16, NULL) == E_NULL
     assert f(NULL, B, C, D, 4, 16, NULL) == E_NULL
     assert f(P(0x10002), B, C, D, 4, 16, NULL) == E_ALIGN
+
+
+def test_quantize_validation(lib):
+    f = lib.mxfp4_quantize
+    assert f(A, B, C, 4, 48, NULL) == E_SHAPE          # k % 32
+    assert f(A, B, C, -1, 64, NULL) == E_SHAPE
+    assert f(NULL, NULL, NULL, 0, 64, NULL) == E2M1_OK
+    assert f(A, NULL, C, 4, 64, NULL) == E_NULL
+    assert f(P(0x10008), B, C, 4, 64, NULL) == E_ALIGN   # x needs 16 bytes
+    assert f(A, P(0x20004), C, 4, 64, NULL) == E_ALIGN   # codes need 8 bytes
+    g = lib.nvfp4_quantize
+    assert g(A, D, B, C, 4, 40, NULL) == E_SHAPE       # k % 16
+    assert g(NULL, NULL, NULL, NULL, 3, 0, NULL) == E2M1_OK
+    assert g(A, NULL, B, C, 4, 64, NULL) == E_NULL     # global scale
+    assert g(A, P(0x40002), B, C, 4, 64, NULL) == E_ALIGN
+    assert g(A, D, P(0x20001), C, 4, 64, NULL) == E_ALIGN
 
 
 def test_ternary_gemm_validation(lib):
