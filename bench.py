@@ -8,7 +8,7 @@ at batch 1 on the Llama-8B MLP shapes (W 14336 x 4096 and W 4096 x 14336, one
 launch each per step), bf16 output. Other workloads (for the per-kernel
 roofline tables): mlp_b4, mlp_b16, ternary, ternary_b1 .. ternary_b16
 (small-batch ternary GEMM), ternary_wl, gather, moe, decode, quantize,
-gemv_small.
+prefill (MXFP4 GEMM, 2048 tokens), gemv_small.
 
 Timing: inputs are resident in HBM before the timed region. The launches of
 one step per weight copy are captured into a HIP graph; W warmup steps are
@@ -57,6 +57,7 @@ KERNEL_SOURCES = {
     "gather": ["gather.hip"],
     "decode": ["decode.hip"],
     "mxquant": ["quantize.hip"],
+    "gemm": ["gemm.hip"],
     "nvquant": ["quantize.hip"],
 }
 COMMON_SOURCES = ["device.hpp", "kernels.hpp", "api.hip"]
@@ -456,6 +457,67 @@ class Quantize(Workload):
                 "sample": f"both quantizers on {rows} of the {self.n} rows, repeated {reps} times, {el:.1f} s"}
 
 
+class Prefill(Workload):
+    """MXFP4 weight GEMM for 2048 activation rows (prefill) through the Llama-8B
+    MLP matrices 14336 x 4096 and 4096 x 14336, bf16 out: bound by the matrix
+    cores, so its roofline is bf16 MFMA."""
+    SHAPES = ((14336, 4096), (4096, 14336))
+    bound = "mfma"
+
+    def __init__(self, rotate_bytes: float, m: int = 2048):
+        import torch
+        import gemm_e2m1_lut_amd as lib
+        self.lib, self.m = lib, m
+        self.name = f"llama8b_mlp_mxfp4_gemm_m{m}"
+        g = _gen(7171)
+        # every launch takes longer than the weights take to stream, so rotating copies
+        # past the Infinity Cache changes nothing: two copies keep the launch pattern
+        self.copies = 2
+        self.weights = [[_mxfp4_dev(g, n, k) for n, k in self.SHAPES] for _ in range(self.copies)]
+        self.x = [torch.randn((m, k), generator=g, device="cuda").to(torch.bfloat16) for _, k in self.SHAPES]
+        self.y = [torch.empty((m, n), dtype=torch.bfloat16, device="cuda") for n, _ in self.SHAPES]
+        per_copy = sum(n * k // 2 + n * k // 32 for n, k in self.SHAPES)
+        self.weight_bytes_per_step = float(per_copy)
+        self.total_bytes_per_step = float(sum(self.alg_bytes(l) for l, _ in self.launches()))
+        self.config = {"workload": self.name, "shapes_NxK": [list(s) for s in self.SHAPES], "tokens": m,
+                       "weights": "MXFP4 (E2M1 codes + E8M0 per 32)", "activations": "bf16", "out": "bf16",
+                       "accumulate": "fp32"}
+
+    def launches(self):
+        out = []
+        for j, (n, k) in enumerate(self.SHAPES):
+            def fn(i, j=j):
+                p, s = self.weights[i % self.copies][j]
+                self.lib.dequant_gemm(p, s, self.x[j], out=self.y[j])
+            out.append((f"gemm_m{self.m}_{n}x{k}", fn))
+        return out
+
+    def alg_bytes(self, label):
+        n, k = (int(v) for v in label.split("_")[2].split("x"))
+        return n * k // 2 + n * k // 32 + self.m * k * 2 + self.m * n * 2
+
+    def alg_flops(self, label):
+        n, k = (int(v) for v in label.split("_")[2].split("x"))
+        return 2.0 * self.m * n * k
+
+    def cpu_baseline(self, budget_s):
+        import oracle
+        n, k = self.SHAPES[0]
+        p, sc = (t.cpu().numpy() for t in self.weights[0][0])
+        xs = self.x[0][:4].view(__import__("torch").int16).cpu().numpy().view(np.uint16)
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.mxfp4_gemv(p, sc, xs, "bf16")
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s or reps >= 200:
+                break
+        tflops = 2.0 * 4 * n * k * reps / el / 1e12
+        return {"value": round(tflops, 6), "unit": "TFLOP/s", "cores": oracle.threads(), "kind": "oracle",
+                "sample": f"4 of the {self.m} activation rows through the {n} x {k} matrix, repeated {reps} "
+                          f"times, {el:.1f} s, fp64 scalar C"}
+
+
 class GemvSmall(Workload):
     def __init__(self, rotate_bytes: float):
         import torch
@@ -567,6 +629,7 @@ WORKLOADS = {
     "gather": Gather,
     "decode": Decode,
     "quantize": Quantize,
+    "prefill": Prefill,
     "gemv_small": GemvSmall,
 }
 
@@ -710,6 +773,10 @@ def main() -> int:
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic["bytes_per_launch"] if traffic else None,
                 "kernel": dom["label"]}
+    if getattr(wl, "bound", "hbm") == "mfma":
+        tflops = wl.alg_flops(dom["label"]) / (dom["avg_us"] * 1e-6) / 1e12
+        roofline.update({"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4)})
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -6,7 +6,7 @@ the HIP sources in csrc/ by build.py. This package is its thin Python binding:
 torch supplies device memory and streams; every step of every operation runs
 in the library's kernels.
 
-Operations: dequant_decode, dequant_gemv, ternary_gemv, ternary_gemm,
+Operations: dequant_decode, dequant_gemv, dequant_gemm, ternary_gemv, ternary_gemm,
 ternary_wl_gemv, nvfp4_embedding_gather, mxfp4_moe_gemm (+
 mxfp4_moe_workspace_size), and the encoders mxfp4_quantize, nvfp4_quantize.
 """
@@ -20,6 +20,7 @@ from ._binding import (  # noqa: F401
     E2M1Error,
     abi_version,
     dequant_decode,
+    dequant_gemm,
     dequant_gemv,
     library_path,
     load_library,

@@ -53,6 +53,7 @@ def load_library() -> ctypes.CDLL:
         "e2m1_strerror": (ctypes.c_char_p, [ctypes.c_int]),
         "dequant_decode": (ctypes.c_int, [vp, vp, vp, i64, i64, vp]),
         "dequant_gemv": (ctypes.c_int, [vp, vp, vp, vp, i32, i64, i64, i64, vp]),
+        "dequant_gemm": (ctypes.c_int, [vp, vp, vp, vp, i32, i64, i64, i64, vp]),
         "mxfp4_quantize": (ctypes.c_int, [vp, vp, vp, i64, i64, vp]),
         "nvfp4_quantize": (ctypes.c_int, [vp, vp, vp, vp, i64, i64, vp]),
         "ternary_gemv": (ctypes.c_int, [vp, vp, vp, vp, i64, i64, vp]),
@@ -157,6 +158,26 @@ def dequant_gemv(packed: torch.Tensor, scales: torch.Tensor, x: torch.Tensor,
     _check("dequant_gemv", load_library().dequant_gemv(_ptr(packed), _ptr(scales), _ptr(xb), _ptr(out),
                                                         code, batch, n, k, _stream(stream)))
     return out[0] if squeeze else out
+
+
+def dequant_gemm(packed: torch.Tensor, scales: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None,
+                 out_dtype: torch.dtype = torch.bfloat16, stream=None) -> torch.Tensor:
+    """MXFP4 W [n, k/2] + E8M0 [n, k/32], bf16 x [m, k] -> y [m, n] (fp32 accumulate), any m."""
+    _need(packed, "packed", _U8)
+    n, half = packed.shape
+    k = 2 * half
+    _need(scales, "scales", _U8, (n, k // 32))
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise ValueError("x must be a [m, k] tensor")
+    m = x.shape[0]
+    _need(x, "x", (torch.bfloat16, torch.int16), (m, k))
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=packed.device)
+    _need(out, "out", (torch.float32, torch.bfloat16), (m, n))
+    code = DTYPE_F32 if out.dtype == torch.float32 else DTYPE_BF16
+    _check("dequant_gemm", load_library().dequant_gemm(_ptr(packed), _ptr(scales), _ptr(x), _ptr(out), code,
+                                                        m, n, k, _stream(stream)))
+    return out
 
 
 # -------------------------------------------------------------- quantize --

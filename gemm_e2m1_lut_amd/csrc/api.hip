@@ -86,6 +86,23 @@ int dequant_gemv(const uint8_t* packed, const uint8_t* scale_e8m0, const uint16_
                                            (int)batch, n, k, as_stream(stream)));
 }
 
+int dequant_gemm(const uint8_t* packed, const uint8_t* scale_e8m0, const uint16_t* x_bf16, void* y,
+                 int y_dtype, int64_t m, int64_t n, int64_t k, void* stream) {
+    if (y_dtype != E2M1_DTYPE_F32 && y_dtype != E2M1_DTYPE_BF16) return E2M1_ERR_DTYPE;
+    if (m < 0 || n < 0 || k < 0 || k % 32 != 0 || m > INT_MAX || n > INT_MAX || k / 32 > INT_MAX ||
+        !mul_ok(m, k) || !mul_ok(n, k) || !mul_ok(m, n) || ((n + 127) / 128) * ((m + 127) / 128) > INT_MAX)
+        return E2M1_ERR_SHAPE;
+    if (m == 0 || n == 0) return E2M1_OK;
+    const int64_t esize = y_dtype == E2M1_DTYPE_F32 ? 4 : 2;
+    if (!y) return E2M1_ERR_NULL;
+    if (!aligned(y, (uintptr_t)esize)) return E2M1_ERR_ALIGN;
+    if (k == 0) return launch_status(fill_zero_bytes(y, m * n * esize, as_stream(stream)));
+    if (!packed || !scale_e8m0 || !x_bf16) return E2M1_ERR_NULL;
+    if (!aligned(packed, 16) || !aligned(x_bf16, 16)) return E2M1_ERR_ALIGN;
+    return launch_status(e2m1::launch_gemm(packed, scale_e8m0, x_bf16, y, y_dtype == E2M1_DTYPE_BF16, m, n, k,
+                                           as_stream(stream)));
+}
+
 int mxfp4_quantize(const uint16_t* x_bf16, uint8_t* packed, uint8_t* scale_e8m0, int64_t rows,
                    int64_t k, void* stream) {
     if (rows < 0 || k < 0 || k % 32 != 0 || !mul_ok(rows, k)) return E2M1_ERR_SHAPE;

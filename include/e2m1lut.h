@@ -111,6 +111,24 @@ int dequant_gemv(const uint8_t* packed, const uint8_t* scale_e8m0, const uint16_
                  void* y, int y_dtype, int64_t batch, int64_t n, int64_t k, void* stream);
 
 /*
+ * dequant_gemm -- y = x . W^T for many activation rows (prefill): the MXFP4
+ * weight matrix decoded on the way into bf16 matrix-core tiles.
+ * Operation: as dequant_gemv ([vLLM-51583] "功能与动机": E2M1 table lookup and
+ * E8M0 scale), for any number of rows of x; the page's comment section
+ * describes the CPU GEMM decoding weight blocks into bf16 tiles. Accumulation
+ * is fp32.
+ *   packed      uint8  [n, k/2]   (16-byte aligned)
+ *   scale_e8m0  uint8  [n, k/32]
+ *   x_bf16      uint16 [m, k]     bf16 patterns (16-byte aligned)
+ *   y           [m, n], E2M1_DTYPE_F32 (fp32) or E2M1_DTYPE_BF16 (bf16 RNE), overwritten
+ * Requires m, n >= 0, k >= 0, k % 32 == 0, m, n and k / 32 at most
+ * 2^31 - 1 and fewer than 2^31 tiles of 128 x 128 outputs. k == 0 writes
+ * zeros. Rows of W or x past n or m are never read.
+ */
+int dequant_gemm(const uint8_t* packed, const uint8_t* scale_e8m0, const uint16_t* x_bf16, void* y,
+                 int y_dtype, int64_t m, int64_t n, int64_t k, void* stream);
+
+/*
  * mxfp4_quantize -- bf16 rows to MXFP4 codes and E8M0 block scales (the
  * encode side of dequant_decode / dequant_gemv / mxfp4_moe_gemm).
  * Operation: the quantizer the MoE test of [vLLM-51583] "关键源码片段" applies
