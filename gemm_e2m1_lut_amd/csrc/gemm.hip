@@ -96,34 +96,6 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint8_t* __restric
     const uint8_t* wsrc = packed + (size_t)min(n0 + (t >> 1), n - 1) * (K / 2);
     const uint8_t* ssrc = scales + (size_t)min(n0 + (t & 127), n - 1) * kc;
 
-    auto issue = [&](uint4 (&xr)[4], uint4& wr, uint32_t& sr, int step) {
-        const int c0 = step * kStepK;
-        // columns past K (the second half of a last half step) read the row's last 8 columns:
-        // finite values that meet zero weights
-#pragma unroll
-        for (int i = 0; i < 4; ++i) xr[i] = *reinterpret_cast<const uint4*>(xsrc[i] + min(c0 + xcol, K - 8));
-        const int blk = min(2 * step + (t & 1), kc - 1);
-        wr = *reinterpret_cast<const uint4*>(wsrc + (size_t)blk * 16);
-        const int b0 = min(2 * step, kc - 1), b1 = min(2 * step + 1, kc - 1);
-        sr = (uint32_t)ssrc[b0] | ((uint32_t)ssrc[b1] << 8);
-    };
-    auto stage = [&](GemmBuf& b, const uint4 (&xr)[4], const uint4& wr, uint32_t sr, int step) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int id = t + kThreads * i;
-            *reinterpret_cast<uint4*>(b.x + (id >> 3) * kXPitch + 8 * (id & 7)) = xr[i];
-        }
-        // a block past K (the second half of a last half step) is staged as zero codes
-        const bool wvalid = 2 * step + (t & 1) < kc;
-        const uint4 wz = wvalid ? wr : make_uint4(0u, 0u, 0u, 0u);
-        uint32_t* wd = reinterpret_cast<uint32_t*>(b.w + (t >> 1) * kWPitch + 16 * (t & 1));
-        wd[0] = wz.x;
-        wd[1] = wz.y;
-        wd[2] = wz.z;
-        wd[3] = wz.w;
-        if (t < kTileN) *reinterpret_cast<uint16_t*>(b.s + 2 * t) = (uint16_t)sr;
-    };
-
     f32x4 acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -132,13 +104,40 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint8_t* __restric
 
     uint4 xr[4], wr;
     uint32_t sr;
-    issue(xr, wr, sr, 0);
-    stage(buf[0], xr, wr, sr, 0);
+// Step `st`'s copies into registers. Columns past K (the second half of a last
+// half step) read the row's last 8 columns: finite values that meet zero weights.
+#define E2M1_GEMM_ISSUE(st)                                                                             \
+    {                                                                                                   \
+        const int c0 = (st) * kStepK;                                                                   \
+        _Pragma("unroll") for (int i = 0; i < 4; ++i) xr[i] =                                          \
+            *reinterpret_cast<const uint4*>(xsrc[i] + min(c0 + xcol, K - 8));                          \
+        wr = *reinterpret_cast<const uint4*>(wsrc + (size_t)min(2 * (st) + (t & 1), kc - 1) * 16);      \
+        sr = (uint32_t)ssrc[min(2 * (st), kc - 1)] | ((uint32_t)ssrc[min(2 * (st) + 1, kc - 1)] << 8);  \
+    }
+// The registers of step `st` into buffer `bb`; a block past K is staged as zero codes.
+#define E2M1_GEMM_STAGE(bb, st)                                                                          \
+    {                                                                                                   \
+        _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                                 \
+            const int id = t + kThreads * i;                                                            \
+            *reinterpret_cast<uint4*>((bb).x + (id >> 3) * kXPitch + 8 * (id & 7)) = xr[i];             \
+        }                                                                                               \
+        const uint32_t keep = 2 * (st) + (t & 1) < kc ? 0xFFFFFFFFu : 0u;                               \
+        uint32_t* wd = reinterpret_cast<uint32_t*>((bb).w + (t >> 1) * kWPitch + 16 * (t & 1));          \
+        wd[0] = wr.x & keep;                                                                            \
+        wd[1] = wr.y & keep;                                                                            \
+        wd[2] = wr.z & keep;                                                                            \
+        wd[3] = wr.w & keep;                                                                            \
+        if (t < kTileN) *reinterpret_cast<uint16_t*>((bb).s + 2 * t) = (uint16_t)sr;                    \
+    }
+
+    E2M1_GEMM_ISSUE(0)
+    E2M1_GEMM_STAGE(buf[0], 0)
     __syncthreads();
     for (int step = 0; step < nsteps; ++step) {
         const GemmBuf& b = buf[step & 1];
-        const bool more = step + 1 < nsteps;   // workgroup-uniform
-        if (more) issue(xr, wr, sr, step + 1);
+        // the next step's copies (the last step repeats its own: staged into the idle buffer, never read)
+        const int nxt = min(step + 1, nsteps - 1);
+        E2M1_GEMM_ISSUE(nxt)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {   // 32-column half steps
             bf16x8 a[4];
@@ -158,9 +157,11 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint8_t* __restric
                 for (int i = 0; i < 4; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bx, acc[i][j], 0, 0, 0);
             }
         }
-        if (more) stage(buf[(step + 1) & 1], xr, wr, sr, step + 1);
+        E2M1_GEMM_STAGE(buf[(step + 1) & 1], nxt)
         __syncthreads();
     }
+#undef E2M1_GEMM_ISSUE
+#undef E2M1_GEMM_STAGE
 
     // lane (g, c) holds rows n0 + wn + 16 i + 4 g .. + 3 of activation row m0 + wm + 16 j + c
 #pragma unroll
