@@ -138,6 +138,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint8_t* __restric
         // the next step's copies (the last step repeats its own: staged into the idle buffer, never read)
         const int nxt = min(step + 1, nsteps - 1);
         E2M1_GEMM_ISSUE(nxt)
+        asm volatile("" ::: "memory");        // the loads stay here, ahead of the step's MFMAs
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {   // 32-column half steps
             bf16x8 a[4];
