@@ -16,6 +16,9 @@ function):
     forced to +0.0.
   * SGLang pull request 34222 digest (prhub.com.cn): NVFP4 embedding,
     dequantised at gather time.
+  * sglang-jax wiki page on the N:M structured sparse matmul: the Sparsifier's
+    encode (top-N of a mask per group of M, positions bit-packed) and decode,
+    and the sparse product.
   * FairyFuse blog post (blog.hotdry.top): 2-bit ternary GEMV with a per-row
     scale, and the widely-linear complex layer y = U x + W conj(x) over four
     such matrices.
@@ -89,6 +92,11 @@ def load():
         "or_e4m3_encode": (u8, [f64]),
         "or_mxfp4_quantize": (ctypes.c_int, [_p(u16), _p(u8), _p(u8), i64, i64]),
         "or_nvfp4_quantize": (ctypes.c_int, [_p(u16), f32, _p(u8), _p(u8), i64, i64]),
+        "or_nm_bits": (ctypes.c_int, [ctypes.c_int]),
+        "or_nm_encode": (ctypes.c_int, [_p(u16), _p(u8), _p(u16), _p(u32), i64, i64, ctypes.c_int, ctypes.c_int]),
+        "or_nm_decode": (ctypes.c_int, [_p(u16), _p(u32), _p(u16), _p(u8), i64, i64, ctypes.c_int, ctypes.c_int]),
+        "or_nm_spmm": (ctypes.c_int, [_p(u16), _p(u32), _p(u16), _p(f64), i64, i64, i64, ctypes.c_int,
+                                      ctypes.c_int]),
         "or_mxfp4_moe": (ctypes.c_int, [_p(u16), _p(u8), _p(u8), _p(u8), _p(u8), _p(ctypes.c_int32),
                                         _p(f32), _p(f64), i64, i64, i64, i64, i64]),
     }
@@ -286,6 +294,53 @@ def nvfp4_quantize(x_bf16_bits, global_scale: float):
                                     _ptr(packed, ctypes.c_uint8), _ptr(bs, ctypes.c_uint8), rows, k),
            "nvfp4_quantize")
     return packed, bs
+
+
+def nm_layout(k: int, n: int, m: int):
+    """(index bits, indices per word, kept values per row, words per row) of N:M sparsity."""
+    bits = max(1, int(load().or_nm_bits(int(m))))
+    packing = 32 // bits
+    per_row = (k // m) * n
+    return bits, packing, per_row, -(-per_row // packing)
+
+
+def nm_encode(dense_bits, mask, n: int, m: int):
+    """bf16 patterns [rows, k] + 0/1 mask -> (values bf16 [rows, (k/m) n], indices uint32 [rows, words])."""
+    d = _arr(dense_bits, np.uint16)
+    mk = _arr(mask, np.uint8)
+    rows, k = d.shape
+    _, _, per_row, words = nm_layout(k, n, m)
+    vals = np.empty((rows, per_row), dtype=np.uint16)
+    meta = np.empty((rows, words), dtype=np.uint32)
+    _check(load().or_nm_encode(_ptr(d, ctypes.c_uint16), _ptr(mk, ctypes.c_uint8), _ptr(vals, ctypes.c_uint16),
+                               _ptr(meta, ctypes.c_uint32), rows, k, n, m), "nm_encode")
+    return vals, meta
+
+
+def nm_decode(values, meta, k: int, n: int, m: int):
+    """-> (dense bf16 patterns [rows, k], mask uint8 [rows, k])."""
+    v = _arr(values, np.uint16)
+    md = _arr(meta, np.uint32)
+    rows = v.shape[0]
+    dense = np.empty((rows, k), dtype=np.uint16)
+    mask = np.empty((rows, k), dtype=np.uint8)
+    _check(load().or_nm_decode(_ptr(v, ctypes.c_uint16), _ptr(md, ctypes.c_uint32), _ptr(dense, ctypes.c_uint16),
+                               _ptr(mask, ctypes.c_uint8), rows, k, n, m), "nm_decode")
+    return dense, mask
+
+
+def nm_spmm(values, meta, x_bits, k: int, n: int, m: int) -> np.ndarray:
+    """y [batch, rows] in fp64 = sparse W [rows, k] times bf16 x [batch, k]."""
+    v = _arr(values, np.uint16)
+    md = _arr(meta, np.uint32)
+    x = _arr(x_bits, np.uint16)
+    if x.ndim == 1:
+        x = x[None, :]
+    rows, batch = v.shape[0], x.shape[0]
+    y = np.empty((batch, rows), dtype=np.float64)
+    _check(load().or_nm_spmm(_ptr(v, ctypes.c_uint16), _ptr(md, ctypes.c_uint32), _ptr(x, ctypes.c_uint16),
+                             _ptr(y, ctypes.c_double), batch, rows, k, n, m), "nm_spmm")
+    return y
 
 
 def nvfp4_gather(table, block_scale, global_scale, ids):

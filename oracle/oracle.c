@@ -18,6 +18,9 @@
  *                   token embedding, dequantised at gather time). Sections
  *                   "实现拆解" and "关键源码片段" (modelopt_quant.py excerpt and
  *                   the test's element-loop reference).
+ *   [NM-wiki]       sglang-jax wiki page on the gap "N:M structured sparse
+ *                   matmul" (tpu-inference's Sparsifier and sparse matmul).
+ *                   Sections "N:M 稀疏原理", "3.1 Sparsifier" and "3.2".
  *   [FairyFuse]     blog.hotdry.top post on FairyFuse (fused ternary kernels,
  *                   multiplication-free CPU inference). Sections
  *                   "三元 GEMV 的乘法消除原理" (ternary GEMV without multiplies),
@@ -477,6 +480,122 @@ int or_nvfp4_quantize(const uint16_t* x, float g, uint8_t* packed, uint8_t* bloc
                 }
                 packed[r * (k / 2) + 8 * b + i / 2] = (uint8_t)(c[0] | (c[1] << 4));
             }
+        }
+    }
+    return bad ? OR_EINVAL : OR_OK;
+}
+
+/* ------------------------------------------------------ N:M structured --- */
+
+/* N:M structured sparsity of [NM-wiki] (sglang-jax wiki page on the N:M
+ * structured sparse matmul gap), sections "N:M 稀疏原理" and "3.1 Sparsifier":
+ * in every group of M consecutive columns of a row, N values are kept. The
+ * encoder takes, per group, the N positions with the largest mask values
+ * (ties to the lower position; with a 0/1 mask holding N ones these are its
+ * ones, in increasing order), gathers the values there, and packs the
+ * in-group positions with next_log2(M) bits each, 32 / bits per 32-bit word,
+ * position i of the sequence at bit (i mod packing) * bits of word
+ * i / packing. The page's listing is abridged (several arrays are undefined)
+ * and does not fix the array layout; the reading taken is one row after the
+ * other: values [rows, (k/M) N] (bf16 here), positions in the same order,
+ * packed per row into ceil((k/M) N / packing) words. */
+int or_nm_bits(int m) {
+    int b = 0;
+    while ((1 << b) < m) ++b;
+    return b;
+}
+
+int or_nm_encode(const uint16_t* dense, const uint8_t* mask, uint16_t* values, uint32_t* meta, int64_t rows,
+                 int64_t k, int nn, int mm) {
+    if (rows < 0 || k < 0 || mm < 1 || mm > 16 || nn < 1 || nn > mm || k % mm != 0) return OR_EINVAL;
+    const int bits = or_nm_bits(mm) > 0 ? or_nm_bits(mm) : 1;
+    const int packing = 32 / bits;
+    const int64_t per_row = (k / mm) * nn;
+    const int64_t words = (per_row + packing - 1) / packing;
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t w = 0; w < words; ++w) meta[r * words + w] = 0u;
+        for (int64_t g = 0; g < k / mm; ++g) {
+            const uint8_t* mg = mask + r * k + g * mm;
+            int taken[16] = {0};
+            int sel[16];
+            for (int j = 0; j < nn; ++j) {   /* top-N of the mask, ties to the lower position */
+                int best = -1;
+                for (int i = 0; i < mm; ++i)
+                    if (!taken[i] && (best < 0 || mg[i] > mg[best])) best = i;
+                taken[best] = 1;
+                sel[j] = best;
+            }
+            for (int a = 0; a < nn; ++a)     /* positions in increasing order */
+                for (int b = a + 1; b < nn; ++b)
+                    if (sel[b] < sel[a]) {
+                        int tmp = sel[a];
+                        sel[a] = sel[b];
+                        sel[b] = tmp;
+                    }
+            for (int j = 0; j < nn; ++j) {
+                const int64_t e = g * nn + j;
+                values[r * per_row + e] = dense[r * k + g * mm + sel[j]];
+                meta[r * words + e / packing] |= (uint32_t)sel[j] << ((e % packing) * bits);
+            }
+        }
+    }
+    return OR_OK;
+}
+
+/* Decode: scatter the values back to their columns of a zero matrix (bf16
+ * patterns) and set the mask; a position repeated within a group is rejected. */
+int or_nm_decode(const uint16_t* values, const uint32_t* meta, uint16_t* dense, uint8_t* mask, int64_t rows,
+                 int64_t k, int nn, int mm) {
+    if (rows < 0 || k < 0 || mm < 1 || mm > 16 || nn < 1 || nn > mm || k % mm != 0) return OR_EINVAL;
+    const int bits = or_nm_bits(mm) > 0 ? or_nm_bits(mm) : 1;
+    const int packing = 32 / bits;
+    const int64_t per_row = (k / mm) * nn;
+    const int64_t words = (per_row + packing - 1) / packing;
+    int bad = 0;
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t c = 0; c < k; ++c) {
+            dense[r * k + c] = 0;
+            mask[r * k + c] = 0;
+        }
+        for (int64_t e = 0; e < per_row; ++e) {
+            const uint32_t pos = (meta[r * words + e / packing] >> ((e % packing) * bits)) & ((1u << bits) - 1u);
+            const int64_t col = (e / nn) * mm + pos;
+            if ((int)pos >= mm || mask[r * k + col]) bad = 1;
+            else {
+                dense[r * k + col] = values[r * per_row + e];
+                mask[r * k + col] = 1;
+            }
+        }
+    }
+    return bad ? OR_EINVAL : OR_OK;
+}
+
+/* Sparse matmul of the same page ("3.2", decompress then a dense product):
+ * y[b][r] = sum over the row's kept entries of value * x[b][column], fp64
+ * sums of the bf16 values times bf16 x, rounded once to fp32. */
+int or_nm_spmm(const uint16_t* values, const uint32_t* meta, const uint16_t* x, double* y64, int64_t batch,
+               int64_t rows, int64_t k, int nn, int mm) {
+    if (batch < 0 || rows < 0 || k < 0 || mm < 1 || mm > 16 || nn < 1 || nn > mm || k % mm != 0)
+        return OR_EINVAL;
+    const int bits = or_nm_bits(mm) > 0 ? or_nm_bits(mm) : 1;
+    const int packing = 32 / bits;
+    const int64_t per_row = (k / mm) * nn;
+    const int64_t words = (per_row + packing - 1) / packing;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t b = 0; b < batch; ++b) {
+            double acc = 0.0;
+            for (int64_t e = 0; e < per_row; ++e) {
+                const uint32_t pos = (meta[r * words + e / packing] >> ((e % packing) * bits)) & ((1u << bits) - 1u);
+                if ((int)pos >= mm) {
+                    bad = 1;
+                    continue;
+                }
+                const int64_t col = (e / nn) * mm + pos;
+                acc += or_double_from_bf16(values[r * per_row + e]) * or_double_from_bf16(x[b * k + col]);
+            }
+            y64[b * rows + r] = acc;
         }
     }
     return bad ? OR_EINVAL : OR_OK;

@@ -15,6 +15,9 @@ Workload shapes (value distributions as stated for each):
     1/3; per-row fp32 scale U[0.01, 0.1]; x fp32 N(0,1).
   * Small-batch ternary GEMM: the ternary GEMV matrix with x fp32
     [batch, k] ~N(0,1), batch 1..16 (4 and 8 measured).
+  * N:M structured-sparse weights (2:4 and 4:8 measured): bf16 values
+    N(0, 0.02) with exactly N kept at uniformly random positions per group of
+    M columns, x bf16 N(0, 1).
   * Widely-linear complex ternary layer, four such 4096 x 4096 matrices
     (U_re, U_im, W_re, W_im), four per-row scales U[0.01, 0.1], x_re and x_im
     fp32 N(0,1).
@@ -40,9 +43,11 @@ def rng(seed: int) -> np.random.Generator:
 
 # ------------------------------------------------------------- primitives --
 
-def bf16_normal(r: np.random.Generator, shape) -> np.ndarray:
-    """bf16 bit patterns (uint16) of fp32 N(0,1) draws, via torch's RNE cast."""
+def bf16_normal(r: np.random.Generator, shape, std: float = 1.0) -> np.ndarray:
+    """bf16 bit patterns (uint16) of fp32 N(0, std^2) draws, via torch's RNE cast."""
     f = r.standard_normal(size=shape, dtype=np.float32)
+    if std != 1.0:
+        f = f * np.float32(std)
     return torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
 
 
@@ -133,6 +138,20 @@ def ternary_case(seed: int = SEED_BASE + 1, n: int = 4096, k: int = 4096):
     scale = r.uniform(0.01, 0.1, size=n).astype(np.float32)
     x = f32_normal(r, (k,))
     return {"packed": packed, "row_scale": scale, "x": x}
+
+
+def nm_case(seed: int = SEED_BASE + 7, n_keep: int = 2, m: int = 4, rows: int = 4096, k: int = 4096,
+            batch: int = 1):
+    """N:M sparse weights: bf16 N(0, 0.02) values, a 0/1 mask with exactly n_keep
+    ones at uniformly random positions in every group of m columns, x bf16 [batch, k]."""
+    r = rng(seed)
+    dense = bf16_normal(r, (rows, k), 0.02)
+    keys = r.random((rows, k // m, m))
+    order = np.argsort(keys, axis=2)
+    mask = np.zeros((rows, k // m, m), dtype=np.uint8)
+    np.put_along_axis(mask, order[:, :, :n_keep], 1, axis=2)
+    x = bf16_normal(r, (batch, k))
+    return {"dense": dense, "mask": mask.reshape(rows, k), "x": x, "n": n_keep, "m": m}
 
 
 def ternary_batch_case(seed: int = SEED_BASE + 6, batch: int = 4, n: int = 4096, k: int = 4096):
