@@ -59,6 +59,7 @@ KERNEL_SOURCES = {
     "mxquant": ["quantize.hip"],
     "gemm": ["gemm.hip"],
     "nvquant": ["quantize.hip"],
+    "nm": ["nm_sparse.hip"],
 }
 COMMON_SOURCES = ["device.hpp", "kernels.hpp", "api.hip"]
 
@@ -518,6 +519,86 @@ class Prefill(Workload):
                           f"times, {el:.1f} s, fp64 scalar C"}
 
 
+class NmSparse(Workload):
+    """N:M structured-sparse bf16 weights (kept values + packed in-group
+    positions) times one activation row through the Llama-8B MLP matrices
+    14336 x 4096 and 4096 x 14336, bf16 out."""
+    SHAPES = ((14336, 4096), (4096, 14336))
+
+    def __init__(self, n_keep: int, m: int, rotate_bytes: float, batch: int = 1):
+        import torch
+        import gemm_e2m1_lut_amd as lib
+        self.lib, self.nn, self.mm, self.batch = lib, n_keep, m, batch
+        self.name = f"llama8b_mlp_{n_keep}of{m}_sparse_bf16_b{batch}"
+        self.bits = 1 if m <= 2 else (m - 1).bit_length()
+        g = _gen(8181 + 16 * n_keep + m)
+        per_copy = sum(self._wbytes(n, k) for n, k in self.SHAPES)
+        self.copies = max(2, math.ceil(rotate_bytes / per_copy))
+        self.weights = []
+        for _ in range(self.copies):
+            ws = []
+            for n, k in self.SHAPES:
+                per_row, words = self._layout(k)
+                vals = (torch.randn((n, per_row), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+                # positions uniform over the group (M is a power of two here, so every field is valid)
+                meta = torch.randint(-2**31, 2**31 - 1, (n, words), dtype=torch.int32, device="cuda", generator=g)
+                ws.append((vals, meta))
+            self.weights.append(ws)
+        self.x = [torch.randn((batch, k), generator=g, device="cuda").to(torch.bfloat16) for _, k in self.SHAPES]
+        self.y = [torch.empty((batch, n), dtype=torch.bfloat16, device="cuda") for n, _ in self.SHAPES]
+        self.weight_bytes_per_step = float(per_copy)
+        self.total_bytes_per_step = float(sum(self.alg_bytes(l) for l, _ in self.launches()))
+        self.config = {"workload": self.name, "shapes_NxK": [list(s) for s in self.SHAPES], "batch": batch,
+                       "weights": f"{n_keep}:{m} sparse, bf16 kept values + {self.bits}-bit positions in uint32",
+                       "activations": "bf16", "out": "bf16", "accumulate": "fp32",
+                       "weight_copies_rotated": self.copies}
+
+    def _layout(self, k):
+        per_row = (k // self.mm) * self.nn
+        packing = 32 // self.bits
+        return per_row, -(-per_row // packing)
+
+    def _wbytes(self, n, k):
+        per_row, words = self._layout(k)
+        return n * (2 * per_row + 4 * words)
+
+    def launches(self):
+        out = []
+        for j, (n, k) in enumerate(self.SHAPES):
+            def fn(i, j=j):
+                v, m = self.weights[i % self.copies][j]
+                self.lib.nm_spmm(v, m, self.x[j], self.nn, self.mm, out=self.y[j])
+            out.append((f"nm_{self.nn}of{self.mm}_{n}x{k}", fn))
+        return out
+
+    def alg_bytes(self, label):
+        n, k = (int(v) for v in label.split("_")[2].split("x"))
+        return self._wbytes(n, k) + self.batch * k * 2 + self.batch * n * 2
+
+    def alg_flops(self, label):
+        n, k = (int(v) for v in label.split("_")[2].split("x"))
+        return 2.0 * self.batch * n * self._layout(k)[0]
+
+    def cpu_baseline(self, budget_s):
+        import oracle
+        import torch
+        host = [(v.view(torch.int16).cpu().numpy().view(np.uint16), m.cpu().numpy().view(np.uint32))
+                for v, m in self.weights[0]]
+        xs = [x.view(torch.int16).cpu().numpy().view(np.uint16) for x in self.x]
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            for (v, m), x, (_, k) in zip(host, xs, self.SHAPES):
+                oracle.nm_spmm(v, m, x, k, self.nn, self.mm)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s or reps >= 200:
+                break
+        return {"value": round(self.weight_bytes_per_step * reps / el / 1e9, 3), "unit": "GB/s",
+                "cores": oracle.threads(), "kind": "oracle",
+                "sample": f"the full step (both MLP shapes, batch {self.batch}) repeated {reps} times, "
+                          f"{el:.1f} s, fp64 scalar C with OpenMP over rows"}
+
+
 class GemvSmall(Workload):
     def __init__(self, rotate_bytes: float):
         import torch
@@ -630,6 +711,8 @@ WORKLOADS = {
     "decode": Decode,
     "quantize": Quantize,
     "prefill": Prefill,
+    "nm_2of4": lambda rb: NmSparse(2, 4, rb),
+    "nm_4of8": lambda rb: NmSparse(4, 8, rb),
     "gemv_small": GemvSmall,
 }
 

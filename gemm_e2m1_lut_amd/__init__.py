@@ -8,7 +8,8 @@ in the library's kernels.
 
 Operations: dequant_decode, dequant_gemv, dequant_gemm, ternary_gemv, ternary_gemm,
 ternary_wl_gemv, nvfp4_embedding_gather, mxfp4_moe_gemm (+
-mxfp4_moe_workspace_size), and the encoders mxfp4_quantize, nvfp4_quantize.
+mxfp4_moe_workspace_size), nm_spmm (N:M structured-sparse weights), and the
+encoders mxfp4_quantize, nvfp4_quantize.
 """
 from ._binding import (  # noqa: F401
     ABI_VERSION,
@@ -29,6 +30,7 @@ from ._binding import (  # noqa: F401
     mxfp4_quantize,
     nvfp4_embedding_gather,
     nvfp4_quantize,
+    nm_spmm,
     strerror,
     ternary_gemm,
     ternary_gemv,

@@ -54,6 +54,7 @@ def load_library() -> ctypes.CDLL:
         "dequant_decode": (ctypes.c_int, [vp, vp, vp, i64, i64, vp]),
         "dequant_gemv": (ctypes.c_int, [vp, vp, vp, vp, i32, i64, i64, i64, vp]),
         "dequant_gemm": (ctypes.c_int, [vp, vp, vp, vp, i32, i64, i64, i64, vp]),
+        "nm_spmm": (ctypes.c_int, [vp, vp, vp, vp, i32, i64, i64, i64, i32, i32, vp]),
         "mxfp4_quantize": (ctypes.c_int, [vp, vp, vp, i64, i64, vp]),
         "nvfp4_quantize": (ctypes.c_int, [vp, vp, vp, vp, i64, i64, vp]),
         "ternary_gemv": (ctypes.c_int, [vp, vp, vp, vp, i64, i64, vp]),
@@ -177,6 +178,31 @@ def dequant_gemm(packed: torch.Tensor, scales: torch.Tensor, x: torch.Tensor, ou
     code = DTYPE_F32 if out.dtype == torch.float32 else DTYPE_BF16
     _check("dequant_gemm", load_library().dequant_gemm(_ptr(packed), _ptr(scales), _ptr(x), _ptr(out), code,
                                                         m, n, k, _stream(stream)))
+    return out
+
+
+def nm_spmm(values: torch.Tensor, meta: torch.Tensor, x: torch.Tensor, n_keep: int, m_group: int,
+            out: torch.Tensor | None = None, out_dtype: torch.dtype = torch.float32, stream=None) -> torch.Tensor:
+    """N:M sparse W (values bf16 [rows, (k/M) N], packed positions int32/uint32 [rows, words]) times
+    bf16 x [batch, k] -> y [batch, rows]."""
+    _need(values, "values", (torch.bfloat16, torch.int16))
+    _need(meta, "meta", (torch.int32, torch.uint32))
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise ValueError("x must be a [batch, k] tensor")
+    batch, k = x.shape
+    _need(x, "x", (torch.bfloat16, torch.int16))
+    rows = values.shape[0]
+    if m_group < 1 or k % m_group != 0 or values.shape[1] != (k // m_group) * n_keep:
+        raise ValueError("values must hold (k / m_group) * n_keep entries per row")
+    bits = 1 if m_group <= 2 else (m_group - 1).bit_length()
+    words = -(-values.shape[1] // (32 // bits))
+    _need(meta, "meta", (torch.int32, torch.uint32), (rows, words))
+    if out is None:
+        out = torch.empty((batch, rows), dtype=out_dtype, device=values.device)
+    _need(out, "out", (torch.float32, torch.bfloat16), (batch, rows))
+    code = DTYPE_F32 if out.dtype == torch.float32 else DTYPE_BF16
+    _check("nm_spmm", load_library().nm_spmm(_ptr(values), _ptr(meta), _ptr(x), _ptr(out), code, batch, rows, k,
+                                              n_keep, m_group, _stream(stream)))
     return out
 
 

@@ -103,6 +103,23 @@ int dequant_gemm(const uint8_t* packed, const uint8_t* scale_e8m0, const uint16_
                                            as_stream(stream)));
 }
 
+int nm_spmm(const uint16_t* values, const uint32_t* meta, const uint16_t* x_bf16, void* y, int y_dtype,
+            int64_t batch, int64_t rows, int64_t k, int n_keep, int m_group, void* stream) {
+    if (y_dtype != E2M1_DTYPE_F32 && y_dtype != E2M1_DTYPE_BF16) return E2M1_ERR_DTYPE;
+    if (batch < 1 || batch > 16 || rows < 0 || k < 0 || m_group < 1 || m_group > 16 || n_keep < 1 ||
+        n_keep > m_group || k % m_group != 0 || rows > INT_MAX || k > INT_MAX / 16 || !mul_ok(rows, k))
+        return E2M1_ERR_SHAPE;
+    if (rows == 0) return E2M1_OK;
+    const int64_t esize = y_dtype == E2M1_DTYPE_F32 ? 4 : 2;
+    if (!y) return E2M1_ERR_NULL;
+    if (!aligned(y, (uintptr_t)esize)) return E2M1_ERR_ALIGN;
+    if (k == 0) return launch_status(fill_zero_bytes(y, batch * rows * esize, as_stream(stream)));
+    if (!values || !meta || !x_bf16) return E2M1_ERR_NULL;
+    if (!aligned(values, 2) || !aligned(meta, 4) || !aligned(x_bf16, 2)) return E2M1_ERR_ALIGN;
+    return launch_status(e2m1::launch_nm_spmm(values, meta, x_bf16, y, y_dtype == E2M1_DTYPE_BF16, batch, rows, k,
+                                              n_keep, m_group, as_stream(stream)));
+}
+
 int mxfp4_quantize(const uint16_t* x_bf16, uint8_t* packed, uint8_t* scale_e8m0, int64_t rows,
                    int64_t k, void* stream) {
     if (rows < 0 || k < 0 || k % 32 != 0 || !mul_ok(rows, k)) return E2M1_ERR_SHAPE;

@@ -28,6 +28,9 @@ hipError_t launch_gemv(const uint8_t* packed, const uint8_t* scales, const uint1
 hipError_t launch_gemm(const uint8_t* packed, const uint8_t* scales, const uint16_t* x, void* y, bool out_bf16,
                        int64_t m, int64_t n, int64_t k, hipStream_t stream);
 
+hipError_t launch_nm_spmm(const uint16_t* values, const uint32_t* meta, const uint16_t* x, void* y, bool out_bf16,
+                          int64_t batch, int64_t rows, int64_t k, int nn, int mm, hipStream_t stream);
+
 hipError_t launch_ternary(const uint32_t* packed, const float* row_scale, const float* x, float* y,
                           int64_t n, int64_t k, hipStream_t stream);
 

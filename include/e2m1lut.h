@@ -11,6 +11,8 @@
  *   [SGLang-34222] prhub.com.cn digest of SGLang pull request 34222: NVFP4
  *                  token embedding dequantised at gather time ("实现拆解",
  *                  "关键源码片段").
+ *   [NM-wiki]      sglang-jax wiki page on the N:M structured sparse matmul
+ *                  gap ("N:M 稀疏原理", "3.1 Sparsifier", "3.2").
  *   [FairyFuse]    blog.hotdry.top post on FairyFuse: 2-bit ternary GEMV with
  *                  add/sub accumulation and a per-row scale
  *                  ("三元 GEMV 的乘法消除原理"), the widely-linear complex
@@ -127,6 +129,30 @@ int dequant_gemv(const uint8_t* packed, const uint8_t* scale_e8m0, const uint16_
  */
 int dequant_gemm(const uint8_t* packed, const uint8_t* scale_e8m0, const uint16_t* x_bf16, void* y,
                  int y_dtype, int64_t m, int64_t n, int64_t k, void* stream);
+
+/*
+ * nm_spmm -- N:M structured-sparse weights times a few activation rows:
+ * y[b][r] = sum over the kept entries of row r of value * x[b][column].
+ * Format: [NM-wiki] "N:M 稀疏原理", "3.1 Sparsifier": in every group of M
+ * consecutive columns of a row N values are kept; their in-group positions
+ * are packed next_log2(M) bits each (1 bit for M = 2), 32 / bits per word,
+ * entry i of a row at bit (i mod packing) * bits of word i / packing; rows
+ * follow one another. Operation: "3.2" (decompress, then multiply), fp32
+ * accumulation.
+ *   values   bf16   [rows, (k/M) N]   kept values, group-major (2-byte aligned)
+ *   meta     uint32 [rows, ceil((k/M) N / packing)]
+ *   x_bf16   bf16   [batch, k]
+ *   y        [batch, rows], E2M1_DTYPE_F32 or E2M1_DTYPE_BF16, overwritten
+ * Requires 1 <= batch <= 16, 1 <= n_keep <= m_group <= 16, k % m_group == 0,
+ * rows, k >= 0 and below 2^31. Positions >= m_group (possible when M is not a
+ * power of two) are not valid; the kernel reads them as the group's last
+ * column. The fastest kernel takes 2:4, 1:4, 4:8, 1:2 and 8:16 with batch
+ * <= 4, batch * k <= 32768, k % 8 == 0, (k/M) N % 8 == 0 and 16-byte aligned
+ * values and x; everything else takes a slower kernel with the same results
+ * up to rounding.
+ */
+int nm_spmm(const uint16_t* values, const uint32_t* meta, const uint16_t* x_bf16, void* y, int y_dtype,
+            int64_t batch, int64_t rows, int64_t k, int n_keep, int m_group, void* stream);
 
 /*
  * mxfp4_quantize -- bf16 rows to MXFP4 codes and E8M0 block scales (the

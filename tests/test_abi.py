@@ -37,7 +37,7 @@ def lib():
 
 def test_header_declares_the_five_operations():
     names = declared_functions()
-    for op in ("dequant_decode", "dequant_gemv", "ternary_gemv", "ternary_gemm", "ternary_wl_gemv", "mxfp4_quantize", "nvfp4_quantize", "dequant_gemm", "nvfp4_embedding_gather",
+    for op in ("dequant_decode", "dequant_gemv", "ternary_gemv", "ternary_gemm", "ternary_wl_gemv", "mxfp4_quantize", "nvfp4_quantize", "dequant_gemm", "nm_spmm", "nvfp4_embedding_gather",
                "mxfp4_moe_gemm", "mxfp4_moe_workspace_size", "e2m1_abi_version", "e2m1_strerror"):
         assert op in names
 
@@ -104,6 +104,20 @@ def test_ternary_validation(lib):
     assert f(A, B, C, NULL, 4, 16, NULL) == E_NULL
     assert f(NULL, B, C, D, 4, 16, NULL) == E_NULL
     assert f(P(0x10002), B, C, D, 4, 16, NULL) == E_ALIGN
+
+
+def test_nm_validation(lib):
+    f = lib.nm_spmm
+    assert f(A, B, C, D, 5, 1, 8, 64, 2, 4, NULL) == E_DTYPE
+    assert f(A, B, C, D, 0, 0, 8, 64, 2, 4, NULL) == E_SHAPE    # batch 0
+    assert f(A, B, C, D, 0, 17, 8, 64, 2, 4, NULL) == E_SHAPE   # batch above 16
+    assert f(A, B, C, D, 0, 1, 8, 64, 5, 4, NULL) == E_SHAPE    # n > m
+    assert f(A, B, C, D, 0, 1, 8, 64, 2, 17, NULL) == E_SHAPE   # m > 16
+    assert f(A, B, C, D, 0, 1, 8, 66, 2, 4, NULL) == E_SHAPE    # k % m
+    assert f(NULL, NULL, NULL, NULL, 0, 1, 0, 64, 2, 4, NULL) == E2M1_OK
+    assert f(A, NULL, C, D, 0, 1, 8, 64, 2, 4, NULL) == E_NULL
+    assert f(A, P(0x20002), C, D, 0, 1, 8, 64, 2, 4, NULL) == E_ALIGN
+    assert f(A, B, C, P(0x40002), 0, 1, 8, 64, 2, 4, NULL) == E_ALIGN
 
 
 def test_gemm_validation(lib):

@@ -1,0 +1,134 @@
+"""GPU parity of nm_spmm (N:M structured-sparse weights times bf16 activations) against the oracle.
+
+Tolerance, derived from the arithmetic: every product of two bf16 values is
+exact in fp32, and each output is a sum of per_row = (k/M) N such products in
+fp32. Both kernels give each lane a sequential chain of about per_row / 64
+additions, then add the 64 lane totals in six DPP steps, so with u = 2^-24 the
+error of an output is at most (per_row / 64 + 8) u sum |w x| (a bound with
+two spare steps). A bf16 output adds at most 2^-8 |y|. The test checks every
+output element against that bound, with sum |w x| from the oracle's product
+of the absolute values.
+
+Covers the five configurations with a compiled kernel (2:4, 1:4, 4:8, 1:2,
+8:16) at batch 1..4, configurations that take the generic kernel (3:16, 2:3,
+5:6, 1:1, 7:8), batches 5..16, activations exactly at and just above the
+staged-LDS limit, rows whose kept count is not a multiple of 8, unaligned
+values, the 4096 x 4096 layer and a 14336 x 4096 MLP layer, bf16 output, empty
+extents and determinism.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_util import bf16, host_f32, say, words
+
+pytestmark = pytest.mark.gpu
+
+FAST = [(2, 4), (1, 4), (4, 8), (1, 2), (8, 16)]
+GENERIC = [(3, 16), (2, 3), (5, 6), (1, 1), (7, 8)]
+
+
+def encode(orc, case):
+    return orc.nm_encode(case["dense"], case["mask"], case["n"], case["m"])
+
+
+def run(g, vals, meta, x, n, m, out_dtype=torch.float32, vals_dev=None):
+    batch = x.shape[0]
+    rows = vals.shape[0]
+    out = torch.full((batch, rows), float("nan"), dtype=out_dtype, device="cuda:0")
+    v = bf16(vals) if vals_dev is None else vals_dev
+    g.nm_spmm(v, words(meta), bf16(x), n, m, out=out)
+    return host_f32(out)
+
+
+def check(g, orc, case, out_dtype=torch.float32, vals_dev=None, label=""):
+    n, m, x = case["n"], case["m"], case["x"]
+    batch, k = x.shape
+    vals, meta = encode(orc, case)
+    rows, per_row = vals.shape
+    say(f"nm_spmm {n}:{m}: batch={batch} rows={rows} k={k} out={out_dtype} {label}")
+    got = run(g, vals, meta, x, n, m, out_dtype, vals_dev)
+    want = orc.nm_spmm(vals, meta, x, k, n, m)
+    mag = orc.nm_spmm(vals & 0x7FFF, meta, x & 0x7FFF, k, n, m)
+    bound = (per_row / 64 + 8) * 2.0 ** -24 * mag + 1e-30
+    if out_dtype == torch.bfloat16:
+        bound = bound + 2.0 ** -8 * np.abs(want)
+    err = np.abs(got.astype(np.float64) - want)
+    assert np.all(np.isfinite(got))
+    worst = np.unravel_index(np.argmax(err / bound), err.shape)
+    assert np.all(err <= bound), f"worst {worst}: got {got[worst]} want {want[worst]} bound {bound[worst]}"
+    return got
+
+
+@pytest.mark.parametrize("n,m", FAST)
+@pytest.mark.parametrize("batch", [1, 2, 3, 4])
+def test_compiled_configurations(gpu, orc, n, m, batch):
+    check(gpu, orc, synth.nm_case(10 * n + m + 100 * batch, n, m, rows=301, k=1024, batch=batch))
+
+
+@pytest.mark.parametrize("n,m", GENERIC)
+def test_generic_configurations(gpu, orc, n, m):
+    check(gpu, orc, synth.nm_case(10 * n + m, n, m, rows=133, k=m * 96, batch=2))
+
+
+@pytest.mark.parametrize("batch", [5, 8, 16])
+def test_larger_batches(gpu, orc, batch):
+    check(gpu, orc, synth.nm_case(200 + batch, 2, 4, rows=77, k=2048, batch=batch))
+
+
+def test_lds_limit(gpu, orc):
+    """batch * k = 32768 bf16 (64 KB) is staged; 4 x 16384 reads x from memory."""
+    check(gpu, orc, synth.nm_case(301, 2, 4, rows=64, k=16384, batch=2), label="at the limit")
+    check(gpu, orc, synth.nm_case(302, 2, 4, rows=64, k=16384, batch=4), label="above the limit")
+
+
+@pytest.mark.parametrize("n,m,k", [(2, 4, 36), (1, 2, 6), (4, 8, 8), (8, 16, 16), (1, 4, 4)])
+def test_short_rows(gpu, orc, n, m, k):
+    """Kept counts that are not a multiple of 8 (or k not a multiple of 8), and rows of one group."""
+    check(gpu, orc, synth.nm_case(400 + k, n, m, rows=70, k=k, batch=3))
+
+
+def test_unaligned_values(gpu, orc):
+    case = synth.nm_case(501, 2, 4, rows=40, k=512, batch=1)
+    vals, _ = encode(orc, case)
+    flat = torch.zeros(vals.size + 1, dtype=torch.bfloat16, device="cuda:0")
+    v = flat[1:].view(vals.shape)
+    v.copy_(bf16(vals))
+    check(gpu, orc, case, vals_dev=v, label="values offset by 2 bytes")
+
+
+@pytest.mark.parametrize("n,m", [(2, 4), (4, 8)])
+def test_llama_layers(gpu, orc, n, m):
+    check(gpu, orc, synth.nm_case(600 + m, n, m, rows=4096, k=4096, batch=1))
+    check(gpu, orc, synth.nm_case(610 + m, n, m, rows=14336, k=4096, batch=1), label="MLP up")
+
+
+@pytest.mark.parametrize("n,m", [(2, 4), (3, 16)])
+def test_bf16_output(gpu, orc, n, m):
+    check(gpu, orc, synth.nm_case(700 + m, n, m, rows=257, k=m * 64, batch=2), out_dtype=torch.bfloat16)
+
+
+def test_empty(gpu, orc):
+    say("nm_spmm: empty extents")
+    x = torch.zeros((2, 0), dtype=torch.bfloat16, device="cuda:0")
+    vals = torch.zeros((5, 0), dtype=torch.bfloat16, device="cuda:0")
+    meta = torch.zeros((5, 0), dtype=torch.int32, device="cuda:0")
+    y = torch.full((2, 5), float("nan"), device="cuda:0")
+    gpu.nm_spmm(vals, meta, x, 2, 4, out=y)
+    assert np.array_equal(host_f32(y), np.zeros((2, 5), np.float32))
+    x = torch.zeros((1, 64), dtype=torch.bfloat16, device="cuda:0")
+    vals = torch.zeros((0, 32), dtype=torch.bfloat16, device="cuda:0")
+    meta = torch.zeros((0, 2), dtype=torch.int32, device="cuda:0")
+    assert gpu.nm_spmm(vals, meta, x, 2, 4).shape == (1, 0)
+
+
+def test_deterministic(gpu, orc):
+    case = synth.nm_case(801, 2, 4, rows=1000, k=4096, batch=2)
+    vals, meta = encode(orc, case)
+    say("nm_spmm: determinism")
+    a = run(gpu, vals, meta, case["x"], 2, 4)
+    b = run(gpu, vals, meta, case["x"], 2, 4)
+    assert np.array_equal(a, b)
