@@ -147,9 +147,10 @@ int dequant_gemm(const uint8_t* packed, const uint8_t* scale_e8m0, const uint16_
  * rows, k >= 0 and below 2^31. Positions >= m_group (possible when M is not a
  * power of two) are not valid; the kernel reads them as the group's last
  * column. The fastest kernel takes 2:4, 1:4, 4:8, 1:2 and 8:16 with batch
- * <= 4, batch * k <= 32768, k % 8 == 0, (k/M) N % 8 == 0 and 16-byte aligned
- * values and x; everything else takes a slower kernel with the same results
- * up to rounding.
+ * <= 4, (k/M) N % 8 == 0, 16-byte aligned values and x, and k up to about
+ * 29000 (one activation row), 15400 (two) or 7700 (three or four), the
+ * activations it stages in 64 KB of LDS; everything else takes a slower kernel
+ * with the same results up to rounding.
  */
 int nm_spmm(const uint16_t* values, const uint32_t* meta, const uint16_t* x_bf16, void* y, int y_dtype,
             int64_t batch, int64_t rows, int64_t k, int n_keep, int m_group, void* stream);

@@ -2,18 +2,19 @@
 
 Tolerance, derived from the arithmetic: every product of two bf16 values is
 exact in fp32, and each output is a sum of per_row = (k/M) N such products in
-fp32. Both kernels give each lane a sequential chain of about per_row / 64
-additions, then add the 64 lane totals in six DPP steps, so with u = 2^-24 the
-error of an output is at most (per_row / 64 + 8) u sum |w x| (a bound with
-two spare steps). A bf16 output adds at most 2^-8 |y|. The test checks every
-output element against that bound, with sum |w x| from the oracle's product
-of the absolute values.
+fp32. Both kernels give each lane a sequential chain over about per_row / 64
+entries (the fast one in v_dot2_f32_bf16 steps of two entries, at most two
+roundings each), then add the 64 lane totals in six DPP steps, so with
+u = 2^-24 the error of an output is at most (per_row / 64 + 8) u sum |w x| (a
+bound with two spare steps). A bf16 output adds at most 2^-8 |y|. The test
+checks every output element against that bound, with sum |w x| from the
+oracle's product of the absolute values.
 
 Covers the five configurations with a compiled kernel (2:4, 1:4, 4:8, 1:2,
 8:16) at batch 1..4, configurations that take the generic kernel (3:16, 2:3,
-5:6, 1:1, 7:8), batches 5..16, activations exactly at and just above the
-staged-LDS limit, rows whose kept count is not a multiple of 8, unaligned
-values, the 4096 x 4096 layer and a 14336 x 4096 MLP layer, bf16 output, empty
+5:6, 1:1, 7:8), batches 5..16, activations at and one span above the
+staged-LDS limit for one, two and four rows, rows whose kept count is not a
+multiple of 8, unaligned values, the 4096 x 4096 layer and a 14336 x 4096 MLP layer, bf16 output, empty
 extents and determinism.
 """
 from __future__ import annotations
@@ -79,10 +80,12 @@ def test_larger_batches(gpu, orc, batch):
     check(gpu, orc, synth.nm_case(200 + batch, 2, 4, rows=77, k=2048, batch=batch))
 
 
-def test_lds_limit(gpu, orc):
-    """batch * k = 32768 bf16 (64 KB) is staged; 4 x 16384 reads x from memory."""
-    check(gpu, orc, synth.nm_case(301, 2, 4, rows=64, k=16384, batch=2), label="at the limit")
-    check(gpu, orc, synth.nm_case(302, 2, 4, rows=64, k=16384, batch=4), label="above the limit")
+@pytest.mark.parametrize("batch,k_in,k_out", [(1, 29120, 29136), (2, 15408, 15424), (4, 7696, 7712)])
+def test_lds_limit(gpu, orc, batch, k_in, k_out):
+    """Activations staged in 64 KB of LDS: 16-column spans padded to 18 (one row), 34 (two
+    interleaved) or 68 (three or four) bf16. k_in is the largest k that fits, k_out the next span."""
+    check(gpu, orc, synth.nm_case(300 + batch, 2, 4, rows=64, k=k_in, batch=batch), label="largest staged k")
+    check(gpu, orc, synth.nm_case(310 + batch, 2, 4, rows=64, k=k_out, batch=batch), label="one span more")
 
 
 @pytest.mark.parametrize("n,m,k", [(2, 4, 36), (1, 2, 6), (4, 8, 8), (8, 16, 16), (1, 4, 4)])
