@@ -89,7 +89,7 @@ int dequant_gemv(const uint8_t* packed, const uint8_t* scale_e8m0, const uint16_
 int dequant_gemm(const uint8_t* packed, const uint8_t* scale_e8m0, const uint16_t* x_bf16, void* y,
                  int y_dtype, int64_t m, int64_t n, int64_t k, void* stream) {
     if (y_dtype != E2M1_DTYPE_F32 && y_dtype != E2M1_DTYPE_BF16) return E2M1_ERR_DTYPE;
-    if (m < 0 || n < 0 || k < 0 || k % 32 != 0 || m > INT_MAX || n > INT_MAX || k / 32 > INT_MAX ||
+    if (m < 0 || n < 0 || k < 0 || k % 32 != 0 || m > INT_MAX || n > INT_MAX || k > E2M1_GEMM_MAX_K ||
         !mul_ok(m, k) || !mul_ok(n, k) || !mul_ok(m, n) || ((n + 127) / 128) * ((m + 127) / 128) > INT_MAX)
         return E2M1_ERR_SHAPE;
     if (m == 0 || n == 0) return E2M1_OK;

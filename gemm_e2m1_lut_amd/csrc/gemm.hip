@@ -14,22 +14,28 @@
 //   * A workgroup of four waves owns a tile of 128 weight rows x 128
 //     activation rows and walks K in steps of 64 columns. Each step, its
 //     threads copy the step's x tile (128 x 64 bf16) and the raw code lines
-//     (128 rows x 32 bytes) and scale bytes of W into LDS with coalesced
-//     16-byte loads, double-buffered: the loads of step s + 1 are issued
-//     before the MFMAs of step s and written to the other buffer after them,
-//     with one barrier per step.
+//     (128 rows x 32 bytes) and scale bytes of W into LDS with 16-byte loads.
+//     The code lines are read with ordinary (cached) loads: each weight tile
+//     is read again by every activation-row tile, and a non-temporal hint
+//     cost 30 % here. Two register sets carry the copies: the loads of step s + 2 are issued
+//     before the MFMAs of step s, the registers of step s + 1 (requested a
+//     step earlier) are written to the other LDS buffer after them, one
+//     barrier per step. x and the scales are read through buffer resources:
+//     plain loads through their restrict pointers were sunk by the compiler
+//     next to their first use, exposing the full load latency every step.
 //   * Waves are laid out 2 x 2 over the tile; each owns 64 weight rows x 64
-//     activation rows as 4 x 4 tiles of v_mfma_f32_16x16x32_bf16. Lane
-//     l = 16 g + r takes 8 codes (4 bytes) of weight row r per 32 columns and
-//     decodes them with four v_cvt_scalef32_pk_bf16_fp4 (two codes each, table
-//     lookup and E8M0 scale in one instruction); every decoded A operand
-//     serves the wave's four activation tiles, so decoding costs one
-//     instruction per MFMA.
-//     B operands are 16-byte LDS reads of x at the same columns.
-//   * D element (weight row 4 g + j, activation row c) sits in lane 16 g + c,
-//     so each lane stores four consecutive outputs of one row of y.
-// Rows past N or M are loaded clamped and not stored; a 32-column half step
-// past K is decoded as zero weights.
+//     activation rows as 2 x 2 tiles of v_mfma_f32_32x32x16_bf16 (on this
+//     part the 32 x 32 form issues twice the flops of v_mfma_f32_16x16x32_bf16
+//     per cycle). Lane l = 32 g + r takes 8 codes (4 bytes) of weight row r
+//     per 16-column slice and decodes them with four
+//     v_cvt_scalef32_pk_bf16_fp4 (two codes each, table lookup and E8M0 scale
+//     in one instruction); each decoded A operand serves two MFMAs. B
+//     operands are 16-byte LDS reads of x at the same columns.
+//   * D element (weight row 8 p + 4 g + j, activation row c) sits in
+//     component 4 p + j of lane 32 g + c, so each lane stores runs of four
+//     consecutive outputs of one row of y.
+// Rows past N or M are loaded clamped and not stored; a 32-column block past
+// K is decoded as zero weights.
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -44,11 +50,16 @@ constexpr int kXPitch = kStepK + 8;          // bf16 per staged x row (16-byte p
 constexpr int kWPitch = 32 + 4;              // bytes per staged code row
 constexpr int kXElems = kTileM * kXPitch;
 constexpr int kWBytes = kTileN * kWPitch;
+constexpr int kXChunks = kTileM * kStepK / 8 / kThreads;   // 16-byte x chunks per thread per step
+constexpr int kBufferWord3 = 0x00020000;     // buffer descriptor word 3 for raw 32-bit access (gfx9 family)
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 struct GemmBuf {
     uint16_t x[kXElems];
     uint8_t w[kWBytes];
-    uint8_t s[kTileN * 2];
+    uint8_t s[kThreads * 2];   // rows < kTileN are read; every thread stores (an unconditional store keeps
+                               // the scale loads where they are issued)
 };
 
 template <bool kBf16Out>
@@ -70,8 +81,10 @@ __device__ __forceinline__ void store4(void* y, int64_t idx, const f32x4& v, boo
     }
 }
 
+// Three waves per SIMD (three workgroups per compute unit: 47 KB of LDS each)
+// caps the kernel at 168 VGPRs; left alone, the compiler takes 224 and fits two.
 template <bool kBf16Out>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(const uint8_t* __restrict__ packed,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void gemm_kernel(const uint8_t* __restrict__ packed,
                                                         const uint8_t* __restrict__ scales,
                                                         const uint16_t* __restrict__ x, void* __restrict__ y,
                                                         int m_rows, int n, int kc) {
@@ -79,7 +92,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint8_t* __restric
     const int t = threadIdx.x;
     const int lane = t & (kWave - 1);
     const int wave = t / kWave;
-    const int g = lane >> 4, r = lane & 15;
+    const int r32 = lane & 31, g2 = lane >> 5;
     const int wn = (wave & 1) * 64, wm = (wave >> 1) * 64;   // the wave's quarter of the tile
     const int K = kc * 32;
     const int nsteps = (kc + 1) / 2;
@@ -88,95 +101,126 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint8_t* __restric
     const int m0 = (blockIdx.x / ntn) * kTileM;
 
     // this thread's share of a step's copies: x chunks t + 256 i (row id / 8, 8 columns each),
-    // code line t (row t / 2, 32-column block t % 2), scale bytes of row t (t < 128)
-    const uint16_t* xsrc[4];
+    // code line t (row t / 2, 32-column block t % 2), scale bytes of row t % 128
+    // resources over this tile's rows only, so every offset is below 128 k * 2 bytes
+    const int mt = min(kTileM, m_rows - m0), nt = min(kTileN, n - n0);
+    const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(x + (size_t)m0 * K), 0, mt * K * 2, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t sres = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(scales + (size_t)n0 * kc), 0, nt * kc, kBufferWord3);
+    uint32_t xoff[kXChunks];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) xsrc[i] = x + (size_t)min(m0 + ((t + kThreads * i) >> 3), m_rows - 1) * K;
-    const int xcol = 8 * (t & 7);   // the same for the four chunks (kThreads is a multiple of 8)
+    for (int i = 0; i < kXChunks; ++i) xoff[i] = 2u * (uint32_t)min((t + kThreads * i) >> 3, mt - 1) * (uint32_t)K;
+    const uint32_t soff = (uint32_t)min(t % kTileN, nt - 1) * (uint32_t)kc;
+    const int xcol = 8 * (t & 7);   // the same for every chunk (kThreads is a multiple of 8)
     const uint8_t* wsrc = packed + (size_t)min(n0 + (t >> 1), n - 1) * (K / 2);
-    const uint8_t* ssrc = scales + (size_t)min(n0 + (t & 127), n - 1) * kc;
 
-    f32x4 acc[4][4];
+    f32x16 acc[2][2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-    uint4 xr[4], wr;
-    uint32_t sr;
-// Step `st`'s copies into registers. Columns past K (the second half of a last
-// half step) read the row's last 8 columns: finite values that meet zero weights.
-#define E2M1_GEMM_ISSUE(st)                                                                             \
+    uint4 xr[2][kXChunks], wr[2];
+    uint32_t s0[2], s1[2];   // a step's two scale bytes, combined only when staged
+// Step `st`'s copies into register set p. Columns past K (the second block of
+// a last half step) read the row's last 8 columns: finite values that meet
+// zero weights.
+#define E2M1_GEMM_ISSUE(st, p)                                                                          \
     {                                                                                                   \
         const int c0 = (st) * kStepK;                                                                   \
-        _Pragma("unroll") for (int i = 0; i < 4; ++i) xr[i] =                                          \
-            *reinterpret_cast<const uint4*>(xsrc[i] + min(c0 + xcol, K - 8));                          \
-        wr = *reinterpret_cast<const uint4*>(wsrc + (size_t)min(2 * (st) + (t & 1), kc - 1) * 16);      \
-        sr = (uint32_t)ssrc[min(2 * (st), kc - 1)] | ((uint32_t)ssrc[min(2 * (st) + 1, kc - 1)] << 8);  \
+        _Pragma("unroll") for (int i = 0; i < kXChunks; ++i) {                                          \
+            const u32x4 v_ = __builtin_amdgcn_raw_buffer_load_b128(                                     \
+                xres, xoff[i] + 2u * (uint32_t)min(c0 + xcol, K - 8), 0, 0);                            \
+            xr[p][i] = make_uint4(v_[0], v_[1], v_[2], v_[3]);                                          \
+        }                                                                                               \
+        wr[p] = *reinterpret_cast<const uint4*>(wsrc + (size_t)min(2 * (st) + (t & 1), kc - 1) * 16);    \
+        s0[p] = __builtin_amdgcn_raw_buffer_load_b8(sres, soff + (uint32_t)min(2 * (st), kc - 1), 0, 0);     \
+        s1[p] = __builtin_amdgcn_raw_buffer_load_b8(sres, soff + (uint32_t)min(2 * (st) + 1, kc - 1), 0, 0); \
     }
-// The registers of step `st` into buffer `bb`; a block past K is staged as zero codes.
-#define E2M1_GEMM_STAGE(bb, st)                                                                          \
+// Register set p (step `st`) into LDS buffer bb; a block past K is staged as zero codes.
+#define E2M1_GEMM_STAGE(bb, st, p)                                                                      \
     {                                                                                                   \
-        _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                                 \
+        _Pragma("unroll") for (int i = 0; i < kXChunks; ++i) {                                          \
             const int id = t + kThreads * i;                                                            \
-            *reinterpret_cast<uint4*>((bb).x + (id >> 3) * kXPitch + 8 * (id & 7)) = xr[i];             \
+            *reinterpret_cast<uint4*>((bb).x + (id >> 3) * kXPitch + 8 * (id & 7)) = xr[p][i];          \
         }                                                                                               \
         const uint32_t keep = 2 * (st) + (t & 1) < kc ? 0xFFFFFFFFu : 0u;                               \
         uint32_t* wd = reinterpret_cast<uint32_t*>((bb).w + (t >> 1) * kWPitch + 16 * (t & 1));          \
-        wd[0] = wr.x & keep;                                                                            \
-        wd[1] = wr.y & keep;                                                                            \
-        wd[2] = wr.z & keep;                                                                            \
-        wd[3] = wr.w & keep;                                                                            \
-        if (t < kTileN) *reinterpret_cast<uint16_t*>((bb).s + 2 * t) = (uint16_t)sr;                    \
+        wd[0] = wr[p].x & keep;                                                                         \
+        wd[1] = wr[p].y & keep;                                                                         \
+        wd[2] = wr[p].z & keep;                                                                         \
+        wd[3] = wr[p].w & keep;                                                                         \
+        *reinterpret_cast<uint16_t*>((bb).s + 2 * t) = (uint16_t)(s0[p] | (s1[p] << 8));                \
+    }
+// The MFMAs of the step held in buffer bb: 16-column slices q, lane group g2
+// taking columns 16 q + 8 g2 .. + 7 of both operands.
+#define E2M1_GEMM_COMPUTE(bb)                                                                           \
+    {                                                                                                   \
+        _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                                 \
+            bf16x8 a[2];                                                                                \
+            _Pragma("unroll") for (int i = 0; i < 2; ++i) {                                             \
+                const int row = wn + 32 * i + r32;                                                      \
+                const uint32_t codes = *reinterpret_cast<const uint32_t*>((bb).w + row * kWPitch + 8 * q + 4 * g2); \
+                const float sc = e8m0_scale((bb).s[2 * row + (q >> 1)]);                                \
+                const u32x4 u = {fp4x2_to_bf16x2<0>(codes, sc), fp4x2_to_bf16x2<1>(codes, sc),          \
+                                 fp4x2_to_bf16x2<2>(codes, sc), fp4x2_to_bf16x2<3>(codes, sc)};         \
+                a[i] = __builtin_bit_cast(bf16x8, u);                                                   \
+            }                                                                                           \
+            _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                             \
+                const bf16x8 bx = *reinterpret_cast<const bf16x8*>((bb).x + (wm + 32 * j + r32) * kXPitch + \
+                                                                   16 * q + 8 * g2);                    \
+                _Pragma("unroll") for (int i = 0; i < 2; ++i)                                           \
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bx, acc[i][j], 0, 0, 0);  \
+            }                                                                                           \
+        }                                                                                               \
+    }
+// Step `step` with parity p: request step + 2 into register set p (free since
+// its step was staged), compute from buffer p, stage register set 1 - p (step
+// + 1) into buffer 1 - p (every wave finished reading it before the last barrier).
+// The last steps re-request their own copies, staged into the idle buffer and never read.
+#define E2M1_GEMM_STEP(step, p)                                                                         \
+    {                                                                                                   \
+        E2M1_GEMM_ISSUE(min((step) + 2, nsteps - 1), p)                                                 \
+        asm volatile("" ::: "memory");   /* the loads stay here, ahead of the step's MFMAs */           \
+        __builtin_amdgcn_sched_barrier(0);                                                              \
+        E2M1_GEMM_COMPUTE(buf[p])                                                                       \
+        __builtin_amdgcn_sched_barrier(0);   /* the staging (and its waits) stays after them */         \
+        E2M1_GEMM_STAGE(buf[1 - (p)], min((step) + 1, nsteps - 1), 1 - (p))                             \
+        __syncthreads();                                                                                \
     }
 
-    E2M1_GEMM_ISSUE(0)
-    E2M1_GEMM_STAGE(buf[0], 0)
+    E2M1_GEMM_ISSUE(0, 0)
+    E2M1_GEMM_STAGE(buf[0], 0, 0)
+    E2M1_GEMM_ISSUE(min(1, nsteps - 1), 1)
     __syncthreads();
-    for (int step = 0; step < nsteps; ++step) {
-        const GemmBuf& b = buf[step & 1];
-        // the next step's copies (the last step repeats its own: staged into the idle buffer, never read)
-        const int nxt = min(step + 1, nsteps - 1);
-        E2M1_GEMM_ISSUE(nxt)
-        asm volatile("" ::: "memory");        // the loads stay here, ahead of the step's MFMAs
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {   // 32-column half steps
-            bf16x8 a[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = wn + 16 * i + r;
-                const uint32_t codes = *reinterpret_cast<const uint32_t*>(b.w + row * kWPitch + 16 * h + 4 * g);
-                const float sc = e8m0_scale(b.s[2 * row + h]);
-                const u32x4 u = {fp4x2_to_bf16x2<0>(codes, sc), fp4x2_to_bf16x2<1>(codes, sc),
-                                 fp4x2_to_bf16x2<2>(codes, sc), fp4x2_to_bf16x2<3>(codes, sc)};
-                a[i] = __builtin_bit_cast(bf16x8, u);
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const bf16x8 bx = *reinterpret_cast<const bf16x8*>(b.x + (wm + 16 * j + r) * kXPitch + 32 * h + 8 * g);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bx, acc[i][j], 0, 0, 0);
-            }
-        }
-        E2M1_GEMM_STAGE(buf[(step + 1) & 1], nxt)
-        __syncthreads();
+    for (int s = 0; s < nsteps; s += 2) {   // unrolled by two: register sets and buffers are static
+        E2M1_GEMM_STEP(s, 0)
+        if (s + 1 < nsteps) E2M1_GEMM_STEP(s + 1, 1)   // workgroup-uniform
     }
-#undef E2M1_GEMM_ISSUE
+#undef E2M1_GEMM_STEP
+#undef E2M1_GEMM_COMPUTE
 #undef E2M1_GEMM_STAGE
+#undef E2M1_GEMM_ISSUE
 
-    // lane (g, c) holds rows n0 + wn + 16 i + 4 g .. + 3 of activation row m0 + wm + 16 j + c
+    // lane l = 32 g2 + c holds, for tile (i, j) and p < 4, rows n0 + wn + 32 i + 8 p + 4 g2 .. + 3
+    // of activation row m0 + wm + 32 j + c (accumulator components 4 p .. 4 p + 3)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int m = m0 + wm + 16 * j + r;
+    for (int j = 0; j < 2; ++j) {
+        const int m = m0 + wm + 32 * j + r32;
         if (m >= m_rows) continue;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int nn = n0 + wn + 16 * i + 4 * g;
-            if (nn >= n) continue;
-            const int count = min(4, n - nn);
-            store4<kBf16Out>(y, (int64_t)m * n + nn, acc[i][j], count == 4, count);
-        }
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const int nn = n0 + wn + 32 * i + 8 * p + 4 * g2;
+                if (nn >= n) continue;
+                const int count = min(4, n - nn);
+                const f32x4 v = {acc[i][j][4 * p], acc[i][j][4 * p + 1], acc[i][j][4 * p + 2], acc[i][j][4 * p + 3]};
+                store4<kBf16Out>(y, (int64_t)m * n + nn, v, count == 4, count);
+            }
     }
 }
 

@@ -123,10 +123,12 @@ int dequant_gemv(const uint8_t* packed, const uint8_t* scale_e8m0, const uint16_
  *   scale_e8m0  uint8  [n, k/32]
  *   x_bf16      uint16 [m, k]     bf16 patterns (16-byte aligned)
  *   y           [m, n], E2M1_DTYPE_F32 (fp32) or E2M1_DTYPE_BF16 (bf16 RNE), overwritten
- * Requires m, n >= 0, k >= 0, k % 32 == 0, m, n and k / 32 at most
- * 2^31 - 1 and fewer than 2^31 tiles of 128 x 128 outputs. k == 0 writes
- * zeros. Rows of W or x past n or m are never read.
+ * Requires m, n >= 0, k >= 0, k % 32 == 0, m and n at most 2^31 - 1,
+ * k <= E2M1_GEMM_MAX_K (each workgroup addresses its 128 rows of x with 32-bit
+ * byte offsets) and fewer than 2^31 tiles of 128 x 128 outputs. k == 0
+ * writes zeros. Rows of W or x past n or m are never read.
  */
+#define E2M1_GEMM_MAX_K 8388576
 int dequant_gemm(const uint8_t* packed, const uint8_t* scale_e8m0, const uint16_t* x_bf16, void* y,
                  int y_dtype, int64_t m, int64_t n, int64_t k, void* stream);
 

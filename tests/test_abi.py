@@ -126,6 +126,7 @@ def test_gemm_validation(lib):
     assert f(A, B, C, D, 0, 4, 8, 40, NULL) == E_SHAPE     # k % 32
     assert f(A, B, C, D, 0, -1, 8, 64, NULL) == E_SHAPE
     assert f(A, B, C, D, 0, 2**31, 8, 64, NULL) == E_SHAPE
+    assert f(A, B, C, D, 0, 4, 8, 8388576 + 32, NULL) == E_SHAPE   # k beyond the 32-bit tile offsets
     assert f(NULL, NULL, NULL, NULL, 0, 0, 8, 64, NULL) == E2M1_OK
     assert f(A, B, C, NULL, 0, 4, 8, 64, NULL) == E_NULL
     assert f(NULL, B, C, D, 1, 4, 8, 64, NULL) == E_NULL
