@@ -801,6 +801,18 @@ def traffic_from_profile(label: str) -> dict | None:
     return entry
 
 
+def cpu_model() -> str:
+    """The host CPU's model name, as /proc/cpuinfo reports it."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -865,6 +877,10 @@ def main() -> int:
     cpu = None
     if not args.no_cpu_baseline:
         cpu = wl.cpu_baseline(args.cpu_budget_s)
+        if cpu is not None:
+            import oracle
+            cpu["cpu_model"] = cpu_model()
+            cpu["build"] = "gcc " + " ".join(oracle.CFLAGS)
 
     line = {
         "metric": METRIC,
