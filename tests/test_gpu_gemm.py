@@ -5,8 +5,9 @@ weights times bf16 x, for any number of rows), rounded to the output dtype
 before comparing; the bar is the GEMV's, rel-L2 <= 1e-3 with fp32
 accumulation. Shapes span one and many 128 x 128 tiles, ragged tiles in both
 directions, K with an odd number of 32-column blocks (a half step of zero
-weights), both output dtypes, and the prefill shape of the benchmark (2048
-tokens through the Llama-8B MLP matrices) on sampled rows and columns.
+weights), both output dtypes, block scales over a wide exponent range, and the
+prefill shape of the benchmark (2048 tokens through the Llama-8B MLP
+matrices) on sampled rows and columns.
 """
 from __future__ import annotations
 
@@ -66,6 +67,14 @@ def test_prefill_shape_sampled(gpu, orc, n, k):
     want = bf16_values(orc.mxfp4_gemv(packed[cols], scales[cols], x[rows], "bf16"))
     err = rel_l2(got[np.ix_(rows, cols)], want)
     assert err <= TOL, err
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_wide_exponent_range(gpu, orc, out_dtype):
+    """E8M0 scales over 100..150 (block values from 2^-27 to 6 * 2^23): the decode's
+    scale operand and the fp32 accumulation across blocks of very different size."""
+    c = synth.mxfp4_gemv_case(77, 300, 1024, batch=140, e_lo=100, e_hi=150)
+    gemm_case(gpu, orc, c["packed"], c["scales"], c["x"], out_dtype)
 
 
 def test_matches_the_gemv_at_small_batch(gpu, orc):

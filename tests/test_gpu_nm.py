@@ -14,7 +14,8 @@ Covers the five configurations with a compiled kernel (2:4, 1:4, 4:8, 1:2,
 8:16) at batch 1..4, configurations that take the generic kernel (3:16, 2:3,
 5:6, 1:1, 7:8), batches 5..16, activations at and one span above the
 staged-LDS limit for one, two and four rows, rows whose kept count is not a
-multiple of 8, unaligned values, the 4096 x 4096 layer and a 14336 x 4096 MLP layer, bf16 output, empty
+multiple of 8, position words drawn at random (repeats within a group),
+unaligned values, the 4096 x 4096 layer and a 14336 x 4096 MLP layer, bf16 output, empty
 extents and determinism.
 """
 from __future__ import annotations
@@ -92,6 +93,30 @@ def test_lds_limit(gpu, orc, batch, k_in, k_out):
 def test_short_rows(gpu, orc, n, m, k):
     """Kept counts that are not a multiple of 8 (or k not a multiple of 8), and rows of one group."""
     check(gpu, orc, synth.nm_case(400 + k, n, m, rows=70, k=k, batch=3))
+
+
+@pytest.mark.parametrize("n,m,batch", [(2, 4, 1), (4, 8, 3), (8, 16, 2), (3, 16, 5)])
+def test_arbitrary_positions(gpu, orc, n, m, batch):
+    """Position fields drawn at random, repeats within a group included: the encoder never
+    writes these, but the product over the kept entries is still defined (every field is
+    below M for M a power of two), and both kernels must follow it."""
+    r = np.random.default_rng(900 + 16 * n + m)
+    k = m * 128
+    rows = 97
+    bits_ = 1 if m <= 2 else (m - 1).bit_length()
+    packing = 32 // bits_
+    per_row = (k // m) * n
+    words_ = -(-per_row // packing)
+    vals = synth.bf16_normal(r, (rows, per_row), 0.02)
+    meta = r.integers(0, 2**32, size=(rows, words_), dtype=np.uint64).astype(np.uint32)
+    if packing * bits_ < 32:   # 3-bit positions: the two spare high bits of each word stay clear
+        meta &= np.uint32((1 << (packing * bits_)) - 1)
+    x = synth.bf16_normal(r, (batch, k))
+    say(f"nm_spmm {n}:{m}: arbitrary positions, batch={batch}")
+    got = run(gpu, vals, meta, x, n, m).astype(np.float64)
+    want = orc.nm_spmm(vals, meta, x, k, n, m)
+    mag = orc.nm_spmm(vals & 0x7FFF, meta, x & 0x7FFF, k, n, m)
+    assert np.all(np.abs(got - want) <= (per_row / 64 + 8) * 2.0 ** -24 * mag + 1e-30)
 
 
 def test_unaligned_values(gpu, orc):
