@@ -699,6 +699,7 @@ class Moe(Workload):
 WORKLOADS = {
     "moe": Moe,
     "mlp_b1": lambda rb: GemvMLP(1, rb),
+    "mlp_b2": lambda rb: GemvMLP(2, rb),
     "mlp_b4": lambda rb: GemvMLP(4, rb),
     "mlp_b16": lambda rb: GemvMLP(16, rb),
     "ternary": Ternary,

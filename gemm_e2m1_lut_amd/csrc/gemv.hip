@@ -24,7 +24,10 @@
 //     Longer rows (K > 16384) are split over the waves of a workgroup, one
 //     chunk per lane, with three rows in flight; short rows (K <= 1024) use
 //     groups of 8 to 32 lanes per row.
-//   * Batch 2..16: the same weight bytes feed bf16 MFMA
+//   * Batch 2..3 with 1024 < K <= 16384: the batch-1 tile kernel with the
+//     activation rows side by side in registers, B dot2 per decoded pair.
+//   * Batch 2..16 otherwise (batch 4..16, or K <= 1024): the same weight
+//     bytes feed bf16 MFMA
 //     (v_mfma_f32_16x16x32_bf16) with the batch as the N dimension: a
 //     workgroup takes a tile of 16 rows, its S waves split K into slices of
 //     1024 columns, each lane decodes its 16-byte chunks straight into A
@@ -235,6 +238,77 @@ __global__ __launch_bounds__(kWave * S) void gemv_b1_tile_kernel(const uint8_t* 
         for (int j = 0; j < S; ++j) sum += part[j][threadIdx.x];
         const int row = tile * 16 + threadIdx.x;
         if (row < n) store_out<kBf16Out>(y, row, sum);
+    }
+}
+
+// Batch 2..3, 32 < K/32 <= 32 S: the batch-1 tile layout above (one
+// workgroup of S waves per tile of 16 rows, lane l taking chunk 32 w + l % 32
+// of rows 2 q + l / 32, two rows x 512 contiguous bytes per load instruction)
+// with the B activation rows' words of the lane's chunk in registers: each
+// decoded code pair meets them in B v_dot2_f32_bf16, so the decode is shared
+// by the batch and nothing but the row totals passes through LDS. The work
+// per weight byte grows with B (one conversion, B dot2 and B shares of the
+// row reductions), which is why from four rows on the matrix-core kernel
+// below takes over.
+template <int S, int B, bool kBf16Out>
+__global__ __launch_bounds__(kWave * S) void gemv_bn_tile_kernel(const uint8_t* packed, const uint8_t* scales,
+                                                                 const uint16_t* __restrict__ x,
+                                                                 void* __restrict__ y, int n, int kc) {
+    __shared__ float part[S][B][16];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int half = lane >> 5, cl = lane & 31;
+    const int c_raw = wv * 32 + cl;
+    const bool cvalid = c_raw < kc;
+    const int c = min(c_raw, kc - 1);
+    const uint4* pv = reinterpret_cast<const uint4*>(packed);
+    uint32_t xr[B][16];
+#pragma unroll
+    for (int b = 0; b < B; ++b) load_x_chunk(xr[b], x + (size_t)b * kc * 32, c, kc);
+    issue_here();
+    const int tile = blockIdx.x;
+    uint4 w[8];
+    uint8_t e[8];   // kept as bytes: widened at use
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const int row = min(tile * 16 + 2 * q + half, n - 1);
+        const int64_t blk = (int64_t)row * kc + c;
+        w[q] = load_nt16(pv + blk);
+        e[q] = scales[blk];
+    }
+    issue_here();
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const float s = e8m0_scale(e[q]);
+        const uint32_t ws[4] = {w[q].x, w[q].y, w[q].z, w[q].w};
+        uint32_t wd[16];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            wd[4 * i + 0] = fp4x2_to_bf16x2<0>(ws[i], s);
+            wd[4 * i + 1] = fp4x2_to_bf16x2<1>(ws[i], s);
+            wd[4 * i + 2] = fp4x2_to_bf16x2<2>(ws[i], s);
+            wd[4 * i + 3] = fp4x2_to_bf16x2<3>(ws[i], s);
+        }
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+            for (int j = 0; j < 16; j += 2) {
+                a0 = dot2_bf16(wd[j], xr[b][j], a0);
+                a1 = dot2_bf16(wd[j + 1], xr[b][j + 1], a1);
+            }
+            const float t = group_total<32>(cvalid ? a0 + a1 : 0.f);   // lanes 31 and 63 hold the half-wave sums
+            if (cl == 31) part[wv][b][2 * q + half] = t;
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x < 16 * B) {
+        const int b = threadIdx.x / 16, r = threadIdx.x % 16;
+        float sum = 0.f;
+#pragma unroll
+        for (int j = 0; j < S; ++j) sum += part[j][b][r];
+        const int row = tile * 16 + r;
+        if (row < n) store_out<kBf16Out>(y, (int64_t)b * n + row, sum);
     }
 }
 
@@ -537,6 +611,28 @@ hipError_t run_b1_tile(const uint8_t* packed, const uint8_t* scales, const uint1
     return hipGetLastError();
 }
 
+template <int S, int B, bool kBf16Out>
+hipError_t run_bn_tile(const uint8_t* packed, const uint8_t* scales, const uint16_t* x, void* y, int n, int kc,
+                       hipStream_t stream) {
+    const int tiles = (n + 15) / 16;   // one workgroup per tile of 16 rows
+    gemv_bn_tile_kernel<S, B, kBf16Out><<<tiles, kWave * S, 0, stream>>>(packed, scales, x, y, n, kc);
+    return hipGetLastError();
+}
+
+template <int B, bool kBf16Out>
+hipError_t dispatch_bn(const uint8_t* packed, const uint8_t* scales, const uint16_t* x, void* y, int n, int kc,
+                       hipStream_t stream) {
+    switch ((kc + 31) / 32) {
+#define E2M1_TILE_CASE(S) \
+    case S: return run_bn_tile<S, B, kBf16Out>(packed, scales, x, y, n, kc, stream);
+        E2M1_TILE_CASE(2) E2M1_TILE_CASE(3) E2M1_TILE_CASE(4) E2M1_TILE_CASE(5) E2M1_TILE_CASE(6)
+        E2M1_TILE_CASE(7) E2M1_TILE_CASE(8) E2M1_TILE_CASE(9) E2M1_TILE_CASE(10) E2M1_TILE_CASE(11)
+        E2M1_TILE_CASE(12) E2M1_TILE_CASE(13) E2M1_TILE_CASE(14) E2M1_TILE_CASE(15)
+        default: return run_bn_tile<16, B, kBf16Out>(packed, scales, x, y, n, kc, stream);
+#undef E2M1_TILE_CASE
+    }
+}
+
 template <int S, bool kBf16Out>
 hipError_t run_b1_split(const uint8_t* packed, const uint8_t* scales, const uint16_t* x, void* y, int n, int kc,
                         hipStream_t stream) {
@@ -646,6 +742,13 @@ hipError_t launch_gemv(const uint8_t* packed, const uint8_t* scales, const uint1
     if (batch == 1 && k <= kB1MaxK)
         return out_bf16 ? dispatch_b1<true>(packed, scales, x, y, nn, kc, stream)
                         : dispatch_b1<false>(packed, scales, x, y, nn, kc, stream);
+    if ((batch == 2 || batch == 3) && kc > 32 && kc <= kMaxSliceWaves * kSliceBlocks) {
+        if (batch == 2)
+            return out_bf16 ? dispatch_bn<2, true>(packed, scales, x, y, nn, kc, stream)
+                            : dispatch_bn<2, false>(packed, scales, x, y, nn, kc, stream);
+        return out_bf16 ? dispatch_bn<3, true>(packed, scales, x, y, nn, kc, stream)
+                        : dispatch_bn<3, false>(packed, scales, x, y, nn, kc, stream);
+    }
     if (batch > 1 && kc <= kMaxSliceWaves * kSliceBlocks)
         return out_bf16 ? run_mfma<true>(batch, packed, scales, x, y, nn, kc, stream)
                         : run_mfma<false>(batch, packed, scales, x, y, nn, kc, stream);
