@@ -20,13 +20,14 @@
 //     whose partial row sums meet in LDS; the hardware streams through the
 //     tiles (one workgroup each), which measured faster on these sizes than
 //     keeping rows in flight from a resident grid. Every weight byte is read
-//     once and the row totals come from DPP reductions over 32 lanes.
+//     once; the eight row-pair totals of a lane are reduced over 32 lanes
+//     together, as a transposed butterfly (v_permlane16_swap and DPP).
 //     Longer rows (K > 16384) are split over the waves of a workgroup, one
 //     chunk per lane, with three rows in flight; short rows (K <= 1024) use
 //     groups of 8 to 32 lanes per row.
-//   * Batch 2..3 with 1024 < K <= 16384: the batch-1 tile kernel with the
+//   * Batch 2..4 with 1024 < K <= 16384: the batch-1 tile kernel with the
 //     activation rows side by side in registers, B dot2 per decoded pair.
-//   * Batch 2..16 otherwise (batch 4..16, or K <= 1024): the same weight
+//   * Batch 2..16 otherwise (batch 5..16, or K <= 1024): the same weight
 //     bytes feed bf16 MFMA
 //     (v_mfma_f32_16x16x32_bf16) with the batch as the N dimension: a
 //     workgroup takes a tile of 16 rows, its S waves split K into slices of
@@ -93,6 +94,95 @@ __device__ __forceinline__ float group_total(float v) {
     if constexpr (G >= 64)   // row_bcast:31 into rows 2 and 3
         v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xC, 0xF, false));
     return v;
+}
+
+// Totals of N per-lane values over each half wave (32 lanes), reduced as a
+// transposed butterfly. Stage s (s = 4 .. 0) pairs every lane with one whose
+// lane-index bit s differs (bit 4 through v_permlane16_swap, bits 3..0
+// through the DPP row mirror, half-row mirror and quad permutations); while a
+// lane holds an even number m of values it halves them, the lane with bit s
+// clear keeping the pair sums of values [0, m/2) and the other those of
+// [m/2, m); with an odd m it adds its partner's values to all of its own.
+// On return v[0 .. half_totals_count<N>()) of lane L hold the totals of
+// value indices half_totals_base<N>(L) + j, and lanes that differ only in the
+// low half_totals_dup_bits<N>() bits of the lane index hold the same ones.
+// Against one five-step DPP reduction per value this costs about 2.5 instead
+// of 5 operations per value for N >= 8, and the independent pairs of a stage
+// fill the DPP wait states.
+template <int N>
+constexpr int half_totals_count() {
+    int m = N;
+    for (int st = 4; st >= 0; --st)
+        if (m % 2 == 0) m /= 2;
+    return m;
+}
+
+template <int N>
+constexpr int half_totals_dup_bits() {
+    int m = N, bits = 0;
+    for (int st = 4; st >= 0; --st) {
+        if (m % 2 == 0) m /= 2;
+        else ++bits;
+    }
+    return bits;
+}
+
+template <int N>
+__device__ __forceinline__ int half_totals_base(int lane) {
+    int m = N, base = 0;
+#pragma unroll
+    for (int st = 4; st >= 0; --st)
+        if (m % 2 == 0) {
+            m /= 2;
+            base += ((lane >> st) & 1) * m;
+        }
+    return base;
+}
+
+template <int St>
+__device__ __forceinline__ float half_partner(float v) {   // lane-index bit St flipped, St < 4
+    if constexpr (St == 3) return dpp_f32<0x140>(v);   // row_mirror: lane i <-> 15 - i
+    if constexpr (St == 2) return dpp_f32<0x141>(v);   // row_half_mirror: i <-> 7 - i
+    if constexpr (St == 1) return dpp_f32<0x4E>(v);    // quad_perm [2,3,0,1]
+    return dpp_f32<0xB1>(v);                           // quad_perm [1,0,3,2]
+}
+
+template <int St, int M>
+__device__ __forceinline__ void half_totals_stage(float* v, int lane) {
+    if constexpr (M % 2 == 0) {
+        constexpr int H = M / 2;
+        const bool upper = (lane >> St) & 1;
+#pragma unroll
+        for (int j = 0; j < H; ++j) {
+            if constexpr (St == 4) {   // rows 2i and 2i+1: even rows keep v[j], odd rows v[j + H]
+                const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[j]), __float_as_uint(v[j + H]),
+                                                                false, false);
+                v[j] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+            } else {
+                const float keep = upper ? v[j + H] : v[j];
+                const float send = upper ? v[j] : v[j + H];
+                v[j] = keep + half_partner<St>(send);
+            }
+        }
+        if constexpr (St > 0) half_totals_stage<St - 1, H>(v, lane);
+    } else {
+#pragma unroll
+        for (int j = 0; j < M; ++j) {
+            if constexpr (St == 4) {
+                const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[j]), __float_as_uint(v[j]),
+                                                                false, false);
+                v[j] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+            } else {
+                v[j] += half_partner<St>(v[j]);
+            }
+        }
+        if constexpr (St > 0) half_totals_stage<St - 1, M>(v, lane);
+    }
+}
+
+template <int N>
+__device__ __forceinline__ void half_totals(float (&v)[N], int lane) {
+    half_totals_stage<4, N>(v, lane);
 }
 
 // Batch 1. A group of G lanes covers one row; lane gl owns the 32-column chunks
@@ -193,8 +283,9 @@ __device__ __forceinline__ void load_x_chunk(uint32_t (&xr)[16], const uint16_t*
 // of rows 2 q + l / 32 (q = 0..7), so each load instruction reads two rows
 // x 512 contiguous bytes. Chunks past the row end are loaded clamped and
 // their partial sums dropped (E2M1 codes times a clamped E8M0 scale are
-// always finite). The 32-lane row sums of the S waves meet in LDS and are
-// summed in a fixed order.
+// always finite). The eight 32-lane row sums of a wave come out of one
+// transposed reduction (half_totals), meet those of the other waves in LDS
+// and are summed in a fixed order.
 template <int S, bool kBf16Out>
 __global__ __launch_bounds__(kWave * S) void gemv_b1_tile_kernel(const uint8_t* packed, const uint8_t* scales,
                                                                  const uint16_t* __restrict__ x,
@@ -225,12 +316,10 @@ __global__ __launch_bounds__(kWave * S) void gemv_b1_tile_kernel(const uint8_t* 
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
         const float p = block_dot(w[q], e8m0_scale(e[q]), xr, 0.f);
-        tot[q] = group_total<32>(cvalid ? p : 0.f);   // lanes 31 and 63 hold the half-wave sums
+        tot[q] = cvalid ? p : 0.f;
     }
-    if (cl == 31) {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) part[wv][2 * q + half] = tot[q];
-    }
+    half_totals(tot, lane);   // lane L: total of row pair q = half_totals_base<8>(L)
+    if ((lane & ((1 << half_totals_dup_bits<8>()) - 1)) == 0) part[wv][2 * half_totals_base<8>(lane) + half] = tot[0];
     __syncthreads();
     if (threadIdx.x < 16) {
         float sum = 0.f;
@@ -241,14 +330,14 @@ __global__ __launch_bounds__(kWave * S) void gemv_b1_tile_kernel(const uint8_t* 
     }
 }
 
-// Batch 2..3, 32 < K/32 <= 32 S: the batch-1 tile layout above (one
+// Batch 2..4, 32 < K/32 <= 32 S: the batch-1 tile layout above (one
 // workgroup of S waves per tile of 16 rows, lane l taking chunk 32 w + l % 32
 // of rows 2 q + l / 32, two rows x 512 contiguous bytes per load instruction)
 // with the B activation rows' words of the lane's chunk in registers: each
 // decoded code pair meets them in B v_dot2_f32_bf16, so the decode is shared
 // by the batch and nothing but the row totals passes through LDS. The work
 // per weight byte grows with B (one conversion, B dot2 and B shares of the
-// row reductions), which is why from four rows on the matrix-core kernel
+// row reductions), which is why from five rows on the matrix-core kernel
 // below takes over.
 template <int S, int B, bool kBf16Out>
 __global__ __launch_bounds__(kWave * S) void gemv_bn_tile_kernel(const uint8_t* packed, const uint8_t* scales,
@@ -277,6 +366,7 @@ __global__ __launch_bounds__(kWave * S) void gemv_bn_tile_kernel(const uint8_t* 
         e[q] = scales[blk];
     }
     issue_here();
+    float tot[8 * B];
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
         const float s = e8m0_scale(e[q]);
@@ -291,14 +381,19 @@ __global__ __launch_bounds__(kWave * S) void gemv_bn_tile_kernel(const uint8_t* 
         }
 #pragma unroll
         for (int b = 0; b < B; ++b) {
-            float a0 = 0.f, a1 = 0.f;
+            float a = 0.f;
 #pragma unroll
-            for (int j = 0; j < 16; j += 2) {
-                a0 = dot2_bf16(wd[j], xr[b][j], a0);
-                a1 = dot2_bf16(wd[j + 1], xr[b][j + 1], a1);
-            }
-            const float t = group_total<32>(cvalid ? a0 + a1 : 0.f);   // lanes 31 and 63 hold the half-wave sums
-            if (cl == 31) part[wv][b][2 * q + half] = t;
+            for (int j = 0; j < 16; ++j) a = dot2_bf16(wd[j], xr[b][j], a);
+            tot[8 * b + q] = cvalid ? a : 0.f;
+        }
+    }
+    half_totals(tot, lane);   // lane L: totals of value indices base + j = 8 b + q
+    if ((lane & ((1 << half_totals_dup_bits<8 * B>()) - 1)) == 0) {
+        const int base = half_totals_base<8 * B>(lane);
+#pragma unroll
+        for (int j = 0; j < half_totals_count<8 * B>(); ++j) {
+            const int idx = base + j;
+            part[wv][idx / 8][2 * (idx % 8) + half] = tot[j];
         }
     }
     __syncthreads();
@@ -742,7 +837,10 @@ hipError_t launch_gemv(const uint8_t* packed, const uint8_t* scales, const uint1
     if (batch == 1 && k <= kB1MaxK)
         return out_bf16 ? dispatch_b1<true>(packed, scales, x, y, nn, kc, stream)
                         : dispatch_b1<false>(packed, scales, x, y, nn, kc, stream);
-    if ((batch == 2 || batch == 3) && kc > 32 && kc <= kMaxSliceWaves * kSliceBlocks) {
+    if (batch >= 2 && batch <= 4 && kc > 32 && kc <= kMaxSliceWaves * kSliceBlocks) {
+        if (batch == 4)
+            return out_bf16 ? dispatch_bn<4, true>(packed, scales, x, y, nn, kc, stream)
+                            : dispatch_bn<4, false>(packed, scales, x, y, nn, kc, stream);
         if (batch == 2)
             return out_bf16 ? dispatch_bn<2, true>(packed, scales, x, y, nn, kc, stream)
                             : dispatch_bn<2, false>(packed, scales, x, y, nn, kc, stream);

@@ -56,8 +56,9 @@ SHAPES = [
     (70001, 2048, 1),                 # many row tiles, ragged last one
     (17000, 16384 + 32, 1),           # > 64 rows per workgroup in the K-split kernel
     (31, 512, 2), (17, 4096 + 32, 3), (9, 1024, 4), (65, 2048, 8), (12, 768, 16),
-    # batch 2 and 3 in the batch-1 tile layout: two to sixteen waves, ragged chunks and rows
+    # batch 2 to 4 in the batch-1 tile layout: two to sixteen waves, ragged chunks and rows
     (47, 1024 + 32, 2), (100, 14336, 2), (33, 16384, 3), (290, 32 * 200 + 32 * 7, 2), (18, 8192, 3),
+    (61, 32 * 77, 4), (35, 16384, 4), (129, 4096, 4),
 ]
 
 
