@@ -44,8 +44,10 @@ __device__ __forceinline__ void dequant_word(uint32_t w, float eff, uint32_t* ou
 // write one contiguous kilobyte per wave-wide store. Every id, code word and
 // scale of a thread's rows is requested (indices clamped into range) before
 // any of them is used, so the dependent id -> row loads of different rows
-// overlap.
-constexpr int kRows = 4;
+// overlap. Sixteen rows per thread put the whole 8192-id workload in flight in
+// one round of workgroups (four rows per thread took two: 22.8-23.1 against
+// 21.7 us for 8192 rows of 4096 channels).
+constexpr int kRows = 16;
 
 __global__ __launch_bounds__(kThreads) void gather_kernel(
     const uint32_t* __restrict__ table, const uint8_t* __restrict__ block_scale,
