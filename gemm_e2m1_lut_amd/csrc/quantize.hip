@@ -15,12 +15,21 @@
 // eff = fl32(e4m3(bs) * g), the product the dequantisation forms.
 //
 // gfx950 design: both are streaming kernels (2 bytes read per element, about
-// half a byte written). MXFP4: two lanes per 32-column block, 16 elements per
-// lane from two 16-byte loads; the block maximum is one DPP exchange with the
-// partner lane; scaling by 2^(127 - e) is exact; rounding to nearest even is
-// integer arithmetic on the fp32 pattern (one mantissa bit kept above 1,
-// rint(2 a) below). NVFP4: one lane per 16-column block. Each lane stores its
-// 16 codes as one 8-byte word; the block scale byte is stored by one lane.
+// half a byte written). The E2M1 rounding is the hardware's:
+// v_cvt_scalef32_pk_fp4_{bf16,f32} turn two values into two E2M1 codes,
+// dividing by 2^E for the exponent field E of the scale operand and rounding
+// to nearest with ties to the even code, saturating at 6 and keeping the sign
+// of zero -- exactly the rule above (checked on the device against it for
+// every finite bf16 pattern at scales 2^-127 .. 2^100 and for 1.3 million
+// fp32 values, including every value within 300 ulps of each rounding
+// boundary). MXFP4: two lanes per 32-column block, 16 elements per lane from
+// two 16-byte loads; the block maximum is an integer maximum of the magnitude
+// patterns (finite bf16 magnitudes order like their patterns) and one DPP
+// exchange with the partner lane; its exponent field gives e, and the codes
+// come straight from the bf16 pairs with scale 2^(e-127), eight conversions
+// per lane. NVFP4: one lane per 16-column block; the quotients fl32(x / eff)
+// are IEEE divisions, converted with scale 1. Each lane stores its 16 codes as
+// one 8-byte word; the block scale byte is stored by one lane.
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -31,23 +40,6 @@ constexpr int kThreads = 256;
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-
-// E2M1 code (sign in bit 3) of the value nearest to v, ties to the even code,
-// |v| above 6 saturating to 6.
-__device__ __forceinline__ uint32_t e2m1_rne(float v) {
-    const uint32_t sign = (__float_as_uint(v) >> 28) & 8u;
-    const float a = fabsf(v);
-    uint32_t code;
-    if (a < 1.0f) {
-        code = (uint32_t)rintf(2.0f * a);   // 0, 0.5 or 1.0 -> codes 0, 1, 2
-    } else {
-        uint32_t b = __float_as_uint(a);
-        b = (b + 0x1FFFFFu + ((b >> 22) & 1u)) & 0xFFC00000u;   // keep one mantissa bit, ties to even
-        const uint32_t E = (b >> 23) - 127u;
-        code = E >= 3u ? 7u : 2u + 2u * E + ((b >> 22) & 1u);
-    }
-    return sign | code;
-}
 
 // E4M3 (e4m3fn) byte of the value nearest to t >= 0, ties to an even
 // mantissa, saturating at 448.
@@ -60,25 +52,39 @@ __device__ __forceinline__ uint32_t e4m3_rne(float t) {
     return code > 0x7Eu ? 0x7Eu : code;
 }
 
-// 16 codes (4 bits each, element 2i in the low nibble of byte i) of 16 values.
-__device__ __forceinline__ uint2 pack16(const uint32_t (&c)[16]) {
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        lo |= c[i] << (4 * i);
-        hi |= c[8 + i] << (4 * i);
-    }
-    return make_uint2(lo, hi);
+// Eight bf16 pairs (16 elements) of one lane.
+__device__ __forceinline__ void load16(const uint16_t* p, uint32_t (&w)[8]) {
+    const uint4 a = load_nt16(p), b = load_nt16(p + 8);
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+    w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
 }
 
-__device__ __forceinline__ void load16(const uint16_t* p, float (&v)[16]) {
-    const uint4 a = load_nt16(p), b = load_nt16(p + 8);
-    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+// Largest magnitude pattern of the 16 bf16 values (finite inputs).
+__device__ __forceinline__ uint32_t amax_pattern(const uint32_t (&w)[8]) {
+    uint32_t m = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        v[2 * i] = bf16_lo(w[i]);
-        v[2 * i + 1] = bf16_hi(w[i]);
+        const uint32_t a = w[i] & 0x7FFF7FFFu;
+        m = max(m, max(a & 0xFFFFu, a >> 16));
     }
+    return m;
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Codes of 16 bf16 values divided by 2^E (E the exponent field of sc):
+// byte i of the result holds element 2 i (low nibble) and 2 i + 1.
+__device__ __forceinline__ uint2 encode16_bf16(const uint32_t (&w)[8], float sc) {
+    uint32_t lo = 0, hi = 0;
+    lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(lo, __builtin_bit_cast(bf16x2_t, w[0]), sc, 0);
+    lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(lo, __builtin_bit_cast(bf16x2_t, w[1]), sc, 1);
+    lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(lo, __builtin_bit_cast(bf16x2_t, w[2]), sc, 2);
+    lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(lo, __builtin_bit_cast(bf16x2_t, w[3]), sc, 3);
+    hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(hi, __builtin_bit_cast(bf16x2_t, w[4]), sc, 0);
+    hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(hi, __builtin_bit_cast(bf16x2_t, w[5]), sc, 1);
+    hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(hi, __builtin_bit_cast(bf16x2_t, w[6]), sc, 2);
+    hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(hi, __builtin_bit_cast(bf16x2_t, w[7]), sc, 3);
+    return make_uint2(lo, hi);
 }
 
 // Lanes 2 j and 2 j + 1 own block j of the flattened input (every row is a
@@ -91,18 +97,15 @@ __global__ __launch_bounds__(kThreads) void mxfp4_quantize_kernel(const uint16_t
     const int64_t block = lane_id >> 1;
     const int half = (int)(lane_id & 1);
     const int64_t blk = block < nblocks ? block : nblocks - 1;   // the last wave may run past the end
-    float v[16];
-    load16(x + blk * 32 + half * 16, v);
-    float m = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
-    m = fmaxf(m, dpp_f32<0xB1>(m));   // the partner lane's half of the block
-    const int e = m > 0.0f ? min(max(__builtin_amdgcn_frexp_expf(m) - 3 + 127, 0), 254) : 0;
-    uint32_t c[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) c[i] = e2m1_rne(ldexpf(v[i], 127 - e));
+    uint32_t w[8];
+    load16(x + blk * 32 + half * 16, w);
+    uint32_t m = amax_pattern(w);
+    m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, true));   // partner lane's half
+    // floor(log2(amax)) - 2 + 127 is the exponent field minus 2 (subnormal and zero maxima give 0)
+    const int e = max((int)(m >> 7) - 2, 0);
+    const uint2 codes = encode16_bf16(w, __uint_as_float((uint32_t)e << 23));
     if (block < nblocks) {
-        *reinterpret_cast<uint2*>(packed + block * 16 + half * 8) = pack16(c);
+        *reinterpret_cast<uint2*>(packed + block * 16 + half * 8) = codes;
         if (half == 0) scales[block] = (uint8_t)e;
     }
 }
@@ -116,18 +119,36 @@ __global__ __launch_bounds__(kThreads) void nvfp4_quantize_kernel(const uint16_t
     const int64_t block = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     if (block >= nblocks) return;
     const float g = *global_scale;
-    float v[16];
-    load16(x + block * 16, v);
-    float m = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+    uint32_t w[8];
+    load16(x + block * 16, w);
+    const float m = __uint_as_float(amax_pattern(w) << 16);
     const uint32_t bs = e4m3_rne(m / (6.0f * g));
     const float eff = e4m3_to_f32(bs) * g;
-    uint32_t c[16];
+    uint32_t lo = 0, hi = 0;
+    if (eff == 0.0f) {   // signed zero codes
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-        c[i] = eff == 0.0f ? ((__float_as_uint(v[i]) >> 28) & 8u) : e2m1_rne(v[i] / eff);
-    *reinterpret_cast<uint2*>(packed + block * 8) = pack16(c);
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t c = ((w[i] >> 12) & 8u) | ((w[i] >> 24) & 0x80u);   // sign of element 2 i, 2 i + 1
+            if (i < 4) lo |= c << (8 * i);
+            else hi |= c << (8 * (i - 4));
+        }
+    } else {
+        float q[16];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            q[2 * i] = bf16_lo(w[i]) / eff;
+            q[2 * i + 1] = bf16_hi(w[i]) / eff;
+        }
+        lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, q[0], q[1], 1.0f, 0);
+        lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, q[2], q[3], 1.0f, 1);
+        lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, q[4], q[5], 1.0f, 2);
+        lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, q[6], q[7], 1.0f, 3);
+        hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, q[8], q[9], 1.0f, 0);
+        hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, q[10], q[11], 1.0f, 1);
+        hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, q[12], q[13], 1.0f, 2);
+        hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, q[14], q[15], 1.0f, 3);
+    }
+    *reinterpret_cast<uint2*>(packed + block * 8) = make_uint2(lo, hi);
     block_scale[block] = (uint8_t)bs;
 }
 
