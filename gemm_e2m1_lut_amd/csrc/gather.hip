@@ -13,8 +13,8 @@
 // consecutive words of a token row, so every store instruction writes one
 // contiguous kilobyte. v_cvt_scalef32_pk_f32_fp4 with scale 1.0 yields the two
 // signed E2M1 values of a byte exactly (code 8 is -0.0), the multiply is one
-// IEEE fp32 multiply, and the bf16 rounding is the integer round-half-even of
-// device.hpp.
+// IEEE fp32 multiply, and the bf16 rounding is v_cvt_pk_bf16_f32 (the integer
+// round-half-even of device.hpp where a NaN can occur).
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -23,16 +23,35 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// One 32-bit code word (eight channels) -> four words of two bf16 each.
+// Two fp32 products -> two bf16, round to nearest even. v_cvt_pk_bf16_f32
+// rounds exactly as f32_to_bf16_rne for every non-NaN input (subnormals and
+// overflow to infinity included; checked on the device over 5 million
+// patterns) but keeps a NaN's sign and payload, so it is used only when no
+// product can be NaN.
+__device__ __forceinline__ uint32_t bf16x2_rne(f32x2 v) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// One 32-bit code word (eight channels) -> four words of two bf16 each. The
+// codes are finite, so the products are NaN only for a non-finite eff (an
+// E4M3 NaN byte or a non-finite global scale); then every NaN is written as
+// 0x7FC0.
 __device__ __forceinline__ void dequant_word(uint32_t w, float eff, uint32_t* out) {
-    const f32x2 v0 = fp4x2_to_f32x2<0>(w, 1.0f);
-    const f32x2 v1 = fp4x2_to_f32x2<1>(w, 1.0f);
-    const f32x2 v2 = fp4x2_to_f32x2<2>(w, 1.0f);
-    const f32x2 v3 = fp4x2_to_f32x2<3>(w, 1.0f);
-    out[0] = pack_bf16x2(v0.x * eff, v0.y * eff);
-    out[1] = pack_bf16x2(v1.x * eff, v1.y * eff);
-    out[2] = pack_bf16x2(v2.x * eff, v2.y * eff);
-    out[3] = pack_bf16x2(v3.x * eff, v3.y * eff);
+    const f32x2 v0 = fp4x2_to_f32x2<0>(w, 1.0f) * eff;
+    const f32x2 v1 = fp4x2_to_f32x2<1>(w, 1.0f) * eff;
+    const f32x2 v2 = fp4x2_to_f32x2<2>(w, 1.0f) * eff;
+    const f32x2 v3 = fp4x2_to_f32x2<3>(w, 1.0f) * eff;
+    if (__builtin_isfinite(eff)) {
+        out[0] = bf16x2_rne(v0);
+        out[1] = bf16x2_rne(v1);
+        out[2] = bf16x2_rne(v2);
+        out[3] = bf16x2_rne(v3);
+    } else {
+        out[0] = pack_bf16x2(v0.x, v0.y);
+        out[1] = pack_bf16x2(v1.x, v1.y);
+        out[2] = pack_bf16x2(v2.x, v2.y);
+        out[3] = pack_bf16x2(v3.x, v3.y);
+    }
 }
 
 // One thread per packed word (8 channels, half of a 16-channel scale group)
