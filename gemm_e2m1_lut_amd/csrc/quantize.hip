@@ -27,8 +27,9 @@
 // patterns (finite bf16 magnitudes order like their patterns) and one DPP
 // exchange with the partner lane; its exponent field gives e, and the codes
 // come straight from the bf16 pairs with scale 2^(e-127), eight conversions
-// per lane. NVFP4: one lane per 16-column block; the quotients fl32(x / eff)
-// are IEEE divisions, converted with scale 1. Each lane stores its 16 codes as
+// per lane. NVFP4: one lane per 16-column block; the codes of fl32(x / eff)
+// come from a reciprocal multiply bracketed on both sides (IEEE divisions
+// only near a rounding boundary), converted with scale 1. Each lane stores its 16 codes as
 // one 8-byte word; the block scale byte is stored by one lane.
 #include "device.hpp"
 #include "kernels.hpp"
@@ -71,6 +72,16 @@ __device__ __forceinline__ uint32_t amax_pattern(const uint32_t (&w)[8]) {
 }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Byte `sel` of `old` replaced by the codes of a (low nibble) and b, scale 1.
+__device__ __forceinline__ uint32_t cvt_fp4_sel(uint32_t old, float a, float b, int sel) {
+    switch (sel) {   // the byte index is an immediate of the instruction
+        case 0: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, 0);
+        case 1: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, 1);
+        case 2: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, 2);
+        default: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, 3);
+    }
+}
 
 // Codes of 16 bf16 values divided by 2^E (E the exponent field of sc):
 // byte i of the result holds element 2 i (low nibble) and 2 i + 1.
@@ -133,20 +144,36 @@ __global__ __launch_bounds__(kThreads) void nvfp4_quantize_kernel(const uint16_t
             else hi |= c << (8 * (i - 4));
         }
     } else {
-        float q[16];
+        // The code of fl32(x / eff) without the divisions where possible: with
+        // q = x * rcp(eff) (v_rcp_f32 within one ulp), fl32(x / eff) lies within
+        // 2^-22 of q relatively, and the E2M1 code is monotonic in q, so when
+        // q (1 - 2^-18) and q (1 + 2^-18) get the same code, fl32(x / eff)
+        // gets it too. A lane with any pair where they differ (q near a
+        // rounding boundary), or with eff outside [2^-125, 2^125], divides.
+        const float rinv = __builtin_amdgcn_rcpf(eff);
+        uint32_t lo2 = 0, hi2 = 0;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            q[2 * i] = bf16_lo(w[i]) / eff;
-            q[2 * i + 1] = bf16_hi(w[i]) / eff;
+            const float q0 = bf16_lo(w[i]) * rinv, q1 = bf16_hi(w[i]) * rinv;
+            const float d0 = q0 * 0x1.00001p-18f, d1 = q1 * 0x1.00001p-18f;
+            if (i < 4) {
+                lo = cvt_fp4_sel(lo, q0 - d0, q1 - d1, i);
+                lo2 = cvt_fp4_sel(lo2, q0 + d0, q1 + d1, i);
+            } else {
+                hi = cvt_fp4_sel(hi, q0 - d0, q1 - d1, i - 4);
+                hi2 = cvt_fp4_sel(hi2, q0 + d0, q1 + d1, i - 4);
+            }
         }
-        lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, q[0], q[1], 1.0f, 0);
-        lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, q[2], q[3], 1.0f, 1);
-        lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, q[4], q[5], 1.0f, 2);
-        lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, q[6], q[7], 1.0f, 3);
-        hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, q[8], q[9], 1.0f, 0);
-        hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, q[10], q[11], 1.0f, 1);
-        hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, q[12], q[13], 1.0f, 2);
-        hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, q[14], q[15], 1.0f, 3);
+        if (lo != lo2 || hi != hi2 || !(eff >= 0x1p-125f && eff <= 0x1p125f)) {
+            lo = 0;
+            hi = 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float q0 = bf16_lo(w[i]) / eff, q1 = bf16_hi(w[i]) / eff;
+                if (i < 4) lo = cvt_fp4_sel(lo, q0, q1, i);
+                else hi = cvt_fp4_sel(hi, q0, q1, i - 4);
+            }
+        }
     }
     *reinterpret_cast<uint2*>(packed + block * 8) = make_uint2(lo, hi);
     block_scale[block] = (uint8_t)bs;
