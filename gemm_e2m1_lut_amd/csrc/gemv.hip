@@ -544,10 +544,17 @@ __global__ __launch_bounds__(kWave * kMaxSliceWaves) void gemv_mfma_kernel(
         uint4 xg[NJ];
         load_x(xg, 0);
         issue_here();
-        // code lines: load (st, q) of lane l is row 8 q + l / 8 of the tile, block 8 st + l % 8
-        // (eight rows x 128 contiguous bytes per instruction); scale bytes straight in MFMA layout
+        // scale bytes straight in MFMA layout, then the code lines: load (st, q) of lane l is row
+        // 8 q + l / 8 of the tile, block 8 st + l % 8 (eight rows x 128 contiguous bytes per
+        // instruction). Loads complete in order: with the scales first, half step 2 st waits only
+        // for the lines of steps <= st, so the first MFMAs overlap the later lines' arrival
+        // (scales last: 14.0 -> 12.9 us at batch 8, 17.3 -> 15.8 at batch 16, 14336 x 4096).
         uint4 wl[kTileSteps][2];
         uint32_t e[kHalfSteps];
+#pragma unroll
+        for (int hs = 0; hs < kHalfSteps; ++hs)
+            e[hs] = srow[min(wv * kSliceBlocks + 8 * (hs >> 1) + g + 4 * (hs & 1), kc - 1)];
+        issue_here();
         const uint8_t* lrow[2];
 #pragma unroll
         for (int q = 0; q < 2; ++q) lrow[q] = packed + (size_t)min(tile * 16 + 8 * q + (lane >> 3), n - 1) * (K / 2);
@@ -557,9 +564,6 @@ __global__ __launch_bounds__(kWave * kMaxSliceWaves) void gemv_mfma_kernel(
 #pragma unroll
             for (int q = 0; q < 2; ++q) wl[st][q] = load_nt16(lrow[q] + (size_t)b * 16);
         }
-#pragma unroll
-        for (int hs = 0; hs < kHalfSteps; ++hs)
-            e[hs] = srow[min(wv * kSliceBlocks + 8 * (hs >> 1) + g + 4 * (hs & 1), kc - 1)];
         issue_here();
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         uint4 wm[2];   // this step's blocks g and g + 4 of row r (MFMA layout)
