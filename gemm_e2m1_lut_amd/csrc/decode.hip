@@ -91,21 +91,44 @@ __device__ __forceinline__ void decode_word(uint32_t p, const BytePlanes& t, uin
 
 constexpr int kThreads = 256;
 
-// One thread per packed word (8 codes): a 4-byte load, the word's scale byte
-// (shared by the 4 words of a 32-column block), one 16-byte store. Consecutive
-// lanes read consecutive words and write consecutive 16-byte pieces, so every
-// wave-wide store instruction writes one contiguous kilobyte.
+// One lane per packed word (8 codes): a 4-byte load, the word's scale byte
+// (shared by the 4 words of a 32-column block), one 16-byte store. A wave
+// takes runs of 64 kWordsPerLane consecutive words, lane l the words
+// 64 j + l: the loads of all kWordsPerLane words (and their scale bytes) are
+// issued before any is decoded, and every store instruction writes one
+// contiguous kilobyte. (One word per lane and iteration kept a single 4-byte
+// load in flight per lane: 29.1 against 27.5 us for 14336 x 4096; four words
+// per lane measured the same as eight, sixteen 29.1 us.)
+constexpr int kWordsPerLane = 8;
+
 __global__ __launch_bounds__(kThreads) void decode_kernel(const uint32_t* __restrict__ packed,
                                                           const uint8_t* __restrict__ scales,
                                                           uint4* __restrict__ out,
                                                           int64_t nwords) {
-    const int64_t stride = (int64_t)gridDim.x * kThreads;
-    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nwords; i += stride) {
-        const uint32_t p = __builtin_nontemporal_load(packed + i);
-        const BytePlanes t = scaled_planes(scales[i >> 2]);
-        uint32_t w[4];
-        decode_word(p, t, w);
-        store_nt16(out + i, w[0], w[1], w[2], w[3]);
+    const int lane = threadIdx.x & (kWave - 1);
+    constexpr int64_t kRun = (int64_t)kWave * kWordsPerLane;   // words per wave and iteration
+    const int64_t nruns = (nwords + kRun - 1) / kRun;
+    const int64_t waves = (int64_t)gridDim.x * (kThreads / kWave);
+    for (int64_t run = (int64_t)blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave; run < nruns;
+         run += waves) {   // wave-uniform
+        const int64_t base = run * kRun + lane;
+        uint32_t p[kWordsPerLane];
+        uint8_t e[kWordsPerLane];
+#pragma unroll
+        for (int j = 0; j < kWordsPerLane; ++j) {
+            const int64_t i = min(base + (int64_t)kWave * j, nwords - 1);
+            p[j] = __builtin_nontemporal_load(packed + i);
+            e[j] = scales[i >> 2];
+        }
+#pragma unroll
+        for (int j = 0; j < kWordsPerLane; ++j) {
+            const int64_t i = base + (int64_t)kWave * j;
+            if (i < nwords) {
+                uint32_t w[4];
+                decode_word(p[j], scaled_planes(e[j]), w);
+                store_nt16(out + i, w[0], w[1], w[2], w[3]);
+            }
+        }
     }
 }
 
@@ -121,7 +144,7 @@ __global__ __launch_bounds__(kThreads) void fill_zero_kernel(uint16_t* __restric
 hipError_t launch_decode(const uint8_t* packed, const uint8_t* scales, uint16_t* out,
                          int64_t nblocks, hipStream_t stream) {
     const int64_t nwords = nblocks * 4;
-    const int64_t want = (nwords + kThreads - 1) / kThreads;
+    const int64_t want = (nwords + (int64_t)kThreads * kWordsPerLane - 1) / ((int64_t)kThreads * kWordsPerLane);
     const int64_t cap = (int64_t)device_cu_count() * 32;
     const int grid = (int)(want < cap ? want : cap);
     decode_kernel<<<grid, kThreads, 0, stream>>>(reinterpret_cast<const uint32_t*>(packed), scales,
