@@ -27,6 +27,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import math
 import os
@@ -65,14 +66,22 @@ KERNEL_SOURCES = {
 COMMON_SOURCES = ["device.hpp"]
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and blank space: edits to comments leave the
+    kernels, and so the counters taken for them, unchanged."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(" ".join(line.split()) for line in text.splitlines() if line.strip())
+
+
 def kernel_source_hash(label: str) -> str:
     family = label.split("_")[0]
     h = hashlib.sha256()
     for name in sorted(KERNEL_SOURCES.get(family, []) + COMMON_SOURCES):
         path = os.path.join(CSRC, name)
         if os.path.exists(path):
-            with open(path, "rb") as fh:
-                h.update(name.encode() + fh.read())
+            with open(path, encoding="utf-8") as fh:
+                h.update((name + _code_only(fh.read())).encode())
     return h.hexdigest()[:16]
 
 

@@ -28,14 +28,14 @@
 //   * Batch 2..4 with 1024 < K <= 16384: the batch-1 tile kernel with the
 //     activation rows side by side in registers, B dot2 per decoded pair.
 //   * Batch 2..16 otherwise (batch 5..16, or K <= 1024): the same weight
-//     bytes feed bf16 MFMA
-//     (v_mfma_f32_16x16x32_bf16) with the batch as the N dimension: a
-//     workgroup takes a tile of 16 rows, its S waves split K into slices of
-//     1024 columns, each lane decodes its 16-byte chunks straight into A
-//     operands and reads the matching x words from the cache hierarchy as B
-//     operands (columns past the batch or the row end read as zero). Every
-//     weight byte is still read once; the S partial 16 x 16 tiles meet in LDS
-//     and are summed in a fixed order.
+//     bytes feed bf16 MFMA (v_mfma_f32_16x16x32_bf16) with the batch as the
+//     N dimension: a workgroup takes a tile of 16 rows, its S waves split K
+//     into slices of 1024 columns; each wave loads its code lines coalesced
+//     (eight rows x 128 bytes per instruction) and turns them into A operands
+//     through a per-wave LDS transpose, and stages each half step's x columns
+//     in LDS for the B operands (rows past the batch and columns past the
+//     row end read as zero). Every weight byte is still read once; the S
+//     partial 16 x 16 tiles meet in LDS and are summed in a fixed order.
 //   * K beyond the tiled kernels (K > 16384 at batch 2..16, K > 32768 at
 //     batch 1): one wave per row, lanes across K, x read per chunk.
 #include "device.hpp"
