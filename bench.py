@@ -839,7 +839,7 @@ def main() -> int:
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
-              "(this build has no multi-GPU path; see DESIGN.md for how it would shard)", file=sys.stderr)
+              "(the library runs on one GPU; its value is that GPU's throughput)", file=sys.stderr)
         return 2
 
     import torch
