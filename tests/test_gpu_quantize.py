@@ -56,7 +56,9 @@ def test_mxfp4_every_bf16_pattern(gpu, orc):
     check_mx(gpu, orc, np.roll(v, 16).reshape(-1, 32))
 
 
-@pytest.mark.parametrize("gs", [1.0, 0.01, 1.0 / 6.0, 3e-5, 7.25])
+# 1e-37 and 1e35 put eff = e4m3(bs) * gs below 2^-125 (tiny blocks: eff subnormal) and above
+# 2^125 (saturated blocks), where the kernel takes the IEEE divisions instead of a reciprocal.
+@pytest.mark.parametrize("gs", [1.0, 0.01, 1.0 / 6.0, 3e-5, 7.25, 1e-37, 1e35])
 def test_nvfp4_every_bf16_pattern(gpu, orc, gs):
     check_nv(gpu, orc, all_finite_bf16().reshape(-1, 64), gs)
 
