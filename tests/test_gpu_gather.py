@@ -41,7 +41,9 @@ def test_every_scale_byte_and_code(gpu, orc):
     table = np.tile(np.arange(256, dtype=np.uint8), (256, 1))        # hidden 512
     bscale = np.repeat(np.arange(256, dtype=np.uint8)[:, None], 32, axis=1)
     ids = np.arange(256, dtype=np.int64)
-    for gs in (0.01, 1.0, 0.37):
+    # 1e-39: products in the bf16 subnormal range; 1e37 and 3e38: products and eff overflow to
+    # infinity (a zero code then gives NaN, written as 0x7FC0)
+    for gs in (0.01, 1.0, 0.37, 1e-39, 1e37, 3e38):
         got = run_gather(gpu, table, bscale, gs, ids)
         want, _ = orc.nvfp4_gather(table, bscale, gs, ids)
         assert np.array_equal(got, want), gs
