@@ -74,9 +74,17 @@ def _code_only(text: str) -> str:
     return "\n".join(" ".join(line.split()) for line in text.splitlines() if line.strip())
 
 
-def kernel_source_hash(label: str) -> str:
+def build_fingerprint() -> str:
+    """The compiler flags and offload target the library is built with: a flag change alters
+    the machine code (and so the counters) as much as a source edit does."""
+    from gemm_e2m1_lut_amd import build as hip_build
+    return " ".join(hip_build.HIPFLAGS)
+
+
+def kernel_source_hash(label: str, flags: str | None = None) -> str:
     family = label.split("_")[0]
     h = hashlib.sha256()
+    h.update((build_fingerprint() if flags is None else flags).encode())
     for name in sorted(KERNEL_SOURCES.get(family, []) + COMMON_SOURCES):
         path = os.path.join(CSRC, name)
         if os.path.exists(path):

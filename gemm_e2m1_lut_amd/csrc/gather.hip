@@ -92,11 +92,16 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(
         }
         uint32_t p[kRows];
         uint32_t sb[kRows];
+        if (vocab > 0) {   // an empty table is never read (it may be NULL): every row is out of range
 #pragma unroll
-        for (int i = 0; i < kRows; ++i) {
-            const int64_t r = (id[i] >= 0 && id[i] < vocab) ? id[i] : 0;
-            p[i] = __builtin_nontemporal_load(table + r * wpr + cc);
-            sb[i] = block_scale[r * (wpr / 2) + (cc >> 1)];
+            for (int i = 0; i < kRows; ++i) {
+                const int64_t r = (id[i] >= 0 && id[i] < vocab) ? id[i] : 0;
+                p[i] = __builtin_nontemporal_load(table + r * wpr + cc);
+                sb[i] = block_scale[r * (wpr / 2) + (cc >> 1)];
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < kRows; ++i) p[i] = sb[i] = 0u;
         }
 #pragma unroll
         for (int i = 0; i < kRows; ++i) {

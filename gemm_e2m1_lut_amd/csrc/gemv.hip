@@ -12,21 +12,22 @@
 //     (zero codes give +/-0, which add nothing to a sum). v_dot2_f32_bf16
 //     multiplies the pair by the matching pair of x and accumulates in fp32:
 //     per byte of weights one conversion and one dot2.
-//   * Batch 1 (the bandwidth-bound case): a wave owns a tile of 16 rows x
-//     1024 columns (32 chunks of one scale block each): eight coalesced
-//     16-byte loads, each covering two rows x 512 bytes, issued at once, with
-//     the 32 lanes of a half-wave on one row and each lane's slice of x in
-//     registers. A workgroup holds the S = K / 1024 waves of one row tile,
-//     whose partial row sums meet in LDS; the hardware streams through the
-//     tiles (one workgroup each), which measured faster on these sizes than
-//     keeping rows in flight from a resident grid. Every weight byte is read
-//     once; the eight row-pair totals of a lane are reduced over 32 lanes
-//     together, as a transposed butterfly (v_permlane16_swap and DPP).
-//     Longer rows (K > 16384) are split over the waves of a workgroup, one
-//     chunk per lane, with three rows in flight; short rows (K <= 1024) use
-//     groups of 8 to 32 lanes per row.
-//   * Batch 2..4 with 1024 < K <= 16384: the batch-1 tile kernel with the
-//     activation rows side by side in registers, B dot2 per decoded pair.
+//   * Batch 1 (the bandwidth-bound case): every load instruction reads one
+//     row x 1 KB contiguous (lane l the 16-byte chunk l of a 64-chunk slice),
+//     each lane's slice of x sits in registers, and every weight load of a
+//     wave is issued before its first use. Up to K = 4096 a single wave owns
+//     four whole rows (two chunks per lane at K = 4096), so nothing passes
+//     through LDS; up to K = 16384 a workgroup of S = K / 2048 waves owns 16
+//     rows, wave w the slice w, and the S partial row sums meet in LDS. The row
+//     sums of a wave come out of one transposed reduction over its 64 lanes
+//     (v_permlane32_swap, v_permlane16_swap and DPP). Every weight byte is read
+//     once. Longer rows (K > 16384) are split over the waves of a workgroup,
+//     one chunk per lane, with three rows in flight; short rows (K <= 1024)
+//     use groups of 8 to 32 lanes per row.
+//   * Batch 2..4 with 1024 < K <= 16384: a workgroup of S = K / 1024 waves
+//     owns 16 rows, each load instruction reads two rows x 512 bytes, and the
+//     B activation rows sit side by side in registers: B dot2 per decoded
+//     pair.
 //   * Batch 2..16 otherwise (batch 5..16, or K <= 1024): the same weight
 //     bytes feed bf16 MFMA (v_mfma_f32_16x16x32_bf16) with the batch as the
 //     N dimension: a workgroup takes a tile of 16 rows, its S waves split K
@@ -96,42 +97,43 @@ __device__ __forceinline__ float group_total(float v) {
     return v;
 }
 
-// Totals of N per-lane values over each half wave (32 lanes), reduced as a
-// transposed butterfly. Stage s (s = 4 .. 0) pairs every lane with one whose
-// lane-index bit s differs (bit 4 through v_permlane16_swap, bits 3..0
-// through the DPP row mirror, half-row mirror and quad permutations); while a
-// lane holds an even number m of values it halves them, the lane with bit s
-// clear keeping the pair sums of values [0, m/2) and the other those of
-// [m/2, m); with an odd m it adds its partner's values to all of its own.
-// On return v[0 .. half_totals_count<N>()) of lane L hold the totals of
-// value indices half_totals_base<N>(L) + j, and lanes that differ only in the
-// low half_totals_dup_bits<N>() bits of the lane index hold the same ones.
-// Against one five-step DPP reduction per value this costs about 2.5 instead
-// of 5 operations per value for N >= 8, and the independent pairs of a stage
-// fill the DPP wait states.
-template <int N>
-constexpr int half_totals_count() {
+// Totals of N per-lane values over aligned groups of 2^(Top+1) lanes (Top = 4:
+// each half wave; Top = 5: the whole wave), reduced as a transposed butterfly.
+// Stage s (s = Top .. 0) pairs every lane with one whose lane-index bit s
+// differs (bit 5 through v_permlane32_swap, bit 4 through v_permlane16_swap,
+// bits 3..0 through the DPP row mirror, half-row mirror and quad
+// permutations); while a lane holds an even number m of values it halves
+// them, the lane with bit s clear keeping the pair sums of values [0, m/2)
+// and the other those of [m/2, m); with an odd m it adds its partner's values
+// to all of its own. On return v[0 .. lane_totals_count<Top, N>()) of lane L
+// hold the totals of value indices lane_totals_base<Top, N>(L) + j, and lanes
+// that differ only in the low lane_totals_dup_bits<Top, N>() bits of the lane
+// index hold the same ones. Against one DPP reduction per value this costs
+// about 2.5 instead of 5 or 6 operations per value for N >= 8, and the
+// independent pairs of a stage fill the DPP wait states.
+template <int Top, int N>
+constexpr int lane_totals_count() {
     int m = N;
-    for (int st = 4; st >= 0; --st)
+    for (int st = Top; st >= 0; --st)
         if (m % 2 == 0) m /= 2;
     return m;
 }
 
-template <int N>
-constexpr int half_totals_dup_bits() {
+template <int Top, int N>
+constexpr int lane_totals_dup_bits() {
     int m = N, bits = 0;
-    for (int st = 4; st >= 0; --st) {
+    for (int st = Top; st >= 0; --st) {
         if (m % 2 == 0) m /= 2;
         else ++bits;
     }
     return bits;
 }
 
-template <int N>
-__device__ __forceinline__ int half_totals_base(int lane) {
+template <int Top, int N>
+__device__ __forceinline__ int lane_totals_base(int lane) {
     int m = N, base = 0;
 #pragma unroll
-    for (int st = 4; st >= 0; --st)
+    for (int st = Top; st >= 0; --st)
         if (m % 2 == 0) {
             m /= 2;
             base += ((lane >> st) & 1) * m;
@@ -140,49 +142,55 @@ __device__ __forceinline__ int half_totals_base(int lane) {
 }
 
 template <int St>
-__device__ __forceinline__ float half_partner(float v) {   // lane-index bit St flipped, St < 4
+__device__ __forceinline__ float lane_partner(float v) {   // lane-index bit St flipped, St < 4
     if constexpr (St == 3) return dpp_f32<0x140>(v);   // row_mirror: lane i <-> 15 - i
     if constexpr (St == 2) return dpp_f32<0x141>(v);   // row_half_mirror: i <-> 7 - i
     if constexpr (St == 1) return dpp_f32<0x4E>(v);    // quad_perm [2,3,0,1]
     return dpp_f32<0xB1>(v);                           // quad_perm [1,0,3,2]
 }
 
+// a + b exchanged across lane-index bit St (5 or 4): lanes with the bit clear
+// get a(L) + a(L ^ 2^St), lanes with it set b(L ^ 2^St) + b(L).
+template <int St>
+__device__ __forceinline__ float swap_sum(float a, float b) {
+    if constexpr (St == 5) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+        return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    } else {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+        return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+}
+
 template <int St, int M>
-__device__ __forceinline__ void half_totals_stage(float* v, int lane) {
+__device__ __forceinline__ void lane_totals_stage(float* v, int lane) {
     if constexpr (M % 2 == 0) {
         constexpr int H = M / 2;
         const bool upper = (lane >> St) & 1;
 #pragma unroll
         for (int j = 0; j < H; ++j) {
-            if constexpr (St == 4) {   // rows 2i and 2i+1: even rows keep v[j], odd rows v[j + H]
-                const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[j]), __float_as_uint(v[j + H]),
-                                                                false, false);
-                v[j] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+            if constexpr (St >= 4) {   // the swap leaves v[j] pairs on bit-clear lanes, v[j + H] pairs on the others
+                v[j] = swap_sum<St>(v[j], v[j + H]);
             } else {
                 const float keep = upper ? v[j + H] : v[j];
                 const float send = upper ? v[j] : v[j + H];
-                v[j] = keep + half_partner<St>(send);
+                v[j] = keep + lane_partner<St>(send);
             }
         }
-        if constexpr (St > 0) half_totals_stage<St - 1, H>(v, lane);
+        if constexpr (St > 0) lane_totals_stage<St - 1, H>(v, lane);
     } else {
 #pragma unroll
         for (int j = 0; j < M; ++j) {
-            if constexpr (St == 4) {
-                const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[j]), __float_as_uint(v[j]),
-                                                                false, false);
-                v[j] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-            } else {
-                v[j] += half_partner<St>(v[j]);
-            }
+            if constexpr (St >= 4) v[j] = swap_sum<St>(v[j], v[j]);
+            else v[j] += lane_partner<St>(v[j]);
         }
-        if constexpr (St > 0) half_totals_stage<St - 1, M>(v, lane);
+        if constexpr (St > 0) lane_totals_stage<St - 1, M>(v, lane);
     }
 }
 
-template <int N>
-__device__ __forceinline__ void half_totals(float (&v)[N], int lane) {
-    half_totals_stage<4, N>(v, lane);
+template <int Top, int N>
+__device__ __forceinline__ void lane_totals(float (&v)[N], int lane) {
+    lane_totals_stage<Top, N>(v, lane);
 }
 
 // Batch 1. A group of G lanes covers one row; lane gl owns the 32-column chunks
@@ -278,62 +286,89 @@ __device__ __forceinline__ void load_x_chunk(uint32_t (&xr)[16], const uint16_t*
     }
 }
 
-// Batch 1, 32 < K/32 <= 32 S: one workgroup of S waves per tile of 16 rows.
-// Wave w owns chunks 32 w .. 32 w + 31; lane l takes chunk 32 w + (l % 32)
-// of rows 2 q + l / 32 (q = 0..7), so each load instruction reads two rows
-// x 512 contiguous bytes. Chunks past the row end are loaded clamped and
-// their partial sums dropped (E2M1 codes times a clamped E8M0 scale are
-// always finite). The eight 32-lane row sums of a wave come out of one
-// transposed reduction (half_totals), meet those of the other waves in LDS
-// and are summed in a fixed order.
-template <int S, bool kBf16Out>
-__global__ __launch_bounds__(kWave * S) void gemv_b1_tile_kernel(const uint8_t* packed, const uint8_t* scales,
+// Batch 1, 32 < K/32 <= 512: a workgroup of S waves owns R consecutive rows;
+// wave w covers the chunks 64 (CPL w + i) + l (i < CPL) of every row, lane l
+// taking those with index l, so each load instruction reads one row x 1 KB
+// contiguous (the fastest read pattern of the platform: one row per
+// instruction instead of two half rows, a quarter fewer x bytes per weight
+// byte at K = 4096). x for the lane's chunks is loaded once, before the
+// weights (loads complete in order, so the first block waits only for x and
+// its own line). Chunks past the row end are loaded clamped and their partial
+// sums dropped (E2M1 codes times a clamped E8M0 scale are always finite). The
+// R row sums of a wave come out of one transposed reduction over the 64
+// lanes; with S = 1 (K <= 64 CPL chunks, one wave per four whole rows, no LDS
+// and no barrier) the lanes that hold them store directly, otherwise the S
+// wave partials meet in LDS and are summed in a fixed order.
+template <int S, int CPL, int R, bool kBf16Out>
+__global__ __launch_bounds__(kWave * S) void gemv_b1_rows_kernel(const uint8_t* packed, const uint8_t* scales,
                                                                  const uint16_t* __restrict__ x,
                                                                  void* __restrict__ y, int n, int kc) {
-    __shared__ float part[S][16];
+    __shared__ float part[S][R];
     const int lane = threadIdx.x & (kWave - 1);
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int half = lane >> 5, cl = lane & 31;
-    const int c_raw = wv * 32 + cl;
-    const bool cvalid = c_raw < kc;
-    const int c = min(c_raw, kc - 1);
+    const int row0 = blockIdx.x * R;
     const uint4* pv = reinterpret_cast<const uint4*>(packed);
-    uint32_t xr[16];
-    load_x_chunk(xr, x, c, kc);
-    issue_here();
-    const int tile = blockIdx.x;
-    uint4 w[8];
-    uint8_t e[8];   // kept as bytes: widened at use
+    int c[CPL];
+    bool cvalid[CPL];
+    uint32_t xr[CPL][16];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        const int row = min(tile * 16 + 2 * q + half, n - 1);
-        const int64_t blk = (int64_t)row * kc + c;
-        w[q] = load_nt16(pv + blk);
-        e[q] = scales[blk];
+    for (int ci = 0; ci < CPL; ++ci) {
+        const int c_raw = (wv * CPL + ci) * kWave + lane;
+        cvalid[ci] = c_raw < kc;
+        c[ci] = min(c_raw, kc - 1);
+        load_x_chunk(xr[ci], x, c_raw, kc);
     }
     issue_here();
-    float tot[8];
+    uint4 w[CPL][R];
+    uint8_t e[CPL][R];   // kept as bytes: widened at use
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        const float p = block_dot(w[q], e8m0_scale(e[q]), xr, 0.f);
-        tot[q] = cvalid ? p : 0.f;
-    }
-    half_totals(tot, lane);   // lane L: total of row pair q = half_totals_base<8>(L)
-    if ((lane & ((1 << half_totals_dup_bits<8>()) - 1)) == 0) part[wv][2 * half_totals_base<8>(lane) + half] = tot[0];
-    __syncthreads();
-    if (threadIdx.x < 16) {
-        float sum = 0.f;
+    for (int ci = 0; ci < CPL; ++ci)
 #pragma unroll
-        for (int j = 0; j < S; ++j) sum += part[j][threadIdx.x];
-        const int row = tile * 16 + threadIdx.x;
-        if (row < n) store_out<kBf16Out>(y, row, sum);
+        for (int r = 0; r < R; ++r) {
+            const int64_t blk = (int64_t)min(row0 + r, n - 1) * kc + c[ci];
+            w[ci][r] = load_nt16(pv + blk);
+            e[ci][r] = scales[blk];
+        }
+    issue_here();
+    float tot[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) tot[r] = 0.f;
+#pragma unroll
+    for (int ci = 0; ci < CPL; ++ci)
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const float p = block_dot(w[ci][r], e8m0_scale(e[ci][r]), xr[ci], 0.f);
+            tot[r] += cvalid[ci] ? p : 0.f;
+        }
+    lane_totals<5>(tot, lane);   // lane L: totals of rows base + j
+    constexpr int kDup = lane_totals_dup_bits<5, R>();
+    const int base = lane_totals_base<5, R>(lane);
+    if constexpr (S == 1) {
+        if ((lane & ((1 << kDup) - 1)) == 0) {
+#pragma unroll
+            for (int j = 0; j < lane_totals_count<5, R>(); ++j)
+                if (row0 + base + j < n) store_out<kBf16Out>(y, row0 + base + j, tot[j]);
+        }
+    } else {
+        if ((lane & ((1 << kDup) - 1)) == 0) {
+#pragma unroll
+            for (int j = 0; j < lane_totals_count<5, R>(); ++j) part[wv][base + j] = tot[j];
+        }
+        __syncthreads();
+        if (threadIdx.x < R) {
+            float sum = 0.f;
+#pragma unroll
+            for (int j = 0; j < S; ++j) sum += part[j][threadIdx.x];
+            const int row = row0 + threadIdx.x;
+            if (row < n) store_out<kBf16Out>(y, row, sum);
+        }
     }
 }
 
-// Batch 2..4, 32 < K/32 <= 32 S: the batch-1 tile layout above (one
-// workgroup of S waves per tile of 16 rows, lane l taking chunk 32 w + l % 32
-// of rows 2 q + l / 32, two rows x 512 contiguous bytes per load instruction)
-// with the B activation rows' words of the lane's chunk in registers: each
+// Batch 2..4, 32 < K/32 <= 32 S: one workgroup of S waves per tile of 16
+// rows, lane l taking chunk 32 w + l % 32 of rows 2 q + l / 32 (two rows x
+// 512 contiguous bytes per load instruction), with the B activation rows'
+// words of the lane's chunk in registers: each
 // decoded code pair meets them in B v_dot2_f32_bf16, so the decode is shared
 // by the batch and nothing but the row totals passes through LDS. The work
 // per weight byte grows with B (one conversion, B dot2 and B shares of the
@@ -387,11 +422,11 @@ __global__ __launch_bounds__(kWave * S) void gemv_bn_tile_kernel(const uint8_t* 
             tot[8 * b + q] = cvalid ? a : 0.f;
         }
     }
-    half_totals(tot, lane);   // lane L: totals of value indices base + j = 8 b + q
-    if ((lane & ((1 << half_totals_dup_bits<8 * B>()) - 1)) == 0) {
-        const int base = half_totals_base<8 * B>(lane);
+    lane_totals<4>(tot, lane);   // lane L: totals of value indices base + j = 8 b + q
+    if ((lane & ((1 << lane_totals_dup_bits<4, 8 * B>()) - 1)) == 0) {
+        const int base = lane_totals_base<4, 8 * B>(lane);
 #pragma unroll
-        for (int j = 0; j < half_totals_count<8 * B>(); ++j) {
+        for (int j = 0; j < lane_totals_count<4, 8 * B>(); ++j) {
             const int idx = base + j;
             part[wv][idx / 8][2 * (idx % 8) + half] = tot[j];
         }
@@ -702,11 +737,11 @@ hipError_t run_b1(const uint8_t* packed, const uint8_t* scales, const uint16_t* 
     return run_b1_r<G, CPL, 4, kBf16Out>(packed, scales, x, y, n, kc, cap4, stream);
 }
 
-template <int S, bool kBf16Out>
-hipError_t run_b1_tile(const uint8_t* packed, const uint8_t* scales, const uint16_t* x, void* y, int n, int kc,
+template <int S, int CPL, int R, bool kBf16Out>
+hipError_t run_b1_rows(const uint8_t* packed, const uint8_t* scales, const uint16_t* x, void* y, int n, int kc,
                        hipStream_t stream) {
-    const int tiles = (n + 15) / 16;   // one workgroup per tile of 16 rows
-    gemv_b1_tile_kernel<S, kBf16Out><<<tiles, kWave * S, 0, stream>>>(packed, scales, x, y, n, kc);
+    const int blocks = (n + R - 1) / R;   // one workgroup per R rows
+    gemv_b1_rows_kernel<S, CPL, R, kBf16Out><<<blocks, kWave * S, 0, stream>>>(packed, scales, x, y, n, kc);
     return hipGetLastError();
 }
 
@@ -746,18 +781,18 @@ hipError_t dispatch_b1(const uint8_t* packed, const uint8_t* scales, const uint1
     if (kc <= 8) return run_b1<8, 1, kBf16Out>(packed, scales, x, y, n, kc, stream);
     if (kc <= 16) return run_b1<16, 1, kBf16Out>(packed, scales, x, y, n, kc, stream);
     if (kc <= 32) return run_b1<32, 1, kBf16Out>(packed, scales, x, y, n, kc, stream);
-    if (kc <= 16 * 32) {
-        switch ((kc + 31) / 32) {
-#define E2M1_TILE_CASE(S) \
-    case S: return run_b1_tile<S, kBf16Out>(packed, scales, x, y, n, kc, stream);
-            E2M1_TILE_CASE(2) E2M1_TILE_CASE(3) E2M1_TILE_CASE(4) E2M1_TILE_CASE(5) E2M1_TILE_CASE(6)
-            E2M1_TILE_CASE(7) E2M1_TILE_CASE(8) E2M1_TILE_CASE(9) E2M1_TILE_CASE(10) E2M1_TILE_CASE(11)
-            E2M1_TILE_CASE(12) E2M1_TILE_CASE(13) E2M1_TILE_CASE(14) E2M1_TILE_CASE(15)
-            default: return run_b1_tile<16, kBf16Out>(packed, scales, x, y, n, kc, stream);
-#undef E2M1_TILE_CASE
-        }
-    }
-    switch ((kc + kWave - 1) / kWave) {
+    // one wave per four whole rows (14336 x 4096: 6.6 us per launch against 6.7
+    // for 16-row tiles of two half-row waves)
+    if (kc <= 64) return run_b1_rows<1, 1, 4, kBf16Out>(packed, scales, x, y, n, kc, stream);
+    if (kc <= 128) return run_b1_rows<1, 2, 4, kBf16Out>(packed, scales, x, y, n, kc, stream);
+    switch ((kc + kWave - 1) / kWave) {   // 16-row tiles, one 64-chunk slice per wave
+        case 3: return run_b1_rows<3, 1, 16, kBf16Out>(packed, scales, x, y, n, kc, stream);
+        case 4: return run_b1_rows<4, 1, 16, kBf16Out>(packed, scales, x, y, n, kc, stream);
+        case 5: return run_b1_rows<5, 1, 16, kBf16Out>(packed, scales, x, y, n, kc, stream);
+        case 6: return run_b1_rows<6, 1, 16, kBf16Out>(packed, scales, x, y, n, kc, stream);
+        case 7: return run_b1_rows<7, 1, 16, kBf16Out>(packed, scales, x, y, n, kc, stream);
+        case 8: return run_b1_rows<8, 1, 16, kBf16Out>(packed, scales, x, y, n, kc, stream);
+        // K > 16384: row slabs streamed through 9..16 waves
         case 9: return run_b1_split<9, kBf16Out>(packed, scales, x, y, n, kc, stream);
         case 10: return run_b1_split<10, kBf16Out>(packed, scales, x, y, n, kc, stream);
         case 11: return run_b1_split<11, kBf16Out>(packed, scales, x, y, n, kc, stream);

@@ -280,7 +280,9 @@ int ternary_wl_gemv(const uint32_t* const packed[4], const float* scale, const f
  *                     err_flag is given, stores 1 there (never cleared by
  *                     the library).
  * Requires vocab >= 0, hidden >= 0, hidden % 16 == 0 (the page's
- * create_weights divisibility guard), num_tokens >= 0.
+ * create_weights divisibility guard), num_tokens >= 0. With vocab == 0 the
+ * table and block_scale may be NULL and are never read: every id is out of
+ * range, so every row is written as zeros and err_flag is set.
  */
 int nvfp4_embedding_gather(const uint8_t* table, const uint8_t* block_scale_e4m3,
                            const float* global_scale, const int64_t* ids, uint16_t* out_bf16,

@@ -39,3 +39,13 @@ def test_every_committed_traffic_record_matches_its_sources():
     stale = [label for label, rec in records.items()
              if "kernel_source_hash" in rec and rec["kernel_source_hash"] != bench.kernel_source_hash(label)]
     assert stale == []
+
+
+def test_build_flags_change_the_fingerprint():
+    """A record taken under other compiler flags or another offload target is stale too."""
+    flags = bench.build_fingerprint()
+    assert "--offload-arch=" in flags
+    same = bench.kernel_source_hash("gemv_b1_14336x4096", flags)
+    assert same == bench.kernel_source_hash("gemv_b1_14336x4096")
+    assert same != bench.kernel_source_hash("gemv_b1_14336x4096", flags.replace("xnack-", "xnack+"))
+    assert same != bench.kernel_source_hash("gemv_b1_14336x4096", flags.replace("-O3", "-O2"))

@@ -84,3 +84,28 @@ def test_empty(gpu):
                                      f32(np.array([1.0], np.float32)),
                                      torch.zeros((0,), dtype=torch.int64, device="cuda:0"))
     assert out.shape == (0, 16)
+
+
+def test_empty_vocabulary(gpu):
+    """vocab == 0 with tokens: the table is never read (NULL is allowed), every row is zeros and
+    the error flag is set (regression: the kernel used to read row 0 of the empty table)."""
+    say("gather: empty vocabulary, NULL table, 5 ids")
+    ids = torch.tensor([0, 1, -1, 7, 2**33], dtype=torch.int64, device="cuda:0")
+    out = torch.full((5, 64), -1, dtype=torch.int16, device="cuda:0")
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    gs = torch.tensor([0.01], dtype=torch.float32, device="cuda:0")
+    lib = gpu.load_library()
+    st = lib.nvfp4_embedding_gather(None, None, gs.data_ptr(), ids.data_ptr(), out.data_ptr(), 0, 64, 5,
+                                    flag.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    torch.cuda.synchronize()
+    assert int(flag.item()) == 1
+    assert int(torch.count_nonzero(out).item()) == 0
+    # through the binding, with an empty (0, hidden/2) table
+    flag.zero_()
+    got = gpu.nvfp4_embedding_gather(torch.zeros((0, 32), dtype=torch.uint8, device="cuda:0"),
+                                     torch.zeros((0, 4), dtype=torch.uint8, device="cuda:0"), gs, ids,
+                                     err_flag=flag)
+    torch.cuda.synchronize()
+    assert int(flag.item()) == 1
+    assert int(torch.count_nonzero(got.view(torch.int16)).item()) == 0

@@ -47,10 +47,12 @@ def test_small_workload_fp32(gpu, orc):
 
 SHAPES = [
     (8, 32, 1), (5, 96, 1), (33, 256, 1), (70, 512, 1), (129, 1024, 1),   # 8 to 32 lanes per row
-    (300, 32 * (64 * 2 + 5), 1),      # row tiles of 16, five waves, the last one ragged
-    (257, 4096, 1), (77, 8192, 1),    # row tiles: four and eight waves, ragged last tile
-    (64, 8192 + 32, 1),               # nine waves, one chunk in the last
-    (1001, 14336, 1),                 # fourteen waves (the down projection's K)
+    (45, 1056, 1), (99, 3104, 1),     # one wave per four rows: one and two chunks per lane, ragged
+    (4099, 4096, 1),                  # one wave per four rows, ragged last group
+    (300, 32 * (64 * 2 + 5), 1),      # row tiles of 16, three waves, the last one ragged
+    (257, 4096, 1), (77, 8192, 1),    # four rows per wave; 16-row tiles of four waves
+    (64, 8192 + 32, 1),               # five waves, one chunk in the last
+    (1001, 14336, 1),                 # seven waves (the down projection's K)
     (40, 16384 + 32 * 3, 1), (50, 32768, 1),   # K-split kernel, 9 and 16 waves
     (20, 32768 + 32, 1),              # beyond the batch-1 kernels -> generic kernel
     (70001, 2048, 1),                 # many row tiles, ragged last one
