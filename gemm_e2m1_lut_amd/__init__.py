@@ -8,7 +8,8 @@ in the library's kernels.
 
 Operations: dequant_decode, dequant_gemv, dequant_gemm, ternary_gemv, ternary_gemm,
 ternary_wl_gemv, nvfp4_embedding_gather, mxfp4_moe_gemm (+
-mxfp4_moe_workspace_size), nm_spmm (N:M structured-sparse weights), and the
+mxfp4_moe_workspace_size, and mxfp4_moe_gemm_noalloc for callers that cannot
+allocate), nm_spmm (N:M structured-sparse weights), and the
 encoders mxfp4_quantize, nvfp4_quantize.
 """
 from ._binding import (  # noqa: F401
@@ -26,6 +27,8 @@ from ._binding import (  # noqa: F401
     library_path,
     load_library,
     mxfp4_moe_gemm,
+    mxfp4_moe_gemm_noalloc,
+    MOE_NOALLOC_WORKSPACE_BYTES,
     mxfp4_moe_workspace_size,
     mxfp4_quantize,
     nvfp4_embedding_gather,

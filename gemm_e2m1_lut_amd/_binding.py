@@ -64,6 +64,8 @@ def load_library() -> ctypes.CDLL:
         "mxfp4_moe_workspace_size": (sz, [i64, i64, i64, i64, i64]),
         "mxfp4_moe_gemm": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i64, i64,
                                           i64, vp]),
+        "mxfp4_moe_gemm_noalloc": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                                  vp]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -384,4 +386,34 @@ def mxfp4_moe_gemm(x: torch.Tensor, w13: torch.Tensor, w13_scale: torch.Tensor, 
                                          _ptr(topk_ids), _ptr(topk_weights), _ptr(out), _ptr(workspace),
                                          workspace.numel(), tokens, hidden, inter, experts, topk,
                                          _stream(stream)))
+    return out
+
+
+# Per-GPU workspace of mxfp4_moe_gemm_noalloc inside the library (E2M1_MOE_NOALLOC_WORKSPACE_BYTES).
+MOE_NOALLOC_WORKSPACE_BYTES = 32 << 20
+
+
+def mxfp4_moe_gemm_noalloc(x: torch.Tensor, w13: torch.Tensor, w13_scale: torch.Tensor, w2: torch.Tensor,
+                           w2_scale: torch.Tensor, topk_ids: torch.Tensor, topk_weights: torch.Tensor,
+                           out: torch.Tensor, stream=None) -> torch.Tensor:
+    """mxfp4_moe_gemm with the library's own fixed per-GPU workspace: nothing is allocated,
+    so `out` must be given. Calls that overlap on one GPU race (they share that workspace)."""
+    _need(x, "x", (torch.bfloat16,))
+    tokens, hidden = x.shape
+    _need(w13, "w13", _U8)
+    experts, two_inter, _ = w13.shape
+    inter = two_inter // 2
+    _need(w13, "w13", _U8, (experts, 2 * inter, hidden // 2))
+    _need(w13_scale, "w13_scale", _U8, (experts, 2 * inter, hidden // 32))
+    _need(w2, "w2", _U8, (experts, hidden, inter // 2))
+    _need(w2_scale, "w2_scale", _U8, (experts, hidden, inter // 32))
+    _need(topk_ids, "topk_ids", (torch.int32,))
+    topk = topk_ids.shape[1]
+    _need(topk_ids, "topk_ids", (torch.int32,), (tokens, topk))
+    _need(topk_weights, "topk_weights", (torch.float32,), (tokens, topk))
+    _need(out, "out", (torch.bfloat16,), (tokens, hidden))
+    _check("mxfp4_moe_gemm_noalloc",
+           load_library().mxfp4_moe_gemm_noalloc(_ptr(x), _ptr(w13), _ptr(w13_scale), _ptr(w2), _ptr(w2_scale),
+                                                 _ptr(topk_ids), _ptr(topk_weights), _ptr(out), tokens, hidden,
+                                                 inter, experts, topk, _stream(stream)))
     return out

@@ -4,6 +4,8 @@
 // synchronises; on a negative status nothing was launched.
 #include <limits.h>
 
+#include <mutex>
+
 #include "e2m1lut.h"
 #include "kernels.hpp"
 
@@ -38,6 +40,34 @@ inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s);
 hipError_t fill_zero_bytes(void* dst, int64_t bytes, hipStream_t stream) {
     // Outputs are arrays of 2- or 4-byte elements: clear them as uint16.
     return e2m1::launch_fill_zero_u16(reinterpret_cast<uint16_t*>(dst), bytes / 2, stream);
+}
+
+// Workspace of mxfp4_moe_gemm_noalloc: one fixed array per GPU, held by the
+// loaded code object until the process ends. In host code `scratch` names a
+// host-side stand-in, not device memory, so it is never passed to a kernel or
+// a copy: its device address is looked up once per device (with that device
+// current, on the first call there) and that address is what the kernels get.
+static __device__ __align__(256) uint8_t scratch[E2M1_MOE_NOALLOC_WORKSPACE_BYTES];
+
+constexpr int kMaxDevices = 64;
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_status[kMaxDevices];
+std::once_flag g_scratch_once[kMaxDevices];
+
+// Device address of the current device's `scratch` array.
+hipError_t scratch_address(void** ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::call_once(g_scratch_once[dev], [dev] {
+        void* p = nullptr;
+        g_scratch_status[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = g_scratch_status[dev] == hipSuccess ? p : nullptr;
+    });
+    if (g_scratch_status[dev] != hipSuccess) return g_scratch_status[dev];
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 }  // namespace
@@ -236,6 +266,23 @@ int mxfp4_moe_gemm(const uint16_t* x, const uint8_t* w13, const uint8_t* w13_sca
     return launch_status(e2m1::launch_moe(x, w13, w13_scale, w2, w2_scale, topk_ids, topk_weights,
                                           out, workspace, tokens, hidden, inter, experts, topk,
                                           as_stream(stream)));
+}
+
+int mxfp4_moe_gemm_noalloc(const uint16_t* x, const uint8_t* w13, const uint8_t* w13_scale,
+                           const uint8_t* w2, const uint8_t* w2_scale, const int32_t* topk_ids,
+                           const float* topk_weights, uint16_t* out, int64_t tokens,
+                           int64_t hidden, int64_t inter, int64_t experts, int64_t topk,
+                           void* stream) {
+    const size_t need = mxfp4_moe_workspace_size(tokens, hidden, inter, experts, topk);
+    if (need == (size_t)-1 || experts > E2M1_MOE_MAX_EXPERTS || hidden > INT_MAX || inter > INT_MAX)
+        return E2M1_ERR_SHAPE;
+    if (need > E2M1_MOE_NOALLOC_WORKSPACE_BYTES) return E2M1_ERR_WORKSPACE;
+    if (tokens == 0 || hidden == 0) return E2M1_OK;
+    void* ws = nullptr;
+    if (scratch_address(&ws) != hipSuccess) return E2M1_ERR_LAUNCH;
+    // the same validation and launches as the workspace entry point
+    return mxfp4_moe_gemm(x, w13, w13_scale, w2, w2_scale, topk_ids, topk_weights, out, ws,
+                          E2M1_MOE_NOALLOC_WORKSPACE_BYTES, tokens, hidden, inter, experts, topk, stream);
 }
 
 }  // extern "C"

@@ -327,6 +327,29 @@ int mxfp4_moe_gemm(const uint16_t* x, const uint8_t* w13, const uint8_t* w13_sca
                    size_t workspace_bytes, int64_t tokens, int64_t hidden, int64_t inter,
                    int64_t experts, int64_t topk, void* stream);
 
+/*
+ * mxfp4_moe_gemm_noalloc -- mxfp4_moe_gemm for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc. Same operation, arguments (minus the workspace),
+ * layouts, kernels and results as mxfp4_moe_gemm; the workspace is instead a
+ * fixed array inside the library, E2M1_MOE_NOALLOC_WORKSPACE_BYTES per GPU,
+ * which every GPU the library is loaded on holds until the process ends. The
+ * call allocates nothing (no hipMalloc, no library allocation).
+ * Returns E2M1_ERR_WORKSPACE, before touching the GPU, when
+ * mxfp4_moe_workspace_size() of the extents exceeds that maximum (32 MiB:
+ * up to 485 tokens at top-4 with hidden = inter = 2880). Every call on one GPU
+ * shares that GPU's array, which keeps the last call's contents (the layer
+ * needs none of it to start at zero): calls that overlap on one GPU (on other
+ * streams or from other host threads) race and must be serialised by the
+ * caller.
+ */
+#define E2M1_MOE_NOALLOC_WORKSPACE_BYTES ((size_t)32 << 20)
+int mxfp4_moe_gemm_noalloc(const uint16_t* x, const uint8_t* w13, const uint8_t* w13_scale,
+                           const uint8_t* w2, const uint8_t* w2_scale, const int32_t* topk_ids,
+                           const float* topk_weights, uint16_t* out, int64_t tokens,
+                           int64_t hidden, int64_t inter, int64_t experts, int64_t topk,
+                           void* stream);
+
 #ifdef __cplusplus
 }
 #endif

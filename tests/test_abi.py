@@ -38,7 +38,8 @@ def lib():
 def test_header_declares_the_five_operations():
     names = declared_functions()
     for op in ("dequant_decode", "dequant_gemv", "ternary_gemv", "ternary_gemm", "ternary_wl_gemv", "mxfp4_quantize", "nvfp4_quantize", "dequant_gemm", "nm_spmm", "nvfp4_embedding_gather",
-               "mxfp4_moe_gemm", "mxfp4_moe_workspace_size", "e2m1_abi_version", "e2m1_strerror"):
+               "mxfp4_moe_gemm", "mxfp4_moe_workspace_size", "mxfp4_moe_gemm_noalloc", "e2m1_abi_version",
+               "e2m1_strerror"):
         assert op in names
 
 
@@ -213,6 +214,22 @@ def test_moe_validation(lib):
     assert f(*args, P(0x90000), small, 4, 48, 64, 2, 1, NULL) == E_SHAPE
     assert f(NULL, *args[1:], P(0x90000), small, 4, 64, 64, 2, 1, NULL) == E_NULL
     assert f(NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 0, 0, 64, 64, 2, 1, NULL) == E2M1_OK
+
+
+def test_moe_noalloc_validation(lib):
+    """The no-allocation MoE rejects, on the host and before any GPU call, extents whose
+    workspace exceeds its fixed per-GPU array."""
+    f = lib.mxfp4_moe_gemm_noalloc
+    ws = lib.mxfp4_moe_workspace_size
+    limit = 32 << 20
+    assert ws(485, 2880, 2880, 32, 4) <= limit < ws(486, 2880, 2880, 32, 4)
+    args = [A, B, C, D, P(0x50000), P(0x60000), P(0x70000), P(0x80000)]
+    assert f(*args, 486, 2880, 2880, 32, 4, NULL) == E_WS
+    assert f(*args, 100000, 64, 64, 2, 1, NULL) == E_WS
+    assert f(NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 486, 2880, 2880, 32, 4, NULL) == E_WS
+    assert f(*args, 4, 48, 64, 2, 1, NULL) == E_SHAPE      # hidden % 32
+    assert f(*args, 4, 64, 64, 513, 1, NULL) == E_SHAPE    # too many experts
+    assert f(NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 0, 64, 64, 2, 1, NULL) == E2M1_OK
 
 
 def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
