@@ -11,11 +11,15 @@
 // A operand of word q, byte b of dword j is the weight of column
 // 16 q + j + 4 b.
 //
-// Activations: X = rint(x 2^S) with |X| <= 2^30, one exponent S per group of
-// values sharing a scale (from their largest |x|), written as four signed
-// base-256 digits. Digit columns of the B operand list, for the same columns
-// and in the same order as the A operand, digit i of X; the int32 products
-// are exact and digit column i is worth 2^(8 i - S).
+// Activations: one exponent S per group of values sharing a scale (from
+// their largest |x|), so that |x 2^S| < 2^30; x 2^S = H + L 2^-30 with H its
+// integer part and L = rint of its fraction times 2^30, both written as four
+// signed base-256 digits. That is a 60-bit fixed point: every element of at
+// least 2^-36 times the group's largest |x| is represented exactly, any other
+// to within 2^-60 times that largest. Digit columns of the B operand list, for the same
+// columns and in the same order as the A operand, digit i of H (worth
+// 2^(8 i - S)) or of L (worth 2^(8 i - S - 30)); the int32 products are
+// exact.
 #pragma once
 
 #include "device.hpp"
@@ -40,18 +44,28 @@ __device__ __forceinline__ float wave_max(float v) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
-// Exponent S with |x 2^S| <= 2^30 for every |x| <= m (m = 0 gives 30).
+// Exponent S with |x 2^S| < 2^30 for every |x| <= m (m = 0 gives 30).
 __device__ __forceinline__ int slice_exponent(float m) {
     return 30 - __builtin_amdgcn_frexp_expf(m);
 }
 
-// The four signed base-256 digits of X = rint(x 2^S), |X| <= 2^30, as the
-// bytes of one word: X + 0x808080 has unsigned low bytes u_i with
-// X = sum (u_i - 128) 256^i + u_3 256^3, and xor 0x80 turns u_i into the
-// int8 pattern of u_i - 128.
-__device__ __forceinline__ uint32_t digits(float x, int S) {
-    const int X = (int)rintf(ldexpf(x, S));
+// The four signed base-256 digits of an integer |X| <= 2^30 as the bytes of
+// one word: X + 0x808080 has unsigned low bytes u_i with X = sum (u_i - 128)
+// 256^i + u_3 256^3, and xor 0x80 turns u_i into the int8 pattern of u_i - 128.
+__device__ __forceinline__ uint32_t digit_bytes(int X) {
     return ((uint32_t)X + 0x00808080u) ^ 0x00808080u;
+}
+
+// Digits of x 2^S (|x 2^S| < 2^30): hi those of the integer part H, lo those
+// of L = rint(fraction 2^30). t, its integer part and the fraction are exact
+// in fp32 (scaling by a power of two, truncation, and the difference of a
+// number and its integer part); only L rounds, for elements with bits below
+// 2^(-S-30).
+__device__ __forceinline__ void digits8(float x, int S, uint32_t& hi, uint32_t& lo) {
+    const float t = ldexpf(x, S);
+    const float h = truncf(t);
+    hi = digit_bytes((int)h);
+    lo = digit_bytes((int)rintf(ldexpf(t - h, 30)));
 }
 
 // 4 x 4 byte transpose: byte b of out[i] = byte i of in[b].

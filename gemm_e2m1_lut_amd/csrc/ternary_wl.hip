@@ -18,18 +18,20 @@
 //     word gives the fields j, j + 4, j + 8, j + 12 as v_perm_b32 selectors
 //     into a 4-byte pool, so one perm decodes four weights (11 VALU
 //     operations per 16-weight word).
-//   * B operand: x_re and x_im in fixed point, X = rint(x 2^S) with
-//     |X| <= 2^30 and one exponent S per part and 256-column slice (from the
-//     slice's largest |x|), written as four signed base-256 digits (one add
-//     and one xor of 0x00808080 turn X into its digit bytes). The eight digit
-//     columns of x_re and x_im fill half of the sixteen B columns.
+//   * B operand: x_re and x_im in fixed point with one exponent S per part
+//     and 256-column slice (from the slice's largest |x|): x 2^S = H +
+//     L 2^-30, H the integer part and L the rounded fraction in units of
+//     2^-30, each written as four signed base-256 digits (one add and one xor
+//     of 0x00808080 turn an integer into its digit bytes). The sixteen digit
+//     columns (H and L of x_re, then of x_im) fill the B operand.
 //   * v_mfma_i32_16x16x64_i8 sums ternary times digit exactly in int32; per
-//     slice the four digit columns are scaled by 2^(8 i - S) into fp32.
-// So every row sum is exact for x on its slice's grid of 2^-S: x is used to
-// within 2^-31 of the slice's largest |x| (more than fp32's own precision
-// for the elements near that maximum), and the only other roundings are a
-// few fp32 additions per row.
-//
+//     slice digit column i of H is scaled by 2^(8 i - S) into fp32, of L by
+//     2^(8 i - S - 30).
+// So every row sum is exact for x on its slice's grid of 2^(-S-30): every
+// element of at least 2^-36 times its slice's largest |x| is used exactly,
+// any other to within 2^-60 times that largest, and the only other roundings
+// are a few fp32 additions per row.
+
 // Work split: a workgroup owns a tile of 16 rows; its waves take 256-column
 // slices (slice s of wave w = w, w + waves, ...). Lane l = 16 g + r loads the
 // 16-byte chunk 4 s + g of row r of each matrix (four words, 64 columns) and
@@ -40,10 +42,10 @@
 // its own slice (lane l: columns 16 q + j + 4 b of chunk l >> 4, word
 // l >> 2 & 3, dword j = l & 3, b = 0..3, for both parts) in its own LDS area
 // and reads them back as B operands, with no workgroup barrier. D element
-// (row 4 g + j, column c) sits in component j of lane 16 g + c: the digit
-// columns of each part are added by DPP within each 16-lane row, the waves
-// through LDS, and one thread per row and component applies the four scales
-// and the signs of the complex product. Inputs the fast kernel cannot take
+// (row 4 g + j, column c) sits in component j of lane 16 g + c: the eight
+// digit columns of each part are added by DPP within each 16-lane row, the
+// waves through LDS, and one thread per row and component applies the four
+// scales and the signs of the complex product. Inputs the fast kernel cannot take
 // (K % 64 != 0, unaligned matrices) use a one-wave-per-row kernel that adds,
 // subtracts or skips each x directly in fp32.
 #include "device.hpp"
@@ -55,8 +57,7 @@ namespace {
 
 constexpr int kMaxWaves = 16;
 constexpr int kSliceChunks = 4;                          // 64-column chunks per wave slice
-constexpr int kVariants = 8;                             // digits 0..3 of x_re, then of x_im
-constexpr int kRowDwords = 16;                           // B operand dwords of one (chunk, variant)
+constexpr int kVariants = 16;                            // H then L digits of x_re, then of x_im
 constexpr int kRowPitch = 20;                            // dwords per row in LDS (spreads the banks)
 constexpr int kWaveDwords = kSliceChunks * kVariants * kRowPitch;
 constexpr int kPartFloats = 4 * 2 * 16;                  // (matrix, part, row) partial sums
@@ -66,7 +67,7 @@ struct WlMats {
 };
 
 size_t wl_lds_bytes(int waves) {
-    return 4u * ((size_t)waves * kWaveDwords + kRowDwords + (size_t)waves * kPartFloats + kPartFloats);
+    return 4u * ((size_t)waves * kWaveDwords + (size_t)waves * kPartFloats + kPartFloats);
 }
 
 // Fast kernel: K % 64 == 0, matrices 16-byte aligned.
@@ -78,8 +79,7 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void ternary_wl_kernel(WlMats ma
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     uint32_t* tab = wl_smem + wave * kWaveDwords;
-    uint32_t* zero = wl_smem + nwaves * kWaveDwords;
-    float* part = reinterpret_cast<float*>(zero + kRowDwords);
+    float* part = reinterpret_cast<float*>(wl_smem + nwaves * kWaveDwords);
     float* tot = part + nwaves * kPartFloats;
     const int g = lane >> 4, r = lane & 15, c = lane & 15;
     const int K = 64 * kq;
@@ -88,10 +88,10 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void ternary_wl_kernel(WlMats ma
     // digit preparation: lane -> chunk pg, word pq, dword pj; columns 64 pg + 16 pq + pj + 4 b
     const int pg = lane >> 4, pq = (lane >> 2) & 3, pj = lane & 3;
     uint32_t* prep_row = tab + pg * kVariants * kRowPitch + 4 * pq + pj;
-    const i32x4* b_row = reinterpret_cast<const i32x4*>(c < kVariants ? tab + (g * kVariants + c) * kRowPitch : zero);
-
-    if (threadIdx.x < kRowDwords) zero[threadIdx.x] = 0u;
-    __syncthreads();
+    const i32x4* b_row = reinterpret_cast<const i32x4*>(tab + (g * kVariants + c) * kRowPitch);
+    // digit column c: part c >> 3 (x_re, x_im), fraction digits for c & 4, digit c & 3
+    const bool c_im = c & 8;
+    const int c_shift = 8 * (c & 3) - ((c & 4) ? 30 : 0);
 
     for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {   // workgroup-uniform
         const int row = min(tile * 16 + r, n - 1);
@@ -127,19 +127,24 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void ternary_wl_kernel(WlMats ma
                                                          fmaxf(fabsf(xr[2]), fabsf(xr[3])))));
             const int Si = slice_exponent(wave_max(fmaxf(fmaxf(fabsf(xi[0]), fabsf(xi[1])),
                                                          fmaxf(fabsf(xi[2]), fabsf(xi[3])))));
-            uint32_t dr[4], di[4], tr[4], ti[4];
+            uint32_t hr[4], lr[4], hi_[4], li[4], t[4];
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
-                dr[b] = digits(xr[b], Sr);
-                di[b] = digits(xi[b], Si);
+                digits8(xr[b], Sr, hr[b], lr[b]);
+                digits8(xi[b], Si, hi_[b], li[b]);
             }
-            transpose4(dr, tr);
-            transpose4(di, ti);
+            transpose4(hr, t);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                prep_row[i * kRowPitch] = tr[i];
-                prep_row[(4 + i) * kRowPitch] = ti[i];
-            }
+            for (int i = 0; i < 4; ++i) prep_row[i * kRowPitch] = t[i];
+            transpose4(lr, t);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) prep_row[(4 + i) * kRowPitch] = t[i];
+            transpose4(hi_, t);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) prep_row[(8 + i) * kRowPitch] = t[i];
+            transpose4(li, t);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) prep_row[(12 + i) * kRowPitch] = t[i];
             __builtin_amdgcn_wave_barrier();   // LDS accesses of one wave complete in order
             i32x4 bq[4];
 #pragma unroll
@@ -155,8 +160,8 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void ternary_wl_kernel(WlMats ma
                     acc[m] = __builtin_amdgcn_mfma_i32_16x16x64_i8(decode_word(ws[q] & mask), bq[q], acc[m], 0, 0, 0);
                 }
             }
-            // digit column c is worth 2^(8 (c & 3) - S) of its part; |acc| <= 2^15, exact in fp32
-            const int e = 8 * (c & 3) - ((c & 4) ? Si : Sr);
+            // digit column c is worth 2^(c_shift - S) of its part; |acc| <= 2^15, exact in fp32
+            const int e = c_shift - (c_im ? Si : Sr);
 #pragma unroll
             for (int m = 0; m < 4; ++m)
 #pragma unroll
@@ -164,7 +169,7 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void ternary_wl_kernel(WlMats ma
             __builtin_amdgcn_wave_barrier();   // the B reads are done before the next slice's digits
         }
 
-        // digits of x_re (columns 0..3) and of x_im (4..7): the sums land in lanes c = 3 and c = 7
+        // digits of x_re (columns 0..7) and of x_im (8..15): the sums land in lanes c = 7 and c = 15
         float s[4][4];
 #pragma unroll
         for (int m = 0; m < 4; ++m)
@@ -173,10 +178,11 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void ternary_wl_kernel(WlMats ma
                 float v = f[m][j];
                 v += dpp_f32<0x111>(v);   // row_shr:1
                 v += dpp_f32<0x112>(v);   // row_shr:2
+                v += dpp_f32<0x114>(v);   // row_shr:4
                 s[m][j] = v;
             }
-        if (c == 3 || c == 7) {
-            float* dst = part + wave * kPartFloats + (c == 7 ? 16 : 0) + 4 * g;
+        if (c == 7 || c == 15) {
+            float* dst = part + wave * kPartFloats + (c == 15 ? 16 : 0) + 4 * g;
 #pragma unroll
             for (int m = 0; m < 4; ++m)
 #pragma unroll

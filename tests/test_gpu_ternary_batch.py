@@ -2,15 +2,15 @@
 
 Tolerance, derived from the arithmetic of the fast kernel: it sums ternary
 weights times a fixed-point rendering of each activation row exactly in int32
-(per row and 256-column slice, X = rint(x 2^S) with 2^-S <= 2^-29 times the
-slice's largest |x|, so each element is off by at most 2^-30 M_b, M_b the
-largest |x| of row b), then rounds at most k/256 + 24 times in fp32 (slice
-sums, digit columns, waves, the row scale), each at most 2^-23 of the row's
-magnitude. Element by element,
-    |y - y_oracle| <= (k/256 + 24) 2^-23 s sum_c |t_c x_b,c| + 2^-30 M_b s sum_c |t_c| + 2^-23 |y_oracle|,
+(per row and 256-column slice, x 2^S = H + L 2^-30 with |x 2^S| < 2^30: every
+element of at least 2^-36 M_b is exact and any other is off by at most
+2^-60 M_b, M_b the largest |x| of row b), then rounds at most k/256 + 24
+times in fp32 (slice sums, digit columns, waves, the row scale), each at most
+2^-23 of the row's magnitude. Element by element,
+    |y - y_oracle| <= (k/256 + 24) 2^-23 s sum_c |t_c x_b,c| + 2^-60 M_b s sum_c |t_c| + 2^-23 |y_oracle|,
 and the relative L2 error over the output stays below 2e-6. Inputs that take
 the per-row ternary GEMV instead (K not a multiple of 64, unaligned weights)
-are held to that kernel's bar, rel-L2 <= 1e-3 (x split into bf16 hi + lo).
+are held to that kernel's bar, rel-L2 <= 1e-3 (plain fp32 adds of x).
 
 Covers the 4096 x 4096 matrix at every batch 1..16, ragged row tiles and
 slices, several slices per wave, workgroups that loop over tiles, rows of
@@ -65,7 +65,7 @@ def check(g, orc, case, packed_dev=None, fast=True):
         mag, cnt = row_sums(case["packed"], case["x"])
         s = np.abs(case["row_scale"].astype(np.float64))[None, :]
         M = np.abs(case["x"]).max(axis=1).astype(np.float64)[:, None]
-        bound = (k / 256 + 24) * 2.0 ** -23 * s * mag + 2.0 ** -30 * M * s * cnt[None, :] + 2.0 ** -23 * np.abs(want)
+        bound = (k / 256 + 24) * 2.0 ** -23 * s * mag + 2.0 ** -60 * M * s * cnt[None, :] + 2.0 ** -23 * np.abs(want)
         assert (np.abs(got - want) <= bound).all()
         assert err <= 2e-6, err
     else:

@@ -2,20 +2,20 @@
 
 Tolerance, derived from the arithmetic of the fast kernel. It sums ternary
 weights times a fixed-point rendering of x exactly in int32: per 256-column
-slice and part, X = rint(x 2^S) with 2^-S <= 2^-29 times the slice's largest
-|x|, so each element is off by at most 2^-30 M (M = largest |x| of that part
-over all of K). The integer sums then pass through at most k/256 + 32 fp32
+slice and part, x 2^S = H + L 2^-30 with |x 2^S| < 2^30, so every element of
+at least 2^-36 M is exact and any other is off by at most 2^-60 M (M = largest
+|x| of that part over all of K). The integer sums then pass through at most k/256 + 32 fp32
 roundings (slice sums, digit columns, waves, scales and the complex
 combination), each at most 2^-23 (2u, to allow for an adder that truncates)
 of the row's magnitude. Hence, element by element,
-    |y - y_oracle| <= (k/256 + 32) 2^-23 mag + 2^-30 (M_re + M_im) cnt + 2^-23 |y_oracle|
+    |y - y_oracle| <= (k/256 + 32) 2^-23 mag + 2^-60 (M_re + M_im) cnt + 2^-23 |y_oracle|
 with mag = sum_m s_m sum_c |t_mc| (|x_re,c| + |x_im,c|) and
 cnt = sum_m s_m sum_c |t_mc|. The one-wave-per-row kernel (plain fp32 adds
 of x) meets the same form with k roundings: its cases use (k + 32) in place
 of (k/256 + 32). On top of that the relative L2 error must stay below 2e-6:
-a correct kernel lands near 1e-7, while losing the lowest digit of x (x kept
-to 24 bits below the slice maximum) or one fp32 piece would show at 1e-6 to
-1e-5.
+a correct kernel lands near 1e-7, while losing the fraction digits of x (x
+kept to 30 bits below the slice maximum) or one fp32 piece would show at 1e-6
+to 1e-5.
 
 Covers the 4096 x 4096 layer (full output), one and several slices per wave,
 workgroups that loop over tiles, ragged row tiles and slices, the
@@ -63,7 +63,7 @@ def bound(case, y64, generic=False):
     mag, cnt = magnitudes(case)
     big = float(np.abs(case["x_re"]).max(initial=0.0)) + float(np.abs(case["x_im"]).max(initial=0.0))
     steps = (k if generic else k / 256) + 32
-    return steps * 2.0 ** -23 * mag + 2.0 ** -30 * big * cnt + 2.0 ** -23 * np.abs(y64)
+    return steps * 2.0 ** -23 * mag + 2.0 ** -60 * big * cnt + 2.0 ** -23 * np.abs(y64)
 
 
 def run(g, case, mats=None):
