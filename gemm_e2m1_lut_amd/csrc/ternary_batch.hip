@@ -12,15 +12,16 @@
 // the four base-256 digits of its integer part, then those of its fraction),
 // so a decoded A operand serves ceil(batch / 2) MFMAs; the int32 sums are
 // exact and each digit column is scaled into fp32 per 256-column slice. A
-// workgroup owns a tile of 16 output rows and its waves take 256-column
-// slices; lane l = 16 g + r loads the 16-byte chunk 4 s + g of row r (four
+// workgroup owns a tile of 16 output rows (one workgroup per tile) and its
+// waves take 256-column slices; lane l = 16 g + r loads the 16-byte chunk 4 s + g of row r (four
 // words) and decodes word q as the A operand of one MFMA per group. Each wave
 // writes the digits of its own slice into its own LDS area (lane l: columns
 // 16 q + j + 4 b of chunk l >> 4, word l >> 2 & 3, dword j = l & 3, b = 0..3,
 // of every row of the group) and reads them back as B operands, with no
 // workgroup barrier. D element (output row 4 g + j, column c) is component j
 // of lane 16 g + c; the eight digit columns of each activation row are added
-// by DPP, the waves through LDS, and the row scale multiplies the total once.
+// by DPP, the waves through LDS (one barrier), and the row scale multiplies
+// the total once.
 // Inputs the fast kernel cannot take (K % 64 != 0, unaligned weights) run the
 // ternary GEMV once per activation row.
 #include "device.hpp"
@@ -38,7 +39,7 @@ constexpr int kRowPitch = 20;                                 // dwords per (chu
 constexpr int kWaveDwords = kSliceChunks * kColumns * kRowPitch;
 
 size_t gemm_lds_bytes(int waves, int groups) {
-    return 4u * ((size_t)waves * kWaveDwords + (size_t)waves * groups * 32 + (size_t)groups * 32);
+    return 4u * ((size_t)waves * kWaveDwords + (size_t)waves * groups * 32);
 }
 
 template <int NG>
@@ -51,122 +52,211 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void ternary_gemm_kernel(const u
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     uint32_t* tab = tg_smem + wave * kWaveDwords;
     float* part = reinterpret_cast<float*>(tg_smem + nwaves * kWaveDwords);   // [waves][NG * 2 rows][16]
-    float* tot = part + nwaves * NG * 32;                                     // [NG * 2 rows][16]
     const int g = lane >> 4, r = lane & 15, c = lane & 15;
     const int K = 64 * kq;
     const int nslices = (kq + kSliceChunks - 1) / kSliceChunks;
-    const int ntiles = (n + 15) / 16;
     // digit preparation: lane -> chunk pg, word pq, dword pj; columns 64 pg + 16 pq + pj + 4 b
     const int pg = lane >> 4, pq = (lane >> 2) & 3, pj = lane & 3;
     uint32_t* prep_row = tab + pg * kColumns * kRowPitch + 4 * pq + pj;
     const i32x4* b_row = reinterpret_cast<const i32x4*>(tab + (g * kColumns + c) * kRowPitch);
     // digit column c: activation row c >> 3 of the group, fraction digits for c & 4, digit c & 3
     const int c_row = c >> 3, c_shift = 8 * (c & 3) - ((c & 4) ? 30 : 0);
+    const int tile = blockIdx.x;   // one tile of 16 output rows per workgroup
+    const int row = min(tile * 16 + r, n - 1);
+    float f[NG][4];
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) f[gi][j] = 0.f;
 
-    for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {   // workgroup-uniform
-        const int row = min(tile * 16 + r, n - 1);
-        float f[NG][4];
+    for (int sl = wave; sl < nslices; sl += nwaves) {   // wave-uniform
+        const int col0 = 256 * sl + 64 * pg + 16 * pq + pj;
+        float xv[kGroupRows][4];   // [row of the group][b]
 #pragma unroll
-        for (int gi = 0; gi < NG; ++gi)
+        for (int bl = 0; bl < kGroupRows; ++bl) {
+            if (bl > 0 && bl >= batch) break;   // uniform: rows past the batch are not prepared
+            const float* xr = x + (int64_t)bl * K;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) f[gi][j] = 0.f;
-
-        for (int sl = wave; sl < nslices; sl += nwaves) {   // wave-uniform
-            const int col0 = 256 * sl + 64 * pg + 16 * pq + pj;
-            float xv[kGroupRows][4];   // [row of the group][b]
+            for (int b = 0; b < 4; ++b) xv[bl][b] = xr[min(col0 + 4 * b, K - 1)];
+        }
+        issue_fence();
+        const int chunk = sl * kSliceChunks + g;
+        const int cc = min(chunk, kq - 1);
+        const uint32_t mask = chunk < kq ? 0xFFFFFFFFu : 0u;
+        const uint4 w = load_nt16(packed + ((int64_t)row * kq + cc) * 4);
+        issue_fence();
+        i32x4 a[4];
 #pragma unroll
-            for (int bl = 0; bl < kGroupRows; ++bl) {
-                if (bl > 0 && bl >= batch) break;   // uniform: rows past the batch are not prepared
-                const float* xr = x + (int64_t)bl * K;
-#pragma unroll
-                for (int b = 0; b < 4; ++b) xv[bl][b] = xr[min(col0 + 4 * b, K - 1)];
-            }
-            issue_fence();
-            const int chunk = sl * kSliceChunks + g;
-            const int cc = min(chunk, kq - 1);
-            const uint32_t mask = chunk < kq ? 0xFFFFFFFFu : 0u;
-            const uint4 w = load_nt16(packed + ((int64_t)row * kq + cc) * 4);
-            issue_fence();
-            i32x4 a[4];
-#pragma unroll
-            for (int gi = 0; gi < NG; ++gi) {
-                const int rows = min(kGroupRows, batch - kGroupRows * gi);   // rows of this group (uniform, >= 1)
-                if (gi > 0) {   // next group's activations
-#pragma unroll
-                    for (int bl = 0; bl < kGroupRows; ++bl) {
-                        if (bl >= rows) break;
-                        const float* xr = x + (int64_t)(kGroupRows * gi + bl) * K;
-#pragma unroll
-                        for (int b = 0; b < 4; ++b) xv[bl][b] = xr[min(col0 + 4 * b, K - 1)];
-                    }
-                }
-                // digit columns of rows past the batch keep whatever integers LDS holds: their
-                // D columns are never read
-                int S[kGroupRows] = {30, 30};
+        for (int gi = 0; gi < NG; ++gi) {
+            const int rows = min(kGroupRows, batch - kGroupRows * gi);   // rows of this group (uniform, >= 1)
+            if (gi > 0) {   // next group's activations
 #pragma unroll
                 for (int bl = 0; bl < kGroupRows; ++bl) {
                     if (bl >= rows) break;
-                    S[bl] = slice_exponent(wave_max(fmaxf(fmaxf(fabsf(xv[bl][0]), fabsf(xv[bl][1])),
-                                                          fmaxf(fabsf(xv[bl][2]), fabsf(xv[bl][3])))));
-                    uint32_t dh[4], dl[4], th[4], tl[4];
+                    const float* xr = x + (int64_t)(kGroupRows * gi + bl) * K;
 #pragma unroll
-                    for (int b = 0; b < 4; ++b) digits8(xv[bl][b], S[bl], dh[b], dl[b]);
-                    transpose4(dh, th);
-                    transpose4(dl, tl);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        prep_row[(8 * bl + i) * kRowPitch] = th[i];
-                        prep_row[(8 * bl + 4 + i) * kRowPitch] = tl[i];
-                    }
+                    for (int b = 0; b < 4; ++b) xv[bl][b] = xr[min(col0 + 4 * b, K - 1)];
                 }
-                if (gi == 0) {   // the weights are decoded once, after the first digits
-                    const uint32_t ws[4] = {w.x & mask, w.y & mask, w.z & mask, w.w & mask};
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) a[q] = decode_word(ws[q]);
-                }
-                __builtin_amdgcn_wave_barrier();   // LDS accesses of one wave complete in order
-                i32x4 acc = {0, 0, 0, 0};
-#pragma unroll
-                for (int q = 0; q < 4; ++q) acc = mfma_i8(a[q], b_row[q], acc);
-                // |acc| <= 256 * 128: exact in fp32
-                const int e = c_shift - (c_row ? S[1] : S[0]);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) f[gi][j] += ldexpf((float)acc[j], e);
-                __builtin_amdgcn_wave_barrier();   // the B reads are done before the next digits
             }
+            // digit columns of rows past the batch keep whatever integers LDS holds: their
+            // D columns are never read
+            int S[kGroupRows] = {30, 30};
+#pragma unroll
+            for (int bl = 0; bl < kGroupRows; ++bl) {
+                if (bl >= rows) break;
+                S[bl] = slice_exponent(wave_max(fmaxf(fmaxf(fabsf(xv[bl][0]), fabsf(xv[bl][1])),
+                                                      fmaxf(fabsf(xv[bl][2]), fabsf(xv[bl][3])))));
+                uint32_t dh[4], dl[4], th[4], tl[4];
+#pragma unroll
+                for (int b = 0; b < 4; ++b) digits8(xv[bl][b], S[bl], dh[b], dl[b]);
+                transpose4(dh, th);
+                transpose4(dl, tl);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    prep_row[(8 * bl + i) * kRowPitch] = th[i];
+                    prep_row[(8 * bl + 4 + i) * kRowPitch] = tl[i];
+                }
+            }
+            if (gi == 0) {   // the weights are decoded once, after the first digits
+                const uint32_t ws[4] = {w.x & mask, w.y & mask, w.z & mask, w.w & mask};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) a[q] = decode_word(ws[q]);
+            }
+            __builtin_amdgcn_wave_barrier();   // LDS accesses of one wave complete in order
+            i32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc = mfma_i8(a[q], b_row[q], acc);
+            // |acc| <= 256 * 128: exact in fp32
+            const int e = c_shift - (c_row ? S[1] : S[0]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) f[gi][j] += ldexpf((float)acc[j], e);
+            __builtin_amdgcn_wave_barrier();   // the B reads are done before the next digits
         }
+    }
 
-        // the eight digit columns of each activation row: the sum lands in lane c = 8 b + 7
+    // the eight digit columns of each activation row: the sum lands in lane c = 8 b + 7
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float v = f[gi][j];
+            v += dpp_f32<0x111>(v);   // row_shr:1
+            v += dpp_f32<0x112>(v);   // row_shr:2
+            v += dpp_f32<0x114>(v);   // row_shr:4
+            f[gi][j] = v;
+        }
+    if ((c & 7) == 7) {
+        float* dst = part + wave * NG * 32 + c_row * 16 + 4 * g;
 #pragma unroll
         for (int gi = 0; gi < NG; ++gi)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                float v = f[gi][j];
-                v += dpp_f32<0x111>(v);   // row_shr:1
-                v += dpp_f32<0x112>(v);   // row_shr:2
-                v += dpp_f32<0x114>(v);   // row_shr:4
-                f[gi][j] = v;
-            }
-        if ((c & 7) == 7) {
-            float* dst = part + wave * NG * 32 + c_row * 16 + 4 * g;
-#pragma unroll
-            for (int gi = 0; gi < NG; ++gi)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) dst[gi * 32 + j] = f[gi][j];
-        }
-        __syncthreads();
-        for (int i = threadIdx.x; i < NG * 32; i += blockDim.x) {
-            float sum = 0.f;
-            for (int wv = 0; wv < nwaves; ++wv) sum += part[wv * NG * 32 + i];
-            tot[i] = sum;
-        }
-        __syncthreads();
-        // tot[b 16 + row] is the ternary row sum of activation row b; the row scale multiplies it once
-        for (int i = threadIdx.x; i < 16 * batch; i += blockDim.x) {
-            const int orow = tile * 16 + (i & 15);
-            if (orow < n) y[(int64_t)(i >> 4) * n + orow] = scale[orow] * tot[i];
-        }
+            for (int j = 0; j < 4; ++j) dst[gi * 32 + j] = f[gi][j];
     }
+    __syncthreads();
+    // part[wave][b 16 + row] holds the wave's share of activation row b; summed over the waves in
+    // a fixed order, then the row scale multiplies the total once
+    for (int i = threadIdx.x; i < 16 * batch; i += blockDim.x) {
+        const int orow = tile * 16 + (i & 15);
+        float sum = 0.f;
+        for (int wv = 0; wv < nwaves; ++wv) sum += part[wv * NG * 32 + i];
+        if (orow < n) y[(int64_t)(i >> 4) * n + orow] = scale[orow] * sum;
+    }
+}
+
+// Batch 1 (ternary_gemv): the kernel above with one activation row, and each
+// wave's SPW slices (slice wave + waves i) known at compile time, so the x
+// and weight loads of all of them are issued before the first is used.
+template <int SPW>
+__global__ __launch_bounds__(kWave * kMaxWaves) void ternary_gemv_i8_kernel(const uint32_t* packed,
+                                                                            const float* scale, const float* x,
+                                                                            float* y, int n, int kq) {
+    extern __shared__ __attribute__((aligned(16))) uint32_t tv_smem[];
+    const int nwaves = blockDim.x / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    uint32_t* tab = tv_smem + wave * kWaveDwords;
+    float* part = reinterpret_cast<float*>(tv_smem + nwaves * kWaveDwords);   // [waves][16]
+    const int g = lane >> 4, r = lane & 15, c = lane & 15;
+    const int K = 64 * kq;
+    const int nslices = (kq + kSliceChunks - 1) / kSliceChunks;
+    const int pg = lane >> 4, pq = (lane >> 2) & 3, pj = lane & 3;
+    uint32_t* prep_row = tab + pg * kColumns * kRowPitch + 4 * pq + pj;
+    const i32x4* b_row = reinterpret_cast<const i32x4*>(tab + (g * kColumns + c) * kRowPitch);
+    const int c_shift = 8 * (c & 3) - ((c & 4) ? 30 : 0);   // columns 0..7: the row's eight digits
+    const int tile = blockIdx.x;
+    const int row = min(tile * 16 + r, n - 1);
+    float xv[SPW][4];
+    uint4 w[SPW];
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) {
+        const int col0 = 256 * min(wave + nwaves * i, nslices - 1) + 64 * pg + 16 * pq + pj;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) xv[i][b] = x[min(col0 + 4 * b, K - 1)];
+    }
+    issue_fence();
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) {
+        const int chunk = (wave + nwaves * i) * kSliceChunks + g;
+        w[i] = load_nt16(packed + ((int64_t)row * kq + min(chunk, kq - 1)) * 4);
+    }
+    issue_fence();
+    float f[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) {
+        const int sl = wave + nwaves * i;
+        if (sl >= nslices) break;   // wave-uniform
+        const int S = slice_exponent(wave_max(fmaxf(fmaxf(fabsf(xv[i][0]), fabsf(xv[i][1])),
+                                                    fmaxf(fabsf(xv[i][2]), fabsf(xv[i][3])))));
+        uint32_t dh[4], dl[4], th[4], tl[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) digits8(xv[i][b], S, dh[b], dl[b]);
+        transpose4(dh, th);
+        transpose4(dl, tl);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            prep_row[q * kRowPitch] = th[q];
+            prep_row[(4 + q) * kRowPitch] = tl[q];
+        }
+        __builtin_amdgcn_wave_barrier();   // LDS accesses of one wave complete in order
+        const int chunk = sl * kSliceChunks + g;
+        const uint32_t mask = chunk < kq ? 0xFFFFFFFFu : 0u;
+        const uint32_t ws[4] = {w[i].x & mask, w[i].y & mask, w[i].z & mask, w[i].w & mask};
+        i32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc = mfma_i8(decode_word(ws[q]), b_row[q], acc);
+        const int e = c_shift - S;   // columns 8..15 hold stale integers and are never read
+#pragma unroll
+        for (int j = 0; j < 4; ++j) f[j] += ldexpf((float)acc[j], e);
+        __builtin_amdgcn_wave_barrier();   // the B reads are done before the next digits
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {   // the eight digit columns: the sum lands in lane c = 7
+        float v = f[j];
+        v += dpp_f32<0x111>(v);   // row_shr:1
+        v += dpp_f32<0x112>(v);   // row_shr:2
+        v += dpp_f32<0x114>(v);   // row_shr:4
+        f[j] = v;
+    }
+    if (c == 7) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) part[wave * 16 + 4 * g + j] = f[j];
+    }
+    __syncthreads();
+    if (threadIdx.x < 16) {
+        float sum = 0.f;
+        for (int wv = 0; wv < nwaves; ++wv) sum += part[wv * 16 + threadIdx.x];
+        const int orow = tile * 16 + threadIdx.x;
+        if (orow < n) y[orow] = scale[orow] * sum;
+    }
+}
+
+template <int SPW>
+hipError_t run_gemv_i8(const uint32_t* packed, const float* scale, const float* x, float* y, int n, int kq,
+                       hipStream_t stream) {
+    const int waves = min(kMaxWaves, (kq + kSliceChunks - 1) / kSliceChunks);
+    const size_t lds = 4u * ((size_t)waves * kWaveDwords + (size_t)waves * 16);
+    ternary_gemv_i8_kernel<SPW><<<(n + 15) / 16, kWave * waves, lds, stream>>>(packed, scale, x, y, n, kq);
+    return hipGetLastError();
 }
 
 template <int NG>
@@ -174,18 +264,8 @@ hipError_t run_gemm(const uint32_t* packed, const float* scale, const float* x, 
                     int kq, hipStream_t stream) {
     const int waves = min(kMaxWaves, (kq + kSliceChunks - 1) / kSliceChunks);
     const size_t lds = gemm_lds_bytes(waves, NG);
-    static int cache[kMaxWaves + 1] = {};   // resident workgroups per compute unit, per wave count
-    if (cache[waves] == 0) {
-        int per_cu = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, ternary_gemm_kernel<NG>, kWave * waves, lds) !=
-                hipSuccess ||
-            per_cu < 1)
-            per_cu = 1;
-        cache[waves] = per_cu;
-    }
-    const int ntiles = (n + 15) / 16;
-    const int grid = min(ntiles, cache[waves] * device_cu_count());
-    ternary_gemm_kernel<NG><<<grid, kWave * waves, lds, stream>>>(packed, scale, x, y, batch, n, kq);
+    const int ntiles = (n + 15) / 16;   // one workgroup per tile: the hardware streams through them
+    ternary_gemm_kernel<NG><<<ntiles, kWave * waves, lds, stream>>>(packed, scale, x, y, batch, n, kq);
     return hipGetLastError();
 }
 
@@ -202,6 +282,15 @@ hipError_t launch_ternary_gemm(const uint32_t* packed, const float* row_scale, c
         return hipSuccess;
     }
     const int nn = (int)n, kq = (int)(k / 64), bb = (int)batch;
+    const int nslices = (kq + kSliceChunks - 1) / kSliceChunks;
+    if (bb == 1 && nslices <= 4 * kMaxWaves) {   // slices per wave known at compile time
+        switch ((nslices + kMaxWaves - 1) / kMaxWaves) {
+            case 1: return run_gemv_i8<1>(packed, row_scale, x, y, nn, kq, stream);
+            case 2: return run_gemv_i8<2>(packed, row_scale, x, y, nn, kq, stream);
+            case 3: return run_gemv_i8<3>(packed, row_scale, x, y, nn, kq, stream);
+            default: return run_gemv_i8<4>(packed, row_scale, x, y, nn, kq, stream);
+        }
+    }
     switch ((bb + kGroupRows - 1) / kGroupRows) {
         case 1: return run_gemm<1>(packed, row_scale, x, y, bb, nn, kq, stream);
         case 2: return run_gemm<2>(packed, row_scale, x, y, bb, nn, kq, stream);

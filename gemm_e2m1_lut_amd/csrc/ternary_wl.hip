@@ -32,7 +32,7 @@
 // any other to within 2^-60 times that largest, and the only other roundings
 // are a few fp32 additions per row.
 
-// Work split: a workgroup owns a tile of 16 rows; its waves take 256-column
+// Work split: a workgroup owns a tile of 16 rows (one workgroup per tile); its waves take 256-column
 // slices (slice s of wave w = w, w + waves, ...). Lane l = 16 g + r loads the
 // 16-byte chunk 4 s + g of row r of each matrix (four words, 64 columns) and
 // decodes word q as the A operand of one MFMA; in that operand byte b of
@@ -84,7 +84,6 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void ternary_wl_kernel(WlMats ma
     const int g = lane >> 4, r = lane & 15, c = lane & 15;
     const int K = 64 * kq;
     const int nslices = (kq + kSliceChunks - 1) / kSliceChunks;
-    const int ntiles = (n + 15) / 16;
     // digit preparation: lane -> chunk pg, word pq, dword pj; columns 64 pg + 16 pq + pj + 4 b
     const int pg = lane >> 4, pq = (lane >> 2) & 3, pj = lane & 3;
     uint32_t* prep_row = tab + pg * kVariants * kRowPitch + 4 * pq + pj;
@@ -93,123 +92,122 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void ternary_wl_kernel(WlMats ma
     const bool c_im = c & 8;
     const int c_shift = 8 * (c & 3) - ((c & 4) ? 30 : 0);
 
-    for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {   // workgroup-uniform
-        const int row = min(tile * 16 + r, n - 1);
-        float sc[4] = {0.f, 0.f, 0.f, 0.f};
-        if (wave == 0) {
+    const int tile = blockIdx.x;   // one tile of 16 rows per workgroup
+    const int row = min(tile * 16 + r, n - 1);
+    float sc[4] = {0.f, 0.f, 0.f, 0.f};
+    if (wave == 0) {
 #pragma unroll
-            for (int m = 0; m < 4; ++m) sc[m] = scale[(int64_t)m * n + row];
+        for (int m = 0; m < 4; ++m) sc[m] = scale[(int64_t)m * n + row];
+    }
+    float f[4][4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) f[m][j] = 0.f;
+
+    for (int sl = wave; sl < nslices; sl += nwaves) {   // wave-uniform
+        float xr[4], xi[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int col = min(256 * sl + 64 * pg + 16 * pq + pj + 4 * b, K - 1);
+            xr[b] = x_re[col];
+            xi[b] = x_im[col];
         }
-        float f[4][4];
+        issue_fence();
+        const int chunk = sl * kSliceChunks + g;
+        const int cc = min(chunk, kq - 1);
+        const uint32_t mask = chunk < kq ? 0xFFFFFFFFu : 0u;
+        uint4 w[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) w[m] = load_nt16(mats.m[m] + ((int64_t)row * kq + cc) * 4);
+        issue_fence();
+        // digits of this slice's x into the wave's LDS area
+        const int Sr = slice_exponent(wave_max(fmaxf(fmaxf(fabsf(xr[0]), fabsf(xr[1])),
+                                                     fmaxf(fabsf(xr[2]), fabsf(xr[3])))));
+        const int Si = slice_exponent(wave_max(fmaxf(fmaxf(fabsf(xi[0]), fabsf(xi[1])),
+                                                     fmaxf(fabsf(xi[2]), fabsf(xi[3])))));
+        uint32_t hr[4], lr[4], hi_[4], li[4], t[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            digits8(xr[b], Sr, hr[b], lr[b]);
+            digits8(xi[b], Si, hi_[b], li[b]);
+        }
+        transpose4(hr, t);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) prep_row[i * kRowPitch] = t[i];
+        transpose4(lr, t);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) prep_row[(4 + i) * kRowPitch] = t[i];
+        transpose4(hi_, t);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) prep_row[(8 + i) * kRowPitch] = t[i];
+        transpose4(li, t);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) prep_row[(12 + i) * kRowPitch] = t[i];
+        __builtin_amdgcn_wave_barrier();   // LDS accesses of one wave complete in order
+        i32x4 bq[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) bq[q] = b_row[q];
+        i32x4 acc[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) acc[m] = i32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const uint32_t ws[4] = {w[m].x, w[m].y, w[m].z, w[m].w};
+                acc[m] = __builtin_amdgcn_mfma_i32_16x16x64_i8(decode_word(ws[q] & mask), bq[q], acc[m], 0, 0, 0);
+            }
+        }
+        // digit column c is worth 2^(c_shift - S) of its part; |acc| <= 2^15, exact in fp32
+        const int e = c_shift - (c_im ? Si : Sr);
 #pragma unroll
         for (int m = 0; m < 4; ++m)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) f[m][j] = 0.f;
+            for (int j = 0; j < 4; ++j) f[m][j] += ldexpf((float)acc[m][j], e);
+        __builtin_amdgcn_wave_barrier();   // the B reads are done before the next slice's digits
+    }
 
-        for (int sl = wave; sl < nslices; sl += nwaves) {   // wave-uniform
-            float xr[4], xi[4];
+    // digits of x_re (columns 0..7) and of x_im (8..15): the sums land in lanes c = 7 and c = 15
+    float s[4][4];
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const int col = min(256 * sl + 64 * pg + 16 * pq + pj + 4 * b, K - 1);
-                xr[b] = x_re[col];
-                xi[b] = x_im[col];
-            }
-            issue_fence();
-            const int chunk = sl * kSliceChunks + g;
-            const int cc = min(chunk, kq - 1);
-            const uint32_t mask = chunk < kq ? 0xFFFFFFFFu : 0u;
-            uint4 w[4];
+    for (int m = 0; m < 4; ++m)
 #pragma unroll
-            for (int m = 0; m < 4; ++m) w[m] = load_nt16(mats.m[m] + ((int64_t)row * kq + cc) * 4);
-            issue_fence();
-            // digits of this slice's x into the wave's LDS area
-            const int Sr = slice_exponent(wave_max(fmaxf(fmaxf(fabsf(xr[0]), fabsf(xr[1])),
-                                                         fmaxf(fabsf(xr[2]), fabsf(xr[3])))));
-            const int Si = slice_exponent(wave_max(fmaxf(fmaxf(fabsf(xi[0]), fabsf(xi[1])),
-                                                         fmaxf(fabsf(xi[2]), fabsf(xi[3])))));
-            uint32_t hr[4], lr[4], hi_[4], li[4], t[4];
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                digits8(xr[b], Sr, hr[b], lr[b]);
-                digits8(xi[b], Si, hi_[b], li[b]);
-            }
-            transpose4(hr, t);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) prep_row[i * kRowPitch] = t[i];
-            transpose4(lr, t);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) prep_row[(4 + i) * kRowPitch] = t[i];
-            transpose4(hi_, t);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) prep_row[(8 + i) * kRowPitch] = t[i];
-            transpose4(li, t);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) prep_row[(12 + i) * kRowPitch] = t[i];
-            __builtin_amdgcn_wave_barrier();   // LDS accesses of one wave complete in order
-            i32x4 bq[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) bq[q] = b_row[q];
-            i32x4 acc[4];
-#pragma unroll
-            for (int m = 0; m < 4; ++m) acc[m] = i32x4{0, 0, 0, 0};
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const uint32_t ws[4] = {w[m].x, w[m].y, w[m].z, w[m].w};
-                    acc[m] = __builtin_amdgcn_mfma_i32_16x16x64_i8(decode_word(ws[q] & mask), bq[q], acc[m], 0, 0, 0);
-                }
-            }
-            // digit column c is worth 2^(c_shift - S) of its part; |acc| <= 2^15, exact in fp32
-            const int e = c_shift - (c_im ? Si : Sr);
-#pragma unroll
-            for (int m = 0; m < 4; ++m)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) f[m][j] += ldexpf((float)acc[m][j], e);
-            __builtin_amdgcn_wave_barrier();   // the B reads are done before the next slice's digits
+        for (int j = 0; j < 4; ++j) {
+            float v = f[m][j];
+            v += dpp_f32<0x111>(v);   // row_shr:1
+            v += dpp_f32<0x112>(v);   // row_shr:2
+            v += dpp_f32<0x114>(v);   // row_shr:4
+            s[m][j] = v;
         }
-
-        // digits of x_re (columns 0..7) and of x_im (8..15): the sums land in lanes c = 7 and c = 15
-        float s[4][4];
+    if (c == 7 || c == 15) {
+        float* dst = part + wave * kPartFloats + (c == 15 ? 16 : 0) + 4 * g;
 #pragma unroll
         for (int m = 0; m < 4; ++m)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                float v = f[m][j];
-                v += dpp_f32<0x111>(v);   // row_shr:1
-                v += dpp_f32<0x112>(v);   // row_shr:2
-                v += dpp_f32<0x114>(v);   // row_shr:4
-                s[m][j] = v;
-            }
-        if (c == 7 || c == 15) {
-            float* dst = part + wave * kPartFloats + (c == 15 ? 16 : 0) + 4 * g;
-#pragma unroll
-            for (int m = 0; m < 4; ++m)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) dst[32 * m + j] = s[m][j];
-        }
-        __syncthreads();
-        for (int i = threadIdx.x; i < kPartFloats; i += blockDim.x) {   // one-wave workgroups take two rounds
-            float sum = 0.f;
-            for (int wv = 0; wv < nwaves; ++wv) sum += part[wv * kPartFloats + i];
-            tot[i] = sum;
-        }
-        __syncthreads();
-        const int t = threadIdx.x;
-        if (t < 32) {
-            const int rr = t & 15, orow = tile * 16 + rr;
-            // tot[(2 m + p) 16 + row]: ternary row sum of matrix m against x_re (p = 0) or x_im (p = 1)
-            const float ur_re = tot[0 * 16 + rr], ur_im = tot[1 * 16 + rr];
-            const float ui_re = tot[2 * 16 + rr], ui_im = tot[3 * 16 + rr];
-            const float wr_re = tot[4 * 16 + rr], wr_im = tot[5 * 16 + rr];
-            const float wi_re = tot[6 * 16 + rr], wi_im = tot[7 * 16 + rr];
-            float y;
-            if (t < 16)   // Re: U_re x_re - U_im x_im + W_re x_re + W_im x_im
-                y = (sc[0] * ur_re - sc[1] * ui_im) + (sc[2] * wr_re + sc[3] * wi_im);
-            else          // Im: U_re x_im + U_im x_re - W_re x_im + W_im x_re
-                y = (sc[0] * ur_im + sc[1] * ui_re) + (sc[3] * wi_re - sc[2] * wr_im);
-            if (orow < n) (t < 16 ? y_re : y_im)[orow] = y;
-        }
+            for (int j = 0; j < 4; ++j) dst[32 * m + j] = s[m][j];
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < kPartFloats; i += blockDim.x) {   // one-wave workgroups take two rounds
+        float sum = 0.f;
+        for (int wv = 0; wv < nwaves; ++wv) sum += part[wv * kPartFloats + i];
+        tot[i] = sum;
+    }
+    __syncthreads();
+    const int t = threadIdx.x;
+    if (t < 32) {
+        const int rr = t & 15, orow = tile * 16 + rr;
+        // tot[(2 m + p) 16 + row]: ternary row sum of matrix m against x_re (p = 0) or x_im (p = 1)
+        const float ur_re = tot[0 * 16 + rr], ur_im = tot[1 * 16 + rr];
+        const float ui_re = tot[2 * 16 + rr], ui_im = tot[3 * 16 + rr];
+        const float wr_re = tot[4 * 16 + rr], wr_im = tot[5 * 16 + rr];
+        const float wi_re = tot[6 * 16 + rr], wi_im = tot[7 * 16 + rr];
+        float y;
+        if (t < 16)   // Re: U_re x_re - U_im x_im + W_re x_re + W_im x_im
+            y = (sc[0] * ur_re - sc[1] * ui_im) + (sc[2] * wr_re + sc[3] * wi_im);
+        else          // Im: U_re x_im + U_im x_re - W_re x_im + W_im x_re
+            y = (sc[0] * ur_im + sc[1] * ui_re) + (sc[3] * wi_re - sc[2] * wr_im);
+        if (orow < n) (t < 16 ? y_re : y_im)[orow] = y;
     }
 }
 
@@ -257,14 +255,6 @@ __global__ __launch_bounds__(256) void ternary_wl_generic_kernel(WlMats mats, co
     }
 }
 
-int wl_resident(int waves, size_t lds) {
-    int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, ternary_wl_kernel, kWave * waves, lds) != hipSuccess ||
-        per_cu < 1)
-        per_cu = 1;
-    return per_cu;
-}
-
 }  // namespace
 
 hipError_t launch_ternary_wl(const uint32_t* const mats[4], const float* scale, const float* x_re,
@@ -278,11 +268,8 @@ hipError_t launch_ternary_wl(const uint32_t* const mats[4], const float* scale, 
         const int kq = (int)(k / 64);
         const int waves = min(kMaxWaves, (kq + kSliceChunks - 1) / kSliceChunks);
         const size_t lds = wl_lds_bytes(waves);
-        static int cache[kMaxWaves + 1] = {};   // resident workgroups per compute unit, per wave count
-        if (cache[waves] == 0) cache[waves] = wl_resident(waves, lds);
-        const int ntiles = (nn + 15) / 16;
-        const int grid = min(ntiles, cache[waves] * device_cu_count());
-        ternary_wl_kernel<<<grid, kWave * waves, lds, stream>>>(wm, scale, x_re, x_im, y_re, y_im, nn, kq);
+        const int ntiles = (nn + 15) / 16;   // one workgroup per tile: the hardware streams through them
+        ternary_wl_kernel<<<ntiles, kWave * waves, lds, stream>>>(wm, scale, x_re, x_im, y_re, y_im, nn, kq);
         return hipGetLastError();
     }
     const int want = (nn + 3) / 4;
