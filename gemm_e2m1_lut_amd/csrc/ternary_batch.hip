@@ -69,16 +69,21 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void ternary_gemm_kernel(const u
 #pragma unroll
         for (int j = 0; j < 4; ++j) f[gi][j] = 0.f;
 
+    // up to four groups keep every activation row of the slice in registers, requested before the
+    // weights; more groups load each group's rows as it starts
+    constexpr int kAhead = NG <= 4 ? NG : 1;
     for (int sl = wave; sl < nslices; sl += nwaves) {   // wave-uniform
         const int col0 = 256 * sl + 64 * pg + 16 * pq + pj;
-        float xv[kGroupRows][4];   // [row of the group][b]
+        float xa[kAhead][kGroupRows][4];   // [group][row of the group][b]
 #pragma unroll
-        for (int bl = 0; bl < kGroupRows; ++bl) {
-            if (bl > 0 && bl >= batch) break;   // uniform: rows past the batch are not prepared
-            const float* xr = x + (int64_t)bl * K;
+        for (int ga = 0; ga < kAhead; ++ga)
 #pragma unroll
-            for (int b = 0; b < 4; ++b) xv[bl][b] = xr[min(col0 + 4 * b, K - 1)];
-        }
+            for (int bl = 0; bl < kGroupRows; ++bl) {
+                const int b_row_x = min(kGroupRows * ga + bl, batch - 1);   // rows past the batch: never prepared
+                const float* xr = x + (int64_t)b_row_x * K;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) xa[ga][bl][b] = xr[min(col0 + 4 * b, K - 1)];
+            }
         issue_fence();
         const int chunk = sl * kSliceChunks + g;
         const int cc = min(chunk, kq - 1);
@@ -89,7 +94,18 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void ternary_gemm_kernel(const u
 #pragma unroll
         for (int gi = 0; gi < NG; ++gi) {
             const int rows = min(kGroupRows, batch - kGroupRows * gi);   // rows of this group (uniform, >= 1)
-            if (gi > 0) {   // next group's activations
+            float xv[kGroupRows][4];
+            if constexpr (kAhead == NG) {
+#pragma unroll
+                for (int bl = 0; bl < kGroupRows; ++bl)
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) xv[bl][b] = xa[gi][bl][b];
+            } else if (gi == 0) {
+#pragma unroll
+                for (int bl = 0; bl < kGroupRows; ++bl)
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) xv[bl][b] = xa[0][bl][b];
+            } else {   // this group's activations
 #pragma unroll
                 for (int bl = 0; bl < kGroupRows; ++bl) {
                     if (bl >= rows) break;
