@@ -253,7 +253,8 @@ int mxfp4_moe_gemm(const uint16_t* x, const uint8_t* w13, const uint8_t* w13_sca
                    size_t workspace_bytes, int64_t tokens, int64_t hidden, int64_t inter,
                    int64_t experts, int64_t topk, void* stream) {
     const size_t need = mxfp4_moe_workspace_size(tokens, hidden, inter, experts, topk);
-    if (need == (size_t)-1 || experts > E2M1_MOE_MAX_EXPERTS || hidden > INT_MAX || inter > INT_MAX)
+    if (need == (size_t)-1 || experts > E2M1_MOE_MAX_EXPERTS || hidden > INT_MAX || inter > INT_MAX ||
+        inter * hidden >= ((int64_t)1 << 31))   // each expert's W13 (and W2) below 2 GiB: 32-bit offsets
         return E2M1_ERR_SHAPE;
     if (tokens == 0 || hidden == 0) return E2M1_OK;
     if (!x || !out || !topk_ids || !topk_weights) return E2M1_ERR_NULL;

@@ -24,6 +24,10 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
+// Word 3 of a buffer resource for raw 32-bit-addressed loads (gfx9 family): bounds-checked
+// against the resource's byte count, zeros outside it.
+constexpr int kBufferWord3 = 0x00020000;
+
 // ------------------------------------------------- streaming loads / stores --
 // Non-temporal (streaming) 16- and 8-byte accesses for data touched once.
 

@@ -51,7 +51,6 @@ constexpr int kWPitch = 32 + 4;              // bytes per staged code row
 constexpr int kXElems = kTileM * kXPitch;
 constexpr int kWBytes = kTileN * kWPitch;
 constexpr int kXChunks = kTileM * kStepK / 8 / kThreads;   // 16-byte x chunks per thread per step
-constexpr int kBufferWord3 = 0x00020000;     // buffer descriptor word 3 for raw 32-bit access (gfx9 family)
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 

@@ -514,7 +514,6 @@ constexpr int kMaxSliceWaves = 16;
 
 constexpr int kXPitch = 128 + 8;                     // bf16 per staged x row (16-byte pad spreads the banks)
 constexpr int kWPitch = 9;                           // uint4 per transposed code row (8 blocks + pad)
-constexpr int kBufferWord3 = 0x00020000;             // buffer descriptor word 3 for raw 32-bit access (gfx9 family)
 
 // Workgroup = S waves on one tile of 16 rows (tiles blockIdx.x, + gridDim.x,
 // ...); wave w owns scale blocks [32 w, 32 w + 32). Lane l = 16 g + r: row r

@@ -189,11 +189,20 @@ __global__ __launch_bounds__(kThreads) void moe_gemm1_kernel(
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wave-uniform
     const int g = lane >> 4, r16 = lane & 15;
-    const int jt = work.blk * kGemm1Cols + wave * 16;   // this wave's 16 columns j
-    const bool tvalid = jt < I;
-    const int tile_row[2] = {jt, I + jt};
     const uint8_t* we = w13 + (size_t)e * 2 * I * (H / 2);
     const uint8_t* se = w13s + (size_t)e * 2 * I * (H / 32);
+    // rows of one line offset per tile: wave w takes j = j0 + P (4 g' + jj) + c for its 16
+    // columns j (c = w % P, 16 P consecutive j per group of P waves), gate rows j and up rows I + j
+    // (I (H / 2) is a multiple of 128: the same offsets)
+    const int P = line_period(H);
+    const int j0 = work.blk * kGemm1Cols + 16 * P * (wave / P) + wave % P;
+    const int row0[2] = {j0, I + j0};
+    const int mb = line_block(we, j0, H);
+    int mbmax = 0;
+    for (int c = 0; c < P; ++c) mbmax = max(mbmax, line_block(we, work.blk * kGemm1Cols + c, H));
+    const int nsteps = engine_steps(H, mbmax);
+    const __amdgpu_buffer_rsrc_t wres =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(we), 0, 2 * I * (H / 2), kBufferWord3);
 
     for (int m0 = 0; m0 < n_e; m0 += kEngineMaxTokens) {
         const int nv = min(kEngineMaxTokens, n_e - m0);
@@ -206,19 +215,45 @@ __global__ __launch_bounds__(kThreads) void moe_gemm1_kernel(
         for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int m = 0; m < 4; ++m) acc[t][m] = f32x4{0.f, 0.f, 0.f, 0.f};
-        Gemm1::run_mt(mt, sh, we, se, H, tile_row, 2 * I, x, (size_t)H, nv, acc);
-        // epilogue: act = silu(gate) * up -> bf16, 4 consecutive j per lane
-        if (tvalid) {
+        Gemm1::run_mt(mt, sh, wres, se, H, row0, P, mb, nsteps, 2 * I, x, (size_t)H, nv, acc);
+        // epilogue: act = silu(gate) * up -> bf16; lane (g, r) holds j = j0 + P (4 g + jj), jj < 4.
+        // With P > 1 the workgroup's 128 j of each token row are interleaved over its waves, so
+        // they meet in LDS (over the token panels, free once every wave is past the product) and
+        // leave as contiguous 16-byte stores.
+        const int jb = work.blk * kGemm1Cols;
+        if (P == 1) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int r = 16 * m + r16;
+                const int j = j0 + 4 * g;
+                if (m < mt && r < nv && j < I) {
+                    const f32x4 gt = acc[0][m], up = acc[1][m];
+                    const uint32_t lo = pack_bf16x2(silu_f32(gt[0]) * up[0], silu_f32(gt[1]) * up[1]);
+                    const uint32_t hi = pack_bf16x2(silu_f32(gt[2]) * up[2], silu_f32(gt[3]) * up[3]);
+                    *reinterpret_cast<uint2*>(act + (size_t)(base + m0 + r) * I + j) = make_uint2(lo, hi);
+                }
+            }
+        } else {
+            uint16_t* stage = &sh.panel[0][0];   // [64 tokens][kGemm1Cols + 8]
+            constexpr int kStagePitch = kGemm1Cols + 8;
+            __syncthreads();   // every wave is done with the panels
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 const int r = 16 * m + r16;
                 if (m < mt && r < nv) {
                     const f32x4 gt = acc[0][m], up = acc[1][m];
-                    const uint32_t lo = pack_bf16x2(silu_f32(gt[0]) * up[0], silu_f32(gt[1]) * up[1]);
-                    const uint32_t hi = pack_bf16x2(silu_f32(gt[2]) * up[2], silu_f32(gt[3]) * up[3]);
-                    const int j = jt + 4 * g;
-                    *reinterpret_cast<uint2*>(act + (size_t)(base + m0 + r) * I + j) = make_uint2(lo, hi);
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj)
+                        stage[r * kStagePitch + (j0 - jb) + P * (4 * g + jj)] =
+                            (uint16_t)f32_to_bf16_rne(silu_f32(gt[jj]) * up[jj]);
                 }
+            }
+            __syncthreads();
+            for (int i = threadIdx.x; i < nv * (kGemm1Cols / 8); i += kThreads) {
+                const int r = i / (kGemm1Cols / 8), c8 = 8 * (i % (kGemm1Cols / 8));
+                if (jb + c8 < I)
+                    *reinterpret_cast<uint4*>(act + (size_t)(base + m0 + r) * I + jb + c8) =
+                        *reinterpret_cast<const uint4*>(stage + r * kStagePitch + c8);
             }
         }
     }
@@ -241,11 +276,18 @@ __global__ __launch_bounds__(kThreads) void moe_gemm2_kernel(
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wave-uniform
     const int g = lane >> 4, r16 = lane & 15;
-    const int ht = work.blk * kGemm2Rows + wave * 16;
-    const bool tvalid = ht < H;
-    const int tile_row[1] = {ht};
     const uint8_t* we = w2 + (size_t)e * H * (I / 2);
     const uint8_t* se = w2s + (size_t)e * H * (I / 32);
+    // rows of one line offset per tile, as in gemm1: h = h0 + P (4 g' + jj) + c
+    const int P = line_period(I);
+    const int h0 = work.blk * kGemm2Rows + 16 * P * (wave / P) + wave % P;
+    const int row0[1] = {h0};
+    const int mb = line_block(we, h0, I);
+    int mbmax = 0;
+    for (int c = 0; c < P; ++c) mbmax = max(mbmax, line_block(we, work.blk * kGemm2Rows + c, I));
+    const int nsteps = engine_steps(I, mbmax);
+    const __amdgpu_buffer_rsrc_t wres =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(we), 0, H * (I / 2), kBufferWord3);
 
     for (int m0 = 0; m0 < n_e; m0 += kEngineMaxTokens) {
         const int nv = min(kEngineMaxTokens, n_e - m0);
@@ -256,15 +298,36 @@ __global__ __launch_bounds__(kThreads) void moe_gemm2_kernel(
         f32x4 acc[1][4];
 #pragma unroll
         for (int m = 0; m < 4; ++m) acc[0][m] = f32x4{0.f, 0.f, 0.f, 0.f};
-        Gemm2::run_mt(mt, sh, we, se, I, tile_row, H, act, (size_t)I, nv, acc);
-        if (tvalid) {
+        Gemm2::run_mt(mt, sh, wres, se, I, row0, P, mb, nsteps, H, act, (size_t)I, nv, acc);
+        // lane (g, r) holds h = h0 + P (4 g + jj), jj < 4: with P > 1 the workgroup's 128 h of each
+        // token row are interleaved over its waves, so they meet in LDS (over the token panels, free
+        // once every wave is past the product) and leave as contiguous 16-byte stores
+        const int hb = work.blk * kGemm2Rows;
+        if (P == 1) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int r = 16 * m + r16;
+                if (m < mt && r < nv && h0 + 4 * g + 3 < H)
+                    *reinterpret_cast<f32x4*>(y + (size_t)(base + m0 + r) * H + h0 + 4 * g) = acc[0][m];
+            }
+        } else {
+            float* stage = reinterpret_cast<float*>(&sh.panel[0][0]);   // [64 tokens][kGemm2Rows + 4]
+            constexpr int kStagePitch = kGemm2Rows + 4;
+            __syncthreads();   // every wave is done with the panels
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 const int r = 16 * m + r16;
                 if (m < mt && r < nv) {
-                    const int h = ht + 4 * g;
-                    *reinterpret_cast<f32x4*>(y + (size_t)(base + m0 + r) * H + h) = acc[0][m];
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) stage[r * kStagePitch + (h0 - hb) + P * (4 * g + jj)] = acc[0][m][jj];
                 }
+            }
+            __syncthreads();
+            for (int i = threadIdx.x; i < nv * (kGemm2Rows / 4); i += kThreads) {
+                const int r = i / (kGemm2Rows / 4), c4 = 4 * (i % (kGemm2Rows / 4));
+                if (hb + c4 + 3 < H)
+                    *reinterpret_cast<f32x4*>(y + (size_t)(base + m0 + r) * H + hb + c4) =
+                        *reinterpret_cast<const f32x4*>(stage + r * kStagePitch + c4);
             }
         }
     }

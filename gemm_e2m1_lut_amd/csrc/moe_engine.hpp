@@ -18,6 +18,17 @@
 //     8 g .. 8 g + 7; v_cvt_scalef32_pk_bf16_fp4 decodes two codes and applies
 //     the block scale in one instruction. The E8M0 byte of each chunk is
 //     loaded by the lane that loads the chunk and takes the same LDS route.
+//   * Line alignment: a row of K/2 bytes need not start on a 128-byte line
+//     (K = 2880: rows start 0, 32, 64 or 96 bytes into a line, repeating every
+//     four rows), and a step's 128 bytes of such a row would straddle two
+//     lines, each then fetched from HBM by two steps. So a tile takes rows of
+//     one line offset 16 mb (stride P, the period of the offsets), and the
+//     wave's step s covers the line-aligned columns [256 s - 32 mb, + 256):
+//     every weight line is requested by exactly one step. The columns before
+//     256 s come from the previous step's token panel (the ring keeps it);
+//     the bytes a window reads before a row's start or past its end meet
+//     zero tokens, and a resource bounded to the matrix returns zeros for
+//     any outside it.
 //   * Tokens: the workgroup stages the step's 256 columns of the pass's token
 //     rows in a triple-buffered LDS panel, requested two steps ahead and
 //     written one step ahead (an L2 round trip per step would otherwise sit
@@ -44,6 +55,7 @@ constexpr int kEngineMaxTokens = 64;                 // token rows per pass (fou
 constexpr int kPanelPitch = kEngineStepCols + 8;     // bf16 per staged token row (16-byte pad spreads banks)
 constexpr int kPanelElems = kEngineMaxTokens * kPanelPitch;
 constexpr int kWBufPitch = 9;                        // uint4 per transposed weight row (8 blocks + pad)
+constexpr int kNonTemporal = 2;                      // cache-policy operand of a buffer load: streaming
 
 // Compiler-only fence: keeps loads where they are written (issued early).
 // Emits no instruction. The weight and token pointers reaching it are not
@@ -53,6 +65,22 @@ __device__ __forceinline__ void engine_fence() {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
 }
+
+// Rows of K/2 bytes from `base`: the byte offset of row r within its 128-byte
+// line repeats with period line_period(K) rows; line_block(base, r, K) is that
+// offset in 16-byte blocks (0..7).
+__host__ __device__ inline int line_period(int K) {
+    int m = (K / 2) & 127, p = 1;
+    while ((m * p) & 127) p *= 2;
+    return p;
+}
+
+__device__ __forceinline__ int line_block(const uint8_t* base, int row, int K) {
+    return (int)(((reinterpret_cast<uintptr_t>(base) + (uintptr_t)row * (uintptr_t)(K / 2)) & 127u) >> 4);
+}
+
+// Steps that cover K for windows shifted by up to mbmax blocks.
+__device__ __forceinline__ int engine_steps(int K, int mbmax) { return (K - 1 + 32 * mbmax) / kEngineStepCols + 1; }
 
 template <int NT>
 struct EngineStep {
@@ -72,19 +100,28 @@ struct MoeEngine {
         int rowidx[kEngineMaxTokens];
     };
 
-    // Weight lines and scales of step `step` for this wave's tiles. tile_row[t]:
-    // first row of tile t; rows are clamped to nrows - 1, blocks to kb - 1.
-    static __device__ __forceinline__ void issue_weights(EngineStep<NT>& b, const uint8_t* w, const uint8_t* ws,
-                                                         int K, const int (&tile_row)[NT], int nrows, int step) {
+    // Weight lines and scales of step `step` for this wave's tiles: tile t is
+    // rows row0[t] + stride i (i < 16), clamped to nrows - 1, each starting 16 mb
+    // bytes into a 128-byte line; lane l loads 16 bytes at 16 (l % 8) of the
+    // step's aligned window of row 8 q + l / 8. Scale blocks are clamped to
+    // [0, kb - 1] (blocks outside the row meet zero tokens).
+    static __device__ __forceinline__ void issue_weights(EngineStep<NT>& b, __amdgpu_buffer_rsrc_t wres,
+                                                         const uint8_t* ws, int K, const int (&row0)[NT],
+                                                         int stride, int mb, int nrows, int step) {
         const int lane = threadIdx.x & (kWave - 1);
         const int kb = K / 32;
-        const int cb = min(8 * step + (lane & 7), kb - 1);
+        const int blk = 8 * step - mb + (lane & 7);
+        const int cb = min(max(blk, 0), kb - 1);
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
-                const int row = min(tile_row[t] + 8 * q + (lane >> 3), nrows - 1);
-                b.w[t][q] = load_nt16(w + (size_t)row * (K / 2) + (size_t)cb * 16);
+                const int row = min(row0[t] + stride * (8 * q + (lane >> 3)), nrows - 1);
+                // may lie before the matrix (row 0, step 0): the unsigned offset is then out of
+                // range and reads zeros
+                const uint32_t off = (uint32_t)(row * (K / 2) + 16 * blk);
+                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(wres, off, 0, kNonTemporal);
+                b.w[t][q] = make_uint4(v.x, v.y, v.z, v.w);
                 b.e[t][q] = ws[(size_t)row * kb + cb];
             }
     }
@@ -117,10 +154,13 @@ struct MoeEngine {
         }
     }
 
-    // acc += step held in b (weights) x token panel.
+    // acc += step held in b (weights) x token panels. The wave's columns are
+    // [256 s - 32 mb, + 256): those before 256 s are read from the previous
+    // step's panel (zero at the first step).
     template <int MTA>
     static __device__ __forceinline__ void compute(const EngineStep<NT>& b, uint4* wbuf, uint8_t* sbuf,
-                                                   const uint16_t* panel, f32x4 (&acc)[NT][4]) {
+                                                   const uint16_t* panel, const uint16_t* prev, bool first,
+                                                   int mb, f32x4 (&acc)[NT][4]) {
         const int lane = threadIdx.x & (kWave - 1);
         const int r = lane & 15, g = lane >> 4;
         // coalesced lines (and their scale bytes) -> MFMA layout through the wave's LDS buffers
@@ -146,6 +186,11 @@ struct MoeEngine {
             float sc[NT];
 #pragma unroll
             for (int t = 0; t < NT; ++t) sc[t] = e8m0_scale(e4[t][h]);
+            // this lane's token columns for block g + 4 h, relative to the step's panel
+            const int cb = 32 * (g + 4 * h - mb);
+            const bool from_prev = cb < 0;
+            const uint16_t* src = (from_prev ? prev : panel) + r * kPanelPitch + (from_prev ? cb + 256 : cb);
+            const bool zero = first && from_prev;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 bf16x8 a[NT];
@@ -156,10 +201,11 @@ struct MoeEngine {
                                      fp4x2_to_bf16x2<2>(wd, sc[t]), fp4x2_to_bf16x2<3>(wd, sc[t])};
                     a[t] = __builtin_bit_cast(bf16x8, u);
                 }
-                const int col = 32 * (g + 4 * h) + 8 * i;
 #pragma unroll
                 for (int m = 0; m < MTA; ++m) {
-                    const bf16x8 bx = *reinterpret_cast<const bf16x8*>(panel + (16 * m + r) * kPanelPitch + col);
+                    u32x4 xw = *reinterpret_cast<const u32x4*>(src + 16 * m * kPanelPitch + 8 * i);
+                    if (zero) xw = u32x4{0u, 0u, 0u, 0u};
+                    const bf16x8 bx = __builtin_bit_cast(bf16x8, xw);
 #pragma unroll
                     for (int t = 0; t < NT; ++t)
                         acc[t][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[t], bx, acc[t][m], 0, 0, 0);
@@ -169,12 +215,12 @@ struct MoeEngine {
     }
 
     // The whole product over K for one pass of MTA token tiles. sh.rowidx
-    // holds the pass's source rows (written and synchronised by the caller).
+    // holds the pass's source rows (written and synchronised by the caller);
+    // nsteps covers the latest window of the workgroup's waves.
     template <int MTA>
-    static __device__ __forceinline__ void run(Shared& sh, const uint8_t* w, const uint8_t* ws, int K,
-                                               const int (&tile_row)[NT], int nrows, const uint16_t* xb,
-                                               size_t xpitch, int nvalid, f32x4 (&acc)[NT][4]) {
-        const int nsteps = (K + kEngineStepCols - 1) / kEngineStepCols;
+    static __device__ __forceinline__ void run(Shared& sh, __amdgpu_buffer_rsrc_t wres, const uint8_t* ws, int K,
+                                               const int (&row0)[NT], int stride, int mb, int nsteps, int nrows,
+                                               const uint16_t* xb, size_t xpitch, int nvalid, f32x4 (&acc)[NT][4]) {
         const int wave = threadIdx.x / kWave;
         uint4* wbuf = sh.wbuf[wave];
         uint8_t* sbuf = sh.sbuf[wave];
@@ -188,7 +234,8 @@ struct MoeEngine {
         uint4 tr[2][MTA];
         // step s: weights requested at s - 2 into buffer s % 3, tokens requested
         // at s - 2 into registers s % 2, written to panel s % 3 at the end of
-        // sub-iteration s - 1. The loop starts two steps early so that the first
+        // sub-iteration s - 1 (panel (s - 1) % 3 still holds step s - 1 during
+        // step s). The loop starts two steps early so that the first
         // sub-iterations only issue loads (and write panel 0). Sub-iterations
         // are unrolled by six so that every buffer index is static.
         for (int it = -2; it < nsteps; it += 6) {
@@ -199,9 +246,11 @@ struct MoeEngine {
                 const int next = min(s + 2, nsteps - 1);
                 issue_tokens<MTA>(tr[bsub & 1], src, K, next);
                 engine_fence();
-                issue_weights(buf[bsub % 3], w, ws, K, tile_row, nrows, next);
+                issue_weights(buf[bsub % 3], wres, ws, K, row0, stride, mb, nrows, next);
                 engine_fence();
-                if (s >= 0) compute<MTA>(buf[(bsub + 1) % 3], wbuf, sbuf, sh.panel[(bsub + 1) % 3], acc);
+                if (s >= 0)
+                    compute<MTA>(buf[(bsub + 1) % 3], wbuf, sbuf, sh.panel[(bsub + 1) % 3], sh.panel[bsub % 3],
+                                 s == 0, mb, acc);
                 engine_fence();
                 // tokens of step s + 1 (requested one sub-iteration ago) -> panel (s + 1) % 3
                 store_tokens<MTA>(tr[(bsub + 1) & 1], sh.panel[(bsub + 2) % 3], K, min(max(s + 1, 0), nsteps - 1));
@@ -211,14 +260,15 @@ struct MoeEngine {
     }
 
     // run<MTA> for MTA = mt (1 <= mt <= 4), chosen once per pass.
-    static __device__ __forceinline__ void run_mt(int mt, Shared& sh, const uint8_t* w, const uint8_t* ws, int K,
-                                                  const int (&tile_row)[NT], int nrows, const uint16_t* xb,
-                                                  size_t xpitch, int nvalid, f32x4 (&acc)[NT][4]) {
+    static __device__ __forceinline__ void run_mt(int mt, Shared& sh, __amdgpu_buffer_rsrc_t wres, const uint8_t* ws,
+                                                  int K, const int (&row0)[NT], int stride, int mb, int nsteps,
+                                                  int nrows, const uint16_t* xb, size_t xpitch, int nvalid,
+                                                  f32x4 (&acc)[NT][4]) {
         switch (mt) {
-            case 1: run<1>(sh, w, ws, K, tile_row, nrows, xb, xpitch, nvalid, acc); break;
-            case 2: run<2>(sh, w, ws, K, tile_row, nrows, xb, xpitch, nvalid, acc); break;
-            case 3: run<3>(sh, w, ws, K, tile_row, nrows, xb, xpitch, nvalid, acc); break;
-            default: run<4>(sh, w, ws, K, tile_row, nrows, xb, xpitch, nvalid, acc); break;
+            case 1: run<1>(sh, wres, ws, K, row0, stride, mb, nsteps, nrows, xb, xpitch, nvalid, acc); break;
+            case 2: run<2>(sh, wres, ws, K, row0, stride, mb, nsteps, nrows, xb, xpitch, nvalid, acc); break;
+            case 3: run<3>(sh, wres, ws, K, row0, stride, mb, nsteps, nrows, xb, xpitch, nvalid, acc); break;
+            default: run<4>(sh, wres, ws, K, row0, stride, mb, nsteps, nrows, xb, xpitch, nvalid, acc); break;
         }
     }
 };

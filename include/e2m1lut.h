@@ -317,7 +317,8 @@ size_t mxfp4_moe_workspace_size(int64_t tokens, int64_t hidden, int64_t inter, i
  *   workspace      device buffer of at least mxfp4_moe_workspace_size()
  *                  bytes, 256-byte aligned; contents need no initialisation
  * Requires hidden % 32 == 0, inter % 32 == 0, 1 <= experts <=
- * E2M1_MOE_MAX_EXPERTS, topk >= 1, tokens >= 0, tokens * topk <= INT_MAX.
+ * E2M1_MOE_MAX_EXPERTS, topk >= 1, tokens >= 0, tokens * topk <= INT_MAX,
+ * inter * hidden < 2^31 (each expert's W13 below 2 GiB).
  * Ids outside [0, experts) are not checked on the host (they live on the
  * device); the kernels skip such slots (they contribute nothing).
  */
