@@ -8,7 +8,10 @@ at batch 1 on the Llama-8B MLP shapes (W 14336 x 4096 and W 4096 x 14336, one
 launch each per step), bf16 output. Other workloads (for the per-kernel
 roofline tables): mlp_b2, mlp_b4, mlp_b16, ternary, ternary_b1 .. ternary_b16
 (small-batch ternary GEMM), ternary_wl, gather, moe, decode, quantize,
-prefill (MXFP4 GEMM, 2048 tokens), gemv_small.
+prefill (MXFP4 GEMM, 2048 tokens), nm_2of4, nm_4of8, gemv_small. Platform
+reference points (libe2m1probe.so): floor (empty launches), stream_31mb and
+stream_31mb_store (a plain read of the headline launch's 31.2 MB, without and
+with a small store), stream_128mb, stream_512mb, mfma_peak.
 
 Timing: inputs are resident in HBM before the timed region. The launches of
 one step per weight copy are captured into a HIP graph; W warmup steps are
@@ -20,8 +23,8 @@ cycled per replay exceed the 256 MB Infinity Cache: every launch reads its
 weights from HBM.
 
 `cpu_baseline` is the CPU oracle (plain C, fp64, OpenMP over rows) timed on a
-bounded sample of the same workload on this host's cores -- a reported
-baseline, not a target.
+bounded sample of the same workload on this host's cores, then again on one
+core (`single_core`) -- a reported baseline, not a target.
 """
 from __future__ import annotations
 
@@ -51,6 +54,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 # The declarations in kernels.hpp and the host-side checks in api.hip compile to
 # no device code; each kernel's launch logic lives in its own source file.
 KERNEL_SOURCES = {
+    "probe": ["../probe/platform_probe.hip"],
     "gemv": ["gemv.hip"],
     "moe": ["moe.hip", "moe_engine.hpp"],
     "ternary": ["ternary.hip", "ternary_batch.hip", "ternary_int8.hpp"],
@@ -85,7 +89,8 @@ def kernel_source_hash(label: str, flags: str | None = None) -> str:
     family = label.split("_")[0]
     h = hashlib.sha256()
     h.update((build_fingerprint() if flags is None else flags).encode())
-    for name in sorted(KERNEL_SOURCES.get(family, []) + COMMON_SOURCES):
+    common = [] if family == "probe" else COMMON_SOURCES
+    for name in sorted(KERNEL_SOURCES.get(family, []) + common):
         path = os.path.join(CSRC, name)
         if os.path.exists(path):
             with open(path, encoding="utf-8") as fh:
@@ -113,9 +118,15 @@ class Workload:
 
     weight_bytes_per_step = 0.0
     total_bytes_per_step = 0.0
+    # a reference-point workload reports its own metric instead of the headline's
+    metric: str | None = None
 
     def cpu_baseline(self, budget_s: float) -> dict | None:
         return None
+
+    def headline(self, ms_per_step: float, per_launch: dict) -> tuple[float, str, bool]:
+        """(value, unit, higher_is_better) of the JSON line for a reference-point workload."""
+        raise NotImplementedError
 
 
 def _gen(seed: int):
@@ -645,6 +656,21 @@ class GemvSmall(Workload):
     def alg_bytes(self, label):
         return 256 * 256 + 256 * 16 + 512 * 2 + 256 * 4
 
+    def cpu_baseline(self, budget_s):
+        import oracle
+        p, s = self.p.cpu().numpy(), self.s.cpu().numpy()
+        x = self.x.view(__import__("torch").int16).cpu().numpy().view(np.uint16)
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.mxfp4_gemv(p, s, x)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s or reps >= 20000:
+                break
+        return {"value": round(self.weight_bytes_per_step * reps / el / 1e9, 4), "unit": "GB/s",
+                "cores": oracle.threads(), "kind": "oracle",
+                "sample": f"the full 256 x 512 GEMV repeated {reps} times, {el:.1f} s"}
+
 
 class Moe(Workload):
     def __init__(self, rotate_bytes: float, E=32, H=2880, I=2880, T=256, topk=4):
@@ -713,7 +739,165 @@ class Moe(Workload):
                           f"repeated {reps} times, {el:.1f} s"}
 
 
+# ------------------------------------------------------ platform probe ---
+# Reference points measured with the simplest kernels (libe2m1probe.so, built
+# beside the library): an empty launch, plain HBM streams of the headline
+# launch's size and larger, and a kernel that keeps every matrix core busy.
+
+PROBE_LIB = os.path.join(ROOT, "gemm_e2m1_lut_amd", "probe", "libe2m1probe.so")
+_probe = None
+# grid sizes of the empty marker launches that `--mark-labels` puts before each launch label
+MARK_BASE = 9001
+
+
+def probe_library():
+    global _probe
+    if _probe is None:
+        import ctypes
+        if not os.path.exists(PROBE_LIB):
+            raise ImportError(f"{PROBE_LIB} is missing: build with `python -m gemm_e2m1_lut_amd.build`")
+        lib = ctypes.CDLL(PROBE_LIB)
+        i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+        for name, res, argt in (("e2m1_probe_empty", i32, [i64, i32, vp]),
+                                ("e2m1_probe_stream_grid", i64, [i64, i32]),
+                                ("e2m1_probe_stream", i32, [vp, i64, vp, i64, i32, i32, vp]),
+                                ("e2m1_probe_mfma", i32, [i64, i32, vp, i64, vp])):
+            fn = getattr(lib, name)
+            fn.restype, fn.argtypes = res, argt
+        _probe = lib
+    return _probe
+
+
+def _stream_handle():
+    import ctypes
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _probe_ok(status: int, what: str) -> None:
+    if status != 0:
+        raise RuntimeError(f"{what} failed with status {status}")
+
+
+def probe_mark(index: int) -> None:
+    """An empty launch of MARK_BASE + index workgroups: in a profiler's dispatch list the
+    kernels between two marks belong to one launch label."""
+    _probe_ok(probe_library().e2m1_probe_empty(MARK_BASE + index, 64, _stream_handle()), "marker")
+
+
+class EmptyFloor(Workload):
+    """Empty kernels, launched back to back from a graph: the per-launch floor."""
+    GRIDS = (1, 3808)
+
+    def __init__(self, rotate_bytes: float):
+        self.name = "empty_kernel_floor"
+        self.copies = 256          # launches of each label per graph
+        self.bound = "latency"
+        self.metric = "per-launch time of an empty kernel (graph replay, back to back)"
+        self.config = {"workload": self.name, "grids": list(self.GRIDS), "block": 64,
+                       "launches_per_graph": self.copies}
+
+    def launches(self):
+        lib = probe_library()
+        out = []
+        for grid in self.GRIDS:
+            def fn(i, grid=grid):
+                _probe_ok(lib.e2m1_probe_empty(grid, 64, _stream_handle()), "empty")
+            out.append((f"probe_empty_{grid}x64", fn))
+        return out
+
+    def alg_bytes(self, label):
+        return 0
+
+    def headline(self, ms_per_step, per_launch):
+        return round(1e3 * max(per_launch.values()), 4), "us", False
+
+
+class HbmStream(Workload):
+    """A plain read of `nbytes` from HBM (16-byte non-temporal loads, every load issued
+    first), optionally with a small store per wave: the streaming ceiling at that size."""
+
+    def __init__(self, nbytes: int, store: bool, rotate_bytes: float, block: int = 64):
+        import torch
+        self.nbytes, self.store, self.block = nbytes, store, block
+        self.name = f"hbm_stream_{nbytes}B" + ("_store" if store else "")
+        self.copies = max(2, math.ceil(rotate_bytes / nbytes))
+        g = _gen(777)
+        self.bufs = [torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device="cuda", generator=g)
+                     for _ in range(self.copies)]
+        self.grid = int(probe_library().e2m1_probe_stream_grid(nbytes, block))
+        if self.grid < 1:
+            raise ValueError(f"no stream grid for {nbytes} bytes")
+        self.out_words = self.grid * block // 64
+        self.out = torch.zeros(self.out_words, dtype=torch.int32, device="cuda")
+        self.label = f"probe_stream{'_store' if store else ''}_{nbytes}B"
+        self.weight_bytes_per_step = float(nbytes)
+        self.total_bytes_per_step = float(self.alg_bytes(self.label))
+        self.metric = f"HBM read rate of a plain {nbytes}-byte stream" + (" with a 4-byte store per wave"
+                                                                        if store else "")
+        self.config = {"workload": self.name, "bytes": nbytes, "grid": self.grid, "block": block,
+                       "loads_per_lane": "8 x 16 B non-temporal", "store": "4 B per wave" if store else "none",
+                       "buffers_rotated": self.copies, "rotated_MB": round(self.copies * nbytes / 1e6, 1)}
+
+    def launches(self):
+        lib = probe_library()
+
+        def fn(i):
+            _probe_ok(lib.e2m1_probe_stream(self.bufs[i % self.copies].data_ptr(), self.nbytes,
+                                            self.out.data_ptr(), self.out_words, self.block,
+                                            1 if self.store else 0, _stream_handle()), "stream")
+        return [(self.label, fn)]
+
+    def alg_bytes(self, label):
+        return self.nbytes + (4 * self.out_words if self.store else 0)
+
+    def headline(self, ms_per_step, per_launch):
+        return round(self.nbytes / (per_launch[self.label] * 1e-3) / 1e9, 2), "GB/s", True
+
+
+class MfmaPeak(Workload):
+    """Four independent v_mfma_f32_32x32x16_bf16 chains per wave, two waves per SIMD: the
+    bf16 matrix-core rate a kernel can reach, and the reading of the MFMA-busy counter
+    for a kernel that keeps the matrix cores saturated."""
+    GRID, ITERS = 512, 2048
+
+    def __init__(self, rotate_bytes: float):
+        import torch
+        self.name = "mfma_bf16_peak"
+        self.copies = 4
+        self.bound = "mfma"
+        self.out = torch.zeros(self.GRID * 256, dtype=torch.float32, device="cuda")
+        self.metric = "bf16 MFMA rate of a kernel of back-to-back independent 32x32x16 MFMAs"
+        self.config = {"workload": self.name, "grid": self.GRID, "block": 256, "iters": self.ITERS,
+                       "chains_per_wave": 4, "instruction": "v_mfma_f32_32x32x16_bf16"}
+
+    def launches(self):
+        lib = probe_library()
+
+        def fn(i):
+            _probe_ok(lib.e2m1_probe_mfma(self.GRID, self.ITERS, self.out.data_ptr(), self.out.numel(),
+                                          _stream_handle()), "mfma")
+        return [("probe_mfma_32x32x16", fn)]
+
+    def alg_bytes(self, label):
+        return 0
+
+    def alg_flops(self, label):
+        return float(self.GRID * 4 * self.ITERS * 4 * 32768)
+
+    def headline(self, ms_per_step, per_launch):
+        return round(self.alg_flops("") / (per_launch["probe_mfma_32x32x16"] * 1e-3) / 1e12, 1), "TFLOP/s", True
+
+
+HEADLINE_BYTES = 14336 * 4096 // 2 + 14336 * 4096 // 32   # one batch-1 MLP GEMV launch's weights
+
 WORKLOADS = {
+    "floor": EmptyFloor,
+    "stream_31mb": lambda rb: HbmStream(HEADLINE_BYTES, False, rb),
+    "stream_31mb_store": lambda rb: HbmStream(HEADLINE_BYTES, True, rb),
+    "stream_128mb": lambda rb: HbmStream(128 << 20, False, rb),
+    "stream_512mb": lambda rb: HbmStream(512 << 20, False, rb),
+    "mfma_peak": MfmaPeak,
     "moe": Moe,
     "mlp_b1": lambda rb: GemvMLP(1, rb),
     "mlp_b2": lambda rb: GemvMLP(2, rb),
@@ -819,16 +1003,64 @@ def traffic_from_profile(label: str) -> dict | None:
     return entry
 
 
-def cpu_model() -> str:
-    """The host CPU's model name, as /proc/cpuinfo reports it."""
+def cpu_description() -> dict:
+    """What identifies the host CPU: /proc/cpuinfo's fields for the first processor (model name,
+    vendor, family, model, stepping, cache size, clock), the number of logical processors, the
+    CPUs this process may run on, and the L2/L3 sizes from sysfs."""
+    info: dict = {}
+    keys = ("model name", "vendor_id", "cpu family", "model", "stepping", "cache size", "cpu MHz",
+            "cpu cores", "siblings")
     try:
         with open("/proc/cpuinfo") as fh:
-            for line in fh:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+            text = fh.read()
+        first = text.split("\n\n")[0]
+        for line in first.splitlines():
+            k, _, v = line.partition(":")
+            k = k.strip()
+            if k in keys and k not in info:
+                info[k] = v.strip()
+        info["logical_processors"] = text.count("processor\t:")
     except OSError:
         pass
-    return "unknown"
+    try:
+        info["affinity_cpus"] = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        pass
+    cache = "/sys/devices/system/cpu/cpu0/cache"
+    for idx in range(8):
+        d = os.path.join(cache, f"index{idx}")
+        try:
+            with open(os.path.join(d, "level")) as fh:
+                level = fh.read().strip()
+            with open(os.path.join(d, "type")) as fh:
+                kind = fh.read().strip()
+            with open(os.path.join(d, "size")) as fh:
+                size = fh.read().strip()
+        except OSError:
+            continue
+        if kind in ("Unified", "Data"):
+            info[f"L{level}{'d' if kind == 'Data' else ''}"] = size
+    return info
+
+
+def run_cpu_baseline(wl, budget_s: float, budget_1core_s: float) -> dict | None:
+    """The oracle on this host: on all its OpenMP threads, then on one."""
+    import oracle
+    cpu = wl.cpu_baseline(budget_s)
+    if cpu is None:
+        return None
+    n0 = oracle.threads()
+    try:
+        oracle.set_threads(1)
+        one = wl.cpu_baseline(budget_1core_s)
+    finally:
+        oracle.set_threads(n0)
+    cpu["single_core"] = {"value": one["value"], "unit": one["unit"], "cores": 1, "sample": one["sample"]}
+    desc = cpu_description()
+    cpu["cpu_model"] = desc.get("model name", "unknown")
+    cpu["cpu"] = desc
+    cpu["build"] = "gcc " + " ".join(oracle.CFLAGS)
+    return cpu
 
 
 def main() -> int:
@@ -843,6 +1075,10 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-mb", type=int, default=0, help="run a plain copy of this size first "
                     "(counter calibration under rocprofv3 --pmc)")
+    ap.add_argument("--mark-labels", action="store_true",
+                    help="before the warmup, run each launch label once after an empty marker launch of "
+                         f"{MARK_BASE} + index workgroups (for attributing profiler records to labels); "
+                         f"with --copy-mb, the copies sit between two marks of {MARK_BASE - 1}")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -859,10 +1095,23 @@ def main() -> int:
     torch.cuda.set_device(0)
 
     if args.copy_mb:
+        if args.mark_labels:
+            probe_mark(-1)
         copy_calibration(args.copy_mb)
+        if args.mark_labels:
+            probe_mark(-1)
 
     wl = WORKLOADS[args.workload](args.rotate_mb * 1e6)
     launches = wl.launches()
+    if args.mark_labels:
+        torch.cuda.synchronize()
+        for j, (_, fn) in enumerate(launches):
+            probe_mark(j)
+            fn(0)
+        probe_mark(len(launches))
+        torch.cuda.synchronize()
+        print(json.dumps({"label_marks": {label: MARK_BASE + j for j, (label, _) in enumerate(launches)},
+                          "end_mark": MARK_BASE + len(launches)}), file=sys.stderr, flush=True)
     for i in range(max(2, wl.copies)):          # eager warmup: fills the library's launch caches
         for _, fn in launches:
             fn(i)
@@ -872,6 +1121,9 @@ def main() -> int:
     per_launch = per_launch_ms(launches, wl.copies, args.steps)
 
     value = wl.weight_bytes_per_step / (ms_per_step * 1e-3) / 1e9
+    unit, higher = "GB/s", True
+    if wl.metric is not None:
+        value, unit, higher = wl.headline(ms_per_step, per_launch)
     pct_hbm = wl.total_bytes_per_step / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS * 100.0
 
     kernels = []
@@ -894,21 +1146,17 @@ def main() -> int:
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = wl.cpu_baseline(args.cpu_budget_s)
-        if cpu is not None:
-            import oracle
-            cpu["cpu_model"] = cpu_model()
-            cpu["build"] = "gcc " + " ".join(oracle.CFLAGS)
+        cpu = run_cpu_baseline(wl, args.cpu_budget_s, args.cpu_budget_s)
 
     line = {
-        "metric": METRIC,
-        "value": round(value, 2),
-        "unit": "GB/s",
+        "metric": wl.metric or METRIC,
+        "value": round(value, 4 if unit == "us" else 2),
+        "unit": unit,
         "n_gpus": 1,
         "steps": steps_timed,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
+        "higher_is_better": higher,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": wl.dtype,

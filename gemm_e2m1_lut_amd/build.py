@@ -3,8 +3,11 @@
     python -m gemm_e2m1_lut_amd.build        # or: from gemm_e2m1_lut_amd.build import build
 
 Every .hip source under csrc/ is compiled to an object in _build/ (in
-parallel), then linked into gemm_e2m1_lut_amd/libe2m1lut.so. Each call
-recompiles everything.
+parallel), then linked into gemm_e2m1_lut_amd/libe2m1lut.so. The platform
+probe (probe/platform_probe.hip: an empty kernel and plain HBM streams, which
+the benchmark runs as reference points) is built beside it into
+probe/libe2m1probe.so; the library never loads it. Each call recompiles
+everything.
 """
 from __future__ import annotations
 
@@ -21,6 +24,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libe2m1lut.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
+PROBE_SRC = os.path.join(PKG, "probe", "platform_probe.hip")
+PROBE_LIB = os.path.join(PKG, "probe", "libe2m1probe.so")
 
 # Target: gfx950 with XNACK off, the MI355X default. Compiled for XNACK off, a
 # load's destination registers may overlap its address (no replay to
@@ -61,23 +66,25 @@ def _run(cmd: list[str]) -> None:
 
 
 def build(jobs: int | None = None) -> str:
-    """Compile every source and link the shared library; returns its path."""
+    """Compile every source, link the shared library and the probe; returns the library's path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
-    srcs = sources()
+    srcs = sources() + [PROBE_SRC]
     objs = [os.path.join(BUILD_DIR, os.path.basename(s)[:-4] + ".o") for s in srcs]
     jobs = jobs or min(len(srcs), int(os.environ.get("MAX_JOBS", "8")))
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         list(ex.map(lambda so: _run([HIPCC, *HIPFLAGS, "-c", so[0], "-o", so[1]]), zip(srcs, objs)))
-    tmp = LIB_PATH + ".tmp"
-    _run([HIPCC, *OFFLOAD, "-shared", "-fPIC", "-o", tmp, *objs])
-    os.replace(tmp, LIB_PATH)
+    for path, linked in ((LIB_PATH, objs[:-1]), (PROBE_LIB, objs[-1:])):
+        tmp = path + ".tmp"
+        _run([HIPCC, *OFFLOAD, "-shared", "-fPIC", "-o", tmp, *linked])
+        os.replace(tmp, path)
     return LIB_PATH
 
 
 def clean() -> None:
     shutil.rmtree(BUILD_DIR, ignore_errors=True)
-    if os.path.exists(LIB_PATH):
-        os.remove(LIB_PATH)
+    for path in (LIB_PATH, PROBE_LIB):
+        if os.path.exists(path):
+            os.remove(path)
 
 
 if __name__ == "__main__":

@@ -1,0 +1,140 @@
+// platform_probe.hip -- the platform limits a per-launch roofline figure is
+// read against, measured with the simplest possible kernels: the time of an
+// empty launch, the time to stream B bytes from HBM with nothing else to do,
+// and a kernel that keeps every SIMD's matrix core busy (the reference point
+// for the MFMA-busy counter). Built into libe2m1probe.so (separate from
+// libe2m1lut.so, which never loads it) and run by the benchmark's probe
+// workloads.
+//
+// C entry points (the benchmark calls them through ctypes):
+//
+//   int e2m1_probe_empty(int64_t grid, int block, void* stream)
+//       Launches an empty kernel of `grid` workgroups of `block` threads
+//       (block 64 or 256, 1 <= grid < 2^31).
+//
+//   int64_t e2m1_probe_stream_grid(int64_t bytes, int block)
+//       The grid e2m1_probe_stream launches for `bytes` (-1 if invalid).
+//
+//   int e2m1_probe_stream(const void* src, int64_t bytes, uint32_t* out,
+//                         int64_t out_words, int block, int store, void* stream)
+//       Reads `bytes` (a positive multiple of 16) from the device buffer
+//       `src` with 16-byte non-temporal loads: each thread issues all eight
+//       of its loads first, and load j of a wave covers 1 KB of consecutive
+//       bytes. With store = 0 nothing is written (a store guarded by a
+//       checksum test no input meets keeps the loads live); with store = 1
+//       every wave writes one 4-byte checksum to out[wave] (out_words must
+//       be at least grid * block / 64): a small output like a GEMV's.
+//
+//   int e2m1_probe_mfma(int64_t grid, int iters, float* out, int64_t out_words,
+//                       void* stream)
+//       grid workgroups of four waves; every wave runs `iters` rounds of four
+//       independent v_mfma_f32_32x32x16_bf16 chains (32768 flops each) on
+//       register operands, then writes one float per thread to out
+//       (out_words >= grid * 256). Flops per launch: grid * 4 * iters * 4 * 32768.
+//
+// All return 0, or -1 for an argument out of range, -2 for a launch error.
+// Every index is clamped to the buffer, so every access is in bounds.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kLoads = 8;
+constexpr uint32_t kNever = 0x9E3779B9u;
+
+template <int kBlock>
+__global__ __launch_bounds__(kBlock) void probe_empty_kernel() {}
+
+template <int kBlock, bool kStore>
+__global__ __launch_bounds__(kBlock) void probe_stream_kernel(const u32x4* __restrict__ src, int64_t n16,
+                                                              uint32_t* __restrict__ out) {
+    const int64_t base = (int64_t)blockIdx.x * kLoads * kBlock + threadIdx.x;
+    u32x4 v[kLoads];
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+        const int64_t i = base + (int64_t)j * kBlock;
+        v[j] = __builtin_nontemporal_load(src + (i < n16 ? i : n16 - 1));
+    }
+    __builtin_amdgcn_sched_barrier(0);  // every load is issued before the first wait
+    uint32_t acc = 0;
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) acc ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
+    if constexpr (kStore) {
+        for (int d = 32; d >= 1; d >>= 1) acc ^= __shfl_xor(acc, d, 64);
+        if ((threadIdx.x & 63) == 0) out[(int64_t)blockIdx.x * (kBlock / 64) + threadIdx.x / 64] = acc;
+    } else {
+        if (acc == kNever) out[0] = acc;
+    }
+}
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__global__ __launch_bounds__(256) void probe_mfma_kernel(int iters, float* __restrict__ out) {
+    bf16x8 a, b;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        a[i] = (__bf16)((float)((threadIdx.x + i) & 7) * 0.125f);
+        b[i] = (__bf16)((float)((threadIdx.x * 3 + i) & 7) * -0.0625f);
+    }
+    f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+    for (int it = 0; it < iters; ++it) {
+        c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
+        c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
+        c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
+    }
+    const f32x16 t = c0 + c1 + c2 + c3;
+    float total = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) total += t[e];
+    out[(int64_t)blockIdx.x * 256 + threadIdx.x] = total;
+}
+
+int64_t stream_grid(int64_t bytes, int block) {
+    if (bytes <= 0 || bytes % 16 != 0 || (block != 64 && block != 256)) return -1;
+    const int64_t per = (int64_t)kLoads * block;
+    const int64_t grid = (bytes / 16 + per - 1) / per;
+    return grid < ((int64_t)1 << 31) ? grid : -1;
+}
+
+}  // namespace
+
+extern "C" int e2m1_probe_empty(int64_t grid, int block, void* stream) {
+    if (grid < 1 || grid >= ((int64_t)1 << 31)) return -1;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (block == 64) probe_empty_kernel<64><<<dim3((unsigned)grid), dim3(64), 0, s>>>();
+    else if (block == 256) probe_empty_kernel<256><<<dim3((unsigned)grid), dim3(256), 0, s>>>();
+    else return -1;
+    return hipGetLastError() == hipSuccess ? 0 : -2;
+}
+
+extern "C" int64_t e2m1_probe_stream_grid(int64_t bytes, int block) { return stream_grid(bytes, block); }
+
+extern "C" int e2m1_probe_stream(const void* src, int64_t bytes, uint32_t* out, int64_t out_words, int block,
+                                 int store, void* stream) {
+    const int64_t grid = stream_grid(bytes, block);
+    if (grid < 0 || src == nullptr || out == nullptr || out_words < 1) return -1;
+    if (store && out_words < grid * (block / 64)) return -1;
+    const u32x4* p = static_cast<const u32x4*>(src);
+    const int64_t n16 = bytes / 16;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const dim3 g((unsigned)grid);
+    if (block == 64) {
+        if (store) probe_stream_kernel<64, true><<<g, dim3(64), 0, s>>>(p, n16, out);
+        else probe_stream_kernel<64, false><<<g, dim3(64), 0, s>>>(p, n16, out);
+    } else {
+        if (store) probe_stream_kernel<256, true><<<g, dim3(256), 0, s>>>(p, n16, out);
+        else probe_stream_kernel<256, false><<<g, dim3(256), 0, s>>>(p, n16, out);
+    }
+    return hipGetLastError() == hipSuccess ? 0 : -2;
+}
+
+extern "C" int e2m1_probe_mfma(int64_t grid, int iters, float* out, int64_t out_words, void* stream) {
+    if (grid < 1 || grid >= ((int64_t)1 << 31) || iters < 1 || out == nullptr || out_words < grid * 256) return -1;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    probe_mfma_kernel<<<dim3((unsigned)grid), dim3(256), 0, s>>>(iters, out);
+    return hipGetLastError() == hipSuccess ? 0 : -2;
+}

@@ -73,6 +73,7 @@ def load():
     sig = {
         "or_abi_version": (ctypes.c_int, []),
         "or_threads": (ctypes.c_int, []),
+        "or_set_threads": (None, [ctypes.c_int]),
         "or_e2m1_magnitude": (f64, [ctypes.c_int]),
         "or_bf16_from_double": (u16, [f64]),
         "or_double_from_bf16": (f64, [u16]),
@@ -124,6 +125,11 @@ def _check(status, what):
 
 def threads() -> int:
     return int(load().or_threads())
+
+
+def set_threads(n: int) -> None:
+    """Thread count of the OpenMP loops from now on (every result is independent of it)."""
+    load().or_set_threads(int(n))
 
 
 # ------------------------------------------------------------------ scalars --

@@ -67,6 +67,15 @@ int or_threads(void) {
 #endif
 }
 
+/* Threads for the loops that follow (n >= 1); results do not depend on it. */
+void or_set_threads(int n) {
+#ifdef _OPENMP
+    omp_set_num_threads(n > 0 ? n : 1);
+#else
+    (void)n;
+#endif
+}
+
 double or_e2m1_magnitude(int index) { return E2M1_MAGNITUDE[index & 7]; }
 
 /* ---------------------------------------------------------------- bf16 --- */

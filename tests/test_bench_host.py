@@ -49,3 +49,58 @@ def test_build_flags_change_the_fingerprint():
     assert same == bench.kernel_source_hash("gemv_b1_14336x4096")
     assert same != bench.kernel_source_hash("gemv_b1_14336x4096", flags.replace("xnack-", "xnack+"))
     assert same != bench.kernel_source_hash("gemv_b1_14336x4096", flags.replace("-O3", "-O2"))
+
+
+def test_cpu_description_names_the_host():
+    d = bench.cpu_description()
+    assert d.get("logical_processors", 0) >= 1
+    assert d.get("affinity_cpus", 0) >= 1
+    assert "model name" in d
+
+
+def test_cpu_baseline_runs_the_oracle_on_one_core_too():
+    import oracle
+
+    class Fake(bench.Workload):
+        def cpu_baseline(self, budget_s):
+            return {"value": float(oracle.threads()), "unit": "GB/s", "cores": oracle.threads(),
+                    "kind": "oracle", "sample": "fake"}
+
+    n0 = oracle.threads()
+    cpu = bench.run_cpu_baseline(Fake(), 0.0, 0.0)
+    assert cpu["cores"] == n0 and cpu["single_core"]["cores"] == 1 and cpu["single_core"]["value"] == 1.0
+    assert oracle.threads() == n0
+    assert cpu["cpu"]["logical_processors"] >= 1
+
+
+def test_profile_kernel_names():
+    import bench_profile as bp
+    assert bp.short_name("(anonymous namespace)::probe_empty_kernel<64>()") == "probe_empty_kernel<64>"
+    assert bp.short_name("void e2m1::(anonymous namespace)::gemv_b1_rows_kernel<1, 2, 4, true>(e2m1::Args)") \
+        == "gemv_b1_rows_kernel<1, 2, 4, true>"
+    assert bp.short_name("void at::native::vectorized_elementwise_kernel<4, at::native::f(at::T&)::{lambda(float)#1}, "
+                         "std::array<char*, 2ul> >(int, char*)").startswith("vectorized_elementwise_kernel<4,")
+
+
+def test_profile_records_are_attributed_by_marks():
+    """Records between a label's mark and the next belong to that label, and so does every
+    later record with the same kernel, grid and workgroup; the copies sit between two marks
+    of MARK_BASE - 1."""
+    import bench_profile as bp
+
+    def rec(i, kernel, grid, wg=256):
+        return {"id": i, "kernel": kernel, "grid": grid, "wg": wg, "counters": {}}
+
+    def mark(i, g):
+        return rec(i, "probe_empty_kernel<64>", g * 64, 64)
+
+    recs = [mark(0, bp.MARK_BASE - 1), rec(1, "copy", 1 << 20), mark(2, bp.MARK_BASE - 1),
+            rec(3, "fill", 512),
+            mark(4, bp.MARK_BASE), rec(5, "k1", 1024), rec(6, "k2", 2048),
+            mark(7, bp.MARK_BASE + 1), rec(8, "k1", 4096),
+            mark(9, bp.MARK_BASE + 2),
+            rec(10, "k1", 1024), rec(11, "k1", 4096), rec(12, "k2", 2048), rec(13, "fill", 512)]
+    per, copies = bp.attribute(recs, ["a", "b"])
+    assert [r["id"] for r in copies] == [1]
+    assert [r["id"] for r in per["a"]] == [5, 6, 10, 12]
+    assert [r["id"] for r in per["b"]] == [8, 11]

@@ -317,3 +317,24 @@ def test_ternary_gemm_rows_are_independent(orc):
     y = orc.ternary_gemm(case["packed"], case["row_scale"], x)
     yp = orc.ternary_gemm(case["packed"], case["row_scale"], x[perm])
     assert np.array_equal(yp, y[perm]) and (y[4] == 0).all()
+
+
+def test_results_do_not_depend_on_the_thread_count(orc):
+    """The CPU baseline times the oracle on one thread and on all of them: OpenMP splits
+    rows only, never a sum, so both give the same bits."""
+    case = synth.mxfp4_gemv_case(77, 96, 512, 2)
+    tc = synth.ternary_case(78, 64, 512)
+    xt = np.random.default_rng(79).standard_normal((3, 512)).astype(np.float32)
+    n0 = orc.threads()
+    try:
+        orc.set_threads(1)
+        one = (orc.mxfp4_gemv_f64(case["packed"], case["scales"], case["x"]),
+               orc.ternary_gemm(tc["packed"], tc["row_scale"], xt, want_f64=True)[1])
+        assert orc.threads() == 1
+        orc.set_threads(max(2, n0))
+        many = (orc.mxfp4_gemv_f64(case["packed"], case["scales"], case["x"]),
+                orc.ternary_gemm(tc["packed"], tc["row_scale"], xt, want_f64=True)[1])
+    finally:
+        orc.set_threads(n0)
+    for a, b in zip(one, many):
+        assert np.array_equal(a, b)
