@@ -11,7 +11,8 @@ roofline tables): mlp_b2, mlp_b4, mlp_b16, ternary, ternary_b1 .. ternary_b16
 prefill (MXFP4 GEMM, 2048 tokens), nm_2of4, nm_4of8, gemv_small. Platform
 reference points (libe2m1probe.so): floor (empty launches), stream_31mb and
 stream_31mb_store (a plain read of the headline launch's 31.2 MB, without and
-with a small store), stream_128mb, stream_512mb, mfma_peak.
+with a 4-byte store per wave), stream_31mb_store1 (one 4-byte store in all),
+stream_128mb, stream_512mb, mfma_peak.
 
 Timing: inputs are resident in HBM before the timed region. The launches of
 one step per weight copy are captured into a HIP graph; W warmup steps are
@@ -817,10 +818,12 @@ class HbmStream(Workload):
     """A plain read of `nbytes` from HBM (16-byte non-temporal loads, every load issued
     first), optionally with a small store per wave: the streaming ceiling at that size."""
 
-    def __init__(self, nbytes: int, store: bool, rotate_bytes: float, block: int = 64):
+    STORES = {0: "", 1: "_store", 2: "_store1"}
+
+    def __init__(self, nbytes: int, store: int, rotate_bytes: float, block: int = 64):
         import torch
         self.nbytes, self.store, self.block = nbytes, store, block
-        self.name = f"hbm_stream_{nbytes}B" + ("_store" if store else "")
+        self.name = f"hbm_stream_{nbytes}B" + self.STORES[store]
         self.copies = max(2, math.ceil(rotate_bytes / nbytes))
         g = _gen(777)
         self.bufs = [torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device="cuda", generator=g)
@@ -830,13 +833,13 @@ class HbmStream(Workload):
             raise ValueError(f"no stream grid for {nbytes} bytes")
         self.out_words = self.grid * block // 64
         self.out = torch.zeros(self.out_words, dtype=torch.int32, device="cuda")
-        self.label = f"probe_stream{'_store' if store else ''}_{nbytes}B"
+        self.label = f"probe_stream{self.STORES[store]}_{nbytes}B"
         self.weight_bytes_per_step = float(nbytes)
         self.total_bytes_per_step = float(self.alg_bytes(self.label))
-        self.metric = f"HBM read rate of a plain {nbytes}-byte stream" + (" with a 4-byte store per wave"
-                                                                        if store else "")
+        stored = {0: "none", 1: "4 B per wave", 2: "4 B by the first wave only"}[store]
+        self.metric = f"HBM read rate of a plain {nbytes}-byte stream" + ("" if store == 0 else f", store {stored}")
         self.config = {"workload": self.name, "bytes": nbytes, "grid": self.grid, "block": block,
-                       "loads_per_lane": "8 x 16 B non-temporal", "store": "4 B per wave" if store else "none",
+                       "loads_per_lane": "8 x 16 B non-temporal", "store": stored,
                        "buffers_rotated": self.copies, "rotated_MB": round(self.copies * nbytes / 1e6, 1)}
 
     def launches(self):
@@ -845,11 +848,11 @@ class HbmStream(Workload):
         def fn(i):
             _probe_ok(lib.e2m1_probe_stream(self.bufs[i % self.copies].data_ptr(), self.nbytes,
                                             self.out.data_ptr(), self.out_words, self.block,
-                                            1 if self.store else 0, _stream_handle()), "stream")
+                                            self.store, _stream_handle()), "stream")
         return [(self.label, fn)]
 
     def alg_bytes(self, label):
-        return self.nbytes + (4 * self.out_words if self.store else 0)
+        return self.nbytes + {0: 0, 1: 4 * self.out_words, 2: 4}[self.store]
 
     def headline(self, ms_per_step, per_launch):
         return round(self.nbytes / (per_launch[self.label] * 1e-3) / 1e9, 2), "GB/s", True
@@ -893,10 +896,11 @@ HEADLINE_BYTES = 14336 * 4096 // 2 + 14336 * 4096 // 32   # one batch-1 MLP GEMV
 
 WORKLOADS = {
     "floor": EmptyFloor,
-    "stream_31mb": lambda rb: HbmStream(HEADLINE_BYTES, False, rb),
-    "stream_31mb_store": lambda rb: HbmStream(HEADLINE_BYTES, True, rb),
-    "stream_128mb": lambda rb: HbmStream(128 << 20, False, rb),
-    "stream_512mb": lambda rb: HbmStream(512 << 20, False, rb),
+    "stream_31mb": lambda rb: HbmStream(HEADLINE_BYTES, 0, rb),
+    "stream_31mb_store": lambda rb: HbmStream(HEADLINE_BYTES, 1, rb),
+    "stream_31mb_store1": lambda rb: HbmStream(HEADLINE_BYTES, 2, rb),
+    "stream_128mb": lambda rb: HbmStream(128 << 20, 0, rb),
+    "stream_512mb": lambda rb: HbmStream(512 << 20, 0, rb),
     "mfma_peak": MfmaPeak,
     "moe": Moe,
     "mlp_b1": lambda rb: GemvMLP(1, rb),
@@ -979,8 +983,8 @@ def per_launch_ms(launches, copies: int, steps: int) -> dict:
 
 
 def copy_calibration(mb: int) -> None:
-    """A plain elementwise copy (read mb MiB, write mb MiB), run three times, for
-    scaling the rocprof FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    """A plain elementwise copy (read mb MiB, write mb MiB), run three times: a kernel of
+    known traffic that checks the byte counts taken from the memory request counters."""
     import torch
     n = mb * (1 << 20) // 4
     src = torch.ones(n, dtype=torch.float32, device="cuda")

@@ -36,6 +36,7 @@ from __future__ import annotations
 import argparse
 import csv
 import glob
+import gzip
 import json
 import os
 import re
@@ -65,6 +66,7 @@ PROFILE_NAMES = {
     "mlp_b1": "gemv_b1_llama8b_mlp", "mlp_b2": "gemv_b2_llama8b_mlp", "mlp_b4": "gemv_b4_llama8b_mlp",
     "mlp_b16": "gemv_b16_llama8b_mlp", "gemv_small": "gemv_b1_256x512",
     "ternary": "ternary_gemv_4096x4096", "ternary_wl": "ternary_wl_4096x4096",
+    "ternary_b1": "ternary_gemm_b1_4096x4096", "ternary_b2": "ternary_gemm_b2_4096x4096",
     "ternary_b4": "ternary_gemm_b4_4096x4096", "ternary_b8": "ternary_gemm_b8_4096x4096",
     "ternary_b16": "ternary_gemm_b16_4096x4096",
     "gather": "nvfp4_gather_200000x4096_8192ids", "decode": "mxfp4_decode_14336x4096",
@@ -72,7 +74,8 @@ PROFILE_NAMES = {
     "nm_2of4": "nm_2of4_b1_llama8b_mlp", "nm_4of8": "nm_4of8_b1_llama8b_mlp",
     "moe": "moe_E32_H2880_I2880_T256_top4",
     "floor": "platform_empty_kernel", "stream_31mb": "platform_hbm_stream_31mb",
-    "stream_31mb_store": "platform_hbm_stream_31mb_store", "stream_128mb": "platform_hbm_stream_128mb",
+    "stream_31mb_store": "platform_hbm_stream_31mb_store", "stream_31mb_store1": "platform_hbm_stream_31mb_store1",
+    "stream_128mb": "platform_hbm_stream_128mb",
     "stream_512mb": "platform_hbm_stream_512mb", "mfma_peak": "platform_mfma_bf16",
 }
 
@@ -116,7 +119,7 @@ def run_all(workload: str, out: str, steps: int, passes: list[str]) -> bool:
     env = dict(os.environ, TMPDIR="/tmp")
     with open(os.path.join(d, "commands.txt"), "w") as fh:
         for name, cmd in commands(workload, out, steps, passes):
-            fh.write(f"{name}: cd /tmp && TMPDIR=/tmp {' '.join(cmd)}\n")
+            fh.write(f"{name}: cd /tmp && TMPDIR=/tmp {' '.join(cmd).replace(ROOT, '<repo>')}\n")
     for name, cmd in commands(workload, out, steps, passes):
         log(f"{workload}: {name} ...")
         t0 = time.time()
@@ -128,7 +131,16 @@ def run_all(workload: str, out: str, steps: int, passes: list[str]) -> bool:
         if rc != 0 and not (rc in (139, -11) and name != "bench" and printed):
             log(f"{workload}: stopping after {name} (exit {rc}); see {d}/{name}.stderr")
             return False
+    _compress(d)
     return True
+
+
+def _compress(d: str) -> None:
+    """gzip the profiler's CSV files (the records of a workload run to tens of MB)."""
+    for path in glob.glob(os.path.join(d, "**", "*.csv"), recursive=True):
+        with open(path, "rb") as src, gzip.open(path + ".gz", "wb", compresslevel=6) as dst:
+            dst.write(src.read())
+        os.remove(path)
 
 
 # ------------------------------------------------------------------ parsing ---
@@ -178,15 +190,20 @@ def _size(row: dict, key: str) -> int:
 
 
 def _find(d: str, suffix: str) -> str | None:
-    hits = sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True))
+    hits = sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True) +
+                  glob.glob(os.path.join(d, "**", f"*{suffix}.gz"), recursive=True))
     return hits[0] if hits else None
+
+
+def _open_text(path: str):
+    return gzip.open(path, "rt") if path.endswith(".gz") else open(path)
 
 
 def dispatches(path: str) -> list[dict]:
     """One record per dispatch: id, kernel short name, grid (work-items), workgroup, and
     either its duration (kernel trace) or its counter values (counter collection)."""
     by_id: dict = {}
-    with open(path) as fh:
+    with _open_text(path) as fh:
         for r in csv.DictReader(fh):
             did = int(r.get("Dispatch_Id") or r.get("Correlation_Id") or len(by_id))
             rec = by_id.get(did)
@@ -390,9 +407,9 @@ def summarize(workload: str, out: str) -> tuple[str, dict]:
     cmd_path = os.path.join(d, "commands.txt")
     if os.path.exists(cmd_path):
         lines.append("Commands (run by python3 bench_profile.py --workload "
-                     f"{workload} --out <dir>; <dir> here {out}):")
+                     f"{workload} --out <dir>; <dir> here {out.replace(ROOT, '<repo>')}):")
         for line in open(cmd_path).read().splitlines():
-            lines.append("  " + line.replace(ROOT, "<repo>"))
+            lines.append("  " + re.sub(r"\S*/(bench\.py|gpurun_out/)", r"<repo>/\1", line))
     return "\n".join(lines) + "\n", records
 
 

@@ -23,7 +23,8 @@
 //       bytes. With store = 0 nothing is written (a store guarded by a
 //       checksum test no input meets keeps the loads live); with store = 1
 //       every wave writes one 4-byte checksum to out[wave] (out_words must
-//       be at least grid * block / 64): a small output like a GEMV's.
+//       be at least grid * block / 64): a small output like a GEMV's; with
+//       store = 2 only the first wave of the grid writes (out[0]).
 //
 //   int e2m1_probe_mfma(int64_t grid, int iters, float* out, int64_t out_words,
 //                       void* stream)
@@ -47,7 +48,7 @@ constexpr uint32_t kNever = 0x9E3779B9u;
 template <int kBlock>
 __global__ __launch_bounds__(kBlock) void probe_empty_kernel() {}
 
-template <int kBlock, bool kStore>
+template <int kBlock, int kStore>
 __global__ __launch_bounds__(kBlock) void probe_stream_kernel(const u32x4* __restrict__ src, int64_t n16,
                                                               uint32_t* __restrict__ out) {
     const int64_t base = (int64_t)blockIdx.x * kLoads * kBlock + threadIdx.x;
@@ -61,9 +62,13 @@ __global__ __launch_bounds__(kBlock) void probe_stream_kernel(const u32x4* __res
     uint32_t acc = 0;
 #pragma unroll
     for (int j = 0; j < kLoads; ++j) acc ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
-    if constexpr (kStore) {
+    if constexpr (kStore == 1) {
         for (int d = 32; d >= 1; d >>= 1) acc ^= __shfl_xor(acc, d, 64);
         if ((threadIdx.x & 63) == 0) out[(int64_t)blockIdx.x * (kBlock / 64) + threadIdx.x / 64] = acc;
+    } else if constexpr (kStore == 2) {
+        for (int d = 32; d >= 1; d >>= 1) acc ^= __shfl_xor(acc, d, 64);
+        if (blockIdx.x == 0 && threadIdx.x == 0) out[0] = acc;
+        else if (acc == kNever) out[0] = acc;
     } else {
         if (acc == kNever) out[0] = acc;
     }
@@ -117,17 +122,19 @@ extern "C" int e2m1_probe_stream(const void* src, int64_t bytes, uint32_t* out, 
                                  int store, void* stream) {
     const int64_t grid = stream_grid(bytes, block);
     if (grid < 0 || src == nullptr || out == nullptr || out_words < 1) return -1;
-    if (store && out_words < grid * (block / 64)) return -1;
+    if (store < 0 || store > 2 || (store == 1 && out_words < grid * (block / 64))) return -1;
     const u32x4* p = static_cast<const u32x4*>(src);
     const int64_t n16 = bytes / 16;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const dim3 g((unsigned)grid);
     if (block == 64) {
-        if (store) probe_stream_kernel<64, true><<<g, dim3(64), 0, s>>>(p, n16, out);
-        else probe_stream_kernel<64, false><<<g, dim3(64), 0, s>>>(p, n16, out);
+        if (store == 1) probe_stream_kernel<64, 1><<<g, dim3(64), 0, s>>>(p, n16, out);
+        else if (store == 2) probe_stream_kernel<64, 2><<<g, dim3(64), 0, s>>>(p, n16, out);
+        else probe_stream_kernel<64, 0><<<g, dim3(64), 0, s>>>(p, n16, out);
     } else {
-        if (store) probe_stream_kernel<256, true><<<g, dim3(256), 0, s>>>(p, n16, out);
-        else probe_stream_kernel<256, false><<<g, dim3(256), 0, s>>>(p, n16, out);
+        if (store == 1) probe_stream_kernel<256, 1><<<g, dim3(256), 0, s>>>(p, n16, out);
+        else if (store == 2) probe_stream_kernel<256, 2><<<g, dim3(256), 0, s>>>(p, n16, out);
+        else probe_stream_kernel<256, 0><<<g, dim3(256), 0, s>>>(p, n16, out);
     }
     return hipGetLastError() == hipSuccess ? 0 : -2;
 }
