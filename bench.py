@@ -6,7 +6,7 @@
 Prints ONE JSON line. The default workload is the headline: MXFP4 dequant-GEMV
 at batch 1 on the Llama-8B MLP shapes (W 14336 x 4096 and W 4096 x 14336, one
 launch each per step), bf16 output. Other workloads (for the per-kernel
-roofline tables): mlp_b2, mlp_b4, mlp_b16, ternary, ternary_b1 .. ternary_b16
+roofline tables): mlp_b2, mlp_b4, mlp_b8, mlp_b16, ternary, ternary_b1 .. ternary_b16
 (small-batch ternary GEMM), ternary_wl, gather, moe, decode, quantize,
 prefill (MXFP4 GEMM, 2048 tokens), nm_2of4, nm_4of8, gemv_small. Platform
 reference points (libe2m1probe.so): floor (empty launches), stream_31mb and
@@ -906,6 +906,7 @@ WORKLOADS = {
     "mlp_b1": lambda rb: GemvMLP(1, rb),
     "mlp_b2": lambda rb: GemvMLP(2, rb),
     "mlp_b4": lambda rb: GemvMLP(4, rb),
+    "mlp_b8": lambda rb: GemvMLP(8, rb),
     "mlp_b16": lambda rb: GemvMLP(16, rb),
     "ternary": Ternary,
     "ternary_wl": TernaryWL,

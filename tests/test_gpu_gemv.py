@@ -61,6 +61,10 @@ SHAPES = [
     # batch 2 to 4 in the batch-1 tile layout: two to sixteen waves, ragged chunks and rows
     (47, 1024 + 32, 2), (100, 14336, 2), (33, 16384, 3), (290, 32 * 200 + 32 * 7, 2), (18, 8192, 3),
     (61, 32 * 77, 4), (35, 16384, 4), (129, 4096, 4),
+    # batch 5 to 16 on the matrix cores: ragged last slice, rows not a multiple of 8 or 16, the down
+    # projection's K; batch 4 at the down projection's K
+    (77, 1024 * 3 + 32 * 5, 5), (130, 14336, 4), (1000, 2080, 7), (1003, 4096, 6), (258, 4096, 16),
+    (33, 14336, 8), (40, 32 * 40, 16),
 ]
 
 
