@@ -12,6 +12,7 @@ prefill (MXFP4 GEMM, 2048 tokens), nm_2of4, nm_4of8, gemv_small. Platform
 reference points (libe2m1probe.so): floor (empty launches), stream_31mb and
 stream_31mb_store (a plain read of the headline launch's 31.2 MB, without and
 with a 4-byte store per wave), stream_31mb_store1 (one 4-byte store in all),
+stream_4mb_store (the 4096 x 4096 ternary matrix's 4 MiB, with a store per wave),
 stream_128mb, stream_512mb, mfma_peak.
 
 Timing: inputs are resident in HBM before the timed region. The launches of
@@ -79,11 +80,15 @@ def _code_only(text: str) -> str:
     return "\n".join(" ".join(line.split()) for line in text.splitlines() if line.strip())
 
 
-def build_fingerprint() -> str:
+def build_fingerprint(flags: list[str] | None = None, root: str | None = None) -> str:
     """The compiler flags and offload target the library is built with: a flag change alters
-    the machine code (and so the counters) as much as a source edit does."""
+    the machine code (and so the counters) as much as a source edit does. Paths inside the
+    checkout are written relative to it, so a copy of the tree elsewhere has the same
+    fingerprint."""
     from gemm_e2m1_lut_amd import build as hip_build
-    return " ".join(hip_build.HIPFLAGS)
+    flags = hip_build.HIPFLAGS if flags is None else flags
+    root = hip_build.ROOT if root is None else root
+    return " ".join(f.replace(root, "<repo>") for f in flags)
 
 
 def kernel_source_hash(label: str, flags: str | None = None) -> str:
@@ -893,12 +898,14 @@ class MfmaPeak(Workload):
 
 
 HEADLINE_BYTES = 14336 * 4096 // 2 + 14336 * 4096 // 32   # one batch-1 MLP GEMV launch's weights
+TERNARY_BYTES = 4096 * 4096 // 4                            # the 4096 x 4096 ternary matrix (2 bits a weight)
 
 WORKLOADS = {
     "floor": EmptyFloor,
     "stream_31mb": lambda rb: HbmStream(HEADLINE_BYTES, 0, rb),
     "stream_31mb_store": lambda rb: HbmStream(HEADLINE_BYTES, 1, rb),
     "stream_31mb_store1": lambda rb: HbmStream(HEADLINE_BYTES, 2, rb),
+    "stream_4mb_store": lambda rb: HbmStream(TERNARY_BYTES, 1, rb),
     "stream_128mb": lambda rb: HbmStream(128 << 20, 0, rb),
     "stream_512mb": lambda rb: HbmStream(512 << 20, 0, rb),
     "mfma_peak": MfmaPeak,

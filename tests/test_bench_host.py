@@ -51,6 +51,16 @@ def test_build_flags_change_the_fingerprint():
     assert same != bench.kernel_source_hash("gemv_b1_14336x4096", flags.replace("-O3", "-O2"))
 
 
+def test_fingerprint_does_not_depend_on_where_the_tree_is():
+    """The GPU runs use a copy of the tree at another path: the include paths in the flags must
+    not change the hash."""
+    from gemm_e2m1_lut_amd import build as hip_build
+    moved = [f.replace(hip_build.ROOT, "/elsewhere/repo") for f in hip_build.HIPFLAGS]
+    assert any(hip_build.ROOT in f for f in hip_build.HIPFLAGS)
+    assert bench.build_fingerprint(moved, "/elsewhere/repo") == bench.build_fingerprint()
+    assert "<repo>" in bench.build_fingerprint()
+
+
 def test_cpu_description_names_the_host():
     d = bench.cpu_description()
     assert d.get("logical_processors", 0) >= 1
