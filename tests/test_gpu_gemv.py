@@ -65,6 +65,8 @@ SHAPES = [
     # projection's K; batch 4 at the down projection's K
     (77, 1024 * 3 + 32 * 5, 5), (130, 14336, 4), (1000, 2080, 7), (1003, 4096, 6), (258, 4096, 16),
     (33, 14336, 8), (40, 32 * 40, 16),
+    # batch above 1 with K beyond the tiled kernels: one wave per row
+    (21, 16384 + 32, 5), (9, 16384 + 64, 2),
 ]
 
 

@@ -54,9 +54,20 @@ def test_workload_32_experts(gpu, orc):
     (2, 288, 64, 100, 2),       # ~100 rows per expert: two token passes
     (8, 2880, 2880, 16, 4),     # the layer's extents with few tokens: some experts get none
     (1, 32, 32, 1, 1),
+    (512, 64, 96, 300, 4),      # the most experts the entry point accepts, ~2 pairs each
 ])
 def test_shapes(gpu, orc, E, H, I, T, topk):
     check(gpu, orc, synth.moe_case(E * 1000 + H + I + T, E, H, I, T, topk))
+
+
+def test_every_token_to_the_same_two_experts(gpu, orc):
+    """Skewed routing: experts 2 and 5 take every pair, 300 each (five token passes of up to
+    64 rows, the last one ragged), the other six experts none."""
+    c = synth.moe_case(77, 8, 160, 96, 300, 2)
+    ids = np.empty_like(c["topk_ids"])
+    ids[:, 0], ids[:, 1] = 2, 5
+    c["topk_ids"] = ids
+    check(gpu, orc, c)
 
 
 def test_zero_first_layer_gives_exact_zero(gpu):
