@@ -7,7 +7,8 @@ Prints ONE JSON line. The default workload is the headline: MXFP4 dequant-GEMV
 at batch 1 on the Llama-8B MLP shapes (W 14336 x 4096 and W 4096 x 14336, one
 launch each per step), bf16 output. Other workloads (for the per-kernel
 roofline tables): mlp_b2, mlp_b4, mlp_b8, mlp_b16, ternary, ternary_b1 .. ternary_b16
-(small-batch ternary GEMM), ternary_wl, gather, moe, decode, quantize,
+(small-batch ternary GEMM), ternary_wl, gather, moe, decode, decode_8192 (the
+same bytes as the gather), quantize,
 prefill (MXFP4 GEMM, 2048 tokens), nm_2of4, nm_4of8, gemv_small. Platform
 reference points (libe2m1probe.so): floor (empty launches), stream_31mb and
 stream_31mb_store (a plain read of the headline launch's 31.2 MB, without and
@@ -425,7 +426,8 @@ class Decode(Workload):
         self.w = [_mxfp4_dev(g, rows, k, 0, 255) for _ in range(self.copies)]
         self.out = torch.empty((rows, k), dtype=torch.bfloat16, device="cuda")
         self.weight_bytes_per_step = float(per_copy)
-        self.total_bytes_per_step = float(self.alg_bytes("decode"))
+        self.label = "decode" if rows == 14336 else f"decode_{rows}x{k}"
+        self.total_bytes_per_step = float(self.alg_bytes(self.label))
         self.dtype = "u16"
         self.config = {"workload": self.name, "out": "bf16 bit patterns", "weight_copies_rotated": self.copies}
 
@@ -433,7 +435,7 @@ class Decode(Workload):
         def fn(i):
             p, s = self.w[i % self.copies]
             self.lib.dequant_decode(p, s, out=self.out)
-        return [("decode", fn)]
+        return [(self.label, fn)]
 
     def alg_bytes(self, label):
         return self.rows * self.k // 2 + self.rows * self.k // 32 + 2 * self.rows * self.k
@@ -924,6 +926,7 @@ WORKLOADS = {
     "ternary_b16": lambda rb: TernaryBatch(16, rb),
     "gather": Gather,
     "decode": Decode,
+    "decode_8192": lambda rb: Decode(rb, rows=8192),
     "quantize": Quantize,
     "prefill": Prefill,
     "nm_2of4": lambda rb: NmSparse(2, 4, rb),

@@ -71,6 +71,7 @@ PROFILE_NAMES = {
     "ternary_b4": "ternary_gemm_b4_4096x4096", "ternary_b8": "ternary_gemm_b8_4096x4096",
     "ternary_b16": "ternary_gemm_b16_4096x4096",
     "gather": "nvfp4_gather_200000x4096_8192ids", "decode": "mxfp4_decode_14336x4096",
+    "decode_8192": "mxfp4_decode_8192x4096",
     "quantize": "quantize_mxfp4_nvfp4_14336x4096", "prefill": "gemm_m2048_llama8b_mlp",
     "nm_2of4": "nm_2of4_b1_llama8b_mlp", "nm_4of8": "nm_4of8_b1_llama8b_mlp",
     "moe": "moe_E32_H2880_I2880_T256_top4",
