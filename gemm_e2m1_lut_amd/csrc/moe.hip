@@ -174,7 +174,8 @@ using Gemm2 = MoeEngine<1>;
 
 // Workgroup (j block, expert): wave w streams gate rows j0 + 16 w .. + 15 and
 // up rows inter + the same j against all of the expert's tokens (64 per pass),
-// then act = silu(gate) * up.
+// then act = silu(gate) * up. kStaged: the block's scale rows are staged in LDS.
+template <bool kStaged>
 __global__ __launch_bounds__(kThreads) void moe_gemm1_kernel(
     const uint16_t* x, const uint8_t* w13, const uint8_t* w13s,
     const int* __restrict__ cnt, const int* __restrict__ off, const int* __restrict__ row_pair,
@@ -195,14 +196,18 @@ __global__ __launch_bounds__(kThreads) void moe_gemm1_kernel(
     // columns j (c = w % P, 16 P consecutive j per group of P waves), gate rows j and up rows I + j
     // (I (H / 2) is a multiple of 128: the same offsets)
     const int P = line_period(H);
-    const int j0 = work.blk * kGemm1Cols + 16 * P * (wave / P) + wave % P;
+    const int jb = work.blk * kGemm1Cols;
+    const int j0 = jb + 16 * P * (wave / P) + wave % P;
     const int row0[2] = {j0, I + j0};
+    const int rb[2] = {jb, I + jb};
     const int mb = line_block(we, j0, H);
     int mbmax = 0;
     for (int c = 0; c < P; ++c) mbmax = max(mbmax, line_block(we, work.blk * kGemm1Cols + c, H));
     const int nsteps = engine_steps(H, mbmax);
     const __amdgpu_buffer_rsrc_t wres =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(we), 0, 2 * I * (H / 2), kBufferWord3);
+    const __amdgpu_buffer_rsrc_t sres =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(se), 0, 2 * I * (H / 32), kBufferWord3);
 
     for (int m0 = 0; m0 < n_e; m0 += kEngineMaxTokens) {
         const int nv = min(kEngineMaxTokens, n_e - m0);
@@ -215,12 +220,11 @@ __global__ __launch_bounds__(kThreads) void moe_gemm1_kernel(
         for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int m = 0; m < 4; ++m) acc[t][m] = f32x4{0.f, 0.f, 0.f, 0.f};
-        Gemm1::run_mt(mt, sh, wres, se, H, row0, P, mb, nsteps, 2 * I, x, (size_t)H, nv, acc);
+        Gemm1::run_mt<kStaged>(mt, sh, wres, se, sres, rb, H, row0, P, mb, nsteps, 2 * I, x, (size_t)H, nv, acc);
         // epilogue: act = silu(gate) * up -> bf16; lane (g, r) holds j = j0 + P (4 g + jj), jj < 4.
         // With P > 1 the workgroup's 128 j of each token row are interleaved over its waves, so
         // they meet in LDS (over the token panels, free once every wave is past the product) and
         // leave as contiguous 16-byte stores.
-        const int jb = work.blk * kGemm1Cols;
         if (P == 1) {
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
@@ -263,6 +267,7 @@ __global__ __launch_bounds__(kThreads) void moe_gemm1_kernel(
 
 // Workgroup (hidden block, expert): wave w streams W2 rows h0 + 16 w .. + 15
 // against the expert's activation rows; fp32 results per (expert row, hidden).
+template <bool kStaged>
 __global__ __launch_bounds__(kThreads) void moe_gemm2_kernel(
     const uint16_t* act, const uint8_t* w2, const uint8_t* w2s,
     const int* __restrict__ cnt, const int* __restrict__ off, float* __restrict__ y, int H, int I, int E) {
@@ -280,14 +285,18 @@ __global__ __launch_bounds__(kThreads) void moe_gemm2_kernel(
     const uint8_t* se = w2s + (size_t)e * H * (I / 32);
     // rows of one line offset per tile, as in gemm1: h = h0 + P (4 g' + jj) + c
     const int P = line_period(I);
-    const int h0 = work.blk * kGemm2Rows + 16 * P * (wave / P) + wave % P;
+    const int hb = work.blk * kGemm2Rows;
+    const int h0 = hb + 16 * P * (wave / P) + wave % P;
     const int row0[1] = {h0};
+    const int rb[1] = {hb};
     const int mb = line_block(we, h0, I);
     int mbmax = 0;
     for (int c = 0; c < P; ++c) mbmax = max(mbmax, line_block(we, work.blk * kGemm2Rows + c, I));
     const int nsteps = engine_steps(I, mbmax);
     const __amdgpu_buffer_rsrc_t wres =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(we), 0, H * (I / 2), kBufferWord3);
+    const __amdgpu_buffer_rsrc_t sres =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(se), 0, H * (I / 32), kBufferWord3);
 
     for (int m0 = 0; m0 < n_e; m0 += kEngineMaxTokens) {
         const int nv = min(kEngineMaxTokens, n_e - m0);
@@ -298,11 +307,10 @@ __global__ __launch_bounds__(kThreads) void moe_gemm2_kernel(
         f32x4 acc[1][4];
 #pragma unroll
         for (int m = 0; m < 4; ++m) acc[0][m] = f32x4{0.f, 0.f, 0.f, 0.f};
-        Gemm2::run_mt(mt, sh, wres, se, I, row0, P, mb, nsteps, H, act, (size_t)I, nv, acc);
+        Gemm2::run_mt<kStaged>(mt, sh, wres, se, sres, rb, I, row0, P, mb, nsteps, H, act, (size_t)I, nv, acc);
         // lane (g, r) holds h = h0 + P (4 g + jj), jj < 4: with P > 1 the workgroup's 128 h of each
         // token row are interleaved over its waves, so they meet in LDS (over the token panels, free
         // once every wave is past the product) and leave as contiguous 16-byte stores
-        const int hb = work.blk * kGemm2Rows;
         if (P == 1) {
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
@@ -394,11 +402,20 @@ hipError_t launch_moe(const uint16_t* x, const uint8_t* w13, const uint8_t* w13s
     moe_route_kernel<<<1, kRouteThreads, 0, stream>>>(ids, P, E, cnt, off, pair_row, row_pair);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
+    // scale rows are staged in LDS where they fit and start 16-byte aligned (every
+    // workgroup's rows then do: 128 rows of K / 32 bytes are a multiple of 16)
+    auto aligned16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
     const int g1 = moe_grid((I + kGemm1Cols - 1) / kGemm1Cols, E);
-    moe_gemm1_kernel<<<g1, kThreads, 0, stream>>>(x, w13, w13s, cnt, off, row_pair, act, H, I, E, (int)topk);
+    if (Gemm1::stages(H) && aligned16(w13s))
+        moe_gemm1_kernel<true><<<g1, kThreads, 0, stream>>>(x, w13, w13s, cnt, off, row_pair, act, H, I, E, (int)topk);
+    else
+        moe_gemm1_kernel<false><<<g1, kThreads, 0, stream>>>(x, w13, w13s, cnt, off, row_pair, act, H, I, E, (int)topk);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     const int g2 = moe_grid((H + kGemm2Rows - 1) / kGemm2Rows, E);
-    moe_gemm2_kernel<<<g2, kThreads, 0, stream>>>(act, w2, w2s, cnt, off, y, H, I, E);
+    if (Gemm2::stages(I) && aligned16(w2s))
+        moe_gemm2_kernel<true><<<g2, kThreads, 0, stream>>>(act, w2, w2s, cnt, off, y, H, I, E);
+    else
+        moe_gemm2_kernel<false><<<g2, kThreads, 0, stream>>>(act, w2, w2s, cnt, off, y, H, I, E);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     const int64_t chunks = tokens * (hidden / 8);
     const int64_t want = (chunks + kThreads - 1) / kThreads;

@@ -16,8 +16,15 @@
 //     (r, g) then holds blocks g and g + 4 of row r. Block b = g + 4 h feeds
 //     four MFMAs, MFMA i taking codes [8 i, 8 i + 8) of the block as k slots
 //     8 g .. 8 g + 7; v_cvt_scalef32_pk_bf16_fp4 decodes two codes and applies
-//     the block scale in one instruction. The E8M0 byte of each chunk is
-//     loaded by the lane that loads the chunk and takes the same LDS route.
+//     the block scale in one instruction.
+//   * Scales: the workgroup's rows are 128 consecutive rows of each tile set,
+//     so their E8M0 bytes are 128 K / 32 consecutive bytes per set. Where they
+//     fit in LDS (NT K / 32 <= 192) the workgroup stages them once per pass
+//     with coalesced 16-byte loads, issued before the first weight loads and
+//     written before the first product, and every lane reads its block's
+//     byte from there. Otherwise (the per-step path) the lane that loads a
+//     weight chunk also loads its scale byte, which takes the chunk's LDS
+//     route; those scattered byte loads cost about an eighth of the kernel.
 //   * Line alignment: a row of K/2 bytes need not start on a 128-byte line
 //     (K = 2880: rows start 0, 32, 64 or 96 bytes into a line, repeating every
 //     four rows), and a step's 128 bytes of such a row would straddle two
@@ -56,6 +63,13 @@ constexpr int kPanelPitch = kEngineStepCols + 8;     // bf16 per staged token ro
 constexpr int kPanelElems = kEngineMaxTokens * kPanelPitch;
 constexpr int kWBufPitch = 9;                        // uint4 per transposed weight row (8 blocks + pad)
 constexpr int kNonTemporal = 2;                      // cache-policy operand of a buffer load: streaming
+constexpr int kStageChunks = 3;                      // 16-byte scale chunks per thread (staged path)
+constexpr int kStageBytes = kStageChunks * kEngineThreads * 16;   // 24 KiB of staged E8M0 rows
+
+template <int N>
+struct StaticInt {
+    static constexpr int value = N;
+};
 
 // Compiler-only fence: keeps loads where they are written (issued early).
 // Emits no instruction. The weight and token pointers reaching it are not
@@ -85,7 +99,7 @@ __device__ __forceinline__ int engine_steps(int K, int mbmax) { return (K - 1 + 
 template <int NT>
 struct EngineStep {
     uint4 w[NT][2];       // coalesced: rows 8 q + lane / 8 of each tile, block lane % 8
-    uint8_t e[NT][2];     // E8M0 bytes of the same chunks (bytes: widened at use)
+    uint8_t e[NT][2];     // per-step path: E8M0 bytes of the same chunks (bytes: widened at use)
 };
 
 template <int NT>
@@ -96,15 +110,49 @@ struct MoeEngine {
     struct Shared {
         uint16_t panel[3][kPanelElems];
         uint4 wbuf[kEngineWaves][kWBufElems];
-        uint8_t sbuf[kEngineWaves][NT * 16 * 8];   // E8M0 bytes, [tile][row][block]
+        union {
+            uint8_t sbuf[kEngineWaves][NT * 16 * 8];    // per-step path: E8M0 bytes, [tile][row][block]
+            alignas(16) uint8_t stage[kStageBytes];     // staged path: [tile set][128 rows][K / 32]
+        };
         int rowidx[kEngineMaxTokens];
     };
 
-    // Weight lines and scales of step `step` for this wave's tiles: tile t is
-    // rows row0[t] + stride i (i < 16), clamped to nrows - 1, each starting 16 mb
-    // bytes into a 128-byte line; lane l loads 16 bytes at 16 (l % 8) of the
-    // step's aligned window of row 8 q + l / 8. Scale blocks are clamped to
-    // [0, kb - 1] (blocks outside the row meet zero tokens).
+    // Whether the workgroup's scale rows for reduction length K fit the stage.
+    static __host__ __device__ constexpr bool stages(int K) { return NT * 128 * (K / 32) <= kStageBytes; }
+
+    // The scale rows [rb[t], rb[t] + 128) of each tile set t (K / 32 bytes each,
+    // 8 K / 32 chunks of 16 bytes per set, read through sres, a resource bounded
+    // to the scale matrix: rows past it read zeros): thread i loads chunks i + 512 c.
+    static __device__ __forceinline__ void issue_scales(uint4 (&v)[kStageChunks], __amdgpu_buffer_rsrc_t sres,
+                                                        int K, const int (&rb)[NT]) {
+        const int kb = K / 32, per = 8 * kb;
+#pragma unroll
+        for (int c = 0; c < kStageChunks; ++c) {
+            const int ch = (int)threadIdx.x + kEngineThreads * c;
+            const int t = NT > 1 && ch >= per ? 1 : 0;
+            // chunks past the stage load offset 0 and are not stored
+            const uint32_t off = ch < NT * per ? (uint32_t)(rb[t] * kb + 16 * (ch - t * per)) : 0u;
+            const u32x4 u = __builtin_amdgcn_raw_buffer_load_b128(sres, off, 0, kNonTemporal);
+            v[c] = make_uint4(u.x, u.y, u.z, u.w);
+        }
+    }
+
+    static __device__ __forceinline__ void store_scales(const uint4 (&v)[kStageChunks], uint8_t* stage, int K) {
+        const int n = NT * 8 * (K / 32);
+#pragma unroll
+        for (int c = 0; c < kStageChunks; ++c) {
+            const int ch = (int)threadIdx.x + kEngineThreads * c;
+            if (ch < n) reinterpret_cast<uint4*>(stage)[ch] = v[c];
+        }
+    }
+
+    // Weight lines (and, on the per-step path, scales) of step `step` for this
+    // wave's tiles: tile t is rows row0[t] + stride i (i < 16), clamped to
+    // nrows - 1, each starting 16 mb bytes into a 128-byte line; lane l loads 16
+    // bytes at 16 (l % 8) of the step's aligned window of row 8 q + l / 8.
+    // Scale blocks are clamped to [0, kb - 1] (blocks outside the row meet zero
+    // tokens).
+    template <bool kStaged>
     static __device__ __forceinline__ void issue_weights(EngineStep<NT>& b, __amdgpu_buffer_rsrc_t wres,
                                                          const uint8_t* ws, int K, const int (&row0)[NT],
                                                          int stride, int mb, int nrows, int step) {
@@ -122,7 +170,7 @@ struct MoeEngine {
                 const uint32_t off = (uint32_t)(row * (K / 2) + 16 * blk);
                 const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(wres, off, 0, kNonTemporal);
                 b.w[t][q] = make_uint4(v.x, v.y, v.z, v.w);
-                b.e[t][q] = ws[(size_t)row * kb + cb];
+                if constexpr (!kStaged) b.e[t][q] = ws[(size_t)row * kb + cb];
             }
     }
 
@@ -154,15 +202,18 @@ struct MoeEngine {
         }
     }
 
-    // acc += step held in b (weights) x token panels. The wave's columns are
+    // acc += step s held in b (weights) x token panels. The wave's columns are
     // [256 s - 32 mb, + 256): those before 256 s are read from the previous
-    // step's panel (zero at the first step).
-    template <int MTA>
+    // step's panel (zero at the first step). Staged scales: lane (r, g) reads
+    // stage[soff[t] + block], soff[t] the start of its row of tile t.
+    template <int MTA, bool kStaged>
     static __device__ __forceinline__ void compute(const EngineStep<NT>& b, uint4* wbuf, uint8_t* sbuf,
-                                                   const uint16_t* panel, const uint16_t* prev, bool first,
-                                                   int mb, f32x4 (&acc)[NT][4]) {
+                                                   const uint8_t* stage, const int (&soff)[NT], int K, int s,
+                                                   const uint16_t* panel, const uint16_t* prev, int mb,
+                                                   f32x4 (&acc)[NT][4]) {
         const int lane = threadIdx.x & (kWave - 1);
         const int r = lane & 15, g = lane >> 4;
+        const bool first = s == 0;
         // coalesced lines (and their scale bytes) -> MFMA layout through the wave's LDS buffers
 #pragma unroll
         for (int t = 0; t < NT; ++t)
@@ -170,16 +221,20 @@ struct MoeEngine {
             for (int q = 0; q < 2; ++q) {
                 const int row = t * 16 + 8 * q + (lane >> 3);
                 wbuf[row * kWBufPitch + (lane & 7)] = b.w[t][q];
-                sbuf[row * 8 + (lane & 7)] = b.e[t][q];
+                if constexpr (!kStaged) sbuf[row * 8 + (lane & 7)] = b.e[t][q];
             }
         uint4 a4[NT][2];
         uint32_t e4[NT][2];
+        const int blk = 8 * s - mb + g;   // this lane's first block of the step (g + 4 h: the second)
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 a4[t][h] = wbuf[(t * 16 + r) * kWBufPitch + g + 4 * h];
-                e4[t][h] = sbuf[(t * 16 + r) * 8 + g + 4 * h];
+                if constexpr (kStaged)
+                    e4[t][h] = stage[soff[t] + min(max(blk + 4 * h, 0), K / 32 - 1)];
+                else
+                    e4[t][h] = sbuf[(t * 16 + r) * 8 + g + 4 * h];
             }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -216,9 +271,12 @@ struct MoeEngine {
 
     // The whole product over K for one pass of MTA token tiles. sh.rowidx
     // holds the pass's source rows (written and synchronised by the caller);
-    // nsteps covers the latest window of the workgroup's waves.
-    template <int MTA>
-    static __device__ __forceinline__ void run(Shared& sh, __amdgpu_buffer_rsrc_t wres, const uint8_t* ws, int K,
+    // nsteps covers the latest window of the workgroup's waves. Staged path:
+    // rb[t] is the first of the workgroup's 128 rows of tile set t (row0[t] +
+    // stride i lies in [rb[t], rb[t] + 128)), sres the scale matrix's resource.
+    template <int MTA, bool kStaged>
+    static __device__ __forceinline__ void run(Shared& sh, __amdgpu_buffer_rsrc_t wres, const uint8_t* ws,
+                                               __amdgpu_buffer_rsrc_t sres, const int (&rb)[NT], int K,
                                                const int (&row0)[NT], int stride, int mb, int nsteps, int nrows,
                                                const uint16_t* xb, size_t xpitch, int nvalid, f32x4 (&acc)[NT][4]) {
         const int wave = threadIdx.x / kWave;
@@ -230,45 +288,68 @@ struct MoeEngine {
             const int row = ((int)threadIdx.x + kEngineThreads * j) >> 5;
             src[j] = xb + (size_t)sh.rowidx[min(row, nvalid - 1)] * xpitch;
         }
+        int soff[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) soff[t] = (128 * t + row0[t] - rb[t] + stride * (int)(threadIdx.x & 15)) * (K / 32);
+        uint4 pre[kStageChunks];
+        // first, so that the wait before their LDS store counts the step loads issued after them
+        if constexpr (kStaged) issue_scales(pre, sres, K, rb);
         EngineStep<NT> buf[3];
         uint4 tr[2][MTA];
-        // step s: weights requested at s - 2 into buffer s % 3, tokens requested
-        // at s - 2 into registers s % 2, written to panel s % 3 at the end of
-        // sub-iteration s - 1 (panel (s - 1) % 3 still holds step s - 1 during
-        // step s). The loop starts two steps early so that the first
-        // sub-iterations only issue loads (and write panel 0). Sub-iterations
-        // are unrolled by six so that every buffer index is static.
-        for (int it = -2; it < nsteps; it += 6) {
-#pragma unroll
-            for (int bsub = 0; bsub < 6; ++bsub) {
-                const int s = it + bsub;   // s + 2 == it + 2 + bsub, it + 2 is a multiple of 6
-                if (s >= nsteps) break;    // workgroup-uniform
-                const int next = min(s + 2, nsteps - 1);
-                issue_tokens<MTA>(tr[bsub & 1], src, K, next);
-                engine_fence();
-                issue_weights(buf[bsub % 3], wres, ws, K, row0, stride, mb, nrows, next);
-                engine_fence();
-                if (s >= 0)
-                    compute<MTA>(buf[(bsub + 1) % 3], wbuf, sbuf, sh.panel[(bsub + 1) % 3], sh.panel[bsub % 3],
-                                 s == 0, mb, acc);
-                engine_fence();
-                // tokens of step s + 1 (requested one sub-iteration ago) -> panel (s + 1) % 3
-                store_tokens<MTA>(tr[(bsub + 1) & 1], sh.panel[(bsub + 2) % 3], K, min(max(s + 1, 0), nsteps - 1));
-                __syncthreads();
+        // Sub-iteration s (from -2): requests the weights and tokens of step s + 2
+        // (weights into buffer (s + 2) % 3, tokens into registers s % 2), computes
+        // step s from buffer s % 3 and panel s % 3 (panel (s - 1) % 3 still holds
+        // step s - 1), then writes the tokens of step s + 1 (requested one
+        // sub-iteration ago) to panel (s + 1) % 3. B = (s + 2) % 6 makes every
+        // buffer index static; the first two sub-iterations only issue loads.
+        auto sub = [&](auto bc, int s) __attribute__((always_inline)) {
+            constexpr int B = decltype(bc)::value;
+            const int next = min(s + 2, nsteps - 1);
+            issue_tokens<MTA>(tr[B & 1], src, K, next);
+            engine_fence();
+            issue_weights<kStaged>(buf[B % 3], wres, ws, K, row0, stride, mb, nrows, next);
+            engine_fence();
+            if (s >= 0)
+                compute<MTA, kStaged>(buf[(B + 1) % 3], wbuf, sbuf, sh.stage, soff, K, s, sh.panel[(B + 1) % 3],
+                                      sh.panel[B % 3], mb, acc);
+            engine_fence();
+            if (s + 1 >= 0) store_tokens<MTA>(tr[(B + 1) & 1], sh.panel[(B + 2) % 3], K, min(s + 1, nsteps - 1));
+            __syncthreads();
+        };
+        // (a peeled prologue makes the compiler spill: the loop form keeps the
+        // buffers in registers)
+        for (int it = -2; it < nsteps; it += 6) {   // exits are workgroup-uniform
+            sub(StaticInt<0>{}, it);
+            if (it + 1 >= nsteps) break;
+            sub(StaticInt<1>{}, it + 1);
+            if constexpr (kStaged) {
+                if (it == -2) {   // the staged scales are in LDS before step 0 is computed
+                    store_scales(pre, sh.stage, K);
+                    __syncthreads();
+                }
             }
+            if (it + 2 >= nsteps) break;
+            sub(StaticInt<2>{}, it + 2);
+            if (it + 3 >= nsteps) break;
+            sub(StaticInt<3>{}, it + 3);
+            if (it + 4 >= nsteps) break;
+            sub(StaticInt<4>{}, it + 4);
+            if (it + 5 >= nsteps) break;
+            sub(StaticInt<5>{}, it + 5);
         }
     }
 
     // run<MTA> for MTA = mt (1 <= mt <= 4), chosen once per pass.
+    template <bool kStaged>
     static __device__ __forceinline__ void run_mt(int mt, Shared& sh, __amdgpu_buffer_rsrc_t wres, const uint8_t* ws,
-                                                  int K, const int (&row0)[NT], int stride, int mb, int nsteps,
-                                                  int nrows, const uint16_t* xb, size_t xpitch, int nvalid,
-                                                  f32x4 (&acc)[NT][4]) {
+                                                  __amdgpu_buffer_rsrc_t sres, const int (&rb)[NT], int K,
+                                                  const int (&row0)[NT], int stride, int mb, int nsteps, int nrows,
+                                                  const uint16_t* xb, size_t xpitch, int nvalid, f32x4 (&acc)[NT][4]) {
         switch (mt) {
-            case 1: run<1>(sh, wres, ws, K, row0, stride, mb, nsteps, nrows, xb, xpitch, nvalid, acc); break;
-            case 2: run<2>(sh, wres, ws, K, row0, stride, mb, nsteps, nrows, xb, xpitch, nvalid, acc); break;
-            case 3: run<3>(sh, wres, ws, K, row0, stride, mb, nsteps, nrows, xb, xpitch, nvalid, acc); break;
-            default: run<4>(sh, wres, ws, K, row0, stride, mb, nsteps, nrows, xb, xpitch, nvalid, acc); break;
+            case 1: run<1, kStaged>(sh, wres, ws, sres, rb, K, row0, stride, mb, nsteps, nrows, xb, xpitch, nvalid, acc); break;
+            case 2: run<2, kStaged>(sh, wres, ws, sres, rb, K, row0, stride, mb, nsteps, nrows, xb, xpitch, nvalid, acc); break;
+            case 3: run<3, kStaged>(sh, wres, ws, sres, rb, K, row0, stride, mb, nsteps, nrows, xb, xpitch, nvalid, acc); break;
+            default: run<4, kStaged>(sh, wres, ws, sres, rb, K, row0, stride, mb, nsteps, nrows, xb, xpitch, nvalid, acc); break;
         }
     }
 };

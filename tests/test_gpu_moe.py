@@ -5,7 +5,10 @@ MFMA operand type); the oracle keeps fp64 throughout and rounds only the
 output, so the tolerance absorbs that rounding. Covers the 32-expert, 2880 /
 2880, 256-token top-4 layer (every output), ragged extents (column steps that
 end mid-way, experts with more tokens than one pass, experts with none),
-the page's zero-code invariant, ids outside the expert range, determinism.
+the page's zero-code invariant, ids outside the expert range, determinism,
+and both ways the kernels read the E8M0 scales: staged in LDS per workgroup
+(the default) and loaded per step (hidden above 3072 for W13, inter above
+6144 for W2, or scale arrays not 16-byte aligned).
 """
 from __future__ import annotations
 
@@ -58,6 +61,39 @@ def test_workload_32_experts(gpu, orc):
 ])
 def test_shapes(gpu, orc, E, H, I, T, topk):
     check(gpu, orc, synth.moe_case(E * 1000 + H + I + T, E, H, I, T, topk))
+
+
+@pytest.mark.parametrize("E,H,I,T,topk", [
+    (2, 3104, 64, 40, 2),       # W13's scale rows too long to stage: per-step scales in the first product
+    (1, 64, 6176, 9, 1),        # W2's scale rows too long to stage: per-step scales in the second product
+])
+def test_scales_loaded_per_step(gpu, orc, E, H, I, T, topk):
+    check(gpu, orc, synth.moe_case(E * 1000 + H + I + T, E, H, I, T, topk))
+
+
+def _unaligned(a: np.ndarray) -> torch.Tensor:
+    # a contiguous device copy whose data starts one byte past a 16-byte boundary
+    flat = torch.zeros(a.size + 16, dtype=torch.uint8, device="cuda:0")
+    v = flat[1:1 + a.size]
+    v.copy_(torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8).ravel()))
+    assert v.data_ptr() % 16 == 1
+    return v.view(a.shape)
+
+
+def test_unaligned_scales_take_the_per_step_path(gpu, orc):
+    """Scale arrays off a 16-byte boundary are read per step; the result is bit-identical
+    to the staged one (same products, same order) and matches the oracle."""
+    c = synth.moe_case(31, 4, 160, 224, 33, 2)
+    say("moe: unaligned scale arrays")
+    staged = run_moe(gpu, c)
+    out = torch.full(c["x"].shape, -1, dtype=torch.int16, device="cuda:0").view(torch.bfloat16)
+    gpu.mxfp4_moe_gemm(bf16(c["x"]), u8(c["w13"]), _unaligned(c["w13_scale"]), u8(c["w2"]),
+                       _unaligned(c["w2_scale"]), i32(c["topk_ids"]), f32(c["topk_weights"]), out=out)
+    per_step = bits(out)
+    assert np.array_equal(per_step, staged)
+    want = bf16_values(orc.mxfp4_moe(c["x"], c["w13"], c["w13_scale"], c["w2"], c["w2_scale"],
+                                     c["topk_ids"], c["topk_weights"]))
+    assert rel_l2(bf16_values(per_step), want) <= TOL
 
 
 def test_every_token_to_the_same_two_experts(gpu, orc):
