@@ -13,7 +13,10 @@
 //   * Weights: each wave loads its tiles' lines with coalesced 16-byte loads
 //     (one instruction = 8 rows x 128 bytes), two steps ahead of use, and
 //     passes them through a private LDS buffer to reach the MFMA layout: lane
-//     (r, g) then holds blocks g and g + 4 of row r. Block b = g + 4 h feeds
+//     (r, g) then holds blocks g and g + 4 of row r. The buffer keeps block b
+//     of row w at 16-byte slot 8 w + (b ^ (w / 2 % 8)), so the coalesced
+//     writes (two rows per 16 lanes) and the MFMA-layout reads (16 rows, one
+//     block) have no bank conflicts. Block b = g + 4 h feeds
 //     four MFMAs, MFMA i taking codes [8 i, 8 i + 8) of the block as k slots
 //     8 g .. 8 g + 7; v_cvt_scalef32_pk_bf16_fp4 decodes two codes and applies
 //     the block scale in one instruction.
@@ -61,7 +64,6 @@ constexpr int kEngineStepCols = 256;
 constexpr int kEngineMaxTokens = 64;                 // token rows per pass (four MFMA tiles)
 constexpr int kPanelPitch = kEngineStepCols + 8;     // bf16 per staged token row (16-byte pad spreads banks)
 constexpr int kPanelElems = kEngineMaxTokens * kPanelPitch;
-constexpr int kWBufPitch = 9;                        // uint4 per transposed weight row (8 blocks + pad)
 constexpr int kNonTemporal = 2;                      // cache-policy operand of a buffer load: streaming
 constexpr int kStageChunks = 3;                      // 16-byte scale chunks per thread (staged path)
 constexpr int kStageBytes = kStageChunks * kEngineThreads * 16;   // 24 KiB of staged E8M0 rows
@@ -104,7 +106,7 @@ struct EngineStep {
 
 template <int NT>
 struct MoeEngine {
-    static constexpr int kWBufElems = NT * 16 * kWBufPitch;   // uint4 per wave
+    static constexpr int kWBufElems = NT * 16 * 8;   // uint4 per wave: [row][block ^ (row / 2 % 8)]
 
     // Shared state of one pass (in LDS, owned by the caller's kernel).
     struct Shared {
@@ -220,7 +222,7 @@ struct MoeEngine {
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
                 const int row = t * 16 + 8 * q + (lane >> 3);
-                wbuf[row * kWBufPitch + (lane & 7)] = b.w[t][q];
+                wbuf[row * 8 + ((lane & 7) ^ ((row >> 1) & 7))] = b.w[t][q];
                 if constexpr (!kStaged) sbuf[row * 8 + (lane & 7)] = b.e[t][q];
             }
         uint4 a4[NT][2];
@@ -230,7 +232,7 @@ struct MoeEngine {
         for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                a4[t][h] = wbuf[(t * 16 + r) * kWBufPitch + g + 4 * h];
+                a4[t][h] = wbuf[(t * 16 + r) * 8 + ((g + 4 * h) ^ ((r >> 1) & 7))];
                 if constexpr (kStaged)
                     e4[t][h] = stage[soff[t] + min(max(blk + 4 * h, 0), K / 32 - 1)];
                 else

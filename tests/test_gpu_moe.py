@@ -8,7 +8,7 @@ end mid-way, experts with more tokens than one pass, experts with none),
 the page's zero-code invariant, ids outside the expert range, determinism,
 and both ways the kernels read the E8M0 scales: staged in LDS per workgroup
 (the default) and loaded per step (hidden above 3072 for W13, inter above
-6144 for W2, or scale arrays not 16-byte aligned).
+3072 for W2, or scale arrays not 16-byte aligned).
 """
 from __future__ import annotations
 
@@ -65,7 +65,7 @@ def test_shapes(gpu, orc, E, H, I, T, topk):
 
 @pytest.mark.parametrize("E,H,I,T,topk", [
     (2, 3104, 64, 40, 2),       # W13's scale rows too long to stage: per-step scales in the first product
-    (1, 64, 6176, 9, 1),        # W2's scale rows too long to stage: per-step scales in the second product
+    (1, 64, 3104, 9, 1),        # W2's scale rows too long to stage: per-step scales in the second product
 ])
 def test_scales_loaded_per_step(gpu, orc, E, H, I, T, topk):
     check(gpu, orc, synth.moe_case(E * 1000 + H + I + T, E, H, I, T, topk))
