@@ -66,6 +66,17 @@ __host__ __device__ inline MoeLayout moe_layout(int64_t tokens, int64_t hidden, 
 
 // ------------------------------------------------------------------ route --
 
+constexpr int kRouteKeep = 4;   // chunks of kRouteThreads pairs whose ranks stay in registers
+
+// One workgroup. Pairs are taken in chunks of kRouteThreads (pair p0 + t by
+// thread t). Within a chunk a pair's rank among the pairs of its wave with the
+// same expert comes from wave ballots (lanes in order); the per-wave counts
+// become per-wave bases with a prefix over the waves (in wave order, after
+// the pairs of earlier chunks), so a pair's row within its expert is base +
+// rank: the order is (token, slot) order and needs no atomics. Rows of the
+// first kRouteKeep chunks stay in registers until the experts' offsets are
+// known; later chunks park them in pair_row. The offsets are an exclusive
+// prefix over the experts (waves of 64 experts, then the wave totals).
 __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(const int32_t* __restrict__ ids,
                                                                   int P, int E, int* __restrict__ cnt,
                                                                   int* __restrict__ off,
@@ -73,66 +84,101 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(const int32_t*
                                                                   int* __restrict__ row_pair) {
     __shared__ int s_wave[kRouteWaves][kMaxExperts];   // per-wave counts, then wave bases
     __shared__ int s_count[kMaxExperts];               // pairs per expert so far
-    __shared__ int s_scan[kMaxExperts];
+    __shared__ int s_off[kMaxExperts];                 // first row of each expert
+    __shared__ int s_wtot[kRouteWaves];                // pairs of each wave's 64 experts
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
     const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
     for (int x = tid; x < E; x += kRouteThreads) s_count[x] = 0;
-    for (int p0 = 0; p0 < P; p0 += kRouteThreads) {
+    // pair p0 + tid: its expert (-1 if none or out of range) and its row within the expert
+    auto chunk = [&](int p0, int& e_out, int& row_out) __attribute__((always_inline)) {
         for (int i = tid; i < kRouteWaves * E; i += kRouteThreads) s_wave[i / E][i % E] = 0;
         __syncthreads();
         const int p = p0 + tid;
         int e = (p < P) ? ids[p] : -1;
-        if (e < 0 || e >= E) {
-            if (p < P) pair_row[p] = -1;
-            e = -1;
-        }
-        // rank among the lanes of this wave with the same expert, in lane order
+        if (e < 0 || e >= E) e = -1;
         int rank = 0;
         uint64_t pending = __ballot(e >= 0);
         while (pending) {
             const int leader = __ffsll((unsigned long long)pending) - 1;
-            const int X = __shfl(e, leader, kWave);
+            const int X = __builtin_amdgcn_readlane(e, leader);   // leader is wave-uniform: no LDS round trip
             const uint64_t m = __ballot(e == X);
             if (e == X) rank = __popcll(m & lower);
             if (lane == leader) s_wave[wave][X] = __popcll(m);
             pending &= ~m;
         }
         __syncthreads();
-        // wave bases per expert, in wave order, continuing from earlier chunks
-        for (int x = tid; x < E; x += kRouteThreads) {
+        for (int x = tid; x < E; x += kRouteThreads) {   // wave bases of expert x, continuing s_count
+            int c[kRouteWaves];
+#pragma unroll
+            for (int w = 0; w < kRouteWaves; ++w) c[w] = s_wave[w][x];
             int run = s_count[x];
+#pragma unroll
             for (int w = 0; w < kRouteWaves; ++w) {
-                const int c = s_wave[w][x];
                 s_wave[w][x] = run;
-                run += c;
+                run += c[w];
             }
             s_count[x] = run;
         }
         __syncthreads();
-        if (e >= 0) pair_row[p] = s_wave[wave][e] + rank;   // stable rank within expert e
+        e_out = e;
+        row_out = e >= 0 ? s_wave[wave][e] + rank : 0;
+        __syncthreads();   // s_wave is cleared by the next chunk
+    };
+    int keep_e[kRouteKeep], keep_r[kRouteKeep];
+#pragma unroll
+    for (int c = 0; c < kRouteKeep; ++c) {
+        keep_e[c] = -1;
+        keep_r[c] = 0;
+        if (c * kRouteThreads < P) chunk(c * kRouteThreads, keep_e[c], keep_r[c]);   // workgroup-uniform
+    }
+    for (int p0 = kRouteKeep * kRouteThreads; p0 < P; p0 += kRouteThreads) {
+        int e, r;
+        chunk(p0, e, r);
+        if (p0 + tid < P) pair_row[p0 + tid] = e >= 0 ? r : -1;
+    }
+    // exclusive prefix of the counts over the experts: expert x = 64 wave + lane
+    {
+        const int x = tid;
+        const int v = x < E ? s_count[x] : 0;
+        int incl = v;
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+            const int u = __shfl_up(incl, d, kWave);
+            if (lane >= d) incl += u;
+        }
+        if (lane == kWave - 1) s_wtot[wave] = incl;
+        __syncthreads();
+        int base = 0;
+        for (int w = 0; w < wave; ++w) base += s_wtot[w];   // wave-uniform
+        if (x < E) {
+            s_off[x] = base + incl - v;
+            cnt[x] = v;
+            off[x] = base + incl - v;
+        }
+        if (x == E - 1) off[E] = base + incl;
         __syncthreads();
     }
-    // inclusive scan of the counts over experts (Hillis-Steele)
-    for (int x = tid; x < E; x += kRouteThreads) s_scan[x] = s_count[x];
-    for (int d = 1; d < E; d <<= 1) {
-        __syncthreads();
-        const int v = (tid < E && tid >= d) ? s_scan[tid - d] : 0;
-        __syncthreads();
-        if (tid < E) s_scan[tid] += v;
+#pragma unroll
+    for (int c = 0; c < kRouteKeep; ++c) {
+        const int p = c * kRouteThreads + tid;
+        if (p < P) {
+            const int e = keep_e[c];
+            if (e >= 0) {
+                const int r = s_off[e] + keep_r[c];
+                pair_row[p] = r;
+                row_pair[r] = p;
+            } else {
+                pair_row[p] = -1;
+            }
+        }
     }
-    __syncthreads();
-    if (tid < E) {
-        cnt[tid] = s_count[tid];
-        off[tid] = s_scan[tid] - s_count[tid];
-    }
-    if (tid == 0) off[E] = s_scan[E - 1];
-    for (int p = tid; p < P; p += kRouteThreads) {
-        const int e = ids[p];
-        if (e >= 0 && e < E) {
-            const int r = s_scan[e] - s_count[e] + pair_row[p];
+    for (int p = kRouteKeep * kRouteThreads + tid; p < P; p += kRouteThreads) {
+        const int r0 = pair_row[p];
+        if (r0 >= 0) {
+            const int r = s_off[ids[p]] + r0;
             pair_row[p] = r;
             row_pair[r] = p;
         }
@@ -354,29 +400,50 @@ __global__ __launch_bounds__(kThreads) void moe_gemm2_kernel(
 
 // --------------------------------------------------------------- combine --
 
-__global__ __launch_bounds__(kThreads) void moe_combine_kernel(const float* __restrict__ y,
-                                                               const int* __restrict__ pair_row,
-                                                               const float* __restrict__ weights,
-                                                               uint16_t* __restrict__ out, int T, int H,
-                                                               int topk) {
+constexpr int kCombineThreads = 256;   // 256-thread workgroups: the 256-token layer fills every compute unit
+
+// out[t] = bf16(sum over slots j, in slot order, of weights[t, j] * y[row of (t, j)]):
+// thread i takes token i / (H / 8), columns 8 (i % (H / 8)) .. + 7. The rows and
+// weights of four slots are read first, then their eight 16-byte y loads, so
+// the slots' latencies overlap; a slot without a row (an expert id outside the
+// range) reads row 0 and adds nothing.
+__global__ __launch_bounds__(kCombineThreads) void moe_combine_kernel(const float* __restrict__ y,
+                                                                      const int* __restrict__ pair_row,
+                                                                      const float* __restrict__ weights,
+                                                                      uint16_t* __restrict__ out, int T, int H,
+                                                                      int topk) {
     const int chunks = H / 8;
     const int64_t total = (int64_t)T * chunks;
-    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total;
-         i += (int64_t)gridDim.x * kThreads) {
+    for (int64_t i = (int64_t)blockIdx.x * kCombineThreads + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * kCombineThreads) {
         const int t = (int)(i / chunks);
         const int c = (int)(i % chunks);
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        for (int j = 0; j < topk; ++j) {
-            const int r = pair_row[t * topk + j];
-            if (r < 0) continue;
-            const float w = weights[t * topk + j];
-            const f32x4* src = reinterpret_cast<const f32x4*>(y + (size_t)r * H + 8 * c);
-            const f32x4 v0 = src[0], v1 = src[1];
+        for (int j0 = 0; j0 < topk; j0 += 4) {
+            int r[4];
+            float w[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                acc[q] += w * v0[q];
-                acc[4 + q] += w * v1[q];
+                const int j = min(j0 + q, topk - 1);
+                r[q] = j0 + q < topk ? pair_row[t * topk + j] : -1;
+                w[q] = weights[t * topk + j];
             }
+            f32x4 v[4][2];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f32x4* src = reinterpret_cast<const f32x4*>(y + (size_t)max(r[q], 0) * H + 8 * c);
+                v[q][0] = src[0];
+                v[q][1] = src[1];
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (r[q] >= 0) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        acc[e] += w[q] * v[q][0][e];
+                        acc[4 + e] += w[q] * v[q][1][e];
+                    }
+                }
         }
         uint4 o;
         o.x = pack_bf16x2(acc[0], acc[1]);
@@ -429,9 +496,9 @@ hipError_t launch_moe(const uint16_t* x, const uint8_t* w13, const uint8_t* w13s
         moe_gemm2_kernel<false><<<g2, kThreads, 0, stream>>>(act, w2, w2s, cnt, off, y, H, I, E);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     const int64_t chunks = tokens * (hidden / 8);
-    const int64_t want = (chunks + kThreads - 1) / kThreads;
-    const int grid = (int)(want < 4096 ? want : 4096);
-    moe_combine_kernel<<<grid, kThreads, 0, stream>>>(y, pair_row, weights, out, (int)tokens, H, (int)topk);
+    const int64_t want = (chunks + kCombineThreads - 1) / kCombineThreads;
+    const int grid = (int)(want < 8192 ? want : 8192);
+    moe_combine_kernel<<<grid, kCombineThreads, 0, stream>>>(y, pair_row, weights, out, (int)tokens, H, (int)topk);
     return hipGetLastError();
 }
 

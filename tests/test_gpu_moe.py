@@ -58,6 +58,7 @@ def test_workload_32_experts(gpu, orc):
     (8, 2880, 2880, 16, 4),     # the layer's extents with few tokens: some experts get none
     (1, 32, 32, 1, 1),
     (512, 64, 96, 300, 4),      # the most experts the entry point accepts, ~2 pairs each
+    (8, 64, 96, 1100, 4),       # 4400 pairs: routing ranks of the fifth 1024-pair chunk go through memory
 ])
 def test_shapes(gpu, orc, E, H, I, T, topk):
     check(gpu, orc, synth.moe_case(E * 1000 + H + I + T, E, H, I, T, topk))
