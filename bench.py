@@ -769,7 +769,8 @@ def probe_library():
         for name, res, argt in (("e2m1_probe_empty", i32, [i64, i32, vp]),
                                 ("e2m1_probe_stream_grid", i64, [i64, i32]),
                                 ("e2m1_probe_stream", i32, [vp, i64, vp, i64, i32, i32, vp]),
-                                ("e2m1_probe_mfma", i32, [i64, i32, vp, i64, vp])):
+                                ("e2m1_probe_mfma", i32, [i64, i32, i32, vp, i64, vp]),
+                                ("e2m1_probe_lds", i32, [vp, i64, i32, vp, i64, vp])):
             fn = getattr(lib, name)
             fn.restype, fn.argtypes = res, argt
         _probe = lib
@@ -866,37 +867,96 @@ class HbmStream(Workload):
 
 
 class MfmaPeak(Workload):
-    """Four independent v_mfma_f32_32x32x16_bf16 chains per wave, two waves per SIMD: the
-    bf16 matrix-core rate a kernel can reach, and the reading of the MFMA-busy counter
-    for a kernel that keeps the matrix cores saturated."""
+    """Four independent bf16 MFMA chains per wave, two waves per SIMD: the matrix-core
+    rate a kernel can reach with one instruction shape (form 32: v_mfma_f32_32x32x16_bf16,
+    form 16: v_mfma_f32_16x16x32_bf16), and the reading of the MFMA-busy counter for a
+    kernel that keeps the matrix cores saturated."""
     GRID, ITERS = 512, 2048
 
-    def __init__(self, rotate_bytes: float):
+    def __init__(self, rotate_bytes: float, form: int = 32):
         import torch
-        self.name = "mfma_bf16_peak"
+        self.form = form
+        self.shape = "32x32x16" if form == 32 else "16x16x32"
+        self.label = f"probe_mfma_{self.shape}"
+        self.name = "mfma_bf16_peak" + ("" if form == 32 else "_16x16x32")
         self.copies = 4
         self.bound = "mfma"
         self.out = torch.zeros(self.GRID * 256, dtype=torch.float32, device="cuda")
-        self.metric = "bf16 MFMA rate of a kernel of back-to-back independent 32x32x16 MFMAs"
+        self.metric = f"bf16 MFMA rate of a kernel of back-to-back independent {self.shape} MFMAs"
         self.config = {"workload": self.name, "grid": self.GRID, "block": 256, "iters": self.ITERS,
-                       "chains_per_wave": 4, "instruction": "v_mfma_f32_32x32x16_bf16"}
+                       "chains_per_wave": 4, "instruction": f"v_mfma_f32_{self.shape}_bf16"}
 
     def launches(self):
         lib = probe_library()
 
         def fn(i):
-            _probe_ok(lib.e2m1_probe_mfma(self.GRID, self.ITERS, self.out.data_ptr(), self.out.numel(),
-                                          _stream_handle()), "mfma")
-        return [("probe_mfma_32x32x16", fn)]
+            _probe_ok(lib.e2m1_probe_mfma(self.GRID, self.ITERS, self.form, self.out.data_ptr(),
+                                          self.out.numel(), _stream_handle()), "mfma")
+        return [(self.label, fn)]
 
     def alg_bytes(self, label):
         return 0
 
     def alg_flops(self, label):
-        return float(self.GRID * 4 * self.ITERS * 4 * 32768)
+        return float(self.GRID * 4 * self.ITERS * 4 * (32768 if self.form == 32 else 16384))
 
     def headline(self, ms_per_step, per_launch):
-        return round(self.alg_flops("") / (per_launch["probe_mfma_32x32x16"] * 1e-3) / 1e12, 1), "TFLOP/s", True
+        return round(self.alg_flops("") / (per_launch[self.label] * 1e-3) / 1e12, 1), "TFLOP/s", True
+
+
+def lds_pattern(name: str, lane: int) -> int:
+    """16-byte LDS slot read by `lane` (0..63) in the LDS read-rate probe. r = lane % 16 and
+    g = lane // 16 are the MFMA operand layout's row and lane group."""
+    r, g = lane % 16, lane // 16
+    return {
+        "contiguous": lane,                                  # 1 KB in lane order
+        "rows33_shift4": 33 * r + 4 * g,                     # padded 528-byte rows, groups 64 bytes apart
+        "rows9_shift1": 9 * r + g,                           # padded 144-byte rows, groups 16 bytes apart
+        "rows8_xor": 8 * r + (g ^ ((r >> 1) & 7)),           # 128-byte rows, block index XOR row / 2
+        "chunk_major": 256 * g + r,                          # 16 rows contiguous per group, groups 4 KB apart
+        "pitch256": 16 * lane,                               # every lane in one bank group
+    }[name]
+
+
+LDS_PATTERNS = ("contiguous", "rows33_shift4", "rows9_shift1", "rows8_xor", "chunk_major", "pitch256")
+
+
+class LdsRead(Workload):
+    """LDS read rate of one lane -> 16-byte slot pattern: one 512-thread workgroup per
+    compute unit, every wave reading the pattern with back-to-back ds_read_b128."""
+    GRID_PER_CU, ITERS = 1, 256
+
+    def __init__(self, rotate_bytes: float, pattern: str):
+        import torch
+        self.pattern = pattern
+        self.name = f"lds_read_{pattern}"
+        self.label = f"probe_lds_{pattern}"
+        self.copies = 4
+        self.bound = "lds"
+        self.grid = self.GRID_PER_CU * torch.cuda.get_device_properties(0).multi_processor_count
+        table = [lds_pattern(pattern, l) for l in range(64)]
+        self.table = torch.tensor(table, dtype=torch.int32, device="cuda")
+        self.out = torch.zeros(self.grid * 512, dtype=torch.int32, device="cuda")
+        self.metric = f"LDS read rate, ds_read_b128, pattern {pattern}, eight waves per compute unit"
+        self.config = {"workload": self.name, "grid": self.grid, "block": 512, "iters": self.ITERS,
+                       "reads_per_lane": 8 * self.ITERS, "slots": table}
+
+    def launches(self):
+        lib = probe_library()
+
+        def fn(i):
+            _probe_ok(lib.e2m1_probe_lds(self.table.data_ptr(), self.grid, self.ITERS, self.out.data_ptr(),
+                                         self.out.numel(), _stream_handle()), "lds")
+        return [(self.label, fn)]
+
+    def alg_bytes(self, label):   # HBM bytes: none (the array lives in LDS)
+        return 0
+
+    def lds_bytes(self) -> float:
+        return float(self.grid * 512 * 16 * 8 * self.ITERS)
+
+    def headline(self, ms_per_step, per_launch):
+        return round(self.lds_bytes() / (per_launch[self.label] * 1e-3) / 1e12, 2), "TB/s", True
 
 
 HEADLINE_BYTES = 14336 * 4096 // 2 + 14336 * 4096 // 32   # one batch-1 MLP GEMV launch's weights
@@ -911,6 +971,7 @@ WORKLOADS = {
     "stream_128mb": lambda rb: HbmStream(128 << 20, 0, rb),
     "stream_512mb": lambda rb: HbmStream(512 << 20, 0, rb),
     "mfma_peak": MfmaPeak,
+    "mfma_peak_16x16x32": lambda rb: MfmaPeak(rb, 16),
     "moe": Moe,
     "mlp_b1": lambda rb: GemvMLP(1, rb),
     "mlp_b2": lambda rb: GemvMLP(2, rb),
@@ -933,6 +994,7 @@ WORKLOADS = {
     "nm_4of8": lambda rb: NmSparse(4, 8, rb),
     "gemv_small": GemvSmall,
 }
+WORKLOADS.update({f"lds_{p}": (lambda p: lambda rb: LdsRead(rb, p))(p) for p in LDS_PATTERNS})
 
 
 # ---------------------------------------------------------------- timing ---
@@ -1158,6 +1220,9 @@ def main() -> int:
         tflops = wl.alg_flops(dom["label"]) / (dom["avg_us"] * 1e-6) / 1e12
         roofline.update({"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4)})
+    elif getattr(wl, "bound", "hbm") == "lds":   # no published per-CU LDS figure to divide by
+        roofline.update({"bound": "lds", "achieved": round(wl.lds_bytes() / (dom["avg_us"] * 1e-6) / 1e12, 2),
+                         "peak": None, "unit": "TB/s", "frac": None})
 
     cpu = None
     if not args.no_cpu_baseline:

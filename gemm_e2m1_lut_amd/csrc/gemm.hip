@@ -24,9 +24,10 @@
 //     plain loads through their restrict pointers were sunk by the compiler
 //     next to their first use, exposing the full load latency every step.
 //   * Waves are laid out 2 x 2 over the tile; each owns 64 weight rows x 64
-//     activation rows as 2 x 2 tiles of v_mfma_f32_32x32x16_bf16 (on this
-//     part the 32 x 32 form issues twice the flops of v_mfma_f32_16x16x32_bf16
-//     per cycle). Lane l = 32 g + r takes 8 codes (4 bytes) of weight row r
+//     activation rows as 2 x 2 tiles of v_mfma_f32_32x32x16_bf16 (each
+//     operand register then serves twice the flops of a 16 x 16 x 32 one, and
+//     back-to-back independent 32 x 32 x 16 MFMAs run about 10 % faster on
+//     this part). Lane l = 32 g + r takes 8 codes (4 bytes) of weight row r
 //     per 16-column slice and decodes them with four
 //     v_cvt_scalef32_pk_bf16_fp4 (two codes each, table lookup and E8M0 scale
 //     in one instruction); each decoded A operand serves two MFMAs. B

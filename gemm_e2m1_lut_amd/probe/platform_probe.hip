@@ -1,8 +1,9 @@
 // platform_probe.hip -- the platform limits a per-launch roofline figure is
 // read against, measured with the simplest possible kernels: the time of an
 // empty launch, the time to stream B bytes from HBM with nothing else to do,
-// and a kernel that keeps every SIMD's matrix core busy (the reference point
-// for the MFMA-busy counter). Built into libe2m1probe.so (separate from
+// a kernel that keeps every SIMD's matrix core busy (the reference point for
+// the MFMA-busy counter; two instruction shapes), and the LDS read rate of a
+// lane -> address pattern. Built into libe2m1probe.so (separate from
 // libe2m1lut.so, which never loads it) and run by the benchmark's probe
 // workloads.
 //
@@ -26,12 +27,22 @@
 //       be at least grid * block / 64): a small output like a GEMV's; with
 //       store = 2 only the first wave of the grid writes (out[0]).
 //
-//   int e2m1_probe_mfma(int64_t grid, int iters, float* out, int64_t out_words,
-//                       void* stream)
+//   int e2m1_probe_mfma(int64_t grid, int iters, int form, float* out,
+//                       int64_t out_words, void* stream)
 //       grid workgroups of four waves; every wave runs `iters` rounds of four
-//       independent v_mfma_f32_32x32x16_bf16 chains (32768 flops each) on
-//       register operands, then writes one float per thread to out
-//       (out_words >= grid * 256). Flops per launch: grid * 4 * iters * 4 * 32768.
+//       independent MFMA chains on register operands, then writes one float
+//       per thread to out (out_words >= grid * 256). form 32:
+//       v_mfma_f32_32x32x16_bf16 (32768 flops each), form 16:
+//       v_mfma_f32_16x16x32_bf16 (16384 flops each). Flops per launch:
+//       grid * 4 * iters * 4 * (flops of one instruction).
+//
+//   int e2m1_probe_lds(const uint32_t* table, int64_t grid, int iters,
+//                      uint32_t* out, int64_t out_words, void* stream)
+//       grid workgroups of eight waves; lane l of every wave reads the
+//       16-byte LDS slot table[l] % 4096 (of a 64 KiB array) 8 * iters times
+//       with ds_read_b128, eight reads back to back per wait, then writes one
+//       word per thread to out (out_words >= grid * 512). LDS bytes read per
+//       launch: grid * 512 * 16 * 8 * iters. `table` holds 64 words.
 //
 // All return 0, or -1 for an argument out of range, -2 for a launch error.
 // Every index is clamped to the buffer, so every access is in bounds.
@@ -77,6 +88,9 @@ __global__ __launch_bounds__(kBlock) void probe_stream_kernel(const u32x4* __res
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <int kForm>
 __global__ __launch_bounds__(256) void probe_mfma_kernel(int iters, float* __restrict__ out) {
     bf16x8 a, b;
 #pragma unroll
@@ -84,18 +98,74 @@ __global__ __launch_bounds__(256) void probe_mfma_kernel(int iters, float* __res
         a[i] = (__bf16)((float)((threadIdx.x + i) & 7) * 0.125f);
         b[i] = (__bf16)((float)((threadIdx.x * 3 + i) & 7) * -0.0625f);
     }
-    f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
-    for (int it = 0; it < iters; ++it) {
-        c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
-        c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
-        c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
-        c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
-    }
-    const f32x16 t = c0 + c1 + c2 + c3;
     float total = 0.f;
+    if constexpr (kForm == 32) {
+        f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+        for (int it = 0; it < iters; ++it) {
+            c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+            c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
+            c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
+            c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
+        }
+        const f32x16 t = c0 + c1 + c2 + c3;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) total += t[e];
+        for (int e = 0; e < 16; ++e) total += t[e];
+    } else {
+        // written out: with the builtin the compiler shuffles these four accumulators through
+        // extra registers every round, which the probe would time instead of the instruction
+        f32x4 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+        for (int it = 0; it < iters; ++it) {
+            asm volatile(
+                "v_mfma_f32_16x16x32_bf16 %0, %4, %5, %0\n"
+                "v_mfma_f32_16x16x32_bf16 %1, %4, %5, %1\n"
+                "v_mfma_f32_16x16x32_bf16 %2, %4, %5, %2\n"
+                "v_mfma_f32_16x16x32_bf16 %3, %4, %5, %3\n"
+                : "+v"(c0), "+v"(c1), "+v"(c2), "+v"(c3)
+                : "v"(a), "v"(b));
+        }
+        const f32x4 t = c0 + c1 + c2 + c3;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) total += t[e];
+    }
     out[(int64_t)blockIdx.x * 256 + threadIdx.x] = total;
+}
+
+// Eight ds_read_b128 of one address per round, one wait per round: the reads
+// of a round are in flight together, so the time per round is set by the LDS
+// read rate of the pattern (with eight waves per workgroup sharing the LDS).
+__global__ __launch_bounds__(512) void probe_lds_kernel(const uint32_t* __restrict__ table, int iters,
+                                                        uint32_t* __restrict__ out) {
+    __shared__ __attribute__((aligned(16))) uint32_t lds[16384];   // the kernel's only LDS variable: address 0
+    for (int i = threadIdx.x; i < 16384; i += 512) lds[i] = (uint32_t)i * 2654435761u;
+    __syncthreads();
+    const int l = threadIdx.x & 63;
+    const uint32_t a = (table[l] % 4096u) * 16u;   // byte address of the lane's slot
+    uint32_t acc = 0;
+    for (int it = 0; it < iters; ++it) {
+        uint32_t x0, x1, x2, x3;
+        asm volatile(
+            "ds_read_b128 v[100:103], %4\n"
+            "ds_read_b128 v[104:107], %4\n"
+            "ds_read_b128 v[108:111], %4\n"
+            "ds_read_b128 v[112:115], %4\n"
+            "ds_read_b128 v[116:119], %4\n"
+            "ds_read_b128 v[120:123], %4\n"
+            "ds_read_b128 v[124:127], %4\n"
+            "ds_read_b128 v[128:131], %4\n"
+            "s_waitcnt lgkmcnt(0)\n"
+            "v_mov_b32 %0, v100\n"
+            "v_mov_b32 %1, v105\n"
+            "v_mov_b32 %2, v110\n"
+            "v_mov_b32 %3, v131\n"
+            : "=v"(x0), "=v"(x1), "=v"(x2), "=v"(x3)
+            : "v"(a)
+            : "memory", "v100", "v101", "v102", "v103", "v104", "v105", "v106", "v107", "v108", "v109", "v110",
+              "v111", "v112", "v113", "v114", "v115", "v116", "v117", "v118", "v119", "v120", "v121", "v122",
+              "v123", "v124", "v125", "v126", "v127", "v128", "v129", "v130", "v131");
+        acc ^= x0 ^ x1 ^ x2 ^ x3;
+    }
+    // keeps the array (and so its LDS allocation) live: the reads above are opaque to the compiler
+    out[(int64_t)blockIdx.x * 512 + threadIdx.x] = acc + lds[(threadIdx.x * 7) & 16383];
 }
 
 int64_t stream_grid(int64_t bytes, int block) {
@@ -139,9 +209,21 @@ extern "C" int e2m1_probe_stream(const void* src, int64_t bytes, uint32_t* out, 
     return hipGetLastError() == hipSuccess ? 0 : -2;
 }
 
-extern "C" int e2m1_probe_mfma(int64_t grid, int iters, float* out, int64_t out_words, void* stream) {
+extern "C" int e2m1_probe_mfma(int64_t grid, int iters, int form, float* out, int64_t out_words, void* stream) {
     if (grid < 1 || grid >= ((int64_t)1 << 31) || iters < 1 || out == nullptr || out_words < grid * 256) return -1;
+    if (form != 16 && form != 32) return -1;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    probe_mfma_kernel<<<dim3((unsigned)grid), dim3(256), 0, s>>>(iters, out);
+    if (form == 32) probe_mfma_kernel<32><<<dim3((unsigned)grid), dim3(256), 0, s>>>(iters, out);
+    else probe_mfma_kernel<16><<<dim3((unsigned)grid), dim3(256), 0, s>>>(iters, out);
+    return hipGetLastError() == hipSuccess ? 0 : -2;
+}
+
+extern "C" int e2m1_probe_lds(const uint32_t* table, int64_t grid, int iters, uint32_t* out, int64_t out_words,
+                              void* stream) {
+    if (table == nullptr || out == nullptr || grid < 1 || grid >= ((int64_t)1 << 31) || iters < 1 ||
+        out_words < grid * 512)
+        return -1;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    probe_lds_kernel<<<dim3((unsigned)grid), dim3(512), 0, s>>>(table, iters, out);
     return hipGetLastError() == hipSuccess ? 0 : -2;
 }
