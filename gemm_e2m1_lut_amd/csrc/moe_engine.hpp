@@ -46,7 +46,12 @@
 //     its B operands from it at the same columns as the A operands, so the
 //     column -> k-slot map is the same for both and the sum over k is
 //     complete. Columns past K are staged as zeros, so weight blocks past the
-//     row end (loaded clamped, finite) add nothing.
+//     row end (loaded clamped, finite) add nothing. Panel rows are padded by
+//     16 bytes; the B-operand reads of this layout (16 rows per 16 lanes,
+//     lane groups 64 bytes apart) run at 0.6 of the LDS's contiguous read
+//     rate, but a chunk-major panel that reads at the full rate takes its
+//     token loads as 64-byte pieces of 16 rows per wave instead of 512-byte
+//     rows, and that measured slower overall.
 //
 // Every load is issued on every path (indices clamped), the token loads of a
 // step before its weight loads, so each wait the compiler places counts
