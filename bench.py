@@ -770,7 +770,8 @@ def probe_library():
                                 ("e2m1_probe_stream_grid", i64, [i64, i32]),
                                 ("e2m1_probe_stream", i32, [vp, i64, vp, i64, i32, i32, vp]),
                                 ("e2m1_probe_mfma", i32, [i64, i32, i32, vp, i64, vp]),
-                                ("e2m1_probe_lds", i32, [vp, i64, i32, vp, i64, vp])):
+                                ("e2m1_probe_lds", i32, [vp, i64, i32, vp, i64, vp]),
+                                ("e2m1_probe_expand", i32, [vp, i64, vp, vp])):
             fn = getattr(lib, name)
             fn.restype, fn.argtypes = res, argt
         _probe = lib
@@ -864,6 +865,43 @@ class HbmStream(Workload):
 
     def headline(self, ms_per_step, per_launch):
         return round(self.nbytes / (per_launch[self.label] * 1e-3) / 1e9, 2), "GB/s", True
+
+
+class ExpandStream(Workload):
+    """Reads `src_bytes` and writes four times as many (16 bytes in, 64 out per chunk, the
+    byte ratio of a 4-bit code to its bf16 decode): the streaming reference of the
+    write-heavy kernels at their sizes."""
+
+    def __init__(self, src_bytes: int, rotate_bytes: float):
+        import torch
+        self.src_bytes = src_bytes
+        self.name = f"hbm_expand_{src_bytes}B"
+        self.label = f"probe_expand_{src_bytes}B"
+        self.copies = max(2, math.ceil(rotate_bytes / (5 * src_bytes)))
+        g = _gen(778)
+        self.src = [torch.randint(0, 256, (src_bytes,), dtype=torch.uint8, device="cuda", generator=g)
+                    for _ in range(self.copies)]
+        self.dst = [torch.empty(4 * src_bytes, dtype=torch.uint8, device="cuda") for _ in range(self.copies)]
+        self.weight_bytes_per_step = float(src_bytes)
+        self.total_bytes_per_step = float(self.alg_bytes(self.label))
+        self.metric = f"HBM rate of a stream reading {src_bytes} bytes and writing {4 * src_bytes}"
+        self.config = {"workload": self.name, "read_bytes": src_bytes, "write_bytes": 4 * src_bytes,
+                       "per_chunk": "16 B non-temporal load, 4 x 16 B non-temporal stores",
+                       "buffers_rotated": self.copies}
+
+    def launches(self):
+        lib = probe_library()
+
+        def fn(i):
+            _probe_ok(lib.e2m1_probe_expand(self.src[i % self.copies].data_ptr(), self.src_bytes,
+                                            self.dst[i % self.copies].data_ptr(), _stream_handle()), "expand")
+        return [(self.label, fn)]
+
+    def alg_bytes(self, label):
+        return 5 * self.src_bytes
+
+    def headline(self, ms_per_step, per_launch):
+        return round(self.alg_bytes("") / (per_launch[self.label] * 1e-3) / 1e9, 2), "GB/s", True
 
 
 class MfmaPeak(Workload):
@@ -970,6 +1008,8 @@ WORKLOADS = {
     "stream_4mb_store": lambda rb: HbmStream(TERNARY_BYTES, 1, rb),
     "stream_128mb": lambda rb: HbmStream(128 << 20, 0, rb),
     "stream_512mb": lambda rb: HbmStream(512 << 20, 0, rb),
+    "expand_29mb": lambda rb: ExpandStream(14336 * 4096 // 2, rb),
+    "expand_17mb": lambda rb: ExpandStream(8192 * 4096 // 2, rb),
     "mfma_peak": MfmaPeak,
     "mfma_peak_16x16x32": lambda rb: MfmaPeak(rb, 16),
     "moe": Moe,

@@ -80,6 +80,7 @@ PROFILE_NAMES = {
     "stream_4mb_store": "platform_hbm_stream_4mb_store", "stream_128mb": "platform_hbm_stream_128mb",
     "stream_512mb": "platform_hbm_stream_512mb", "mfma_peak": "platform_mfma_bf16",
     "mfma_peak_16x16x32": "platform_mfma_bf16_16x16x32",
+    "expand_29mb": "platform_hbm_expand_29mb_to_117mb", "expand_17mb": "platform_hbm_expand_17mb_to_67mb",
     **{f"lds_{p}": f"platform_lds_read_{p}" for p in ("contiguous", "rows33_shift4", "rows9_shift1", "rows8_xor",
                                                       "chunk_major", "pitch256")},
 }

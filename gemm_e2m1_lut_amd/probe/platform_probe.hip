@@ -36,6 +36,17 @@
 //       v_mfma_f32_16x16x32_bf16 (16384 flops each). Flops per launch:
 //       grid * 4 * iters * 4 * (flops of one instruction).
 //
+//   int e2m1_probe_expand(const void* src, int64_t src_bytes, void* dst,
+//                         void* stream)
+//       Reads src_bytes (a positive multiple of 16) with 16-byte non-temporal
+//       loads and writes four times as many bytes to dst: 16-byte chunk j of
+//       src (bitwise inverted) goes to chunk j of each of the four
+//       src_bytes-long planes of dst, with non-temporal stores, so every load
+//       and store instruction of a wave covers 1 KB of consecutive bytes;
+//       each thread issues its eight loads first. The byte ratio of a 4-bit
+//       code to its bf16 decode (1 : 4): the streaming reference of the
+//       write-heavy kernels.
+//
 //   int e2m1_probe_lds(const uint32_t* table, int64_t grid, int iters,
 //                      uint32_t* out, int64_t out_words, void* stream)
 //       grid workgroups of eight waves; lane l of every wave reads the
@@ -130,6 +141,28 @@ __global__ __launch_bounds__(256) void probe_mfma_kernel(int iters, float* __res
     out[(int64_t)blockIdx.x * 256 + threadIdx.x] = total;
 }
 
+// Read one 16-byte chunk, write it to four planes: eight chunks per thread, every load first.
+__global__ __launch_bounds__(256) void probe_expand_kernel(const u32x4* __restrict__ src, int64_t n16,
+                                                           u32x4* __restrict__ dst) {
+    const int64_t base = (int64_t)blockIdx.x * kLoads * 256 + threadIdx.x;
+    u32x4 v[kLoads];
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+        const int64_t i = base + (int64_t)j * 256;
+        v[j] = __builtin_nontemporal_load(src + (i < n16 ? i : n16 - 1));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // chunks past the end (the grid's tail) rewrite the last chunk with its own value: no branch
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+        const int64_t i = base + (int64_t)j * 256;
+        const u32x4 w = ~v[j];
+        u32x4* d = dst + (i < n16 ? i : n16 - 1);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) __builtin_nontemporal_store(w, d + q * n16);
+    }
+}
+
 // Eight ds_read_b128 of one address per round, one wait per round: the reads
 // of a round are in flight together, so the time per round is set by the LDS
 // read rate of the pattern (with eight waves per workgroup sharing the LDS).
@@ -215,6 +248,16 @@ extern "C" int e2m1_probe_mfma(int64_t grid, int iters, int form, float* out, in
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (form == 32) probe_mfma_kernel<32><<<dim3((unsigned)grid), dim3(256), 0, s>>>(iters, out);
     else probe_mfma_kernel<16><<<dim3((unsigned)grid), dim3(256), 0, s>>>(iters, out);
+    return hipGetLastError() == hipSuccess ? 0 : -2;
+}
+
+extern "C" int e2m1_probe_expand(const void* src, int64_t src_bytes, void* dst, void* stream) {
+    if (src == nullptr || dst == nullptr || src_bytes <= 0 || src_bytes % 16 != 0) return -1;
+    const int64_t n16 = src_bytes / 16;
+    const int64_t grid = (n16 + (int64_t)kLoads * 256 - 1) / ((int64_t)kLoads * 256);
+    if (grid >= ((int64_t)1 << 31)) return -1;
+    probe_expand_kernel<<<dim3((unsigned)grid), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(
+        static_cast<const u32x4*>(src), n16, static_cast<u32x4*>(dst));
     return hipGetLastError() == hipSuccess ? 0 : -2;
 }
 
