@@ -92,6 +92,15 @@ def test_profile_kernel_names():
                          "std::array<char*, 2ul> >(int, char*)").startswith("vectorized_elementwise_kernel<4,")
 
 
+def test_every_workload_has_a_profile_name():
+    """bench_profile.py names each workload's summary file; a workload added to bench.py
+    without a name would write profiles/<workload>.txt under its bare key."""
+    import bench
+    import bench_profile as bp
+    assert set(bench.WORKLOADS) == set(bp.PROFILE_NAMES)
+    assert len(set(bp.PROFILE_NAMES.values())) == len(bp.PROFILE_NAMES)
+
+
 def test_profile_records_are_attributed_by_marks():
     """Records between a label's mark and the next belong to that label, and so does every
     later record with the same kernel, grid and workgroup; the copies sit between two marks
