@@ -1006,6 +1006,7 @@ WORKLOADS = {
     "stream_31mb_store": lambda rb: HbmStream(HEADLINE_BYTES, 1, rb),
     "stream_31mb_store1": lambda rb: HbmStream(HEADLINE_BYTES, 2, rb),
     "stream_4mb_store": lambda rb: HbmStream(TERNARY_BYTES, 1, rb),
+    "stream_17mb_store": lambda rb: HbmStream(4 * TERNARY_BYTES, 1, rb),   # the widely-linear layer's four matrices
     "stream_128mb": lambda rb: HbmStream(128 << 20, 0, rb),
     "stream_512mb": lambda rb: HbmStream(512 << 20, 0, rb),
     "expand_29mb": lambda rb: ExpandStream(14336 * 4096 // 2, rb),

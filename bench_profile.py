@@ -77,7 +77,7 @@ PROFILE_NAMES = {
     "moe": "moe_E32_H2880_I2880_T256_top4",
     "floor": "platform_empty_kernel", "stream_31mb": "platform_hbm_stream_31mb",
     "stream_31mb_store": "platform_hbm_stream_31mb_store", "stream_31mb_store1": "platform_hbm_stream_31mb_store1",
-    "stream_4mb_store": "platform_hbm_stream_4mb_store", "stream_128mb": "platform_hbm_stream_128mb",
+    "stream_4mb_store": "platform_hbm_stream_4mb_store", "stream_17mb_store": "platform_hbm_stream_17mb_store", "stream_128mb": "platform_hbm_stream_128mb",
     "stream_512mb": "platform_hbm_stream_512mb", "mfma_peak": "platform_mfma_bf16",
     "mfma_peak_16x16x32": "platform_mfma_bf16_16x16x32",
     "expand_29mb": "platform_hbm_expand_29mb_to_117mb", "expand_17mb": "platform_hbm_expand_17mb_to_67mb",

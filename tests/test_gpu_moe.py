@@ -61,6 +61,7 @@ def test_workload_32_experts(gpu, orc):
     (8, 64, 96, 1100, 4),       # 4400 pairs: routing ranks of the fifth 1024-pair chunk go through memory
     (2, 256, 1024, 40, 2),      # W2 rows of 512 bytes: four steps, every row on a 128-byte line
     (1, 64, 1056, 20, 1),       # W2 rows of 528 bytes: line offsets in steps of 16 bytes (period 8), five steps
+    (8, 64, 96, 40, 6),         # top-6: the combine's second group of slots is partly empty
 ])
 def test_shapes(gpu, orc, E, H, I, T, topk):
     check(gpu, orc, synth.moe_case(E * 1000 + H + I + T, E, H, I, T, topk))
