@@ -7,7 +7,8 @@ accumulation. Shapes span one and many 128 x 128 tiles, ragged tiles in both
 directions, K with an odd number of 32-column blocks (a half step of zero
 weights), both output dtypes, block scales over a wide exponent range, and the
 prefill shape of the benchmark (2048 tokens through the Llama-8B MLP
-matrices) on sampled rows and columns.
+matrices) on sampled rows and columns, and the largest K the entry point
+accepts under a full 128-row tile.
 """
 from __future__ import annotations
 
@@ -97,3 +98,25 @@ def test_empty_and_zero_k(gpu):
                          torch.zeros((5, 1), dtype=torch.uint8, device="cuda:0"),
                          torch.zeros((0, 32), dtype=torch.bfloat16, device="cuda:0"))
     assert e.shape == (0, 5)
+
+
+@pytest.mark.slow
+def test_largest_k(gpu, orc):
+    """k = E2M1_GEMM_MAX_K under a full 128-row tile: the workgroup's x offsets reach
+    2 * 128 * k bytes, just under 2^31 (its 32-bit byte offsets). Rows 0, 1, 126 and 127 of x
+    carry data and are checked against the oracle; every other row is zero, so its outputs
+    must be exact zeros."""
+    k, m, n = 8388576, 128, 20
+    r = np.random.default_rng(synth.SEED_BASE + 71)
+    packed, scales = synth.mxfp4_matrix(r, n, k)
+    rows = [0, 1, 126, 127]
+    x = np.zeros((m, k), np.uint16)
+    x[rows] = synth.bf16_normal(r, (len(rows), k))
+    say(f"gemm: largest k = {k}, m = {m}, n = {n}")
+    out = torch.full((m, n), float("nan"), dtype=torch.float32, device="cuda:0")
+    gpu.dequant_gemm(u8(packed), u8(scales), bf16(x), out=out)
+    got = host_f32(out).astype(np.float64)
+    want = orc.mxfp4_gemv(packed, scales, x[rows], "f32").astype(np.float64)
+    assert np.isfinite(got).all()
+    assert rel_l2(got[rows], want) <= TOL
+    assert (got[np.setdiff1d(np.arange(m), rows)] == 0).all()
