@@ -100,6 +100,14 @@ def test_unaligned_scales_take_the_per_step_path(gpu, orc):
     assert rel_l2(bf16_values(per_step), want) <= TOL
 
 
+@pytest.mark.slow
+def test_largest_expert(gpu, orc):
+    """hidden 32768, inter 65504: one expert's W13 (inter * hidden bytes) just under the 2 GiB
+    the entry point accepts, so the weight offsets of the first product reach the top of their
+    32-bit range; its scale rows are too long to stage (per-step scale loads)."""
+    check(gpu, orc, synth.moe_case(91, 1, 32768, 65504, 2, 1))
+
+
 def test_every_token_to_the_same_two_experts(gpu, orc):
     """Skewed routing: experts 2 and 5 take every pair, 300 each (five token passes of up to
     64 rows, the last one ragged), the other six experts none."""
