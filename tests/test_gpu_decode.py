@@ -3,8 +3,8 @@
 Covers every packed byte at every E8M0 exponent (the normative range 2..252
 plus the wrapping ends), the MXFP4 GEMV workload's decode sweep (exponents
 100..150), the zero bytes at all 256 exponents, a block mixing zero and
-non-zero codes, random matrices with a ragged row count, determinism, and
-empty inputs. Outputs are poisoned before each launch so an unwritten element
+non-zero codes, random matrices with a ragged row count, determinism, empty
+inputs, and a matrix of more than 2^31 elements (64-bit indexing). Outputs are poisoned before each launch so an unwritten element
 cannot pass.
 """
 from __future__ import annotations
@@ -83,3 +83,21 @@ def test_deterministic_and_empty(gpu):
     assert np.array_equal(a, b)
     empty = gpu.dequant_decode(u8(np.zeros((0, 16), np.uint8)), u8(np.zeros((0, 1), np.uint8)))
     assert empty.shape == (0, 32)
+
+
+@pytest.mark.slow
+def test_more_than_2_pow_31_elements(gpu, orc):
+    """65537 x 32768 codes: 2^31 + 32768 elements, a 4 GiB output, so every index is past the
+    32-bit range at the end. Rows at the start, on both sides of element 2^31 (row 65536 starts
+    there) and the last row are compared bit for bit; the output is poisoned first."""
+    rows, k = 65537, 32768
+    r = np.random.default_rng(synth.SEED_BASE + 73)
+    packed = r.integers(0, 256, (rows, k // 2), dtype=np.uint8)
+    scales = r.integers(100, 151, (rows, k // 32), dtype=np.uint8)
+    say(f"decode: {rows} x {k} ({rows * k} elements)")
+    out = torch.full((rows, k), -1, dtype=torch.int16, device="cuda:0")
+    gpu.dequant_decode(u8(packed), u8(scales), out=out)
+    sel = [0, 1, 65534, 65535, 65536]
+    got = bits(out[sel])
+    want = orc.mxfp4_decode(packed[sel], scales[sel])
+    assert np.array_equal(got, want)

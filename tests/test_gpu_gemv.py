@@ -3,8 +3,9 @@
 The oracle's fp64 result is rounded to the output dtype before comparing
 (fp32, or bf16 round-to-nearest-even). Shapes span several tiles, ragged row
 counts and ragged 32-column chunk counts per lane, every batch size path,
-both output dtypes, and the Llama-8B MLP shapes at batch 1, 4 and 16 (the
-full outputs, exactly as the benchmark launches them).
+both output dtypes, the Llama-8B MLP shapes at batch 1, 4 and 16 (the full
+outputs, exactly as the benchmark launches them), and more than 2 GiB of codes
+(sampled rows).
 """
 from __future__ import annotations
 
@@ -120,3 +121,23 @@ def test_deterministic(gpu):
     a = host_f32(gpu.dequant_gemv(*args))
     b = host_f32(gpu.dequant_gemv(*args))
     assert np.array_equal(a, b)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("batch", [1, 4])
+def test_more_than_2_gib_of_codes(gpu, orc, batch):
+    """140000 x 32768: 2.29 GB of codes, so the byte offsets of the last rows are past the
+    32-bit range. The first and last 64 rows of the output are compared with the oracle."""
+    n, k = 140000, 32768
+    r = np.random.default_rng(synth.SEED_BASE + 74 + batch)
+    packed = r.integers(0, 256, (n, k // 2), dtype=np.uint8)
+    scales = r.integers(120, 135, (n, k // 32), dtype=np.uint8)
+    x = synth.bf16_normal(r, (batch, k))
+    say(f"gemv: n={n} k={k} batch={batch} ({n * k // 2} bytes of codes)")
+    out = torch.full((batch, n), float("nan"), dtype=torch.float32, device="cuda:0")
+    gpu.dequant_gemv(u8(packed), u8(scales), bf16(x), out_dtype=torch.float32, out=out)
+    got = host_f32(out).astype(np.float64)
+    sel = np.r_[0:64, n - 64:n]
+    want = orc.mxfp4_gemv(packed[sel], scales[sel], x, "f32").astype(np.float64)
+    assert np.isfinite(got).all()
+    assert rel_l2(got[:, sel], want) <= TOL
