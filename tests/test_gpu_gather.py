@@ -2,8 +2,8 @@
 
 Covers the 200000 x 4096 table with 8192 ids (every gathered element), every
 E4M3 scale byte against every code, the 16-channel path (hidden % 32 != 0),
-ids outside the vocabulary (zero rows + flag), ids of any shape, and the
-empty call. Outputs are poisoned before each launch.
+ids outside the vocabulary (zero rows + flag), ids of any shape, the
+empty call, and a table of more than 2 GiB of codes (sampled ids). Outputs are poisoned before each launch.
 """
 from __future__ import annotations
 
@@ -109,3 +109,22 @@ def test_empty_vocabulary(gpu):
     torch.cuda.synchronize()
     assert int(flag.item()) == 1
     assert int(torch.count_nonzero(got.view(torch.int16)).item()) == 0
+
+
+@pytest.mark.slow
+def test_table_past_2_gib(gpu, orc):
+    """1100000 x 4096: 2.25 GB of codes, so the rows past id 1048575 start beyond the 32-bit
+    byte range. 96 ids (the first rows, the rows around 2^20, the last rows, random ones) are
+    compared with the oracle run on just those rows."""
+    vocab, hidden = 1_100_000, 4096
+    r = np.random.default_rng(synth.SEED_BASE + 81)
+    table = r.integers(0, 256, (vocab, hidden // 2), dtype=np.uint8)
+    bscale = r.integers(0x20, 0x59, (vocab, hidden // 16), dtype=np.uint8)   # E4M3 2^-3 .. 2^4
+    fixed = np.array([0, 1, 1048575, 1048576, 1048577, vocab - 2, vocab - 1], np.int64)
+    ids = np.concatenate([fixed, r.integers(1_000_000, vocab, 89)]).astype(np.int64)
+    say(f"gather: vocab={vocab} hidden={hidden} ({table.size} bytes of codes), {ids.size} ids")
+    got = run_gather(gpu, table, bscale, 0.01, ids)
+    uniq, local = np.unique(ids, return_inverse=True)
+    want, bad = orc.nvfp4_gather(table[uniq], bscale[uniq], 0.01, local.astype(np.int64))
+    assert bad == 0
+    assert np.array_equal(got, want)

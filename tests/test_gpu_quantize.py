@@ -7,7 +7,8 @@ fl32(e4m3 * g), fl32(x / eff)) before rounding. Covers every finite bf16
 pattern (as block contents, so every element value meets every nearby
 exponent), random weights at the Llama-8B MLP shape 14336 x 4096, rows of
 very different magnitude, blocks with a single non-zero, a ragged last wave,
-the round trip through the library's own decoders, and empty extents.
+the round trip through the library's own decoders, empty extents, and more
+than 2^31 elements (sampled rows).
 """
 from __future__ import annotations
 
@@ -108,3 +109,28 @@ def test_empty(gpu):
     assert c.shape == (0, 32) and s.shape == (0, 2)
     c, s = gpu.nvfp4_quantize(x, torch.ones(1, device="cuda:0"))
     assert c.shape == (0, 32) and s.shape == (0, 4)
+
+
+@pytest.mark.slow
+def test_more_than_2_pow_31_elements(gpu, orc):
+    """65537 x 32768 bf16 (2^31 + 32768 elements, 4.3 GB): the element offsets of the last row
+    and the code offsets of the last two rows are past the 32-bit range. Rows 0, 1, 65534,
+    65535 and 65536 of both quantizers are compared bit for bit with the oracle."""
+    rows, k = 65537, 32768
+    r = np.random.default_rng(31)
+    x = r.integers(0, 1 << 16, (rows, k), dtype=np.uint16)
+    np.bitwise_and(x, 0xBFFF, out=x)   # exponent field below 128: every value finite
+    sel = np.array([0, 1, rows - 3, rows - 2, rows - 1])
+    sel_dev = torch.from_numpy(sel).to("cuda:0")
+    say(f"quantize: rows={rows} k={k} ({rows * k} elements)")
+    xd = bf16(x)
+    codes, scales = gpu.mxfp4_quantize(xd)
+    want_c, want_s = orc.mxfp4_quantize(x[sel])
+    assert np.array_equal(scales[sel_dev].cpu().numpy(), want_s)
+    assert np.array_equal(codes[sel_dev].cpu().numpy(), want_c)
+    del codes, scales
+    gs = 2.0 / (6 * 448)   # every |x| < 2: the block scales stay inside E4M3
+    codes, bs = gpu.nvfp4_quantize(xd, f32(np.array([gs], np.float32)))
+    want_c, want_b = orc.nvfp4_quantize(x[sel], gs)
+    assert np.array_equal(bs[sel_dev].cpu().numpy(), want_b)
+    assert np.array_equal(codes[sel_dev].cpu().numpy(), want_c)

@@ -15,8 +15,8 @@ are held to that kernel's bar, rel-L2 <= 1e-3 (plain fp32 adds of x).
 Covers the 4096 x 4096 matrix at every batch 1..16, ragged row tiles and
 slices, several slices per wave, workgroups that loop over tiles, rows of
 very different magnitude (one exponent per row and slice), all-zero rows,
-every field position with exact results, the fallback path, empty extents
-and determinism.
+every field position with exact results, the fallback path, empty extents,
+determinism, and more than 2 GiB of weights (sampled rows).
 """
 from __future__ import annotations
 
@@ -142,3 +142,30 @@ def test_empty_and_deterministic(gpu):
     assert e.shape == (3, 0)
     case = synth.ternary_batch_case(8, 6, 512, 4096)
     assert np.array_equal(run(gpu, case), run(gpu, case))
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("batch", [1, 4])
+def test_more_than_2_gib_of_weights(gpu, orc, batch):
+    """540000 x 16384: 2.21 GB of packed weights, so the word offsets of the rows past 524287
+    are beyond the 32-bit byte range. The first and last 64 output rows are held to the fast
+    kernel's element bound against the oracle run on just those rows."""
+    n, k = 540_000, 16384
+    r = np.random.default_rng(synth.SEED_BASE + 91 + batch)
+    w = r.integers(0, 1 << 32, (n, k // 16), dtype=np.uint32)
+    np.bitwise_xor(w, (w >> np.uint32(1)) & w & np.uint32(0x55555555), out=w)   # field 3 -> 2: all valid
+    case = {"packed": w, "row_scale": r.uniform(0.01, 0.1, size=n).astype(np.float32),
+            "x": synth.f32_normal(r, (batch, k))}
+    say(f"ternary_gemm: batch={batch} n={n} k={k} ({w.nbytes} bytes of weights)")
+    got = run(gpu, case)
+    sel = np.r_[0:64, n - 64:n]
+    sub = {"packed": w[sel], "row_scale": case["row_scale"][sel], "x": case["x"]}
+    _, want = orc.ternary_gemm(sub["packed"], sub["row_scale"], sub["x"], want_f64=True)
+    g = got[:, sel]
+    mag, cnt = row_sums(sub["packed"], sub["x"])
+    s = np.abs(sub["row_scale"].astype(np.float64))[None, :]
+    M = np.abs(sub["x"]).max(axis=1).astype(np.float64)[:, None]
+    bound = (k / 256 + 24) * 2.0 ** -23 * s * mag + 2.0 ** -60 * M * s * cnt[None, :] + 2.0 ** -23 * np.abs(want)
+    assert np.isfinite(got).all()
+    assert (np.abs(g - want) <= bound).all()
+    assert rel_l2(g, want) <= 2e-6
