@@ -10,7 +10,10 @@
 //
 // gfx950 design. With hundreds of activation rows the product is bound by
 // the matrix cores (2 m flops per 0.53 bytes of weights), so the kernel is a
-// tiled bf16 MFMA GEMM whose weight operand is decoded on the way in:
+// tiled bf16 MFMA GEMM whose weight operand is decoded on the way in. Two
+// forms share the MFMA work: the direct-to-LDS form (K % 64 == 0, below the
+// first) copies each step's tiles into LDS with buffer_load ... lds, and the
+// register form here serves any K % 32 == 0:
 //   * A workgroup of four waves owns a tile of 128 weight rows x 128
 //     activation rows and walks K in steps of 64 columns. Each step, its
 //     threads copy the step's x tile (128 x 64 bf16) and the raw code lines
@@ -224,6 +227,197 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     }
 }
 
+// ---------------------------------------------------- direct-to-LDS form --
+//
+// Eight waves on a tile of 256 weight rows x 128 activation rows (4 x 2
+// waves, each 64 x 64 as 2 x 2 v_mfma_f32_32x32x16_bf16, as above), with
+// every per-step copy made by the memory pipeline itself: buffer_load ... lds
+// writes each lane's 2, 4 or 16 bytes straight into LDS (lane l of an
+// instruction at base + max(size, 4) * l), so no register holds a copy and no
+// ds_write stages one, and the x tile of a step serves twice the weight rows.
+// kStages LDS buffers rotate; step s + kStages - 1 is requested right after
+// the barrier that opens step s (its buffer was last read in step s - 1).
+// Steps are kSK = 64 columns (80 KB of LDS, two workgroups per compute unit)
+// or 128 (150 KB, fewer barriers per flop) columns. The layouts are chosen
+// through the lanes' source addresses:
+//   * x: 16-byte chunk c of row r at slot c ^ (r / 2 % 8) (64 columns) or
+//     c ^ (r % 16) (128) of its row, so a B-operand read (16 rows x one
+//     chunk per 16 lanes) touches 16 different bank groups;
+//   * codes: word j of a row's kSK / 2 bytes at slot j ^ (r / R % W), R rows
+//     per 256-byte request and W words per row;
+//   * scales: 2-byte loads (two 32-column blocks), which the memory pipeline
+//     writes zero-extended into a 4-byte slot per lane.
+// The compiler does not see these loads (inline asm, which also keeps them in
+// place): every wave waits for its own with s_waitcnt vmcnt before the
+// barrier, and requests past the last step read out of range (zeros, no
+// memory access), so the count is the same every step, and the last wait
+// drains them before the workgroup's LDS is released.
+
+// lane's kBytes (2, 4 or 16) at byte offset voff of the buffer -> LDS lds + max(kBytes, 4) * lane
+// (two bytes land zero-extended in a 4-byte slot)
+template <int kBytes>
+__device__ __forceinline__ void lds_load(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t lds) {
+    if constexpr (kBytes == 16)
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                     :: "s"(lds), "v"(voff), "s"(rsrc) : "memory");
+    else if constexpr (kBytes == 4)
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                     :: "s"(lds), "v"(voff), "s"(rsrc) : "memory");
+    else
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_ushort %1, %2, 0 offen lds"
+                     :: "s"(lds), "v"(voff), "s"(rsrc) : "memory");
+}
+
+template <int kN>
+__device__ __forceinline__ void wait_vm() {
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kN) : "memory");
+}
+
+constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;   // a buffer offset past any resource's range
+
+// kWN waves along the weight rows (tile of 64 kWN rows) x 2 along the activation rows (128);
+// steps of kSK columns (64 or 128).
+template <int kWN, int kSK>
+struct GemmDmaBuf {
+    static constexpr int kRows = 64 * kWN;
+    uint16_t x[kTileM * kSK];               // [row][kSK], 16-byte chunks swizzled
+    uint32_t w[kRows * (kSK / 8)];          // [row][kSK / 8 words], words swizzled
+    uint32_t s[2 * kWN][kWave];             // [wave][lane]: scale pairs of rows 32 wave + lane % 32
+};
+
+template <bool kBf16Out, int kStages, int kWN, int kSK>
+__global__ __launch_bounds__(128 * kWN) void gemm_dma_kernel(const uint8_t* __restrict__ packed,
+                                                             const uint8_t* __restrict__ scales,
+                                                             const uint16_t* __restrict__ x, void* __restrict__ y,
+                                                             int m_rows, int n, int kc) {
+    constexpr int kRows = 64 * kWN;                 // weight rows per tile
+    constexpr int kChunks = kSK / 8;                // 16-byte x chunks per row and step (8 or 16)
+    constexpr int kWords = kSK / 8;                 // 4-byte code words per row and step (8 or 16)
+    constexpr int kXRowsPer = 1024 / (2 * kSK);     // x rows per 1 KB request
+    constexpr int kXLoads = kTileM / kXRowsPer / (2 * kWN);          // per wave and step
+    constexpr int kWRowsPer = 64 / kWords;          // code rows per 256-byte request
+    constexpr int kWLoads = kRows / kWRowsPer / (2 * kWN);           // per wave and step
+    constexpr int kPerStep = kXLoads + kWLoads + 1;                  // + one scale request
+    constexpr int kQ = kSK / 16;                    // 16-column slices per step
+    static_assert(kXLoads * kXRowsPer * 2 * kWN == kTileM && kWLoads * kWRowsPer * 2 * kWN == kRows, "requests");
+    __shared__ __attribute__((aligned(16))) GemmDmaBuf<kWN, kSK> buf[kStages];
+    const int t = threadIdx.x;
+    const int lane = t & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(t / kWave);
+    const int r32 = lane & 31, g2 = lane >> 5;
+    const int wn = (wave % kWN) * 64, wm = (wave / kWN) * 64;
+    const int K = kc * 32;
+    const int nsteps = K / kSK;
+    const int ntn = (n + kRows - 1) / kRows;
+    const int n0 = (blockIdx.x % ntn) * kRows;
+    const int m0 = (blockIdx.x / ntn) * kTileM;
+    const int mt = min(kTileM, m_rows - m0), nt = min(kRows, n - n0);
+    const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(x + (size_t)m0 * K), 0, mt * K * 2, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(packed + (size_t)n0 * (K / 2)), 0, nt * (K / 2), kBufferWord3);
+    const __amdgpu_buffer_rsrc_t sres = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(scales + (size_t)n0 * kc), 0, nt * kc, kBufferWord3);
+
+    // x: chunk c of row r at slot c ^ (r % kChunks) (kSK = 128) or c ^ (r / 2 % 8) (kSK = 64);
+    // codes: word j of row r at slot j ^ (r / kWRowsPer % kWords); both spread the 16 rows of a
+    // 16-lane read over the banks
+    auto xswz = [](int r) __attribute__((always_inline)) { return kChunks == 16 ? (r & 15) : ((r >> 1) & 7); };
+    auto wswz = [](int r) __attribute__((always_inline)) { return (r / kWRowsPer) % kWords; };
+    uint32_t xoff[kXLoads], woff[kWLoads];
+#pragma unroll
+    for (int i = 0; i < kXLoads; ++i) {
+        const int row = kXRowsPer * (kXLoads * wave + i) + lane / kChunks, slot = lane % kChunks;
+        xoff[i] = 2u * ((uint32_t)min(row, mt - 1) * (uint32_t)K + 8u * (uint32_t)(slot ^ xswz(row)));
+    }
+#pragma unroll
+    for (int i = 0; i < kWLoads; ++i) {
+        const int row = kWRowsPer * (kWLoads * wave + i) + lane / kWords, slot = lane % kWords;
+        woff[i] = (uint32_t)min(row, nt - 1) * (uint32_t)(K / 2) + 4u * (uint32_t)(slot ^ wswz(row));
+    }
+    // scales: lane l takes row 32 wave + l % 32, bytes 2 (l / 32) .. + 1 of its kSK / 32 per step
+    // (kSK = 64: only lanes < 32 load)
+    const uint32_t soff = (uint32_t)min(32 * wave + r32, nt - 1) * (uint32_t)kc + 2u * (uint32_t)g2;
+    const bool slane = kSK == 128 || lane < 32;
+    auto issue = [&](int st, int stage) __attribute__((always_inline)) {
+        const bool live = st < nsteps;
+        GemmDmaBuf<kWN, kSK>& b = buf[stage];
+        const uint32_t xb = (uint32_t)(uintptr_t)&b.x[0], wb = (uint32_t)(uintptr_t)&b.w[0];
+#pragma unroll
+        for (int i = 0; i < kXLoads; ++i)
+            lds_load<16>(xres, live ? xoff[i] + 2u * kSK * (uint32_t)st : kOutOfRange,
+                         __builtin_amdgcn_readfirstlane(xb + 1024u * (uint32_t)(kXLoads * wave + i)));
+#pragma unroll
+        for (int i = 0; i < kWLoads; ++i)
+            lds_load<4>(wres, live ? woff[i] + (kSK / 2) * (uint32_t)st : kOutOfRange,
+                        __builtin_amdgcn_readfirstlane(wb + 256u * (uint32_t)(kWLoads * wave + i)));
+        lds_load<2>(sres, live && slane ? soff + (kSK / 32) * (uint32_t)st : kOutOfRange,
+                    __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&b.s[wave][0]));
+    };
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+#pragma unroll
+    for (int st = 0; st < kStages - 1; ++st) issue(st, st);
+    for (int s0 = 0; s0 < nsteps; s0 += kStages) {   // unrolled by the stage count: buffer indices are static
+#pragma unroll
+        for (int p = 0; p < kStages; ++p) {
+            const int s = s0 + p;
+            if (s >= nsteps) break;   // workgroup-uniform
+            wait_vm<kPerStep * (kStages - 2)>();   // this wave's requests of step s are in LDS
+            __syncthreads();                        // everyone's are, and step s - 1 is computed
+            issue(s + kStages - 1, (p + kStages - 1) % kStages);
+            const GemmDmaBuf<kWN, kSK>& b = buf[p];
+#pragma unroll
+            for (int q = 0; q < kQ; ++q) {
+                bf16x8 a[2];
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const int row = wn + 32 * i + r32;
+                    const uint32_t codes = b.w[row * kWords + ((2 * q + g2) ^ wswz(row))];
+                    const int blk = q >> 1;   // the step's 32-column block
+                    const uint32_t pair = b.s[row >> 5][(row & 31) + 32 * (blk >> 1)];
+                    const float sc = e8m0_scale((pair >> (8 * (blk & 1))) & 0xFFu);
+                    const u32x4 u = {fp4x2_to_bf16x2<0>(codes, sc), fp4x2_to_bf16x2<1>(codes, sc),
+                                     fp4x2_to_bf16x2<2>(codes, sc), fp4x2_to_bf16x2<3>(codes, sc)};
+                    a[i] = __builtin_bit_cast(bf16x8, u);
+                }
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const int xr = wm + 32 * j + r32;
+                    const bf16x8 bx = *reinterpret_cast<const bf16x8*>(&b.x[xr * kSK + 8 * ((2 * q + g2) ^ xswz(xr))]);
+#pragma unroll
+                    for (int i = 0; i < 2; ++i)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bx, acc[i][j], 0, 0, 0);
+                }
+            }
+        }
+    }
+    wait_vm<0>();   // the requests past the last step have landed before the workgroup ends
+
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int m = m0 + wm + 32 * j + r32;
+        if (m >= m_rows) continue;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const int nn = n0 + wn + 32 * i + 8 * p + 4 * g2;
+                if (nn >= n) continue;
+                const int count = min(4, n - nn);
+                const f32x4 v = {acc[i][j][4 * p], acc[i][j][4 * p + 1], acc[i][j][4 * p + 2], acc[i][j][4 * p + 3]};
+                store4<kBf16Out>(y, (int64_t)m * n + nn, v, count == 4, count);
+            }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const uint8_t* packed, const uint8_t* scales, const uint16_t* x, void* y, bool out_bf16,
@@ -231,6 +425,27 @@ hipError_t launch_gemm(const uint8_t* packed, const uint8_t* scales, const uint1
     const int ntn = (int)((n + kTileN - 1) / kTileN);
     const int ntm = (int)((m + kTileM - 1) / kTileM);
     const dim3 grid((unsigned)(ntn * ntm));
+    if (k % 64 == 0) {
+        // weight tiles of 256 rows; with two or more tiles per compute unit, 64-column steps
+        // (80 KB of LDS: two workgroups per compute unit), otherwise 128-column steps
+        // (fewer barriers per flop; one workgroup per compute unit either way)
+        const int ntn4 = (int)((n + 255) / 256);
+        const dim3 grid4((unsigned)(ntn4 * ntm));
+        const bool wide = k % 128 == 0 && (int64_t)ntn4 * ntm < 2 * (int64_t)device_cu_count();
+        const int kc = (int)(k / 32);
+        if (wide) {
+            if (out_bf16)
+                gemm_dma_kernel<true, 3, 4, 128><<<grid4, 512, 0, stream>>>(packed, scales, x, y, (int)m, (int)n, kc);
+            else
+                gemm_dma_kernel<false, 3, 4, 128><<<grid4, 512, 0, stream>>>(packed, scales, x, y, (int)m, (int)n, kc);
+        } else {
+            if (out_bf16)
+                gemm_dma_kernel<true, 3, 4, 64><<<grid4, 512, 0, stream>>>(packed, scales, x, y, (int)m, (int)n, kc);
+            else
+                gemm_dma_kernel<false, 3, 4, 64><<<grid4, 512, 0, stream>>>(packed, scales, x, y, (int)m, (int)n, kc);
+        }
+        return hipGetLastError();
+    }
     if (out_bf16)
         gemm_kernel<true><<<grid, kThreads, 0, stream>>>(packed, scales, x, y, (int)m, (int)n, (int)(k / 32));
     else

@@ -3,9 +3,10 @@
 The oracle is the MXFP4 product of the GEMV (fp64 sums of the decoded
 weights times bf16 x, for any number of rows), rounded to the output dtype
 before comparing; the bar is the GEMV's, rel-L2 <= 1e-3 with fp32
-accumulation. Shapes span one and many 128 x 128 tiles, ragged tiles in both
+accumulation. Shapes span one and many tiles, ragged tiles in both
 directions, K with an odd number of 32-column blocks (a half step of zero
-weights), both output dtypes, block scales over a wide exponent range, and the
+weights, the register form), K % 128 == 64 and K % 128 == 0 (the
+direct-to-LDS form's two step widths), both output dtypes, block scales over a wide exponent range, and the
 prefill shape of the benchmark (2048 tokens through the Llama-8B MLP
 matrices) on sampled rows and columns, and the largest K the entry point
 accepts under a full 128-row tile.
@@ -44,6 +45,7 @@ def gemm_case(g, orc, packed, scales, x, out_dtype):
 @pytest.mark.parametrize("m,n,k", [
     (1, 16, 32), (17, 40, 64), (128, 128, 64), (130, 300, 96),   # one tile .. ragged, odd block count
     (256, 512, 1024), (129, 129, 2048 + 32), (300, 1000, 4096), (513, 257, 512),
+    (64, 300, 192), (257, 513, 320),   # K % 128 == 64: the direct-to-LDS form's 64-column steps, ragged tiles
 ])
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
 def test_shapes(gpu, orc, m, n, k, out_dtype):
@@ -101,12 +103,14 @@ def test_empty_and_zero_k(gpu):
 
 
 @pytest.mark.slow
-def test_largest_k(gpu, orc):
-    """k = E2M1_GEMM_MAX_K under a full 128-row tile: the workgroup's x offsets reach
-    2 * 128 * k bytes, just under 2^31 (its 32-bit byte offsets). Rows 0, 1, 126 and 127 of x
-    carry data and are checked against the oracle; every other row is zero, so its outputs
-    must be exact zeros."""
-    k, m, n = 8388576, 128, 20
+@pytest.mark.parametrize("k", [8388576, 8388480])
+def test_largest_k(gpu, orc, k):
+    """k = E2M1_GEMM_MAX_K (the register form: an odd number of 32-column blocks) and the largest
+    multiple of 128 below it (the direct-to-LDS form) under a full 128-row tile: the workgroup's
+    x offsets reach 2 * 128 * k bytes, just under 2^31 (its 32-bit byte offsets). Rows 0, 1, 126
+    and 127 of x carry data and are checked against the oracle; every other row is zero, so its
+    outputs must be exact zeros."""
+    m, n = 128, 20
     r = np.random.default_rng(synth.SEED_BASE + 71)
     packed, scales = synth.mxfp4_matrix(r, n, k)
     rows = [0, 1, 126, 127]
