@@ -515,8 +515,9 @@ constexpr int kMaxSliceWaves = 16;
 constexpr int kXPitch = 128 + 8;                     // bf16 per staged x row (16-byte pad spreads the banks)
 constexpr int kWPitch = 9;                           // uint4 per transposed code row (8 blocks + pad)
 
-// Workgroup = S waves on one tile of 16 rows (tiles blockIdx.x, + gridDim.x,
-// ...); wave w owns scale blocks [32 w, 32 w + 32). Lane l = 16 g + r: row r
+// Workgroup = S waves on one tile of 16 RT rows (tiles blockIdx.x, +
+// gridDim.x, ...); wave w owns scale blocks [32 w, 32 w + 32) of all of them,
+// and each staged x operand serves the RT 16-row MFMA tiles. Lane l = 16 g + r: row r
 // of the tile for the A operand and batch column r for the B operand; in half
 // step hs = 2 s + h it loads block b = 32 w + 8 s + g + 4 h (the two halves of
 // a 128-byte line of the row are half steps h = 0, 1). MFMA (hs, i) takes
@@ -533,11 +534,11 @@ constexpr int kWPitch = 9;                           // uint4 per transposed cod
 // slice, then the x loads of half step hs + 1 right after half step hs is
 // staged; one wave writes and reads its own area, and LDS accesses of a wave
 // complete in order, so no barrier is needed.
-template <bool kBf16Out, int NJ>
-__global__ __launch_bounds__(kWave * kMaxSliceWaves) void gemv_mfma_kernel(
+template <bool kBf16Out, int NJ, int RT, int kMaxW>
+__global__ __launch_bounds__(kWave * kMaxW) void gemv_mfma_kernel(
     const uint8_t* packed, const uint8_t* scales, const uint16_t* x, void* __restrict__ y,
     int batch, int n, int kc) {
-    __shared__ f32x4 part[kMaxSliceWaves][kWave];
+    __shared__ f32x4 part[RT][kMaxW][kWave];
     extern __shared__ __attribute__((aligned(16))) uint16_t gemv_xs[];
     constexpr int kXRows = 4 * NJ;
     constexpr int kHalfSteps = 2 * kTileSteps;
@@ -546,10 +547,10 @@ __global__ __launch_bounds__(kWave * kMaxSliceWaves) void gemv_mfma_kernel(
     const int nwaves = blockDim.x / kWave;
     const int r = lane & 15, g = lane >> 4;
     const int K = kc * 32;
-    const int ntiles = (n + 15) / 16;
+    const int ntiles = (n + 16 * RT - 1) / (16 * RT);
     const bool bvalid = r < batch;
-    uint16_t* xs = gemv_xs + wv * (kXRows * kXPitch + 8 * kWPitch * 16);
-    uint4* wbuf = reinterpret_cast<uint4*>(xs + kXRows * kXPitch);   // 16 rows x kWPitch uint4
+    uint16_t* xs = gemv_xs + wv * (kXRows * kXPitch + 8 * kWPitch * 16 * RT);
+    uint4* wbuf = reinterpret_cast<uint4*>(xs + kXRows * kXPitch);   // RT x 16 rows x kWPitch uint4
     // staging: chunk j of a lane is row 4 j + (lane >> 4), columns 8 (lane & 15) .. + 7 of the half step
     uint16_t* xdst = xs + (lane >> 4) * kXPitch + 8 * (lane & 15);
     const uint16_t* xread = xs + min(r, batch - 1) * kXPitch + 32 * g;
@@ -573,8 +574,10 @@ __global__ __launch_bounds__(kWave * kMaxSliceWaves) void gemv_mfma_kernel(
     };
 
     for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {   // workgroup-uniform
-        const int row = min(tile * 16 + r, n - 1);
-        const uint8_t* srow = scales + (size_t)row * kc;
+        const uint8_t* srow[RT];
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+            srow[t] = scales + (size_t)min(tile * 16 * RT + 16 * t + r, n - 1) * kc;
         uint4 xg[NJ];
         load_x(xg, 0);
         issue_here();
@@ -583,29 +586,41 @@ __global__ __launch_bounds__(kWave * kMaxSliceWaves) void gemv_mfma_kernel(
         // instruction). Loads complete in order: with the scales first, half step 2 st waits only
         // for the lines of steps <= st, so the first MFMAs overlap the later lines' arrival
         // (scales last: 14.0 -> 12.9 us at batch 8, 17.3 -> 15.8 at batch 16, 14336 x 4096).
-        uint4 wl[kTileSteps][2];
-        uint32_t e[kHalfSteps];
+        uint4 wl[kTileSteps][RT][2];
+        uint32_t e[RT][kHalfSteps];
 #pragma unroll
-        for (int hs = 0; hs < kHalfSteps; ++hs)
-            e[hs] = srow[min(wv * kSliceBlocks + 8 * (hs >> 1) + g + 4 * (hs & 1), kc - 1)];
+        for (int t = 0; t < RT; ++t)
+#pragma unroll
+            for (int hs = 0; hs < kHalfSteps; ++hs)
+                e[t][hs] = srow[t][min(wv * kSliceBlocks + 8 * (hs >> 1) + g + 4 * (hs & 1), kc - 1)];
         issue_here();
-        const uint8_t* lrow[2];
+        const uint8_t* lrow[RT][2];
 #pragma unroll
-        for (int q = 0; q < 2; ++q) lrow[q] = packed + (size_t)min(tile * 16 + 8 * q + (lane >> 3), n - 1) * (K / 2);
+        for (int t = 0; t < RT; ++t)
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+                lrow[t][q] = packed + (size_t)min(tile * 16 * RT + 16 * t + 8 * q + (lane >> 3), n - 1) * (K / 2);
 #pragma unroll
         for (int st = 0; st < kTileSteps; ++st) {
             const int b = min(wv * kSliceBlocks + 8 * st + (lane & 7), kc - 1);
 #pragma unroll
-            for (int q = 0; q < 2; ++q) wl[st][q] = load_nt16(lrow[q] + (size_t)b * 16);
+            for (int t = 0; t < RT; ++t)
+#pragma unroll
+                for (int q = 0; q < 2; ++q) wl[st][t][q] = load_nt16(lrow[t][q] + (size_t)b * 16);
         }
         issue_here();
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        uint4 wm[2];   // this step's blocks g and g + 4 of row r (MFMA layout)
+        f32x4 acc[RT];
+#pragma unroll
+        for (int t = 0; t < RT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        uint4 wm[RT][2];   // this step's blocks g and g + 4 of row r of each tile (MFMA layout)
 #pragma unroll
         for (int hs = 0; hs < kHalfSteps; ++hs) {
             if ((hs & 1) == 0) {   // a new step: its code lines through the wave's LDS transpose
 #pragma unroll
-                for (int q = 0; q < 2; ++q) wbuf[(8 * q + (lane >> 3)) * kWPitch + (lane & 7)] = wl[hs >> 1][q];
+                for (int t = 0; t < RT; ++t)
+#pragma unroll
+                    for (int q = 0; q < 2; ++q)
+                        wbuf[(16 * t + 8 * q + (lane >> 3)) * kWPitch + (lane & 7)] = wl[hs >> 1][t][q];
             }
 #pragma unroll
             for (int j = 0; j < NJ; ++j) *reinterpret_cast<uint4*>(xdst + 4 * j * kXPitch) = xg[j];
@@ -614,32 +629,47 @@ __global__ __launch_bounds__(kWave * kMaxSliceWaves) void gemv_mfma_kernel(
             issue_here();
             __builtin_amdgcn_wave_barrier();
             if ((hs & 1) == 0) {
-                wm[0] = wbuf[r * kWPitch + g];
-                wm[1] = wbuf[r * kWPitch + g + 4];
+#pragma unroll
+                for (int t = 0; t < RT; ++t) {
+                    wm[t][0] = wbuf[(16 * t + r) * kWPitch + g];
+                    wm[t][1] = wbuf[(16 * t + r) * kWPitch + g + 4];
+                }
             }
             const bool valid = bvalid && (wv * kSliceBlocks + 8 * (hs >> 1) + g + 4 * (hs & 1) < kc);
-            const float sc = e8m0_scale(e[hs]);
-            const uint4 wh = wm[hs & 1];
-            const uint32_t ws[4] = {wh.x, wh.y, wh.z, wh.w};
+            float sc[RT];
+            uint32_t ws[RT][4];
+#pragma unroll
+            for (int t = 0; t < RT; ++t) {
+                sc[t] = e8m0_scale(e[t][hs]);
+                const uint4 wh = wm[t][hs & 1];
+                ws[t][0] = wh.x;
+                ws[t][1] = wh.y;
+                ws[t][2] = wh.z;
+                ws[t][3] = wh.w;
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const u32x4 a = {fp4x2_to_bf16x2<0>(ws[i], sc), fp4x2_to_bf16x2<1>(ws[i], sc),
-                                 fp4x2_to_bf16x2<2>(ws[i], sc), fp4x2_to_bf16x2<3>(ws[i], sc)};
                 const u32x4 xv = *reinterpret_cast<const u32x4*>(xread + 8 * i);
                 const u32x4 bz = {valid ? xv.x : 0u, valid ? xv.y : 0u, valid ? xv.z : 0u, valid ? xv.w : 0u};
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                               __builtin_bit_cast(bf16x8, bz), acc, 0, 0, 0);
+#pragma unroll
+                for (int t = 0; t < RT; ++t) {
+                    const u32x4 a = {fp4x2_to_bf16x2<0>(ws[t][i], sc[t]), fp4x2_to_bf16x2<1>(ws[t][i], sc[t]),
+                                     fp4x2_to_bf16x2<2>(ws[t][i], sc[t]), fp4x2_to_bf16x2<3>(ws[t][i], sc[t])};
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                                      __builtin_bit_cast(bf16x8, bz), acc[t], 0, 0, 0);
+                }
             }
             __builtin_amdgcn_wave_barrier();   // this half step's reads come before the next writes
         }
-        part[wv][lane] = acc;
+#pragma unroll
+        for (int t = 0; t < RT; ++t) part[t][wv][lane] = acc[t];
         __syncthreads();
-        // thread t sums element (row 4 g + j, batch c) over the slices: t = 64 j + 16 g + c
-        for (int t = threadIdx.x; t < 4 * kWave; t += blockDim.x) {
-            const int j = t / kWave, l = t & (kWave - 1);
-            const int c = l & 15, orow = tile * 16 + 4 * (l >> 4) + j;
+        // thread i sums element (row 16 t + 4 g + j, batch c) over the slices: i = 256 t + 64 j + 16 g + c
+        for (int i = threadIdx.x; i < 4 * kWave * RT; i += blockDim.x) {
+            const int t = i / (4 * kWave), j = (i / kWave) & 3, l = i & (kWave - 1);
+            const int c = l & 15, orow = tile * 16 * RT + 16 * t + 4 * (l >> 4) + j;
             float sum = 0.f;
-            for (int q = 0; q < nwaves; ++q) sum += part[q][l][j];
+            for (int q = 0; q < nwaves; ++q) sum += part[t][q][l][j];
             if (c < batch && orow < n) store_out<kBf16Out>(y, (int64_t)c * n + orow, sum);
         }
         __syncthreads();
@@ -830,25 +860,36 @@ hipError_t dispatch_generic(int batch, const uint8_t* packed, const uint8_t* sca
 #undef E2M1_GEMV_CASE
 }
 
-template <bool kBf16Out, int NJ>
-hipError_t run_mfma_nj(int batch, const uint8_t* packed, const uint8_t* scales, const uint16_t* x, void* y,
-                       int n, int kc, hipStream_t stream) {
+template <bool kBf16Out, int NJ, int RT, int kMaxW>
+hipError_t run_mfma_cfg(int batch, const uint8_t* packed, const uint8_t* scales, const uint16_t* x, void* y,
+                        int n, int kc, hipStream_t stream) {
     const int waves = (kc + kSliceBlocks - 1) / kSliceBlocks;
-    const int ntiles = (n + 15) / 16;
-    const size_t lds = (size_t)waves * (4 * NJ * kXPitch * sizeof(uint16_t) + 16 * kWPitch * sizeof(uint4));
+    const int ntiles = (n + 16 * RT - 1) / (16 * RT);
+    const size_t lds = (size_t)waves * (4 * NJ * kXPitch * sizeof(uint16_t) + 16 * RT * kWPitch * sizeof(uint4));
     static int cache[kMaxSliceWaves + 1] = {};   // resident workgroups per compute unit, per wave count
     int& per_cu = cache[waves];
     if (per_cu == 0) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(gemv_mfma_kernel<kBf16Out, NJ>),
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(gemv_mfma_kernel<kBf16Out, NJ, RT, kMaxW>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gemv_mfma_kernel<kBf16Out, NJ>, kWave * waves,
-                                                         lds) != hipSuccess ||
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gemv_mfma_kernel<kBf16Out, NJ, RT, kMaxW>,
+                                                         kWave * waves, lds) != hipSuccess ||
             per_cu < 1)
             per_cu = 1;
     }
     const int grid = min(ntiles, per_cu * device_cu_count());
-    gemv_mfma_kernel<kBf16Out, NJ><<<grid, kWave * waves, lds, stream>>>(packed, scales, x, y, batch, n, kc);
+    gemv_mfma_kernel<kBf16Out, NJ, RT, kMaxW><<<grid, kWave * waves, lds, stream>>>(packed, scales, x, y, batch, n, kc);
     return hipGetLastError();
+}
+
+// Up to eight waves (K <= 8192): two 16-row tiles per wave, so each staged x
+// operand serves two MFMAs and every x byte is read once per 32 rows; more
+// waves (128 VGPRs each at 16 waves) keep one tile per wave.
+template <bool kBf16Out, int NJ>
+hipError_t run_mfma_nj(int batch, const uint8_t* packed, const uint8_t* scales, const uint16_t* x, void* y,
+                       int n, int kc, hipStream_t stream) {
+    const int waves = (kc + kSliceBlocks - 1) / kSliceBlocks;
+    if (waves <= 8) return run_mfma_cfg<kBf16Out, NJ, 2, 8>(batch, packed, scales, x, y, n, kc, stream);
+    return run_mfma_cfg<kBf16Out, NJ, 1, kMaxSliceWaves>(batch, packed, scales, x, y, n, kc, stream);
 }
 
 template <bool kBf16Out>
