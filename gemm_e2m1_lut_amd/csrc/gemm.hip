@@ -254,7 +254,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
 // drains them before the workgroup's LDS is released.
 
 // lane's kBytes (2, 4 or 16) at byte offset voff of the buffer -> LDS lds + max(kBytes, 4) * lane
-// (two bytes land zero-extended in a 4-byte slot)
+// (two bytes land zero-extended in a 4-byte slot). The LDS address goes through M0, which the asm
+// sets itself; nothing else in these kernels uses M0.
 template <int kBytes>
 __device__ __forceinline__ void lds_load(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t lds) {
     if constexpr (kBytes == 16)
