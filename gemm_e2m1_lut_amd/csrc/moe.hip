@@ -19,11 +19,13 @@
 //      read once for all tokens of its expert; the epilogue applies
 //      silu(gate) * up in fp32 and stores the activation as bf16 (the MFMA
 //      operand type of gemm2).
-//   3. gemm2: the same engine over W2, two 16-row tiles per wave (rows h and
-//      h + 128), 256 hidden rows per workgroup, with the activations as
-//      operand; fp32 results per (expert row, hidden). Two tiles per wave
-//      halve the token panel bytes staged per weight byte (one tile: 58.5 µs
-//      for the 32-expert 2880 x 2880 layer, two: 52.4 µs).
+//   3. gemm2: the same engine over W2, three 16-row tiles per wave (rows h,
+//      h + 128 and h + 256), 384 hidden rows per workgroup and passes of up to
+//      48 activation rows, with the activations as operand; fp32 results per
+//      (expert row, hidden). Several tiles per wave divide the token panel
+//      bytes staged per weight byte, and with three the 2880-row layer's
+//      8 x 32 workgroups fill 256 compute units once (one tile: 58.5 us for
+//      the 32-expert 2880 x 2880 layer, two: 52.4 us, three: 44.0 us).
 //   4. combine: out[t] = bf16(sum over slots, in slot order, of weight * y).
 //   Lane layout of the MFMA (checked on the device): lane l holds row l % 16
 //   of A and column l % 16 of B, k = 8 * (l / 16) + 0..7; D row 4 * (l / 16) +
@@ -43,7 +45,9 @@ constexpr int kRouteWaves = kRouteThreads / kWave;
 
 constexpr int kThreads = kEngineThreads;             // 8 waves
 constexpr int kGemm1Cols = kEngineWaves * 16;         // 128 intermediate columns per block (gate + up tiles)
-constexpr int kGemm2Rows = kEngineWaves * 32;         // 256 hidden rows per block (two tiles per wave)
+constexpr int kG2Tiles = 3;                           // gemm2: 16-row tiles per wave
+constexpr int kG2Tokens = 48;                         // gemm2: activation rows per pass
+constexpr int kGemm2Rows = kEngineWaves * 16 * kG2Tiles;   // 384 hidden rows per block
 
 struct MoeLayout {
     size_t cnt, off, pair_row, row_pair, act, y, total;
@@ -218,7 +222,8 @@ inline int moe_grid(int blocks_per_expert, int experts) {
 // ----------------------------------------------------------------- gemm1 --
 
 using Gemm1 = MoeEngine<2>;
-using Gemm2 = MoeEngine<2>;
+using Gemm2 = MoeEngine<kG2Tiles, kG2Tokens>;
+static_assert(sizeof(Gemm2::Shared::panel) >= kG2Tokens * (kGemm2Rows + 4) * sizeof(float), "gemm2 staging");
 
 // Workgroup (j block, expert): wave w streams gate rows j0 + 16 w .. + 15 and
 // up rows inter + the same j against all of the expert's tokens (64 per pass),
@@ -313,8 +318,8 @@ __global__ __launch_bounds__(kThreads) void moe_gemm1_kernel(
 
 // ----------------------------------------------------------------- gemm2 --
 
-// Workgroup (hidden block, expert): wave w streams the W2 rows of its two
-// tiles (h0 + P i and h0 + 128 + P i, i < 16) against the expert's activation
+// Workgroup (hidden block, expert): wave w streams the W2 rows of its three
+// tiles (h0 + 128 t + P i, t < 3, i < 16) against the expert's activation
 // rows; fp32 results per (expert row, hidden).
 template <bool kStaged>
 __global__ __launch_bounds__(kThreads) void moe_gemm2_kernel(
@@ -336,8 +341,12 @@ __global__ __launch_bounds__(kThreads) void moe_gemm2_kernel(
     const int P = line_period(I);
     const int hb = work.blk * kGemm2Rows;
     const int h0 = hb + 16 * P * (wave / P) + wave % P;
-    const int row0[2] = {h0, h0 + 128};   // 128 rows of I / 2 bytes: the same line offsets
-    const int rb[2] = {hb, hb + 128};
+    int row0[kG2Tiles], rb[kG2Tiles];   // tiles 128 rows apart: rows of I / 2 bytes keep their line offsets
+#pragma unroll
+    for (int t = 0; t < kG2Tiles; ++t) {
+        row0[t] = h0 + 128 * t;
+        rb[t] = hb + 128 * t;
+    }
     const int mb = line_block(we, h0, I);
     int mbmax = 0;
     for (int c = 0; c < P; ++c) mbmax = max(mbmax, line_block(we, work.blk * kGemm2Rows + c, I));
@@ -347,15 +356,15 @@ __global__ __launch_bounds__(kThreads) void moe_gemm2_kernel(
     const __amdgpu_buffer_rsrc_t sres =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(se), 0, H * (I / 32), kBufferWord3);
 
-    for (int m0 = 0; m0 < n_e; m0 += kEngineMaxTokens) {
-        const int nv = min(kEngineMaxTokens, n_e - m0);
+    for (int m0 = 0; m0 < n_e; m0 += kG2Tokens) {
+        const int nv = min(kG2Tokens, n_e - m0);
         const int mt = (nv + 15) / 16;
         __syncthreads();
         if ((int)threadIdx.x < nv) sh.rowidx[threadIdx.x] = base + m0 + threadIdx.x;
         __syncthreads();
-        f32x4 acc[2][4];
+        f32x4 acc[kG2Tiles][4];
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < kG2Tiles; ++t)
 #pragma unroll
             for (int m = 0; m < 4; ++m) acc[t][m] = f32x4{0.f, 0.f, 0.f, 0.f};
         Gemm2::run_mt<kStaged>(mt, sh, wres, se, sres, rb, I, row0, P, mb, nsteps, H, act, (size_t)I, nv, acc);
@@ -364,22 +373,22 @@ __global__ __launch_bounds__(kThreads) void moe_gemm2_kernel(
         // once every wave is past the product) and leave as contiguous 16-byte stores
         if (P == 1) {
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
+            for (int t = 0; t < kG2Tiles; ++t)
 #pragma unroll
-                for (int m = 0; m < 4; ++m) {
+                for (int m = 0; m < kG2Tokens / 16; ++m) {
                     const int r = 16 * m + r16;
                     const int h = h0 + 128 * t + 4 * g;
                     if (m < mt && r < nv && h + 3 < H)
                         *reinterpret_cast<f32x4*>(y + (size_t)(base + m0 + r) * H + h) = acc[t][m];
                 }
         } else {
-            float* stage = reinterpret_cast<float*>(&sh.panel[0][0]);   // [64 tokens][kGemm2Rows + 4]
+            float* stage = reinterpret_cast<float*>(&sh.panel[0][0]);   // [48 tokens][kGemm2Rows + 4]
             constexpr int kStagePitch = kGemm2Rows + 4;
             __syncthreads();   // every wave is done with the panels
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
+            for (int t = 0; t < kG2Tiles; ++t)
 #pragma unroll
-                for (int m = 0; m < 4; ++m) {
+                for (int m = 0; m < kG2Tokens / 16; ++m) {
                     const int r = 16 * m + r16;
                     if (m < mt && r < nv) {
 #pragma unroll

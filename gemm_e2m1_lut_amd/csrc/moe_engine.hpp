@@ -66,12 +66,10 @@ namespace e2m1 {
 constexpr int kEngineWaves = 8;
 constexpr int kEngineThreads = kEngineWaves * kWave;
 constexpr int kEngineStepCols = 256;
-constexpr int kEngineMaxTokens = 64;                 // token rows per pass (four MFMA tiles)
+constexpr int kEngineMaxTokens = 64;                 // token rows per pass, at most (four MFMA tiles)
 constexpr int kPanelPitch = kEngineStepCols + 8;     // bf16 per staged token row (16-byte pad spreads banks)
-constexpr int kPanelElems = kEngineMaxTokens * kPanelPitch;
 constexpr int kNonTemporal = 2;                      // cache-policy operand of a buffer load: streaming
-constexpr int kStageChunks = 3;                      // 16-byte scale chunks per thread (staged path)
-constexpr int kStageBytes = kStageChunks * kEngineThreads * 16;   // 24 KiB of staged E8M0 rows
+constexpr int kStageMaxBlocks = 96;                  // staged path: scale rows of up to 96 blocks (K <= 3072)
 
 template <int N>
 struct StaticInt {
@@ -109,9 +107,14 @@ struct EngineStep {
     uint8_t e[NT][2];     // per-step path: E8M0 bytes of the same chunks (bytes: widened at use)
 };
 
-template <int NT>
+// NT 16-row tiles per wave (tile sets of 128 rows per workgroup), passes of
+// up to kMaxTok token rows.
+template <int NT, int kMaxTok = kEngineMaxTokens>
 struct MoeEngine {
     static constexpr int kWBufElems = NT * 16 * 8;   // uint4 per wave: [row][block ^ (row / 2 % 8)]
+    static constexpr int kPanelElems = kMaxTok * kPanelPitch;
+    static constexpr int kStageBytes = NT * 128 * kStageMaxBlocks;                      // staged E8M0 rows
+    static constexpr int kStageChunks = (kStageBytes + kEngineThreads * 16 - 1) / (kEngineThreads * 16);
 
     // Shared state of one pass (in LDS, owned by the caller's kernel).
     struct Shared {
@@ -121,7 +124,7 @@ struct MoeEngine {
             uint8_t sbuf[kEngineWaves][NT * 16 * 8];    // per-step path: E8M0 bytes, [tile][row][block]
             alignas(16) uint8_t stage[kStageBytes];     // staged path: [tile set][128 rows][K / 32]
         };
-        int rowidx[kEngineMaxTokens];
+        int rowidx[kMaxTok];
     };
 
     // Whether the workgroup's scale rows for reduction length K fit the stage.
@@ -136,7 +139,9 @@ struct MoeEngine {
 #pragma unroll
         for (int c = 0; c < kStageChunks; ++c) {
             const int ch = (int)threadIdx.x + kEngineThreads * c;
-            const int t = NT > 1 && ch >= per ? 1 : 0;
+            int t = 0;   // tile set of the chunk: compares, no division
+#pragma unroll
+            for (int u = 1; u < NT; ++u) t += ch >= u * per ? 1 : 0;
             // chunks past the stage load offset 0 and are not stored
             const uint32_t off = ch < NT * per ? (uint32_t)(rb[t] * kb + 16 * (ch - t * per)) : 0u;
             const u32x4 u = __builtin_amdgcn_raw_buffer_load_b128(sres, off, 0, kNonTemporal);
@@ -352,11 +357,12 @@ struct MoeEngine {
                                                   __amdgpu_buffer_rsrc_t sres, const int (&rb)[NT], int K,
                                                   const int (&row0)[NT], int stride, int mb, int nsteps, int nrows,
                                                   const uint16_t* xb, size_t xpitch, int nvalid, f32x4 (&acc)[NT][4]) {
+        constexpr int kTop = kMaxTok / 16;
         switch (mt) {
             case 1: run<1, kStaged>(sh, wres, ws, sres, rb, K, row0, stride, mb, nsteps, nrows, xb, xpitch, nvalid, acc); break;
             case 2: run<2, kStaged>(sh, wres, ws, sres, rb, K, row0, stride, mb, nsteps, nrows, xb, xpitch, nvalid, acc); break;
-            case 3: run<3, kStaged>(sh, wres, ws, sres, rb, K, row0, stride, mb, nsteps, nrows, xb, xpitch, nvalid, acc); break;
-            default: run<4, kStaged>(sh, wres, ws, sres, rb, K, row0, stride, mb, nsteps, nrows, xb, xpitch, nvalid, acc); break;
+            case 3: run<(kTop < 3 ? kTop : 3), kStaged>(sh, wres, ws, sres, rb, K, row0, stride, mb, nsteps, nrows, xb, xpitch, nvalid, acc); break;
+            default: run<kTop, kStaged>(sh, wres, ws, sres, rb, K, row0, stride, mb, nsteps, nrows, xb, xpitch, nvalid, acc); break;
         }
     }
 };
