@@ -275,6 +275,8 @@ class TernaryBatch(Workload):
         self.scale = torch.from_numpy(self.host["row_scale"]).cuda()
         self.x = torch.from_numpy(self.host["x"]).cuda()
         self.y = torch.empty(batch, n, device="cuda")
+        need = lib.ternary_gemm_workspace_size(batch, n, k)   # the digit pre-pass's buffer, made once
+        self.ws = torch.empty(need, dtype=torch.uint8, device="cuda") if need > 0 else None
         self.weight_bytes_per_step = float(per_copy + 4 * n)
         self.label = f"ternarygemm_b{batch}"
         self.total_bytes_per_step = float(self.alg_bytes(self.label))
@@ -284,7 +286,7 @@ class TernaryBatch(Workload):
 
     def launches(self):
         def fn(i):
-            self.lib.ternary_gemm(self.packed[i % self.copies], self.scale, self.x, out=self.y)
+            self.lib.ternary_gemm(self.packed[i % self.copies], self.scale, self.x, out=self.y, workspace=self.ws)
         return [(self.label, fn)]
 
     def alg_bytes(self, label):

@@ -6,7 +6,7 @@ the HIP sources in csrc/ by build.py. This package is its thin Python binding:
 torch supplies device memory and streams; every step of every operation runs
 in the library's kernels.
 
-Operations: dequant_decode, dequant_gemv, dequant_gemm, ternary_gemv, ternary_gemm,
+Operations: dequant_decode, dequant_gemv, dequant_gemm, ternary_gemv, ternary_gemm (+ workspace size),
 ternary_wl_gemv, nvfp4_embedding_gather, mxfp4_moe_gemm (+
 mxfp4_moe_workspace_size, and mxfp4_moe_gemm_noalloc for callers that cannot
 allocate), nm_spmm (N:M structured-sparse weights), and the
@@ -36,6 +36,7 @@ from ._binding import (  # noqa: F401
     nm_spmm,
     strerror,
     ternary_gemm,
+    ternary_gemm_workspace_size,
     ternary_gemv,
     ternary_wl_gemv,
 )

@@ -17,7 +17,7 @@ import torch
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libe2m1lut.so")
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
 GEMV_MAX_BATCH = 16
@@ -58,7 +58,8 @@ def load_library() -> ctypes.CDLL:
         "mxfp4_quantize": (ctypes.c_int, [vp, vp, vp, i64, i64, vp]),
         "nvfp4_quantize": (ctypes.c_int, [vp, vp, vp, vp, i64, i64, vp]),
         "ternary_gemv": (ctypes.c_int, [vp, vp, vp, vp, i64, i64, vp]),
-        "ternary_gemm": (ctypes.c_int, [vp, vp, vp, vp, i64, i64, i64, vp]),
+        "ternary_gemm_workspace_size": (sz, [i64, i64, i64]),
+        "ternary_gemm": (ctypes.c_int, [vp, vp, vp, vp, vp, sz, i64, i64, i64, vp]),
         "ternary_wl_gemv": (ctypes.c_int, [ctypes.POINTER(vp), vp, vp, vp, vp, vp, i64, i64, vp]),
         "nvfp4_embedding_gather": (ctypes.c_int, [vp, vp, vp, vp, vp, i64, i64, i64, vp, vp]),
         "mxfp4_moe_workspace_size": (sz, [i64, i64, i64, i64, i64]),
@@ -267,9 +268,18 @@ def ternary_gemv(packed: torch.Tensor, row_scale: torch.Tensor, x: torch.Tensor,
     return out
 
 
+def ternary_gemm_workspace_size(batch: int, n: int, k: int) -> int:
+    size = load_library().ternary_gemm_workspace_size(batch, n, k)
+    if size == ctypes.c_size_t(-1).value:
+        raise ValueError("invalid ternary GEMM extents")
+    return int(size)
+
+
 def ternary_gemm(packed: torch.Tensor, row_scale: torch.Tensor, x: torch.Tensor,
-                 out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """Ternary W packed int32/uint32 [n, k/16], fp32 scale [n], fp32 x [batch, k] -> y [batch, n]."""
+                 out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                 stream=None) -> torch.Tensor:
+    """Ternary W packed int32/uint32 [n, k/16], fp32 scale [n], fp32 x [batch, k] -> y [batch, n].
+    `workspace` (uint8, at least ternary_gemm_workspace_size bytes) is allocated when not given."""
     _need(packed, "packed", (torch.int32, torch.uint32))
     n, words = packed.shape
     k = 16 * words
@@ -281,8 +291,14 @@ def ternary_gemm(packed: torch.Tensor, row_scale: torch.Tensor, x: torch.Tensor,
     if out is None:
         out = torch.empty((batch, n), dtype=torch.float32, device=packed.device)
     _need(out, "out", (torch.float32,), (batch, n))
-    _check("ternary_gemm", load_library().ternary_gemm(_ptr(packed), _ptr(row_scale), _ptr(x), _ptr(out),
-                                                        batch, n, k, _stream(stream)))
+    need = ternary_gemm_workspace_size(batch, n, k)
+    if workspace is None and need > 0:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=packed.device)
+    if workspace is not None:
+        _need(workspace, "workspace", _U8)
+    _check("ternary_gemm", load_library().ternary_gemm(
+        _ptr(packed), _ptr(row_scale), _ptr(x), _ptr(out), _ptr(workspace),
+        0 if workspace is None else workspace.numel(), batch, n, k, _stream(stream)))
     return out
 
 

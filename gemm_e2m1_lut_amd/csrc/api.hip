@@ -83,7 +83,7 @@ const char* e2m1_strerror(int status) {
         case E2M1_ERR_SHAPE: return "invalid extent: negative, too large, or breaking a divisibility rule";
         case E2M1_ERR_ALIGN: return "a pointer is not aligned as the kernel's loads require";
         case E2M1_ERR_DTYPE: return "unknown output dtype code";
-        case E2M1_ERR_WORKSPACE: return "workspace missing or smaller than mxfp4_moe_workspace_size()";
+        case E2M1_ERR_WORKSPACE: return "workspace missing or smaller than the entry point's *_workspace_size()";
         case E2M1_ERR_LAUNCH: return "the HIP runtime reported an error at kernel launch";
         default: return "unknown status";
     }
@@ -183,18 +183,32 @@ int ternary_gemv(const uint32_t* packed, const float* row_scale, const float* x,
     return launch_status(e2m1::launch_ternary(packed, row_scale, x, y, n, k, as_stream(stream)));
 }
 
-int ternary_gemm(const uint32_t* packed, const float* row_scale, const float* x, float* y,
-                 int64_t batch, int64_t n, int64_t k, void* stream) {
-    if (batch < 1 || batch > E2M1_TERNARY_MAX_BATCH || n < 0 || k < 0 || k % 16 != 0 || n > INT_MAX ||
-        k / 16 > INT_MAX / 64 || !mul_ok(n, k) || !mul_ok(batch * 4, k) || !mul_ok(batch * 4, n))
-        return E2M1_ERR_SHAPE;
+static bool ternary_gemm_shape_ok(int64_t batch, int64_t n, int64_t k) {
+    return batch >= 1 && batch <= E2M1_TERNARY_MAX_BATCH && n >= 0 && k >= 0 && k % 16 == 0 && n <= INT_MAX &&
+           k / 16 <= INT_MAX / 64 && mul_ok(n, k) && mul_ok(batch * 4, k) && mul_ok(batch * 4, n);
+}
+
+size_t ternary_gemm_workspace_size(int64_t batch, int64_t n, int64_t k) {
+    if (!ternary_gemm_shape_ok(batch, n, k)) return SIZE_MAX;
+    return n == 0 ? 0 : e2m1::ternary_gemm_workspace_bytes(batch, k);
+}
+
+int ternary_gemm(const uint32_t* packed, const float* row_scale, const float* x, float* y, void* workspace,
+                 size_t workspace_bytes, int64_t batch, int64_t n, int64_t k, void* stream) {
+    if (!ternary_gemm_shape_ok(batch, n, k)) return E2M1_ERR_SHAPE;
     if (n == 0) return E2M1_OK;
     if (!y) return E2M1_ERR_NULL;
     if (!aligned(y, 4)) return E2M1_ERR_ALIGN;
     if (k == 0) return launch_status(fill_zero_bytes(y, batch * n * 4, as_stream(stream)));
     if (!packed || !row_scale || !x) return E2M1_ERR_NULL;
     if (!aligned(packed, 4) || !aligned(x, 4) || !aligned(row_scale, 4)) return E2M1_ERR_ALIGN;
-    return launch_status(e2m1::launch_ternary_gemm(packed, row_scale, x, y, batch, n, k, as_stream(stream)));
+    const size_t need = e2m1::ternary_gemm_workspace_bytes(batch, k);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return E2M1_ERR_WORKSPACE;
+        if (!aligned(workspace, 256)) return E2M1_ERR_ALIGN;
+    }
+    return launch_status(
+        e2m1::launch_ternary_gemm(packed, row_scale, x, y, batch, n, k, workspace, as_stream(stream)));
 }
 
 int ternary_wl_gemv(const uint32_t* const packed[4], const float* scale, const float* x_re,

@@ -34,8 +34,10 @@ hipError_t launch_nm_spmm(const uint16_t* values, const uint32_t* meta, const ui
 hipError_t launch_ternary(const uint32_t* packed, const float* row_scale, const float* x, float* y,
                           int64_t n, int64_t k, hipStream_t stream);
 
+// Device workspace launch_ternary_gemm uses for (batch, k); 0 where it takes the one-launch kernels.
+size_t ternary_gemm_workspace_bytes(int64_t batch, int64_t k);
 hipError_t launch_ternary_gemm(const uint32_t* packed, const float* row_scale, const float* x, float* y,
-                               int64_t batch, int64_t n, int64_t k, hipStream_t stream);
+                               int64_t batch, int64_t n, int64_t k, void* workspace, hipStream_t stream);
 
 hipError_t launch_ternary_wl(const uint32_t* const mats[4], const float* scale, const float* x_re,
                              const float* x_im, float* y_re, float* y_im, int64_t n, int64_t k,

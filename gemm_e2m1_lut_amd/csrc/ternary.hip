@@ -66,7 +66,7 @@ hipError_t launch_ternary(const uint32_t* packed, const float* row_scale, const 
                           int64_t n, int64_t k, hipStream_t stream) {
     // K % 64 == 0 with 16-byte aligned weights: the int8 matrix-core kernel at batch 1
     if (k % 64 == 0 && (reinterpret_cast<uintptr_t>(packed) & 15u) == 0)
-        return launch_ternary_gemm(packed, row_scale, x, y, 1, n, k, stream);
+        return launch_ternary_gemm(packed, row_scale, x, y, 1, n, k, nullptr, stream);   // batch 1: no workspace
     const int nn = (int)n;
     const int want = (nn + kWavesPerBlock - 1) / kWavesPerBlock;
     static int cap = 0;

@@ -22,7 +22,13 @@
 // of lane 16 g + c; the eight digit columns of each activation row are added
 // by DPP, the waves through LDS (one barrier), and the row scale multiplies
 // the total once.
-// Inputs the fast kernel cannot take (K % 64 != 0, unaligned weights) run the
+// Every workgroup prepares the digits of every activation row this way, so
+// their VALU work (about 225 instructions per group of two rows per wave)
+// grows with the batch in each of the n / 16 tiles. From seven rows on the
+// digits are instead prepared once per call by a launch of their own into the
+// caller's workspace, already in the B-operand layout, and the GEMM loads them
+// (1 KB contiguous per instruction) and does no digit arithmetic.
+// Inputs the fast kernels cannot take (K % 64 != 0, unaligned weights) run the
 // ternary GEMV once per activation row.
 #include "device.hpp"
 #include "kernels.hpp"
@@ -36,7 +42,14 @@ constexpr int kSliceChunks = 4;                               // 64-column chunk
 constexpr int kColumns = 16;                                  // B columns: 2 rows x 8 digits
 constexpr int kGroupRows = 2;                                 // activation rows per MFMA
 constexpr int kRowPitch = 20;                                 // dwords per (chunk, column) row in LDS
-constexpr int kWaveDwords = kSliceChunks * kColumns * kRowPitch;
+// dwords per chunk: 16 more than its 16 rows, so the four chunks' rows start 16 banks apart and the
+// digit writes of a wave (one dword per lane, the four chunks side by side) meet no bank twice
+constexpr int kChunkPitch = kColumns * kRowPitch + 16;
+constexpr int kWaveDwords = kSliceChunks * kChunkPitch;
+// From this batch on the digits are prepared once per call (4096 x 4096, event us, one launch against
+// two: B = 2 4.65 / 6.24, B = 4 6.24 / 7.22, B = 8 9.7 / 8.6, B = 16 16.4 / 11.35): the pre-pass is
+// a launch of a few µs, and the GEMM then reads 8 bytes of digits per activation element per tile.
+constexpr int kPrepassMinBatch = 7;
 
 size_t gemm_lds_bytes(int waves, int groups) {
     return 4u * ((size_t)waves * kWaveDwords + (size_t)waves * groups * 32);
@@ -57,8 +70,8 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void ternary_gemm_kernel(const u
     const int nslices = (kq + kSliceChunks - 1) / kSliceChunks;
     // digit preparation: lane -> chunk pg, word pq, dword pj; columns 64 pg + 16 pq + pj + 4 b
     const int pg = lane >> 4, pq = (lane >> 2) & 3, pj = lane & 3;
-    uint32_t* prep_row = tab + pg * kColumns * kRowPitch + 4 * pq + pj;
-    const i32x4* b_row = reinterpret_cast<const i32x4*>(tab + (g * kColumns + c) * kRowPitch);
+    uint32_t* prep_row = tab + pg * kChunkPitch + 4 * pq + pj;
+    const i32x4* b_row = reinterpret_cast<const i32x4*>(tab + g * kChunkPitch + c * kRowPitch);
     // digit column c: activation row c >> 3 of the group, fraction digits for c & 4, digit c & 3
     const int c_row = c >> 3, c_shift = 8 * (c & 3) - ((c & 4) ? 30 : 0);
     const int tile = blockIdx.x;   // one tile of 16 output rows per workgroup
@@ -69,14 +82,13 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void ternary_gemm_kernel(const u
 #pragma unroll
         for (int j = 0; j < 4; ++j) f[gi][j] = 0.f;
 
-    // up to four groups keep every activation row of the slice in registers, requested before the
-    // weights; more groups load each group's rows as it starts
-    constexpr int kAhead = NG <= 4 ? NG : 1;
+    // every activation row of the slice is kept in registers, requested before the weights (this
+    // form runs up to three groups)
     for (int sl = wave; sl < nslices; sl += nwaves) {   // wave-uniform
         const int col0 = 256 * sl + 64 * pg + 16 * pq + pj;
-        float xa[kAhead][kGroupRows][4];   // [group][row of the group][b]
+        float xa[NG][kGroupRows][4];   // [group][row of the group][b]
 #pragma unroll
-        for (int ga = 0; ga < kAhead; ++ga)
+        for (int ga = 0; ga < NG; ++ga)
 #pragma unroll
             for (int bl = 0; bl < kGroupRows; ++bl) {
                 const int b_row_x = min(kGroupRows * ga + bl, batch - 1);   // rows past the batch: never prepared
@@ -95,25 +107,10 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void ternary_gemm_kernel(const u
         for (int gi = 0; gi < NG; ++gi) {
             const int rows = min(kGroupRows, batch - kGroupRows * gi);   // rows of this group (uniform, >= 1)
             float xv[kGroupRows][4];
-            if constexpr (kAhead == NG) {
 #pragma unroll
-                for (int bl = 0; bl < kGroupRows; ++bl)
+            for (int bl = 0; bl < kGroupRows; ++bl)
 #pragma unroll
-                    for (int b = 0; b < 4; ++b) xv[bl][b] = xa[gi][bl][b];
-            } else if (gi == 0) {
-#pragma unroll
-                for (int bl = 0; bl < kGroupRows; ++bl)
-#pragma unroll
-                    for (int b = 0; b < 4; ++b) xv[bl][b] = xa[0][bl][b];
-            } else {   // this group's activations
-#pragma unroll
-                for (int bl = 0; bl < kGroupRows; ++bl) {
-                    if (bl >= rows) break;
-                    const float* xr = x + (int64_t)(kGroupRows * gi + bl) * K;
-#pragma unroll
-                    for (int b = 0; b < 4; ++b) xv[bl][b] = xr[min(col0 + 4 * b, K - 1)];
-                }
-            }
+                for (int b = 0; b < 4; ++b) xv[bl][b] = xa[gi][bl][b];
             // digit columns of rows past the batch keep whatever integers LDS holds: their
             // D columns are never read
             int S[kGroupRows] = {30, 30};
@@ -179,6 +176,136 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void ternary_gemm_kernel(const u
     }
 }
 
+// Two-launch form (batch >= kPrepassMinBatch, a workspace given): the digits above depend only
+// on x, so ternary_digits_kernel prepares them once per launch instead of once per tile. One wave
+// per (group gi of two activation rows, 256-column slice sl) computes them exactly as above and
+// stores them already in the B-operand layout: operand q of lane l for (gi, sl) is the 16 bytes
+// at ((gi * nslices + sl) * 4 + q) * 1024 + 16 l of the digit area, so the GEMM's loads read
+// 1 KB contiguous per instruction; the exponent S of activation row b and slice sl follows at
+// [b][sl]. Rows past the batch get zero digits and S = 30.
+__global__ __launch_bounds__(kWave) void ternary_digits_kernel(const float* __restrict__ x,
+                                                               uint32_t* __restrict__ dig,
+                                                               int* __restrict__ sexp, int batch, int kq) {
+    const int sl = blockIdx.x, gi = blockIdx.y, nslices = gridDim.x;
+    const int lane = threadIdx.x;
+    const int K = 64 * kq;
+    const int pg = lane >> 4, pq = (lane >> 2) & 3, pj = lane & 3;
+    const int col0 = 256 * sl + 64 * pg + 16 * pq + pj;
+    float xv[kGroupRows][4];
+#pragma unroll
+    for (int bl = 0; bl < kGroupRows; ++bl) {
+        const float* xr = x + (int64_t)min(kGroupRows * gi + bl, batch - 1) * K;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) xv[bl][b] = xr[min(col0 + 4 * b, K - 1)];
+    }
+    // dword 4 pq + pj of row (chunk pg, digit column c): operand pq of lane 16 pg + c, dword pj
+    uint32_t* dst = dig + ((int64_t)(gi * nslices + sl) * 4 + pq) * 256 + 16 * 4 * pg + pj;
+#pragma unroll
+    for (int bl = 0; bl < kGroupRows; ++bl) {
+        const bool live = kGroupRows * gi + bl < batch;   // wave-uniform
+        const int S = live ? slice_exponent(wave_max(fmaxf(fmaxf(fabsf(xv[bl][0]), fabsf(xv[bl][1])),
+                                                           fmaxf(fabsf(xv[bl][2]), fabsf(xv[bl][3])))))
+                           : 30;
+        uint32_t dh[4], dl[4], th[4], tl[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) digits8(xv[bl][b], S, dh[b], dl[b]);
+        transpose4(dh, th);
+        transpose4(dl, tl);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            dst[(8 * bl + i) * 4] = live ? th[i] : 0u;
+            dst[(8 * bl + 4 + i) * 4] = live ? tl[i] : 0u;
+        }
+        if (lane == 0) sexp[(int64_t)(kGroupRows * gi + bl) * nslices + sl] = S;
+    }
+}
+
+// The GEMM of the two-launch form: the tile, slice and MFMA structure of ternary_gemm_kernel, with
+// each group's four B operands and two exponents loaded (group gi + 1's requested before group
+// gi's products) instead of prepared, so the waves do no digit arithmetic and use no LDS until
+// the cross-wave sum.
+template <int NG>
+__global__ __launch_bounds__(kWave * kMaxWaves) void ternary_gemm_pre_kernel(const uint32_t* packed,
+                                                                             const float* scale,
+                                                                             const uint32_t* dig,
+                                                                             const int* sexp, float* y,
+                                                                             int batch, int n, int kq) {
+    extern __shared__ __attribute__((aligned(16))) float tp_part[];   // [waves][NG * 2 rows][16]
+    const int nwaves = blockDim.x / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int g = lane >> 4, r = lane & 15, c = lane & 15;
+    const int nslices = (kq + kSliceChunks - 1) / kSliceChunks;
+    const int c_row = c >> 3, c_shift = 8 * (c & 3) - ((c & 4) ? 30 : 0);
+    const int tile = blockIdx.x;
+    const int row = min(tile * 16 + r, n - 1);
+    float f[NG][4];
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) f[gi][j] = 0.f;
+    for (int sl = wave; sl < nslices; sl += nwaves) {   // wave-uniform
+        const i32x4* ops = reinterpret_cast<const i32x4*>(dig) + (int64_t)sl * 4 * 64 + lane;
+        const int* se = sexp + (int64_t)c_row * nslices + sl;
+        const int64_t gstride = (int64_t)nslices * 4 * 64;   // i32x4 per group
+        i32x4 bq[2][4];
+        int sv[2];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) bq[0][q] = ops[q * 64];
+        sv[0] = se[0];
+        issue_fence();
+        const int chunk = sl * kSliceChunks + g;
+        const uint32_t mask = chunk < kq ? 0xFFFFFFFFu : 0u;
+        const uint4 w = load_nt16(packed + ((int64_t)row * kq + min(chunk, kq - 1)) * 4);
+        issue_fence();
+        i32x4 a[4];
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+            if (gi + 1 < NG) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) bq[(gi + 1) & 1][q] = ops[(gi + 1) * gstride + q * 64];
+                sv[(gi + 1) & 1] = se[(int64_t)(gi + 1) * kGroupRows * nslices];
+                issue_fence();
+            }
+            if (gi == 0) {
+                const uint32_t ws[4] = {w.x & mask, w.y & mask, w.z & mask, w.w & mask};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) a[q] = decode_word(ws[q]);
+            }
+            i32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc = mfma_i8(a[q], bq[gi & 1][q], acc);
+            const int e = c_shift - sv[gi & 1];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) f[gi][j] += ldexpf((float)acc[j], e);
+        }
+    }
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float v = f[gi][j];
+            v += dpp_f32<0x111>(v);   // row_shr:1
+            v += dpp_f32<0x112>(v);   // row_shr:2
+            v += dpp_f32<0x114>(v);   // row_shr:4
+            f[gi][j] = v;
+        }
+    if ((c & 7) == 7) {
+        float* dst = tp_part + wave * NG * 32 + c_row * 16 + 4 * g;
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) dst[gi * 32 + j] = f[gi][j];
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < 16 * batch; i += blockDim.x) {
+        const int orow = tile * 16 + (i & 15);
+        float sum = 0.f;
+        for (int wv = 0; wv < nwaves; ++wv) sum += tp_part[wv * NG * 32 + i];
+        if (orow < n) y[(int64_t)(i >> 4) * n + orow] = scale[orow] * sum;
+    }
+}
+
 // Batch 1 (ternary_gemv): the kernel above with one activation row, and each
 // wave's SPW slices (slice wave + waves i) known at compile time, so the x
 // and weight loads of all of them are issued before the first is used.
@@ -196,8 +323,8 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void ternary_gemv_i8_kernel(cons
     const int K = 64 * kq;
     const int nslices = (kq + kSliceChunks - 1) / kSliceChunks;
     const int pg = lane >> 4, pq = (lane >> 2) & 3, pj = lane & 3;
-    uint32_t* prep_row = tab + pg * kColumns * kRowPitch + 4 * pq + pj;
-    const i32x4* b_row = reinterpret_cast<const i32x4*>(tab + (g * kColumns + c) * kRowPitch);
+    uint32_t* prep_row = tab + pg * kChunkPitch + 4 * pq + pj;
+    const i32x4* b_row = reinterpret_cast<const i32x4*>(tab + g * kChunkPitch + c * kRowPitch);
     const int c_shift = 8 * (c & 3) - ((c & 4) ? 30 : 0);   // columns 0..7: the row's eight digits
     const int tile = blockIdx.x;
     const int row = min(tile * 16 + r, n - 1);
@@ -275,20 +402,42 @@ hipError_t run_gemv_i8(const uint32_t* packed, const float* scale, const float* 
     return hipGetLastError();
 }
 
+static_assert(kPrepassMinBatch % 2 == 1, "a group of two rows never straddles the two forms");
+
 template <int NG>
 hipError_t run_gemm(const uint32_t* packed, const float* scale, const float* x, float* y, int batch, int n,
-                    int kq, hipStream_t stream) {
-    const int waves = min(kMaxWaves, (kq + kSliceChunks - 1) / kSliceChunks);
-    const size_t lds = gemm_lds_bytes(waves, NG);
+                    int kq, void* workspace, hipStream_t stream) {
+    const int nslices = (kq + kSliceChunks - 1) / kSliceChunks;
+    const int waves = min(kMaxWaves, nslices);
     const int ntiles = (n + 15) / 16;   // one workgroup per tile: the hardware streams through them
-    ternary_gemm_kernel<NG><<<ntiles, kWave * waves, lds, stream>>>(packed, scale, x, y, batch, n, kq);
-    return hipGetLastError();
+    if constexpr (2 * NG > kPrepassMinBatch) {   // every batch of NG groups is >= kPrepassMinBatch
+        if (workspace == nullptr) return hipErrorInvalidValue;
+        uint32_t* dig = static_cast<uint32_t*>(workspace);
+        int* sexp = reinterpret_cast<int*>(dig + (size_t)NG * nslices * 1024);
+        ternary_digits_kernel<<<dim3(nslices, NG), kWave, 0, stream>>>(x, dig, sexp, batch, kq);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        ternary_gemm_pre_kernel<NG><<<ntiles, kWave * waves, 4u * (size_t)waves * NG * 32, stream>>>(
+            packed, scale, dig, sexp, y, batch, n, kq);
+        return hipGetLastError();
+    } else {
+        const size_t lds = gemm_lds_bytes(waves, NG);
+        ternary_gemm_kernel<NG><<<ntiles, kWave * waves, lds, stream>>>(packed, scale, x, y, batch, n, kq);
+        return hipGetLastError();
+    }
 }
 
 }  // namespace
 
+size_t ternary_gemm_workspace_bytes(int64_t batch, int64_t k) {
+    if (batch < kPrepassMinBatch || k % 64 != 0) return 0;
+    const int64_t groups = (batch + kGroupRows - 1) / kGroupRows;
+    const int64_t nslices = (k / 64 + kSliceChunks - 1) / kSliceChunks;
+    return (size_t)(groups * nslices) * (4096 + 4 * kGroupRows);
+}
+
 hipError_t launch_ternary_gemm(const uint32_t* packed, const float* row_scale, const float* x, float* y,
-                               int64_t batch, int64_t n, int64_t k, hipStream_t stream) {
+                               int64_t batch, int64_t n, int64_t k, void* workspace, hipStream_t stream) {
     const bool fast = k % 64 == 0 && (reinterpret_cast<uintptr_t>(packed) & 15u) == 0;
     if (!fast) {
         for (int64_t b = 0; b < batch; ++b) {
@@ -308,14 +457,14 @@ hipError_t launch_ternary_gemm(const uint32_t* packed, const float* row_scale, c
         }
     }
     switch ((bb + kGroupRows - 1) / kGroupRows) {
-        case 1: return run_gemm<1>(packed, row_scale, x, y, bb, nn, kq, stream);
-        case 2: return run_gemm<2>(packed, row_scale, x, y, bb, nn, kq, stream);
-        case 3: return run_gemm<3>(packed, row_scale, x, y, bb, nn, kq, stream);
-        case 4: return run_gemm<4>(packed, row_scale, x, y, bb, nn, kq, stream);
-        case 5: return run_gemm<5>(packed, row_scale, x, y, bb, nn, kq, stream);
-        case 6: return run_gemm<6>(packed, row_scale, x, y, bb, nn, kq, stream);
-        case 7: return run_gemm<7>(packed, row_scale, x, y, bb, nn, kq, stream);
-        default: return run_gemm<8>(packed, row_scale, x, y, bb, nn, kq, stream);
+        case 1: return run_gemm<1>(packed, row_scale, x, y, bb, nn, kq, workspace, stream);
+        case 2: return run_gemm<2>(packed, row_scale, x, y, bb, nn, kq, workspace, stream);
+        case 3: return run_gemm<3>(packed, row_scale, x, y, bb, nn, kq, workspace, stream);
+        case 4: return run_gemm<4>(packed, row_scale, x, y, bb, nn, kq, workspace, stream);
+        case 5: return run_gemm<5>(packed, row_scale, x, y, bb, nn, kq, workspace, stream);
+        case 6: return run_gemm<6>(packed, row_scale, x, y, bb, nn, kq, workspace, stream);
+        case 7: return run_gemm<7>(packed, row_scale, x, y, bb, nn, kq, workspace, stream);
+        default: return run_gemm<8>(packed, row_scale, x, y, bb, nn, kq, workspace, stream);
     }
 }
 

@@ -59,7 +59,10 @@ constexpr int kMaxWaves = 16;
 constexpr int kSliceChunks = 4;                          // 64-column chunks per wave slice
 constexpr int kVariants = 16;                            // H then L digits of x_re, then of x_im
 constexpr int kRowPitch = 20;                            // dwords per row in LDS (spreads the banks)
-constexpr int kWaveDwords = kSliceChunks * kVariants * kRowPitch;
+// dwords per chunk: 16 more than its rows, so the four chunks' rows start 16 banks apart and the
+// digit writes of a wave (one dword per lane, the four chunks side by side) meet no bank twice
+constexpr int kChunkPitch = kVariants * kRowPitch + 16;
+constexpr int kWaveDwords = kSliceChunks * kChunkPitch;
 constexpr int kPartFloats = 4 * 2 * 16;                  // (matrix, part, row) partial sums
 
 struct WlMats {
@@ -86,8 +89,8 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void ternary_wl_kernel(WlMats ma
     const int nslices = (kq + kSliceChunks - 1) / kSliceChunks;
     // digit preparation: lane -> chunk pg, word pq, dword pj; columns 64 pg + 16 pq + pj + 4 b
     const int pg = lane >> 4, pq = (lane >> 2) & 3, pj = lane & 3;
-    uint32_t* prep_row = tab + pg * kVariants * kRowPitch + 4 * pq + pj;
-    const i32x4* b_row = reinterpret_cast<const i32x4*>(tab + (g * kVariants + c) * kRowPitch);
+    uint32_t* prep_row = tab + pg * kChunkPitch + 4 * pq + pj;
+    const i32x4* b_row = reinterpret_cast<const i32x4*>(tab + g * kChunkPitch + c * kRowPitch);
     // digit column c: part c >> 3 (x_re, x_im), fraction digits for c & 4, digit c & 3
     const bool c_im = c & 8;
     const int c_shift = 8 * (c & 3) - ((c & 4) ? 30 : 0);

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define E2M1LUT_ABI_VERSION 1
+#define E2M1LUT_ABI_VERSION 2
 
 /* Status codes (0 = success, negative = rejected before launch or launch error). */
 #define E2M1_OK 0
@@ -215,6 +215,13 @@ int ternary_gemv(const uint32_t* packed, const float* row_scale, const float* x,
                  int64_t n, int64_t k, void* stream);
 
 /*
+ * ternary_gemm_workspace_size -- bytes of device workspace ternary_gemm needs
+ * for these extents: 0 where it runs without one (batch below 7, k % 64 !=
+ * 0, an empty problem), (size_t)-1 for extents ternary_gemm rejects.
+ */
+size_t ternary_gemm_workspace_size(int64_t batch, int64_t n, int64_t k);
+
+/*
  * ternary_gemm -- small-batch ternary GEMM: y[b][i] = row_scale[i] * sum_k t(i,k) * x[b][k].
  * Operation: [FairyFuse] "三元 GEMV 的乘法消除原理" applied to `batch`
  * activation rows at once, the batched fusion for speculative decoding that
@@ -223,17 +230,25 @@ int ternary_gemv(const uint32_t* packed, const float* row_scale, const float* x,
  *   row_scale  fp32   [n]
  *   x          fp32   [batch, k] (4-byte aligned)
  *   y          fp32   [batch, n], overwritten
+ *   workspace  device buffer of at least ternary_gemm_workspace_size()
+ *              bytes, 256-byte aligned, contents need no initialisation
+ *              (may be NULL where that size is 0); the call writes it, so
+ *              calls that overlap in time need workspaces of their own
  * Requires 1 <= batch <= E2M1_TERNARY_MAX_BATCH, n >= 0, k >= 0,
  * k % 16 == 0. k == 0 writes zeros. A field with both bits set reads as 0;
- * x must be finite. The fast kernel (k % 64 == 0, 16-byte aligned packed)
- * sums ternary times a fixed-point rendering of x exactly (each element to
- * within 2^-31 of the largest |x| of its row and 256-column slice) and rounds
- * in fp32 only a few times per output; other inputs run ternary_gemv once
- * per row of x.
+ * x must be finite. The fast kernels (k % 64 == 0, 16-byte aligned packed)
+ * sum ternary times a fixed-point rendering of x exactly (each element of at
+ * least 2^-36 of the largest |x| of its row and 256-column slice exactly, any
+ * other to within 2^-60 of that largest) and round in fp32 only a few times
+ * per output; from batch 7 on the fixed-point digits are prepared once per
+ * call in the workspace by a launch of their own. Other inputs run
+ * ternary_gemv once per row of x.
+ * Errors: E2M1_ERR_WORKSPACE when a workspace is needed and missing or too
+ * small, E2M1_ERR_ALIGN when it is not 256-byte aligned.
  */
 #define E2M1_TERNARY_MAX_BATCH 16
-int ternary_gemm(const uint32_t* packed, const float* row_scale, const float* x, float* y,
-                 int64_t batch, int64_t n, int64_t k, void* stream);
+int ternary_gemm(const uint32_t* packed, const float* row_scale, const float* x, float* y, void* workspace,
+                 size_t workspace_bytes, int64_t batch, int64_t n, int64_t k, void* stream);
 
 /*
  * ternary_wl_gemv -- widely-linear complex ternary layer y = U x + W conj(x).

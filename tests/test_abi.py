@@ -38,7 +38,7 @@ def lib():
 def test_header_declares_the_five_operations():
     names = declared_functions()
     for op in ("dequant_decode", "dequant_gemv", "ternary_gemv", "ternary_gemm", "ternary_wl_gemv", "mxfp4_quantize", "nvfp4_quantize", "dequant_gemm", "nm_spmm", "nvfp4_embedding_gather",
-               "mxfp4_moe_gemm", "mxfp4_moe_workspace_size", "mxfp4_moe_gemm_noalloc", "e2m1_abi_version",
+               "mxfp4_moe_gemm", "mxfp4_moe_workspace_size", "ternary_gemm_workspace_size", "mxfp4_moe_gemm_noalloc", "e2m1_abi_version",
                "e2m1_strerror"):
         assert op in names
 
@@ -55,7 +55,7 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_version_and_messages(lib):
-    assert lib.e2m1_abi_version() == 1
+    assert lib.e2m1_abi_version() == 2   # 2: ternary_gemm takes a workspace
     for code in (0, -1, -2, -3, -4, -5, -6):
         assert lib.e2m1_strerror(code)
     assert lib.e2m1_strerror(12345) == b"unknown status"
@@ -153,15 +153,33 @@ def test_quantize_validation(lib):
 
 def test_ternary_gemm_validation(lib):
     f = lib.ternary_gemm
-    assert f(A, B, C, D, 0, 4, 16, NULL) == E_SHAPE    # batch 0
-    assert f(A, B, C, D, 17, 4, 16, NULL) == E_SHAPE   # batch above 16
-    assert f(A, B, C, D, 2, 4, 24, NULL) == E_SHAPE    # k % 16
-    assert f(A, B, C, D, 2, -1, 16, NULL) == E_SHAPE
-    assert f(NULL, NULL, NULL, NULL, 3, 0, 16, NULL) == E2M1_OK
-    assert f(A, B, C, NULL, 2, 4, 16, NULL) == E_NULL
-    assert f(A, NULL, C, D, 2, 4, 16, NULL) == E_NULL
-    assert f(A, B, P(0x30002), D, 2, 4, 16, NULL) == E_ALIGN
-    assert f(P(0x10001), B, C, D, 2, 4, 16, NULL) == E_ALIGN
+    W = P(0x70000)   # a 256-byte aligned workspace address
+    assert f(A, B, C, D, W, 1 << 20, 0, 4, 16, NULL) == E_SHAPE    # batch 0
+    assert f(A, B, C, D, W, 1 << 20, 17, 4, 16, NULL) == E_SHAPE   # batch above 16
+    assert f(A, B, C, D, W, 1 << 20, 2, 4, 24, NULL) == E_SHAPE    # k % 16
+    assert f(A, B, C, D, W, 1 << 20, 2, -1, 16, NULL) == E_SHAPE
+    assert f(NULL, NULL, NULL, NULL, NULL, 0, 3, 0, 16, NULL) == E2M1_OK
+    assert f(A, B, C, NULL, W, 1 << 20, 2, 4, 16, NULL) == E_NULL
+    assert f(A, NULL, C, D, W, 1 << 20, 2, 4, 16, NULL) == E_NULL
+    assert f(A, B, P(0x30002), D, W, 1 << 20, 2, 4, 16, NULL) == E_ALIGN
+    assert f(P(0x10001), B, C, D, W, 1 << 20, 2, 4, 16, NULL) == E_ALIGN
+    need = lib.ternary_gemm_workspace_size(8, 4, 64)
+    assert f(A, B, C, D, NULL, 0, 8, 4, 64, NULL) == E_WS              # needed and missing
+    assert f(A, B, C, D, W, need - 1, 8, 4, 64, NULL) == E_WS          # too small
+    assert f(A, B, C, D, P(0x70010), need, 8, 4, 64, NULL) == E_ALIGN  # not 256-byte aligned
+
+
+def test_ternary_gemm_workspace_size(lib):
+    f = lib.ternary_gemm_workspace_size
+    invalid = ctypes.c_size_t(-1).value
+    assert f(1, 4, 4096) == 0 and f(6, 4, 4096) == 0   # batch 1 to 6: the one-launch kernels
+    assert f(8, 4, 4096 + 16) == 0         # k % 64 != 0: ternary_gemv per row
+    assert f(8, 0, 4096) == 0              # empty
+    # per (group of two rows, 256-column slice): 4 KiB of digits and two exponents
+    assert f(8, 4, 4096) == 4 * 16 * (4096 + 8)
+    assert f(16, 4, 4096) == 8 * 16 * (4096 + 8)
+    assert f(7, 4, 64 * 5) == 4 * 2 * (4096 + 8)
+    assert f(0, 4, 64) == invalid and f(17, 4, 64) == invalid and f(2, 4, 24) == invalid
 
 
 def test_ternary_wl_validation(lib):

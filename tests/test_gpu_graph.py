@@ -74,6 +74,8 @@ def test_graph_replays_match_eager(gpu):
         "yng": torch.empty((5, 70), dtype=torch.bfloat16, device=dev),
     }
     ws = torch.empty(gpu.mxfp4_moe_workspace_size(24, 256, 320, 8, 2), dtype=torch.uint8, device=dev)
+    tws = torch.empty(gpu.ternary_gemm_workspace_size(ins["tbx"].shape[0], ins["tbp"].shape[0], ins["tbx"].shape[1]),
+                      dtype=torch.uint8, device=dev)   # the digit pre-pass's buffer
 
     def run_all():
         gpu.dequant_decode(ins["gp"], ins["gs"], out=outs["dec"])
@@ -83,7 +85,7 @@ def test_graph_replays_match_eager(gpu):
         gpu.nvfp4_embedding_gather(ins["table"], ins["bsc"], ins["gsc"], ins["ids"], out=outs["emb"])
         gpu.mxfp4_moe_gemm(ins["mx"], ins["w13"], ins["w13s"], ins["w2"], ins["w2s"], ins["mid"], ins["mw"],
                            out=outs["moe"], workspace=ws)
-        gpu.ternary_gemm(ins["tbp"], ins["tbs"], ins["tbx"], out=outs["ytb"])
+        gpu.ternary_gemm(ins["tbp"], ins["tbs"], ins["tbx"], out=outs["ytb"], workspace=tws)
         gpu.ternary_wl_gemv(ins["wlp"], ins["wls"], ins["wlr"], ins["wli"], out=(outs["wlr"], outs["wli"]))
         gpu.dequant_gemm(ins["ggp"], ins["ggs"], ins["ggx"], out=outs["ygg"])
         gpu.mxfp4_quantize(ins["qx"], out=(outs["mxc"], outs["mxs"]))

@@ -16,7 +16,8 @@ Covers the 4096 x 4096 matrix at every batch 1..16, ragged row tiles and
 slices, several slices per wave, workgroups that loop over tiles, rows of
 very different magnitude (one exponent per row and slice), all-zero rows,
 every field position with exact results, the fallback path, empty extents,
-determinism, and more than 2 GiB of weights (sampled rows).
+determinism, the digit workspace (uninitialised, reused, too small), and more
+than 2 GiB of weights (sampled rows).
 """
 from __future__ import annotations
 
@@ -144,8 +145,28 @@ def test_empty_and_deterministic(gpu):
     assert np.array_equal(run(gpu, case), run(gpu, case))
 
 
+def test_workspace_needs_no_initialisation_and_is_reusable(gpu):
+    """From batch 7 on the fixed-point digits are prepared in the caller's workspace by a launch
+    of their own. One buffer sized for batch 16 and filled with 0xFF serves a batch-16 call and
+    then a batch-9 call (odd: the last group's second row lies past the batch) over a ragged last
+    slice; each result is bit-identical to a call with a freshly allocated workspace. A workspace
+    one byte short is refused."""
+    say("ternary_gemm: workspace reuse")
+    n, k = 300, 4096 + 64 * 3
+    ws = torch.full((gpu.ternary_gemm_workspace_size(16, n, k),), 0xFF, dtype=torch.uint8, device="cuda:0")
+    for batch in (16, 9):
+        case = synth.ternary_batch_case(40 + batch, batch, n, k)
+        fresh = run(gpu, case)
+        out = torch.full((batch, n), float("nan"), device="cuda:0")
+        gpu.ternary_gemm(words(case["packed"]), f32(case["row_scale"]), f32(case["x"]), out=out, workspace=ws)
+        assert np.array_equal(host_f32(out), fresh), batch
+    short = ws[:gpu.ternary_gemm_workspace_size(9, n, k) - 1]
+    with pytest.raises(gpu.E2M1Error):
+        gpu.ternary_gemm(words(case["packed"]), f32(case["row_scale"]), f32(case["x"]), workspace=short)
+
+
 @pytest.mark.slow
-@pytest.mark.parametrize("batch", [1, 4])
+@pytest.mark.parametrize("batch", [1, 4, 16])
 def test_more_than_2_gib_of_weights(gpu, orc, batch):
     """540000 x 16384: 2.21 GB of packed weights, so the word offsets of the rows past 524287
     are beyond the 32-bit byte range. The first and last 64 output rows are held to the fast
