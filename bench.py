@@ -1026,6 +1026,7 @@ WORKLOADS = {
     "ternary_b1": lambda rb: TernaryBatch(1, rb),
     "ternary_b2": lambda rb: TernaryBatch(2, rb),
     "ternary_b4": lambda rb: TernaryBatch(4, rb),
+    "ternary_b6": lambda rb: TernaryBatch(6, rb),
     "ternary_b8": lambda rb: TernaryBatch(8, rb),
     "ternary_b16": lambda rb: TernaryBatch(16, rb),
     "gather": Gather,

@@ -68,7 +68,8 @@ PROFILE_NAMES = {
     "mlp_b16": "gemv_b16_llama8b_mlp", "gemv_small": "gemv_b1_256x512",
     "ternary": "ternary_gemv_4096x4096", "ternary_wl": "ternary_wl_4096x4096",
     "ternary_b1": "ternary_gemm_b1_4096x4096", "ternary_b2": "ternary_gemm_b2_4096x4096",
-    "ternary_b4": "ternary_gemm_b4_4096x4096", "ternary_b8": "ternary_gemm_b8_4096x4096",
+    "ternary_b4": "ternary_gemm_b4_4096x4096", "ternary_b6": "ternary_gemm_b6_4096x4096",
+    "ternary_b8": "ternary_gemm_b8_4096x4096",
     "ternary_b16": "ternary_gemm_b16_4096x4096",
     "gather": "nvfp4_gather_200000x4096_8192ids", "decode": "mxfp4_decode_14336x4096",
     "decode_8192": "mxfp4_decode_8192x4096",

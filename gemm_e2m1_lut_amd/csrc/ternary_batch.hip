@@ -24,7 +24,7 @@
 // the total once.
 // Every workgroup prepares the digits of every activation row this way, so
 // their VALU work (about 225 instructions per group of two rows per wave)
-// grows with the batch in each of the n / 16 tiles. From seven rows on the
+// grows with the batch in each of the n / 16 tiles. From five rows on the
 // digits are instead prepared once per call by a launch of their own into the
 // caller's workspace, already in the B-operand layout, and the GEMM loads them
 // (1 KB contiguous per instruction) and does no digit arithmetic.
@@ -47,9 +47,11 @@ constexpr int kRowPitch = 20;                                 // dwords per (chu
 constexpr int kChunkPitch = kColumns * kRowPitch + 16;
 constexpr int kWaveDwords = kSliceChunks * kChunkPitch;
 // From this batch on the digits are prepared once per call (4096 x 4096, event us, one launch against
-// two: B = 2 4.65 / 6.24, B = 4 6.24 / 7.22, B = 8 9.7 / 8.6, B = 16 16.4 / 11.35): the pre-pass is
-// a launch of a few µs, and the GEMM then reads 8 bytes of digits per activation element per tile.
-constexpr int kPrepassMinBatch = 7;
+// two: B = 4 6.17 / 6.6 (estimated from B = 6 and 8), B = 6 7.97 / 7.16, B = 8 9.7 / 7.74, B = 16
+// 16.4 / 10.28): the pre-pass is a launch of a few µs, and the GEMM then reads 8 bytes of digits per
+// activation element for every two tiles.
+constexpr int kPrepassMinBatch = 5;
+constexpr int kPreWaves = 8;                                  // waves per workgroup of the two-launch GEMM
 
 size_t gemm_lds_bytes(int waves, int groups) {
     return 4u * ((size_t)waves * kWaveDwords + (size_t)waves * groups * 32);
@@ -176,7 +178,7 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void ternary_gemm_kernel(const u
     }
 }
 
-// Two-launch form (batch >= kPrepassMinBatch, a workspace given): the digits above depend only
+// Two-launch form (batch >= kPrepassMinBatch): the digits above depend only
 // on x, so ternary_digits_kernel prepares them once per launch instead of once per tile. One wave
 // per (group gi of two activation rows, 256-column slice sl) computes them exactly as above and
 // stores them already in the B-operand layout: operand q of lane l for (gi, sl) is the 16 bytes
@@ -185,9 +187,13 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void ternary_gemm_kernel(const u
 // [b][sl]. Rows past the batch get zero digits and S = 30.
 __global__ __launch_bounds__(kWave) void ternary_digits_kernel(const float* __restrict__ x,
                                                                uint32_t* __restrict__ dig,
-                                                               int* __restrict__ sexp, int batch, int kq) {
+                                                               int* __restrict__ sexp, float* __restrict__ y,
+                                                               int batch, int n, int kq) {
     const int sl = blockIdx.x, gi = blockIdx.y, nslices = gridDim.x;
     const int lane = threadIdx.x;
+    // y starts at zero: the GEMM's two K halves each add their share
+    const int64_t ny = (int64_t)batch * n, nthreads = (int64_t)kWave * nslices * gridDim.y;
+    for (int64_t i = ((int64_t)gi * nslices + sl) * kWave + lane; i < ny; i += nthreads) y[i] = 0.f;
     const int K = 64 * kq;
     const int pg = lane >> 4, pq = (lane >> 2) & 3, pj = lane & 3;
     const int col0 = 256 * sl + 64 * pg + 16 * pq + pj;
@@ -220,31 +226,40 @@ __global__ __launch_bounds__(kWave) void ternary_digits_kernel(const float* __re
     }
 }
 
-// The GEMM of the two-launch form: the tile, slice and MFMA structure of ternary_gemm_kernel, with
+// The GEMM of the two-launch form: the slice and MFMA structure of ternary_gemm_kernel, with
 // each group's four B operands and two exponents loaded (group gi + 1's requested before group
-// gi's products) instead of prepared, so the waves do no digit arithmetic and use no LDS until
-// the cross-wave sum.
+// gi's products) instead of prepared. Each wave takes two 16-row tiles (rows 32 blockIdx.x + 16 t
+// + r), so every loaded operand serves two MFMAs, and the workgroups of blockIdx.y = 0 and 1 take
+// the first and the second half of the slices (256 workgroups at n = 4096). Each half adds
+// fl(scale * its sum over its waves) into y, which the pre-pass zeroed: with exactly two addends
+// onto zero the result does not depend on their order (0 + a = a, a + b = b + a).
 template <int NG>
-__global__ __launch_bounds__(kWave * kMaxWaves) void ternary_gemm_pre_kernel(const uint32_t* packed,
+__global__ __launch_bounds__(kWave * kPreWaves) void ternary_gemm_pre_kernel(const uint32_t* packed,
                                                                              const float* scale,
                                                                              const uint32_t* dig,
                                                                              const int* sexp, float* y,
                                                                              int batch, int n, int kq) {
-    extern __shared__ __attribute__((aligned(16))) float tp_part[];   // [waves][NG * 2 rows][16]
+    extern __shared__ __attribute__((aligned(16))) float tp_part[];   // [waves][NG][2 tiles][2 rows][16]
     const int nwaves = blockDim.x / kWave;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int g = lane >> 4, r = lane & 15, c = lane & 15;
     const int nslices = (kq + kSliceChunks - 1) / kSliceChunks;
+    const int half = (nslices + 1) / 2;
+    const int sl0 = blockIdx.y * half, sl1 = min(nslices, sl0 + half);
     const int c_row = c >> 3, c_shift = 8 * (c & 3) - ((c & 4) ? 30 : 0);
-    const int tile = blockIdx.x;
-    const int row = min(tile * 16 + r, n - 1);
-    float f[NG][4];
+    const int rows0 = blockIdx.x * 32;
+    int64_t rbase[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) rbase[t] = (int64_t)min(rows0 + 16 * t + r, n - 1) * kq;
+    float f[NG][2][4];
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) f[gi][j] = 0.f;
-    for (int sl = wave; sl < nslices; sl += nwaves) {   // wave-uniform
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) f[gi][t][j] = 0.f;
+    for (int sl = sl0 + wave; sl < sl1; sl += nwaves) {   // wave-uniform
         const i32x4* ops = reinterpret_cast<const i32x4*>(dig) + (int64_t)sl * 4 * 64 + lane;
         const int* se = sexp + (int64_t)c_row * nslices + sl;
         const int64_t gstride = (int64_t)nslices * 4 * 64;   // i32x4 per group
@@ -256,9 +271,11 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void ternary_gemm_pre_kernel(con
         issue_fence();
         const int chunk = sl * kSliceChunks + g;
         const uint32_t mask = chunk < kq ? 0xFFFFFFFFu : 0u;
-        const uint4 w = load_nt16(packed + ((int64_t)row * kq + min(chunk, kq - 1)) * 4);
+        uint4 w[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) w[t] = load_nt16(packed + (rbase[t] + min(chunk, kq - 1)) * 4);
         issue_fence();
-        i32x4 a[4];
+        i32x4 a[2][4];
 #pragma unroll
         for (int gi = 0; gi < NG; ++gi) {
             if (gi + 1 < NG) {
@@ -268,41 +285,54 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void ternary_gemm_pre_kernel(con
                 issue_fence();
             }
             if (gi == 0) {
-                const uint32_t ws[4] = {w.x & mask, w.y & mask, w.z & mask, w.w & mask};
 #pragma unroll
-                for (int q = 0; q < 4; ++q) a[q] = decode_word(ws[q]);
+                for (int t = 0; t < 2; ++t) {
+                    const uint32_t ws[4] = {w[t].x & mask, w[t].y & mask, w[t].z & mask, w[t].w & mask};
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) a[t][q] = decode_word(ws[q]);
+                }
             }
-            i32x4 acc = {0, 0, 0, 0};
-#pragma unroll
-            for (int q = 0; q < 4; ++q) acc = mfma_i8(a[q], bq[gi & 1][q], acc);
             const int e = c_shift - sv[gi & 1];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) f[gi][j] += ldexpf((float)acc[j], e);
+            for (int t = 0; t < 2; ++t) {
+                i32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc = mfma_i8(a[t][q], bq[gi & 1][q], acc);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) f[gi][t][j] += ldexpf((float)acc[j], e);
+            }
         }
     }
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            float v = f[gi][j];
-            v += dpp_f32<0x111>(v);   // row_shr:1
-            v += dpp_f32<0x112>(v);   // row_shr:2
-            v += dpp_f32<0x114>(v);   // row_shr:4
-            f[gi][j] = v;
-        }
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float v = f[gi][t][j];
+                v += dpp_f32<0x111>(v);   // row_shr:1
+                v += dpp_f32<0x112>(v);   // row_shr:2
+                v += dpp_f32<0x114>(v);   // row_shr:4
+                f[gi][t][j] = v;
+            }
     if ((c & 7) == 7) {
-        float* dst = tp_part + wave * NG * 32 + c_row * 16 + 4 * g;
+        float* dst = tp_part + wave * NG * 64 + c_row * 16 + 4 * g;
 #pragma unroll
         for (int gi = 0; gi < NG; ++gi)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) dst[gi * 32 + j] = f[gi][j];
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) dst[gi * 64 + t * 32 + j] = f[gi][t][j];
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < 16 * batch; i += blockDim.x) {
-        const int orow = tile * 16 + (i & 15);
+    // o = (activation row b, tile t, row i): b = 2 gi + c_row
+    for (int o = threadIdx.x; o < 32 * batch; o += blockDim.x) {
+        const int b = o >> 5, t = (o >> 4) & 1, i = o & 15;
+        const int orow = rows0 + 16 * t + i;
+        const int idx = (b >> 1) * 64 + t * 32 + (b & 1) * 16 + i;
         float sum = 0.f;
-        for (int wv = 0; wv < nwaves; ++wv) sum += tp_part[wv * NG * 32 + i];
-        if (orow < n) y[(int64_t)(i >> 4) * n + orow] = scale[orow] * sum;
+        for (int wv = 0; wv < nwaves; ++wv) sum += tp_part[wv * NG * 64 + idx];
+        if (orow < n) atomicAdd(y + (int64_t)b * n + orow, scale[orow] * sum);
     }
 }
 
@@ -414,11 +444,12 @@ hipError_t run_gemm(const uint32_t* packed, const float* scale, const float* x, 
         if (workspace == nullptr) return hipErrorInvalidValue;
         uint32_t* dig = static_cast<uint32_t*>(workspace);
         int* sexp = reinterpret_cast<int*>(dig + (size_t)NG * nslices * 1024);
-        ternary_digits_kernel<<<dim3(nslices, NG), kWave, 0, stream>>>(x, dig, sexp, batch, kq);
+        ternary_digits_kernel<<<dim3(nslices, NG), kWave, 0, stream>>>(x, dig, sexp, y, batch, n, kq);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        ternary_gemm_pre_kernel<NG><<<ntiles, kWave * waves, 4u * (size_t)waves * NG * 32, stream>>>(
-            packed, scale, dig, sexp, y, batch, n, kq);
+        const int pwaves = min(kPreWaves, (nslices + 1) / 2);
+        ternary_gemm_pre_kernel<NG><<<dim3((n + 31) / 32, 2), kWave * pwaves, 4u * (size_t)pwaves * NG * 64,
+                                      stream>>>(packed, scale, dig, sexp, y, batch, n, kq);
         return hipGetLastError();
     } else {
         const size_t lds = gemm_lds_bytes(waves, NG);

@@ -216,7 +216,7 @@ int ternary_gemv(const uint32_t* packed, const float* row_scale, const float* x,
 
 /*
  * ternary_gemm_workspace_size -- bytes of device workspace ternary_gemm needs
- * for these extents: 0 where it runs without one (batch below 7, k % 64 !=
+ * for these extents: 0 where it runs without one (batch below 5, k % 64 !=
  * 0, an empty problem), (size_t)-1 for extents ternary_gemm rejects.
  */
 size_t ternary_gemm_workspace_size(int64_t batch, int64_t n, int64_t k);
@@ -240,7 +240,7 @@ size_t ternary_gemm_workspace_size(int64_t batch, int64_t n, int64_t k);
  * sum ternary times a fixed-point rendering of x exactly (each element of at
  * least 2^-36 of the largest |x| of its row and 256-column slice exactly, any
  * other to within 2^-60 of that largest) and round in fp32 only a few times
- * per output; from batch 7 on the fixed-point digits are prepared once per
+ * per output; from batch 5 on the fixed-point digits are prepared once per
  * call in the workspace by a launch of their own. Other inputs run
  * ternary_gemv once per row of x.
  * Errors: E2M1_ERR_WORKSPACE when a workspace is needed and missing or too

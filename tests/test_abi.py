@@ -172,13 +172,13 @@ def test_ternary_gemm_validation(lib):
 def test_ternary_gemm_workspace_size(lib):
     f = lib.ternary_gemm_workspace_size
     invalid = ctypes.c_size_t(-1).value
-    assert f(1, 4, 4096) == 0 and f(6, 4, 4096) == 0   # batch 1 to 6: the one-launch kernels
+    assert f(1, 4, 4096) == 0 and f(4, 4, 4096) == 0   # batch 1 to 4: the one-launch kernels
     assert f(8, 4, 4096 + 16) == 0         # k % 64 != 0: ternary_gemv per row
     assert f(8, 0, 4096) == 0              # empty
     # per (group of two rows, 256-column slice): 4 KiB of digits and two exponents
     assert f(8, 4, 4096) == 4 * 16 * (4096 + 8)
     assert f(16, 4, 4096) == 8 * 16 * (4096 + 8)
-    assert f(7, 4, 64 * 5) == 4 * 2 * (4096 + 8)
+    assert f(5, 4, 64 * 5) == 3 * 2 * (4096 + 8)
     assert f(0, 4, 64) == invalid and f(17, 4, 64) == invalid and f(2, 4, 24) == invalid
 
 

@@ -146,7 +146,7 @@ def test_empty_and_deterministic(gpu):
 
 
 def test_workspace_needs_no_initialisation_and_is_reusable(gpu):
-    """From batch 7 on the fixed-point digits are prepared in the caller's workspace by a launch
+    """From batch 5 on the fixed-point digits are prepared in the caller's workspace by a launch
     of their own. One buffer sized for batch 16 and filled with 0xFF serves a batch-16 call and
     then a batch-9 call (odd: the last group's second row lies past the batch) over a ragged last
     slice; each result is bit-identical to a call with a freshly allocated workspace. A workspace
