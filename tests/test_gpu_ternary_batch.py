@@ -88,6 +88,8 @@ def test_workload_4096_every_batch(gpu, orc, batch):
     (7, 17, 8192 + 64),   # three slices for wave 0, one chunk in the last
     (4, 40000, 1024),     # more tiles than resident workgroups
     (11, 9000, 4096 + 64),
+    (6, 50, 64),          # one slice from batch 5 on: the second half of the slices is empty and adds +0
+    (9, 31, 256),         # one full slice, odd batch
 ])
 def test_fast_kernel_shapes(gpu, orc, batch, n, k):
     check(gpu, orc, synth.ternary_batch_case(batch * 1000 + n + k, batch, n, k))
