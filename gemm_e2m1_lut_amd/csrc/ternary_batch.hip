@@ -27,7 +27,11 @@
 // grows with the batch in each of the n / 16 tiles. From five rows on the
 // digits are instead prepared once per call by a launch of their own into the
 // caller's workspace, already in the B-operand layout, and the GEMM loads them
-// (1 KB contiguous per instruction) and does no digit arithmetic.
+// (1 KB contiguous per instruction) and does no digit arithmetic; there each
+// wave serves two 16-row tiles and the two halves of the slices run in
+// workgroups of their own, each adding its share into y (zeroed by the
+// pre-pass; two addends onto zero, so the result does not depend on their
+// order).
 // Inputs the fast kernels cannot take (K % 64 != 0, unaligned weights) run the
 // ternary GEMV once per activation row.
 #include "device.hpp"
