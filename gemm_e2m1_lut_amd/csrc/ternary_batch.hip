@@ -307,26 +307,23 @@ __global__ __launch_bounds__(kWave * kPreWaves) void ternary_gemm_pre_kernel(con
             }
         }
     }
+    // the eight digit columns of each activation row: lane (g, c) ends with the totals of values
+    // (c & 7) NG + m of the flattened [gi][t][j] (NG of them)
+    float v[NG * 8];
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi)
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                float v = f[gi][t][j];
-                v += dpp_f32<0x111>(v);   // row_shr:1
-                v += dpp_f32<0x112>(v);   // row_shr:2
-                v += dpp_f32<0x114>(v);   // row_shr:4
-                f[gi][t][j] = v;
-            }
-    if ((c & 7) == 7) {
+            for (int j = 0; j < 4; ++j) v[(gi * 2 + t) * 4 + j] = f[gi][t][j];
+    digit_lane_totals(v, lane);
+    {
         float* dst = tp_part + wave * NG * 64 + c_row * 16 + 4 * g;
 #pragma unroll
-        for (int gi = 0; gi < NG; ++gi)
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) dst[gi * 64 + t * 32 + j] = f[gi][t][j];
+        for (int m = 0; m < NG; ++m) {
+            const int fi = (c & 7) * NG + m, gi = fi >> 3, t = (fi >> 2) & 1, j = fi & 3;
+            dst[gi * 64 + t * 32 + j] = v[m];
+        }
     }
     __syncthreads();
     // o = (activation row b, tile t, row i): b = 2 gi + c_row

@@ -22,6 +22,8 @@
 // exact.
 #pragma once
 
+#include <type_traits>
+
 #include "device.hpp"
 
 namespace e2m1 {
@@ -107,6 +109,27 @@ __device__ __forceinline__ float row16_max(float v) {
     v = fmaxf(v, dpp_f32<0x141>(v));
     v = fmaxf(v, dpp_f32<0x140>(v));
     return v;
+}
+
+// Totals over the eight lanes that differ in lane bits 0..2 (the eight digit columns of an
+// activation row), transposed: three pairings (row_half_mirror across bit 2, then quad_perm across
+// bits 1 and 0) each halve the values a lane keeps, the lane whose bit is set keeping the upper
+// half. On return v[0 .. M/8) of lane L hold the totals of value indices (L & 7) (M/8) + m.
+template <int M>
+__device__ __forceinline__ void digit_lane_totals(float (&v)[M], int lane) {
+    static_assert(M % 8 == 0, "eight lanes, M / 8 values each");
+    auto step = [&](auto ctrl, int bit, int h) {
+        const bool upper = (lane >> bit) & 1;
+#pragma unroll
+        for (int j = 0; j < h; ++j) {
+            const float keep = upper ? v[j + h] : v[j];
+            const float send = upper ? v[j] : v[j + h];
+            v[j] = keep + dpp_f32<decltype(ctrl)::value>(send);
+        }
+    };
+    step(std::integral_constant<int, 0x141>{}, 2, M / 2);   // row_half_mirror: lane i <-> 7 - i
+    step(std::integral_constant<int, 0x4E>{}, 1, M / 4);    // quad_perm [2,3,0,1]
+    step(std::integral_constant<int, 0xB1>{}, 0, M / 8);    // quad_perm [1,0,3,2]
 }
 
 __device__ __forceinline__ i32x4 mfma_i8(i32x4 a, i32x4 b, i32x4 c) {
