@@ -229,7 +229,9 @@ size_t ternary_gemm_workspace_size(int64_t batch, int64_t n, int64_t k);
  *   packed     uint32 [n, k/16]  (4-byte aligned)
  *   row_scale  fp32   [n]
  *   x          fp32   [batch, k] (4-byte aligned)
- *   y          fp32   [batch, n], overwritten
+ *   y          fp32   [batch, n], overwritten (from batch 5: zeroed by the
+ *              first launch, then two fp32 atomic adds per element, so it
+ *              must be ordinary device memory from hipMalloc)
  *   workspace  device buffer of at least ternary_gemm_workspace_size()
  *              bytes, 256-byte aligned, contents need no initialisation
  *              (may be NULL where that size is 0); the call writes it, so
