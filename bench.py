@@ -209,6 +209,29 @@ class GemvMLP(Workload):
                           f"{el:.1f} s, fp64 scalar C with OpenMP over rows"}
 
 
+class GemvMLPGrouped(GemvMLP):
+    """The batch-1 MLP step with both products in one dequant_gemv_grouped call (one launch)."""
+    LABEL = "gemv_b1_grouped_14336x4096+4096x14336"
+
+    def __init__(self, rotate_bytes: float):
+        super().__init__(1, rotate_bytes)
+        self.name = "llama8b_mlp_mxfp4_gemv_b1_grouped"
+        self.config["workload"] = self.name
+        self.config["launch"] = "both products in one dequant_gemv_grouped call"
+
+    def launches(self):
+        def fn(i):
+            mats = [(p, s, x[0]) for (p, s), x in zip(self.weights[i % self.copies], self.x)]
+            self.lib.dequant_gemv_grouped(mats, out_dtype=self.y[0].dtype, outs=[y[0] for y in self.y])
+        return [(self.LABEL, fn)]
+
+    def alg_bytes(self, label):
+        return sum(n * k // 2 + n * k // 32 + k * 2 + n * 2 for n, k in self.SHAPES)
+
+    def alg_flops(self, label):
+        return sum(2.0 * n * k for n, k in self.SHAPES)
+
+
 class Ternary(Workload):
     def __init__(self, rotate_bytes: float, n: int = 4096, k: int = 4096):
         import torch
@@ -1017,6 +1040,7 @@ WORKLOADS = {
     "mfma_peak_16x16x32": lambda rb: MfmaPeak(rb, 16),
     "moe": Moe,
     "mlp_b1": lambda rb: GemvMLP(1, rb),
+    "mlp_b1_grouped": GemvMLPGrouped,
     "mlp_b2": lambda rb: GemvMLP(2, rb),
     "mlp_b4": lambda rb: GemvMLP(4, rb),
     "mlp_b8": lambda rb: GemvMLP(8, rb),

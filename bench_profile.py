@@ -63,7 +63,7 @@ PASSES = {
 
 # profile file name per workload
 PROFILE_NAMES = {
-    "mlp_b1": "gemv_b1_llama8b_mlp", "mlp_b2": "gemv_b2_llama8b_mlp", "mlp_b4": "gemv_b4_llama8b_mlp",
+    "mlp_b1": "gemv_b1_llama8b_mlp", "mlp_b1_grouped": "gemv_b1_grouped_llama8b_mlp", "mlp_b2": "gemv_b2_llama8b_mlp", "mlp_b4": "gemv_b4_llama8b_mlp",
     "mlp_b8": "gemv_b8_llama8b_mlp",
     "mlp_b16": "gemv_b16_llama8b_mlp", "gemv_small": "gemv_b1_256x512",
     "ternary": "ternary_gemv_4096x4096", "ternary_wl": "ternary_wl_4096x4096",

@@ -6,7 +6,7 @@ the HIP sources in csrc/ by build.py. This package is its thin Python binding:
 torch supplies device memory and streams; every step of every operation runs
 in the library's kernels.
 
-Operations: dequant_decode, dequant_gemv, dequant_gemm, ternary_gemv, ternary_gemm (+ workspace size),
+Operations: dequant_decode, dequant_gemv, dequant_gemv_grouped, dequant_gemm, ternary_gemv, ternary_gemm (+ workspace size),
 ternary_wl_gemv, nvfp4_embedding_gather, mxfp4_moe_gemm (+
 mxfp4_moe_workspace_size, and mxfp4_moe_gemm_noalloc for callers that cannot
 allocate), nm_spmm (N:M structured-sparse weights), and the
@@ -24,6 +24,7 @@ from ._binding import (  # noqa: F401
     dequant_decode,
     dequant_gemm,
     dequant_gemv,
+    dequant_gemv_grouped,
     library_path,
     load_library,
     mxfp4_moe_gemm,

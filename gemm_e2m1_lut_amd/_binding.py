@@ -54,6 +54,9 @@ def load_library() -> ctypes.CDLL:
         "dequant_decode": (ctypes.c_int, [vp, vp, vp, i64, i64, vp]),
         "dequant_gemv": (ctypes.c_int, [vp, vp, vp, vp, i32, i64, i64, i64, vp]),
         "dequant_gemm": (ctypes.c_int, [vp, vp, vp, vp, i32, i64, i64, i64, vp]),
+        "dequant_gemv_grouped": (ctypes.c_int, [i32, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                                ctypes.POINTER(vp), ctypes.POINTER(i64), ctypes.POINTER(i64),
+                                                i32, vp]),
         "nm_spmm": (ctypes.c_int, [vp, vp, vp, vp, i32, i64, i64, i64, i32, i32, vp]),
         "mxfp4_quantize": (ctypes.c_int, [vp, vp, vp, i64, i64, vp]),
         "nvfp4_quantize": (ctypes.c_int, [vp, vp, vp, vp, i64, i64, vp]),
@@ -162,6 +165,40 @@ def dequant_gemv(packed: torch.Tensor, scales: torch.Tensor, x: torch.Tensor,
     _check("dequant_gemv", load_library().dequant_gemv(_ptr(packed), _ptr(scales), _ptr(xb), _ptr(out),
                                                         code, batch, n, k, _stream(stream)))
     return out[0] if squeeze else out
+
+
+def dequant_gemv_grouped(mats, out_dtype: torch.dtype = torch.float32, outs=None, stream=None) -> list:
+    """[y_g = W_g x_g for (packed_g, scales_g, x_g) in mats]: independent batch-1 products in shared launches.
+    x_g is bf16 [k_g] (or [1, k_g]); y_g comes back with x_g's leading shape."""
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out_dtype must be torch.float32 or torch.bfloat16")
+    mats = list(mats)
+    if outs is not None and len(outs) != len(mats):
+        raise ValueError(f"{len(outs)} outputs for {len(mats)} matrices")
+    res, xs, ns, ks = [], [], [], []
+    for g, (packed, scales, x) in enumerate(mats):
+        _need(packed, "packed", _U8)
+        n, half = packed.shape
+        k = 2 * half
+        _need(scales, "scales", _U8, (n, k // 32))
+        squeeze = x.dim() == 1
+        xb = x.unsqueeze(0) if squeeze else x
+        _need(xb, "x", (torch.bfloat16,), (1, k))
+        out = torch.empty((1, n), dtype=out_dtype, device=packed.device) if outs is None else outs[g]
+        _need(out, "out", (out_dtype,), (1, n) if out.dim() == 2 else (n,))
+        res.append(out[0] if (squeeze and out.dim() == 2) else out)
+        xs.append(xb)
+        ns.append(n)
+        ks.append(k)
+    cnt = len(mats)
+    arr = ctypes.c_void_p * max(cnt, 1)
+    a64 = ctypes.c_int64 * max(cnt, 1)
+    code = DTYPE_F32 if out_dtype == torch.float32 else DTYPE_BF16
+    _check("dequant_gemv_grouped", load_library().dequant_gemv_grouped(
+        cnt, arr(*[m[0].data_ptr() for m in mats]), arr(*[m[1].data_ptr() for m in mats]),
+        arr(*[x.data_ptr() for x in xs]), arr(*[o.data_ptr() for o in res]), a64(*ns), a64(*ks), code,
+        _stream(stream)))
+    return res
 
 
 def dequant_gemm(packed: torch.Tensor, scales: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None,

@@ -116,6 +116,42 @@ int dequant_gemv(const uint8_t* packed, const uint8_t* scale_e8m0, const uint16_
                                            (int)batch, n, k, as_stream(stream)));
 }
 
+static_assert(E2M1_GEMV_MAX_GROUPS == e2m1::kGemvGroupMax, "group limit of the header and the kernels");
+
+int dequant_gemv_grouped(int count, const uint8_t* const* packed, const uint8_t* const* scale_e8m0,
+                         const uint16_t* const* x_bf16, void* const* y, const int64_t* n, const int64_t* k,
+                         int y_dtype, void* stream) {
+    if (y_dtype != E2M1_DTYPE_F32 && y_dtype != E2M1_DTYPE_BF16) return E2M1_ERR_DTYPE;
+    if (count < 0 || count > E2M1_GEMV_MAX_GROUPS) return E2M1_ERR_SHAPE;
+    if (count == 0) return E2M1_OK;
+    if (!packed || !scale_e8m0 || !x_bf16 || !y || !n || !k) return E2M1_ERR_NULL;
+    const int64_t esize = y_dtype == E2M1_DTYPE_F32 ? 4 : 2;
+    for (int g = 0; g < count; ++g) {   // everything checked before the first launch
+        if (n[g] < 0 || k[g] < 0 || k[g] % 32 != 0 || n[g] > INT_MAX || k[g] / 32 > INT_MAX / 64 ||
+            !mul_ok(n[g], k[g]))
+            return E2M1_ERR_SHAPE;
+        if (n[g] == 0) continue;
+        if (!y[g]) return E2M1_ERR_NULL;
+        if (!aligned(y[g], (uintptr_t)esize)) return E2M1_ERR_ALIGN;
+        if (k[g] == 0) continue;
+        if (!packed[g] || !scale_e8m0[g] || !x_bf16[g]) return E2M1_ERR_NULL;
+        if (!aligned(packed[g], 16) || !aligned(x_bf16[g], 16)) return E2M1_ERR_ALIGN;
+    }
+    e2m1::GemvMatrix mats[E2M1_GEMV_MAX_GROUPS];
+    int m = 0;
+    for (int g = 0; g < count; ++g) {
+        if (n[g] == 0) continue;
+        if (k[g] == 0) {
+            const hipError_t err = fill_zero_bytes(y[g], n[g] * esize, as_stream(stream));
+            if (err != hipSuccess) return launch_status(err);
+            continue;
+        }
+        mats[m++] = e2m1::GemvMatrix{packed[g], scale_e8m0[g], x_bf16[g], y[g], n[g], k[g]};
+    }
+    if (m == 0) return E2M1_OK;
+    return launch_status(e2m1::launch_gemv_group(mats, m, y_dtype == E2M1_DTYPE_BF16, as_stream(stream)));
+}
+
 int dequant_gemm(const uint8_t* packed, const uint8_t* scale_e8m0, const uint16_t* x_bf16, void* y,
                  int y_dtype, int64_t m, int64_t n, int64_t k, void* stream) {
     if (y_dtype != E2M1_DTYPE_F32 && y_dtype != E2M1_DTYPE_BF16) return E2M1_ERR_DTYPE;

@@ -299,14 +299,12 @@ __device__ __forceinline__ void load_x_chunk(uint32_t (&xr)[16], const uint16_t*
 // lanes; with S = 1 (K <= 64 CPL chunks, one wave per four whole rows, no LDS
 // and no barrier) the lanes that hold them store directly, otherwise the S
 // wave partials meet in LDS and are summed in a fixed order.
+// The tile of rows row0 .. row0 + R - 1 for wave wv of S (part: S x R floats
+// of LDS shared by the S waves; unused when S == 1).
 template <int S, int CPL, int R, bool kBf16Out>
-__global__ __launch_bounds__(kWave * S) void gemv_b1_rows_kernel(const uint8_t* packed, const uint8_t* scales,
-                                                                 const uint16_t* __restrict__ x,
-                                                                 void* __restrict__ y, int n, int kc) {
-    __shared__ float part[S][R];
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int row0 = blockIdx.x * R;
+__device__ __forceinline__ void b1_rows_tile(const uint8_t* packed, const uint8_t* scales,
+                                             const uint16_t* __restrict__ x, void* __restrict__ y, int n,
+                                             int kc, int row0, int wv, int lane, float (*part)[R]) {
     const uint4* pv = reinterpret_cast<const uint4*>(packed);
     int c[CPL];
     bool cvalid[CPL];
@@ -363,6 +361,63 @@ __global__ __launch_bounds__(kWave * S) void gemv_b1_rows_kernel(const uint8_t* 
             if (row < n) store_out<kBf16Out>(y, row, sum);
         }
     }
+}
+
+template <int S, int CPL, int R, bool kBf16Out>
+__global__ __launch_bounds__(kWave * S) void gemv_b1_rows_kernel(const uint8_t* packed, const uint8_t* scales,
+                                                                 const uint16_t* __restrict__ x,
+                                                                 void* __restrict__ y, int n, int kc) {
+    __shared__ float part[S][R];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    b1_rows_tile<S, CPL, R, kBf16Out>(packed, scales, x, y, n, kc, blockIdx.x * R, wv, lane, part);
+}
+
+// Several independent batch-1 products in one launch (e.g. the projections of
+// one layer that read the same or different activations): the fixed cost of a
+// launch (dispatch, ramp-up, drain and the final write-back, about 1.5-2 us
+// here) is paid once for all their weight bytes instead of once per matrix.
+// Each matrix keeps the tiling it gets alone: K <= 2048 / 4096 as S
+// independent one-wave tiles of four whole rows per workgroup (kind 0 / 1),
+// 4096 < K <= 16384 as one 16-row tile of S waves (kind 2, every such matrix
+// of a launch needing the same S). Workgroups map to matrices through
+// ascending first-block indices (scalar, uniform per workgroup).
+constexpr int kGroupMax = 8;
+constexpr int kGroupRows = 16;   // rows of a multi-wave tile
+struct B1Group {
+    const uint8_t* packed;
+    const uint8_t* scales;
+    const uint16_t* x;
+    void* y;
+    int n, kc, kind, block0;
+};
+struct B1GroupSet {
+    B1Group g[kGroupMax];
+    int count;
+};
+
+template <int S, bool kBf16Out>
+__global__ __launch_bounds__(kWave * S) void gemv_b1_group_kernel(const B1GroupSet set) {
+    __shared__ float part[S][kGroupRows];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int blk = blockIdx.x;
+    B1Group g = set.g[0];   // constant indices only: the selection stays in scalar registers
+#pragma unroll
+    for (int i = 1; i < kGroupMax; ++i)
+        if (i < set.count && blk >= set.g[i].block0) g = set.g[i];
+    const int local = blk - g.block0;
+    if (g.kind == 2) {
+        b1_rows_tile<S, 1, kGroupRows, kBf16Out>(g.packed, g.scales, g.x, g.y, g.n, g.kc, local * kGroupRows, wv,
+                                                 lane, part);
+        return;
+    }
+    const int row0 = (local * S + wv) * 4;   // one-wave tiles: wave-uniform exit past the last row
+    if (row0 >= g.n) return;
+    if (g.kind == 0)
+        b1_rows_tile<1, 1, 4, kBf16Out>(g.packed, g.scales, g.x, g.y, g.n, g.kc, row0, 0, lane, nullptr);
+    else
+        b1_rows_tile<1, 2, 4, kBf16Out>(g.packed, g.scales, g.x, g.y, g.n, g.kc, row0, 0, lane, nullptr);
 }
 
 // Batch 2..4, 32 < K/32 <= 32 S: one workgroup of S waves per tile of 16
@@ -903,6 +958,45 @@ hipError_t run_mfma(int batch, const uint8_t* packed, const uint8_t* scales, con
     }
 }
 
+template <int S, bool kBf16Out>
+hipError_t run_b1_group(const B1GroupSet& set, int blocks, hipStream_t stream) {
+    gemv_b1_group_kernel<S, kBf16Out><<<blocks, kWave * S, 0, stream>>>(set);
+    return hipGetLastError();
+}
+
+// One launch of up to kGroupMax matrices whose multi-wave tiles (kind 2) all
+// have S waves; S also sets how many one-wave tiles a workgroup of kind 0 / 1
+// holds.
+template <bool kBf16Out>
+hipError_t launch_b1_set(const GemvMatrix* const* mats, int count, int S, hipStream_t stream) {
+    B1GroupSet set{};
+    set.count = count;
+    int64_t blocks = 0;
+    int slot = 0;
+    // multi-wave tiles take the first block indices: the dispatcher starts
+    // them first, and the shorter one-wave workgroups fill the slots around
+    // them (issued after them, the one-wave blocks would fill the machine
+    // and the long tiles would run alone at the end)
+    for (int pass = 0; pass < 2; ++pass)
+        for (int i = 0; i < count; ++i) {
+            const GemvMatrix& m = *mats[i];
+            const int kc = (int)(m.k / 32), n = (int)m.n;
+            const int kind = kc <= 64 ? 0 : kc <= 128 ? 1 : 2;
+            if ((kind == 2) != (pass == 0)) continue;
+            set.g[slot++] = B1Group{m.packed, m.scales, m.x, m.y, n, kc, kind, (int)blocks};
+            blocks += kind == 2 ? (n + kGroupRows - 1) / kGroupRows : (n + 4 * S - 1) / (4 * S);
+        }
+    if (blocks * kWave * S > (int64_t)UINT32_MAX) return hipErrorInvalidValue;   // grid past the launch limit
+    switch (S) {
+        case 3: return run_b1_group<3, kBf16Out>(set, blocks, stream);
+        case 5: return run_b1_group<5, kBf16Out>(set, blocks, stream);
+        case 6: return run_b1_group<6, kBf16Out>(set, blocks, stream);
+        case 7: return run_b1_group<7, kBf16Out>(set, blocks, stream);
+        case 8: return run_b1_group<8, kBf16Out>(set, blocks, stream);
+        default: return run_b1_group<4, kBf16Out>(set, blocks, stream);
+    }
+}
+
 }  // namespace
 
 // Largest K of the batch-1 kernels: 16 waves of 64 lanes, one 32-column chunk
@@ -931,6 +1025,39 @@ hipError_t launch_gemv(const uint8_t* packed, const uint8_t* scales, const uint1
                         : run_mfma<false>(batch, packed, scales, x, y, nn, kc, stream);
     return out_bf16 ? dispatch_generic<true>(batch, packed, scales, x, y, nn, kc, stream)
                     : dispatch_generic<false>(batch, packed, scales, x, y, nn, kc, stream);
+}
+
+// Matrices with K > 16384 run alone (their kernels stream row slabs); the
+// others share launches, one per distinct multi-wave tile width S.
+hipError_t launch_gemv_group(const GemvMatrix* mats, int count, bool out_bf16, hipStream_t stream) {
+    const GemvMatrix* pend[kGroupMax];
+    for (int i = 0; i < count; ++i)
+        if (mats[i].k > 16 * 1024) {
+            const hipError_t err = launch_gemv(mats[i].packed, mats[i].scales, mats[i].x, mats[i].y, out_bf16, 1,
+                                               mats[i].n, mats[i].k, stream);
+            if (err != hipSuccess) return err;
+        }
+    bool done[kGemvGroupMax] = {};
+    for (int first = 0; first < count; ++first) {
+        if (done[first] || mats[first].k > 16 * 1024) continue;
+        // the launch's S: that of the first pending multi-wave matrix, else 4
+        int S = 4;
+        for (int i = first; i < count; ++i) {
+            const int kc = (int)(mats[i].k / 32);
+            if (!done[i] && kc > 128 && kc <= 512) { S = (kc + 63) / 64; break; }
+        }
+        int np = 0;
+        for (int i = first; i < count && np < kGroupMax; ++i) {
+            const int kc = (int)(mats[i].k / 32);
+            if (done[i] || kc > 512 || (kc > 128 && (kc + 63) / 64 != S)) continue;
+            pend[np++] = &mats[i];
+            done[i] = true;
+        }
+        const hipError_t err = out_bf16 ? launch_b1_set<true>(pend, np, S, stream)
+                                        : launch_b1_set<false>(pend, np, S, stream);
+        if (err != hipSuccess) return err;
+    }
+    return hipSuccess;
 }
 
 }  // namespace e2m1

@@ -25,6 +25,18 @@ hipError_t launch_nvfp4_quantize(const uint16_t* x, const float* global_scale, u
 hipError_t launch_gemv(const uint8_t* packed, const uint8_t* scales, const uint16_t* x, void* y,
                        bool out_bf16, int batch, int64_t n, int64_t k, hipStream_t stream);
 
+// One batch-1 product of a grouped launch (host-side descriptor).
+struct GemvMatrix {
+    const uint8_t* packed;
+    const uint8_t* scales;
+    const uint16_t* x;
+    void* y;
+    int64_t n, k;
+};
+constexpr int kGemvGroupMax = 64;   // E2M1_GEMV_MAX_GROUPS
+// count <= kGemvGroupMax matrices with n >= 1 and k >= 32 (validated by the caller).
+hipError_t launch_gemv_group(const GemvMatrix* mats, int count, bool out_bf16, hipStream_t stream);
+
 hipError_t launch_gemm(const uint8_t* packed, const uint8_t* scales, const uint16_t* x, void* y, bool out_bf16,
                        int64_t m, int64_t n, int64_t k, hipStream_t stream);
 

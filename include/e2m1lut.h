@@ -112,6 +112,32 @@ int dequant_decode(const uint8_t* packed, const uint8_t* scale_e8m0, uint16_t* o
 int dequant_gemv(const uint8_t* packed, const uint8_t* scale_e8m0, const uint16_t* x_bf16,
                  void* y, int y_dtype, int64_t batch, int64_t n, int64_t k, void* stream);
 
+/* Most matrices one dequant_gemv_grouped call accepts. */
+#define E2M1_GEMV_MAX_GROUPS 64
+
+/*
+ * dequant_gemv_grouped -- several independent batch-1 dequant_gemv products
+ * (matrix g applied to its own activation row) issued together, e.g. the
+ * projections of one layer that do not depend on each other. Operation: per
+ * matrix exactly that of dequant_gemv at batch 1 ([vLLM-51583] "实现拆解"
+ * item 2: the unpack feeding a product); the products share launches (for
+ * K <= 16384 one launch holds up to eight matrices), so the fixed cost of a
+ * launch is paid once for all their weight bytes.
+ *   count                    number of matrices, 0 <= count <= E2M1_GEMV_MAX_GROUPS
+ *   packed[g], scale_e8m0[g], x_bf16[g], y[g]
+ *                            device pointers laid out as in dequant_gemv with
+ *                            batch 1, n = n[g], k = k[g] (same alignments);
+ *                            the pointer arrays themselves and n, k are host
+ *                            memory, read during the call only
+ *   n[g], k[g]               as in dequant_gemv (n >= 0, k >= 0, k % 32 == 0)
+ * Every y[g] is overwritten; outputs must not overlap each other or any
+ * input. All arguments are validated before anything is launched: on an
+ * error nothing is written.
+ */
+int dequant_gemv_grouped(int count, const uint8_t* const* packed, const uint8_t* const* scale_e8m0,
+                         const uint16_t* const* x_bf16, void* const* y, const int64_t* n, const int64_t* k,
+                         int y_dtype, void* stream);
+
 /*
  * dequant_gemm -- y = x . W^T for many activation rows (prefill): the MXFP4
  * weight matrix decoded on the way into bf16 matrix-core tiles.

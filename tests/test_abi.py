@@ -97,6 +97,31 @@ def test_gemv_validation(lib):
     assert f(P(0x10001), B, C, D, 1, 1, 8, 64, NULL) == E_ALIGN
 
 
+def test_gemv_grouped_validation(lib):
+    f = lib.dequant_gemv_grouped
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+
+    def call(count, packed, scales, x, y, n, k, dtype=0):
+        arr = vp * max(len(packed), 1)
+        a64 = i64 * max(len(n), 1)
+        return f(count, arr(*packed), arr(*scales), arr(*x), arr(*y), a64(*n), a64(*k), dtype, NULL)
+
+    ok = ([0x10000, 0x50000], [0x20000, 0x60000], [0x30000, 0x70000], [0x40000, 0x80000])
+    assert call(2, *ok, [8, 8], [64, 64], dtype=7) == E_DTYPE
+    assert call(65, *ok, [8, 8], [64, 64]) == E_SHAPE      # more matrices than the limit
+    assert call(-1, *ok, [8, 8], [64, 64]) == E_SHAPE
+    assert f(0, None, None, None, None, None, None, 0, NULL) == E2M1_OK
+    assert f(1, None, None, None, None, None, None, 0, NULL) == E_NULL
+    assert call(2, *ok, [8, 8], [64, 40]) == E_SHAPE       # k % 32 in the second matrix
+    assert call(2, *ok, [8, 2**31], [64, 64]) == E_SHAPE
+    assert call(2, ok[0], ok[1], ok[2], [0x40000, 0], [8, 8], [64, 64]) == E_NULL
+    assert call(2, ok[0], ok[1], ok[2], [0, 0], [0, 0], [64, 64]) == E2M1_OK   # n = 0: nothing to write
+    assert call(2, ok[0], [0x20000, 0], ok[2], ok[3], [8, 8], [64, 64]) == E_NULL
+    assert call(2, ok[0], ok[1], ok[2], [0x40000, 0x80002], [8, 8], [64, 64]) == E_ALIGN   # fp32 y
+    assert call(2, ok[0], ok[1], [0x30000, 0x70008], ok[3], [8, 8], [64, 64], 1) == E_ALIGN   # x
+    assert call(2, [0x10000, 0x50001], ok[1], ok[2], ok[3], [8, 8], [64, 64], 1) == E_ALIGN
+
+
 def test_ternary_validation(lib):
     f = lib.ternary_gemv
     assert f(A, B, C, D, 4, 24, NULL) == E_SHAPE   # k % 16
