@@ -131,8 +131,9 @@ int dequant_gemv(const uint8_t* packed, const uint8_t* scale_e8m0, const uint16_
  *                            memory, read during the call only
  *   n[g], k[g]               as in dequant_gemv (n >= 0, k >= 0, k % 32 == 0)
  * Every y[g] is overwritten; outputs must not overlap each other or any
- * input. All arguments are validated before anything is launched: on an
- * error nothing is written.
+ * input. All arguments are validated before anything is launched, so a
+ * validation error writes nothing; E2M1_ERR_LAUNCH can follow launches that
+ * already ran, and then some outputs are written and others not.
  */
 int dequant_gemv_grouped(int count, const uint8_t* const* packed, const uint8_t* const* scale_e8m0,
                          const uint16_t* const* x_bf16, void* const* y, const int64_t* n, const int64_t* k,
